@@ -1,0 +1,400 @@
+"""Pins for the CPU oracle (CPU only).
+
+The pages print no worked numeric example for the quantized linear, so each
+oracle function is pinned to something other than itself: closed forms,
+format definitions (tests/golden/*.txt), invariants of the mechanism and
+brute force on tiny inputs.  Each pin is chosen so that a plausible slip
+(dropped term, wrong sign, wrong index, transposed operand, wrong tie rule)
+fails at least one test.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import w4a4_oracle as O
+from w4a4_post_quantized_channel_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _sections(path):
+    out, cur = {}, None
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        if line.startswith("["):
+            cur = line.strip("[]").strip()
+            out[cur] = []
+        else:
+            out[cur].append(line.split())
+    return out
+
+
+# --------------------------------------------------------------------- FWHT
+def test_hadamard_orthogonal_and_sylvester():
+    H = O.hadamard_matrix(64)
+    assert np.array_equal(H @ H.T, 64 * np.eye(64, dtype=np.int64))
+    assert np.array_equal(H, H.T)
+    assert np.all(H[0] == 1) and np.all(H[:, 0] == 1)
+    # Sylvester recursion H_2n = [[H, H], [H, -H]]
+    h32 = O.hadamard_matrix(32)
+    assert np.array_equal(H, np.block([[h32, h32], [h32, -h32]]))
+
+
+def test_fwht_one_hot_gives_hadamard_rows():
+    H = O.hadamard_matrix(64)
+    K = 192
+    for i in [0, 1, 3, 37, 63, 64, 100, 191]:
+        x = np.zeros((1, K))
+        x[0, i] = 1.0
+        y = O.transform(x, None, 64, dtype=np.float64)[0]
+        b, j = divmod(i, 64)
+        expect = np.zeros(K)
+        expect[64 * b:64 * b + 64] = H[j] / 8.0
+        assert np.array_equal(y, expect), i
+
+
+def test_fwht_matches_dense_product():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((9, 256)).astype(np.float32)
+    H = O.hadamard_matrix(64).astype(np.float64) / 8.0
+    dense = np.concatenate([x[:, 64 * b:64 * b + 64].astype(np.float64) @ H
+                            for b in range(4)], axis=1)
+    fast = O.transform(x, None, 64)
+    assert fast.dtype == np.float32
+    assert np.max(np.abs(fast - dense)) <= 1e-6 * np.max(np.abs(dense))
+
+
+def test_fwht_is_an_involution_on_small_integers():
+    rng = np.random.default_rng(8)
+    x = rng.integers(-50, 50, size=(5, 128)).astype(np.float32)
+    y = O.transform(O.transform(x, None, 64), None, 64)
+    assert np.array_equal(y, x)
+
+
+def test_fwht_stage_order_matters_only_by_rounding():
+    # unnormalised FWHT of integers equals H x exactly
+    rng = np.random.default_rng(9)
+    x = rng.integers(-9, 9, size=(3, 64)).astype(np.float32)
+    H = O.hadamard_matrix(64)
+    assert np.array_equal(O.fwht_blocks(x).astype(np.int64), x.astype(np.int64) @ H.T)
+
+
+@pytest.mark.parametrize("order", ["smooth_then_rotate", "rotate_then_smooth"])
+def test_folding_reproduces_float_linear(order):
+    # FoldQuantVLA Proposition 1: (X S^-1 R)(W S R)^T = X W^T in exact arithmetic
+    c = WL.linear_case(8, 48, 256, seed=11, n_outliers=4, outlier_gain=20.0)
+    s64 = c.s.astype(np.float64)
+    xa = O.transform(c.x, 1.0 / s64, 64, order, dtype=np.float64)
+    wa = O.transform(c.w, s64, 64, order, dtype=np.float64)
+    ref = c.x.astype(np.float64) @ c.w.astype(np.float64).T
+    got = xa @ wa.T
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_smoothing_is_applied_per_channel_before_rotation():
+    # Scaling channel j of x by c and its smoothing factor by 1/c leaves the
+    # transformed row unchanged (powers of two keep it exact).
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2, 64)).astype(np.float32)
+    inv = np.abs(rng.standard_normal(64)).astype(np.float32) + 0.5
+    y0 = O.transform(x, inv, 64)
+    x2 = x.copy(); x2[:, 5] *= 4
+    inv2 = inv.copy(); inv2[5] /= 4
+    assert np.array_equal(O.transform(x2, inv2, 64), y0)
+    # with rotation off, smoothing is a plain per-channel product
+    assert np.array_equal(O.transform(x, inv, 0), (x * inv).astype(np.float32))
+
+
+# ------------------------------------------------------------ int quantizer
+def test_golden_onehot_fwht_int4():
+    g = _sections(os.path.join(GOLDEN, "fwht_int4_onehot.txt"))
+    inp = dict((k, v) for k, v in g["input"])
+    K, i, val = int(inp["K"]), int(inp["index"]), float(inp["value"])
+    x = np.zeros((1, K), np.float32)
+    x[0, i] = val
+    q = O.quantize_operand(x, None, "int4", 64)
+    pattern = [int(v) for v in g["codes_block1_pattern"][0]]
+    assert np.all(q["codes"][0, :64] == 0)
+    assert np.array_equal(q["codes"][0, 64:], np.tile(pattern, 16))
+    assert q["scales"][0] == np.float32(np.float32(0.625) / np.float32(7))
+    hexrow = g["packed_row_hex"][0][0]
+    assert q["packed"][0].tobytes().hex() == hexrow
+
+
+def _brute_nearest_int(v, lo, hi):
+    cands = np.arange(lo, hi + 1)
+    out = []
+    for t in np.asarray(v, np.float64).ravel():
+        d = np.abs(cands - t)
+        best = cands[d == d.min()]
+        if len(best) > 1:
+            best = best[best % 2 == 0]
+        out.append(best[0])
+    return np.array(out).reshape(np.shape(v))
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_int_quantizer_brute_force_rounding(qmax):
+    rng = np.random.default_rng(13)
+    y = (rng.standard_normal((6, 64)) * rng.uniform(0.01, 50, (6, 1))).astype(np.float32)
+    codes, step, v = O.quantize_int(y, qmax)
+    assert np.array_equal(codes, _brute_nearest_int(v, -qmax - 1, qmax))
+    # exact half-integer pre-rounding values go to the even neighbour
+    halves = np.array([[0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 6.5, -7.5]], np.float32)
+    assert np.array_equal(_brute_nearest_int(halves, -8, 7), [[0, 2, 2, 0, -2, -2, 6, -8]])
+    assert np.array_equal(np.clip(np.rint(halves), -8, 7), [[0, 2, 2, -0, -2, -2, 6, -8]])
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_int_quantizer_invariants(qmax):
+    rng = np.random.default_rng(14)
+    y = (rng.standard_normal((400, 96)) * rng.lognormal(0, 2, (400, 1))).astype(np.float32)
+    y[3] = 0.0
+    codes, step, v = O.quantize_int(y, qmax)
+    # scale definition
+    amax = np.abs(y).max(axis=1)
+    assert np.array_equal(step, (amax / np.float32(qmax)).astype(np.float32))
+    # zero row
+    assert step[3] == 0 and np.all(codes[3] == 0)
+    nz = step > 0
+    # every non-zero row reaches +-qmax and never the (unreachable) -qmax-1
+    assert np.all(np.abs(codes[nz]).max(axis=1) == qmax)
+    assert codes.min() >= -qmax
+    # dequantisation error within half a step
+    dq = O.dequantize_int(codes, step).astype(np.float64)
+    err = np.abs(dq - y)
+    assert np.all(err <= step[:, None].astype(np.float64) * 0.5 * (1 + 1e-5) + 1e-30)
+    # quantize-dequantize is idempotent on its own output
+    codes2, _, _ = O.quantize_int(O.dequantize_int(codes, step), qmax)
+    assert np.array_equal(codes2, codes)
+
+
+def test_int_quantizer_sign_and_scale_equivariance():
+    rng = np.random.default_rng(15)
+    y = rng.standard_normal((50, 64)).astype(np.float32)
+    c1, s1, _ = O.quantize_int(y, 7)
+    c2, s2, _ = O.quantize_int(-y, 7)
+    assert np.array_equal(c2, -c1) and np.array_equal(s1, s2)
+    c3, s3, _ = O.quantize_int(y * np.float32(4), 7)
+    assert np.array_equal(c3, c1) and np.array_equal(s3, s1 * 4)
+
+
+# ------------------------------------------------------------ NVFP4 codecs
+def test_golden_e2m1_and_e4m3_tables():
+    g = _sections(os.path.join(GOLDEN, "nvfp4_codec.txt"))
+    for code, val in g["e2m1_decode"]:
+        got = O.e2m1_value(int(code, 16))
+        assert got == float(val) and np.signbit(got) == val.startswith("-")
+    for val, code in g["e2m1_encode"]:
+        assert int(O.e2m1_encode(float(val))) == int(code, 16), val
+    for code, val in g["e4m3_decode"]:
+        assert O.e4m3_value(int(code, 16)) == float(val)
+    for val, code in g["e4m3_encode"]:
+        assert int(O.e4m3_encode(float(val))) == int(code, 16), val
+    assert np.isnan(O.e4m3_value(0x7F)) and np.isnan(O.e4m3_value(0xFF))
+
+
+def test_e4m3_grid_is_the_full_finite_format():
+    vals = O.e4m3_value(np.arange(0x7F))
+    assert np.all(np.diff(vals) > 0)          # strictly increasing positive codes
+    assert vals[0] == 0 and vals[-1] == 448
+    # every finite E4M3 value is a 4-significant-bit dyadic number
+    for v in vals[1:]:
+        m, e = np.frexp(v)
+        assert (m * 16) == np.floor(m * 16)
+
+
+def _brute_nearest_grid(v, values, codes):
+    out = []
+    for t in np.asarray(v, np.float64).ravel():
+        d = np.abs(values - t)
+        cand = codes[d == d.min()]
+        if len(cand) > 1:
+            cand = cand[cand % 2 == 0]
+        out.append(cand[0])
+    return np.array(out)
+
+
+def test_e2m1_encode_brute_force():
+    rng = np.random.default_rng(16)
+    v = np.concatenate([rng.uniform(-8, 8, 3000),
+                        np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -6.0])])
+    got = O.e2m1_encode(v)
+    mag = np.minimum(np.abs(v), 6.0)
+    grid = O.e2m1_value(np.arange(8))
+    want_mag = _brute_nearest_grid(mag, grid, np.arange(8))
+    want = np.where((v < 0) & (want_mag != 0), want_mag | 8, want_mag)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_encode_brute_force():
+    rng = np.random.default_rng(17)
+    codes = np.arange(0x7F)
+    grid = O.e4m3_value(codes)
+    mids = (grid[1:] + grid[:-1]) / 2
+    v = np.concatenate([np.exp(rng.uniform(np.log(1e-4), np.log(600), 3000)), mids, grid])
+    got = O.e4m3_encode(v)
+    want = _brute_nearest_grid(np.minimum(v, 448.0), grid, codes)
+    assert np.array_equal(got, want)
+
+
+def test_nvfp4_quantizer_invariants():
+    rng = np.random.default_rng(18)
+    y = (rng.standard_normal((64, 256)) * rng.lognormal(0, 1.5, (64, 1))).astype(np.float32)
+    y[5, 16:32] = 0.0
+    g = O.nvfp4_tensor_scale(np.abs(y).max())
+    codes, e, sv, v = O.quantize_nvfp4(y, g)
+    assert codes.shape == y.shape and e.shape == (64, 16)
+    # zero block -> zero scale and zero codes
+    assert e[5, 1] == 0 and np.all(codes[5, 16:32] == 0)
+    # the largest block of the tensor maps to the largest finite scale
+    assert e.max() == 0x7E
+    # blocks whose scale is in the normal E4M3 range reach the largest element code
+    mag = codes & 7
+    normal = sv >= 2.0 ** -6
+    assert np.all(mag.reshape(64, 16, 16).max(axis=2)[normal] == 7)
+    # element codes are the nearest E2M1 values of y / S
+    S = (O.e4m3_value(e).astype(np.float32) * np.float32(g)).astype(np.float32)
+    Sx = np.repeat(S, 16, axis=1)
+    ok = Sx > 0
+    ratio = np.zeros_like(y)
+    ratio[ok] = (y[ok] / Sx[ok]).astype(np.float32)
+    assert np.array_equal(codes, O.e2m1_encode(ratio))
+    # quantize-dequantize is idempotent for a fixed tensor scale
+    dq = O.dequantize_nvfp4(codes, e, g).astype(np.float32)
+    codes2, e2, _, _ = O.quantize_nvfp4(dq, g)
+    assert np.array_equal(codes2, codes) and np.array_equal(e2, e)
+
+
+# ----------------------------------------------------------------- packing
+def test_packing_layout_and_roundtrip():
+    codes = np.array([[1, -2, 7, -8]], np.int8)
+    p = O.pack_nibbles(codes)
+    assert p.tolist() == [[0xE1, 0x87]]
+    rng = np.random.default_rng(19)
+    c = rng.integers(-8, 8, size=(7, 64)).astype(np.int8)
+    assert np.array_equal(O.int4_from_nibbles(O.unpack_nibbles(O.pack_nibbles(c))), c)
+
+
+# -------------------------------------------------------------------- GEMM
+def test_int_gemm_brute_force_and_closed_forms():
+    rng = np.random.default_rng(20)
+    for (M, N, K) in [(1, 1, 64), (3, 5, 64), (7, 4, 128)]:
+        a = rng.integers(-8, 8, size=(M, K))
+        w = rng.integers(-8, 8, size=(N, K))
+        acc = O.int_gemm(a, w)
+        brute = np.zeros((M, N), np.int64)
+        for m in range(M):
+            for n in range(N):
+                t = 0
+                for k in range(K):
+                    t += int(a[m, k]) * int(w[n, k])
+                brute[m, n] = t
+        assert np.array_equal(acc, brute)
+    K = 8192
+    assert O.int_gemm(np.full((2, K), 7), np.full((3, K), 7)).tolist() == [[49 * K] * 3] * 2
+    alt = np.tile([7, -7], K // 2)
+    assert np.all(O.int_gemm(np.full((1, K), 7), alt[None]) == 0)
+    assert O.int_gemm(np.full((1, K), -128), np.full((1, K), -128))[0, 0] == 16384 * K
+
+
+def test_dequant_epilogue_orientation():
+    acc = np.array([[1, 2, 3], [4, 5, 6]])
+    y = O.dequant_epilogue(acc, np.array([10.0, 100.0]), np.array([1.0, 2.0, 4.0]))
+    assert y.tolist() == [[10, 40, 120], [400, 1000, 2400]]
+
+
+def test_nvfp4_gemm_equals_blockwise_integer_form():
+    # y = g_a g_w sum_b value(e_a) value(e_w) sum_{k in b} value(c_a) value(c_w)
+    rng = np.random.default_rng(21)
+    M, N, K = 3, 4, 64
+    ya = rng.standard_normal((M, K)).astype(np.float32)
+    yw = rng.standard_normal((N, K)).astype(np.float32)
+    ga, gw = O.nvfp4_tensor_scale(np.abs(ya).max()), O.nvfp4_tensor_scale(np.abs(yw).max())
+    ca, ea, _, _ = O.quantize_nvfp4(ya, ga)
+    cw, ew, _, _ = O.quantize_nvfp4(yw, gw)
+    got = O.dequantize_nvfp4(ca, ea, ga) @ O.dequantize_nvfp4(cw, ew, gw).T
+    want = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            tot = 0.0
+            for b in range(K // 16):
+                P = 0
+                for k in range(16 * b, 16 * b + 16):
+                    P += int(2 * O.e2m1_value(ca[m, k])) * int(2 * O.e2m1_value(cw[n, k]))
+                tot += O.e4m3_value(ea[m, b]) * O.e4m3_value(ew[n, b]) * P / 4.0
+            want[m, n] = float(ga) * float(gw) * tot
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+# ------------------------------------------------------------------ branch
+def test_branches_brute_force():
+    rng = np.random.default_rng(22)
+    M, K, N, r = 3, 10, 4, 2
+    x = rng.standard_normal((M, K))
+    l1 = rng.standard_normal((K, r))
+    lw = rng.standard_normal((N, r))
+    y = O.lowrank_branch(x, l1, lw)
+    for m in range(M):
+        for n in range(N):
+            t = sum(sum(x[m, k] * l1[k, j] for k in range(K)) * lw[n, j] for j in range(r))
+            assert abs(y[m, n] - t) < 1e-12
+    idx = np.array([1, 7])
+    yo = O.outlier_branch(x, idx, lw)
+    for m in range(M):
+        for n in range(N):
+            assert abs(yo[m, n] - (x[m, 1] * lw[n, 0] + x[m, 7] * lw[n, 1])) < 1e-12
+    assert np.all(O.outlier_branch(x, np.zeros(0, int), np.zeros((N, 0))) == 0)
+
+
+def test_lowrank_case_reconstructs_float_weight():
+    c = WL.linear_case(16, 64, 128, seed=23, lowrank=4)
+    l1, lw = c.branch["l1"].astype(np.float64), c.branch["lw"].astype(np.float64)
+    recon = lw @ l1.T + c.w.astype(np.float64)
+    assert np.max(np.abs(recon - c.w_full)) < 1e-6
+
+
+def test_outlier_case_selects_top_energy_channels():
+    c = WL.linear_case(32, 16, 256, seed=24, fmt="nvfp4", n_outliers=8,
+                       outlier_gain=30.0, keep_channels=8)
+    assert np.array_equal(np.sort(c.branch["idx"]), c.meta["outliers"])
+    assert np.all(c.inv_s[c.branch["idx"]] == 0) and np.all(c.s[c.branch["idx"]] == 0)
+    # the quantized path carries nothing for the kept channels
+    q = O.quantize_operand(c.x, c.inv_s, "nvfp4", 0)
+    assert np.all(q["y"][:, c.branch["idx"]] == 0)
+
+
+# ------------------------------------------------------------- whole path
+def test_whole_path_tiny_consistency():
+    c = WL.workload("tiny")
+    out = O.linear(c)
+    A, W = out["a"], out["w"]
+    # accumulators from packed codes
+    a = O.int4_from_nibbles(O.unpack_nibbles(A["packed"]))
+    w = O.int4_from_nibbles(O.unpack_nibbles(W["packed"]))
+    assert np.array_equal(O.int_gemm(a, w), out["acc"])
+    # quantized product approximates the float linear (sanity, no bound from the pages)
+    ref = c.x.astype(np.float64) @ c.w.astype(np.float64).T
+    sqnr = 10 * np.log10(np.sum(ref ** 2) / np.sum((out["y"] - ref) ** 2))
+    assert sqnr > 10.0
+    # rotation + smoothing beat plain per-token int4 on outlier-heavy input
+    plain = O.quantize_operand(c.x, None, "int4", 0)
+    plainw = O.quantize_operand(c.w, None, "int4", 0)
+    yp = O.dequant_epilogue(O.int_gemm(plain["codes"], plainw["codes"]), plain["scales"], plainw["scales"])
+    sqnr_plain = 10 * np.log10(np.sum(ref ** 2) / np.sum((yp - ref) ** 2))
+    assert sqnr > sqnr_plain
+
+
+def test_whole_path_nvfp4_and_branch_small():
+    c = WL.linear_case(48, 40, 320, seed=25, fmt="nvfp4", n_outliers=8,
+                       outlier_gain=30.0, keep_channels=8)
+    out = O.linear(c)
+    ref = c.x.astype(np.float64) @ c.w_full.astype(np.float64).T
+    sqnr = 10 * np.log10(np.sum(ref ** 2) / np.sum((out["y"] - ref) ** 2))
+    assert sqnr > 15.0
+    # branch contribution is exactly the kept-channel product
+    assert np.allclose(out["y"] - out["y_main"],
+                       c.x[:, c.branch["idx"]].astype(np.float64) @ c.branch["lw"].astype(np.float64).T)
