@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-linear hot path on one MI355X.
+
+A step is one pass of the whole per-call path over one batch of synthetic
+input, with inputs resident in HBM: ``quantize_act`` (smoothing, FWHT-64,
+per-token quantization) then the GEMM with its dequant epilogue and, where
+the workload has one, the fused 16-bit branch.  Weight packing is offline
+and outside the timed region.
+
+Default workload: the batch-1, 64-token action-expert step (a W4A4
+projection 64x2048x2048 and a W8A8 down projection 64x2048x8192).  The
+4096-token NVFP4 video-latent projection (4096x5120x5120 with 64 kept
+bf16 channels) is measured in the same run and reported under "also".
+
+Metric: effective TOPS = 2*M*N*K (summed over the step's projections) / time.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+PEAK_TFLOPS = {"i8": 5000.0, "f16": 2500.0, "bf16": 2500.0, "fp4": 10100.0}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="batch1", choices=["batch1", "video4096", "prefill", "lowrank", "tiny"])
+    p.add_argument("--no-also", action="store_true", help="skip the secondary 4096-token measurement")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample duration")
+    return p.parse_args()
+
+
+def build_step(names, torch):
+    from w4a4_post_quantized_channel_amd import pipeline, workloads as WL
+    layers = []
+    for n in names:
+        case = WL.workload(n)
+        layer, t = pipeline.build_layer(case, device="cuda")
+        layer.buffers(case.M, t["x"].device)
+        layers.append((case, layer, t))
+    torch.cuda.synchronize()
+
+    def step():
+        for case, layer, t in layers:
+            layer.forward(t["x"])
+    return layers, step
+
+
+def gemm_bytes(case):
+    """Algorithmic HBM bytes of one GEMM launch: packed weight and activation
+    codes, their scales, the output and the branch operands."""
+    M, N, K = case.M, case.N, case.K
+    code = {"int4": 0.5, "int8": 1.0, "nvfp4": 0.5}[case.fmt]
+    if case.fmt == "nvfp4":
+        scales = (M + N) * K / 16
+    else:
+        scales = 4 * (M + N)
+    out = M * N * (4 if case.y_dtype == "f32" else 2)
+    br = 0
+    if case.branch is not None:
+        r = case.branch["lw"].shape[1]
+        ra = 2 * r if case.branch["kind"] == "lowrank" else r
+        br = 2 * (M * ra + N * r)
+    return code * (M + N) * K + scales + out + br
+
+
+def time_region(torch, step, steps, warmup, kernel_events=None):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def dominant_kernel_time(torch, case, layer, t, steps):
+    """Average duration of the GEMM launch alone, HIP events on the launch stream."""
+    b = layer.buffers(case.M, t["x"].device)
+    layer.forward(t["x"])
+    from w4a4_post_quantized_channel_amd import ops
+    br = None
+    if layer.branch is not None:
+        br = ops.branch_desc(b["br_a"], layer.branch["lw"])
+
+    def gemm():
+        if case.fmt == "int8":
+            ops.w8a8_linear(b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K, branch=br,
+                            y=b["y"], workspace=b["ws"])
+        else:
+            ops.w4a4_linear(b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K, case.fmt,
+                            alpha=layer.alpha, branch=br, y=b["y"], workspace=b["ws"])
+    return time_region(torch, gemm, steps, max(5, steps // 10))
+
+
+def quant_kernel_time(torch, case, layer, t, steps):
+    from w4a4_post_quantized_channel_amd import ops
+    b = layer.buffers(case.M, t["x"].device)
+
+    def q():
+        ops.quantize_act(t["x"], layer.inv_s, case.fmt, fwht_block=layer.fwht_block, order=layer.order,
+                         tensor_scale=layer.g_a, codes=b["codes"], scales=b["scales"])
+    return time_region(torch, q, steps, max(5, steps // 10))
+
+
+def cpu_baseline(names, target_s):
+    """The oracle as it stands, on the host cores: per-call path (activation
+    transform + quantization, GEMM, epilogue, branch) with weights packed
+    beforehand, repeated until about ``target_s`` seconds of CPU work."""
+    import numpy as np
+    from oracle import w4a4_oracle as O
+    from w4a4_post_quantized_channel_amd import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    prepared = []
+    for n in names:
+        c = WL.workload(n)
+        W = O.quantize_operand(c.w, c.s, c.fmt)
+        g_a = None
+        if c.fmt == "nvfp4":
+            g_a = O.nvfp4_tensor_scale(O.transformed_amax(c.x, c.inv_s))
+        prepared.append((c, W, g_a))
+
+    def one_call(c, W, g_a):
+        A = O.quantize_operand(c.x, c.inv_s, c.fmt, g=g_a)
+        if c.fmt in ("int4", "int8"):
+            y = O.dequant_epilogue(O.int_gemm(A["codes"], W["codes"]), A["scales"], W["scales"])
+        else:
+            y = O.dequantize_nvfp4(A["codes"], A["scales"], A["g"]) @ O.dequantize_nvfp4(
+                W["codes"], W["scales"], W["g"]).T
+        if c.branch is not None:
+            if c.branch["kind"] == "lowrank":
+                y = y + O.lowrank_branch(c.x, c.branch["l1"], c.branch["lw"])
+            else:
+                y = y + O.outlier_branch(c.x, c.branch["idx"], c.branch["lw"])
+        return y
+
+    ops_per = sum(2.0 * c.M * c.N * c.K for c, _, _ in prepared)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for c, W, g_a in prepared:
+            one_call(c, W, g_a)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    return {"value": ops_per * reps / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} repetitions of the full step ({', '.join(names)}), "
+                      f"{el:.1f} s, weights packed beforehand",
+            "ms_per_step": el / reps * 1e3}
+
+
+WORKLOADS = {
+    "batch1": (["decode_w4a4", "decode_w8a8"],
+               "batch-1 64-token action-expert step: W4A4 64x2048x2048 + W8A8 64x2048x8192, "
+               "smoothing + FWHT-64 + per-token quantization"),
+    "video4096": (["video_nvfp4"], "4096-token video-latent projection, NVFP4 W4A4 4096x5120x5120 "
+                                   "+ 64 kept bf16 channels"),
+    "prefill": (["prefill_gate_up", "prefill_down"], "512-token backbone prefill: gate/up W4A4 "
+                                                     "512x16384x2048 + down W4A4 512x2048x8192"),
+    "lowrank": (["lowrank"], "1024-token low-rank-protected W4A4 1024x3072x3072 + rank-32 bf16 branch"),
+    "tiny": (["tiny"], "tiny W4A4 16x256x256 (fp32 in/out)"),
+}
+
+
+def measure(torch, wl, steps, warmup):
+    names, desc = WORKLOADS[wl]
+    layers, step = build_step(names, torch)
+    ms = time_region(torch, step, steps, warmup)
+    flops = sum(2.0 * c.M * c.N * c.K for c, _, _ in layers)
+    # dominant kernel = the GEMM of the largest projection
+    c, layer, t = max(layers, key=lambda e: e[0].M * e[0].N * e[0].K)
+    ksteps = max(20, steps)
+    k_ms = dominant_kernel_time(torch, c, layer, t, ksteps)
+    q_ms = quant_kernel_time(torch, c, layer, t, ksteps)
+    flop_k = 2.0 * c.M * c.N * c.K
+    bytes_k = gemm_bytes(c)
+    mtype = {"int4": "i8", "int8": "i8", "nvfp4": "f16"}[c.fmt]
+    intensity = flop_k / bytes_k
+    ridge = PEAK_TFLOPS[mtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": bytes_k / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flop_k / (k_ms * 1e-3) / 1e12, "peak": PEAK_TFLOPS[mtype],
+                "unit": "TFLOP/s" if mtype != "i8" else "TOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = f"{'w8a8_linear' if c.fmt == 'int8' else 'w4a4_linear'} {c.fmt} {c.M}x{c.N}x{c.K}"
+    roof["kernel_us"] = k_ms * 1e3
+    roof["algorithmic_bytes"] = bytes_k
+    qbytes = c.M * c.K * (2 if c.x_dtype == "bf16" else 4) + c.M * c.K * (1 if c.fmt == "int8" else 0.5) + (
+        c.M * c.K / 16 if c.fmt == "nvfp4" else 4 * c.M)
+    quant = {"kernel": f"quantize_act {c.fmt} {c.M}x{c.K}", "us": q_ms * 1e3,
+             "achieved_GBs": qbytes / (q_ms * 1e-3) / 1e9, "frac_hbm": qbytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return {"names": names, "desc": desc, "ms": ms, "flops": flops, "roofline": roof, "quantize": quant,
+            "per_call_us": {n: None for n in names}}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (every box here has one GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    r = measure(torch, a.workload, a.steps, a.warmup)
+    out = {
+        "metric": "W4A4 linear effective TOPS + us/call (batch-1 64-token and 4096-token shapes)",
+        "value": r["flops"] / (r["ms"] * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": r["ms"],
+        "us_per_call": r["ms"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["roofline"]["kernel"].startswith("w4a4_linear nvfp4") and "f16" or "i8",
+        "data": "synthetic (seeded; shapes and outlier statistics of the workload descriptions)",
+        "config": {"workload": r["desc"], "projections": r["names"]},
+        "roofline": r["roofline"],
+        "quantize_kernel": r["quantize"],
+    }
+    if a.workload == "batch1" and not a.no_also:
+        v = measure(torch, "video4096", max(10, a.steps // 10), max(3, a.warmup // 4))
+        out["also"] = {"workload": v["desc"], "value": v["flops"] / (v["ms"] * 1e-3) / 1e12, "unit": "TOPS",
+                       "us_per_call": v["ms"] * 1e3, "roofline": v["roofline"], "quantize_kernel": v["quantize"]}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(r["names"], a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * w4a4.h -- C ABI of the MI355X (gfx950) quantized-linear library.
+ *
+ * The library implements the deployment path of a low-bit linear layer as
+ * the pages on world-action / vision-language-action quantization describe
+ * it: per-channel smoothing, a block-64 Walsh-Hadamard rotation, dynamic
+ * per-token 4-bit (or 8-bit, or NVFP4) activation quantization, a W4A4 (or
+ * W8A8, or NVFP4) GEMM with a dequantising epilogue, and an optional 16-bit
+ * low-rank or kept-channel branch added to the output.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array pointer is a DEVICE pointer (memory from hipMalloc or a
+ *    PyTorch CUDA/HIP tensor) unless stated otherwise.  The caller owns every
+ *    buffer; the library never allocates, frees or keeps a pointer after it
+ *    returns.
+ *  - Every call is asynchronous on ``stream`` (a hipStream_t; NULL = the
+ *    null stream).  Device-side faults surface at the caller's next
+ *    synchronisation.
+ *  - Return value: W4A4_OK (0) or a negative w4a4_status.  All argument
+ *    checks run on the host before anything is launched; on error nothing
+ *    is launched and no output is written.  w4a4_last_error() returns a
+ *    thread-local message describing the last failure.
+ *  - Row-major storage with an explicit row stride ("ld", in elements) for
+ *    floating-point inputs/outputs.  Quantized codes are dense row-major.
+ *  - M == 0 or N == 0 is a valid no-op.
+ *  - NaN / Inf in inputs give unspecified (but memory-safe) results.
+ *
+ * Packed layouts (produced by quantize_act / pack_weights, consumed by the
+ * linear entry points):
+ *  - INT4 : R x K/2 bytes, row-major; byte j of a row holds code 2j in its
+ *           low nibble and code 2j+1 in its high nibble, two's complement
+ *           (-8..7).  scales: fp32[R], one step per row.
+ *  - INT8 : R x K bytes (int8 codes).  scales: fp32[R].
+ *  - NVFP4: R x K/2 bytes of E2M1 nibbles (same nibble order; sign bit 3,
+ *           exponent bits 2..1 with bias 1, mantissa bit 0).  scales:
+ *           R x K/16 bytes of OCP E4M3 (E4M3FN, bias 7, max 448), one per 16
+ *           consecutive K elements.  The fp32 tensor scale g travels in the
+ *           w4a4_qdesc (quantize / pack) and in ``alpha`` (linear).
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A4_ABI_VERSION 1
+#define W4A4_MAX_BRANCH 128 /* largest branch width (rank or kept channels) */
+
+typedef enum w4a4_status {
+  W4A4_OK = 0,
+  W4A4_ERR_INVALID_ARG = -1,       /* null pointer, negative size, bad stride */
+  W4A4_ERR_UNSUPPORTED_SHAPE = -2, /* K not a multiple of the required block */
+  W4A4_ERR_MISALIGNED = -3,        /* pointer / row stride not 16-byte aligned */
+  W4A4_ERR_UNSUPPORTED_FORMAT = -4,/* format / dtype / option combination */
+  W4A4_ERR_WORKSPACE = -5,         /* workspace given but too small */
+  W4A4_ERR_LAUNCH_FAILED = -6      /* HIP launch error (see w4a4_last_error) */
+} w4a4_status;
+
+/* Code formats. */
+enum { W4A4_FMT_INT4 = 0, W4A4_FMT_INT8 = 1, W4A4_FMT_NVFP4 = 2 };
+/* Element types of float inputs / outputs.  I32 = raw integer accumulators. */
+enum { W4A4_DT_F32 = 0, W4A4_DT_BF16 = 1, W4A4_DT_I32 = 2 };
+/* Order of the two transforms applied before quantization. */
+enum { W4A4_ORDER_SMOOTH_THEN_ROTATE = 0, W4A4_ORDER_ROTATE_THEN_SMOOTH = 1 };
+/* 16-bit branch kinds. */
+enum { W4A4_BRANCH_NONE = 0, W4A4_BRANCH_BF16 = 1 };
+
+/* Quantizer descriptor.
+ *  fmt          W4A4_FMT_*.
+ *  fwht_block   0 (no rotation) or 64 (block Walsh-Hadamard, FoldQuantVLA
+ *               contribution 2: FWHT with block size 64).  The rotation is
+ *               the Sylvester-ordered Hadamard scaled by 1/8, evaluated in
+ *               fp32 with butterfly stages 1, 2, 4, 8, 16, 32.
+ *  order        W4A4_ORDER_*: smoothing then rotation (FoldQuantVLA's order)
+ *               or rotation then smoothing (QuantWAMs Eq. 1 order, A R S^-1).
+ *  tensor_scale NVFP4 only: the fp32 per-tensor scale g (> 0, finite).
+ */
+typedef struct w4a4_qdesc {
+  int32_t fmt;
+  int32_t fwht_block;
+  int32_t order;
+  float tensor_scale;
+} w4a4_qdesc;
+
+/* 16-bit branch fused into the linear epilogue (Q-WAM abstract: a 16-bit
+ * low-rank branch next to the 4-bit complement; QuantWAMs sec. 4.2: BF16
+ * bypass of kept channels).  Adds  sum_j a[m, j] * b[n, j mod r]  for
+ * j < ra to every output, in fp32 after the dequantised main product.
+ *  a   bf16, M x ra, row stride lda (elements).  For a rank-r factor product
+ *      (x L1) L2 it holds the hi and lo bf16 halves of x L1 (ra = 2r,
+ *      produced by w4a4_lowrank_project); for kept channels it holds
+ *      x[:, idx] (ra = r).
+ *  b   bf16, N x r, row stride ldb: L2 transposed, or W[:, idx].
+ *  r   1..W4A4_MAX_BRANCH; ra is r or 2r.
+ */
+typedef struct w4a4_branch {
+  int32_t kind;
+  int32_t r;
+  int32_t ra;
+  int32_t reserved;
+  const void* a;
+  int64_t lda;
+  const void* b;
+  int64_t ldb;
+} w4a4_branch;
+
+/* quantize_act -- runtime activation quantizer.
+ * FoldQuantVLA contribution 2 (channel scaling, FWHT-64, dynamic per-token
+ * quantization without timestep tables) and contribution 4 (INT4
+ * activations); QuantWAMs sec. 3.1 Eq. 1 (the quantizer receives A R S^-1).
+ *
+ *  x          M x K activations, x_dtype BF16 or F32, row stride ldx >= K.
+ *  inv_smooth fp32[K] per-channel factors multiplied into x (1/s), or NULL.
+ *  q          format, rotation, order; NVFP4 needs q->tensor_scale.
+ *  codes      output, packed layout of q->fmt (R = M).
+ *  scales     output: fp32[M] steps (INT4/INT8; step = fp32(amax/7) or
+ *             fp32(amax/127), codes = clamp(rne(fp32(y/step)))) or
+ *             M x K/16 E4M3 bytes (NVFP4).
+ * Shape rules: K % 16 == 0; K % 64 == 0 when fwht_block == 64.
+ * Alignment: x, codes 16-byte aligned; ldx * elem_size % 16 == 0.
+ */
+int quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                 const float* inv_smooth, const w4a4_qdesc* q,
+                 void* codes, void* scales, void* stream);
+
+/* pack_weights -- offline weight packing with the inverse transform folded
+ * in (FoldQuantVLA contribution 1: the inverse of every activation transform
+ * is folded into each consuming weight; QuantWAMs sec. 3.2: the common
+ * Hadamard rotation is fused into the weights).  Same arithmetic as
+ * quantize_act on the N rows of W (one scale per output channel), with the
+ * smoothing factors s multiplied instead of 1/s.
+ *  w       N x K weights (BF16 or F32), row stride ldw.
+ *  smooth  fp32[K] factors s, or NULL.
+ *  codes / scales as quantize_act with R = N.
+ */
+int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                 const float* smooth, const w4a4_qdesc* q,
+                 void* codes, void* scales, void* stream);
+
+/* w4a4_linear -- y = alpha * dequant(A_codes . W_codes^T) (+ branch).
+ * FoldQuantVLA contribution 4 (W4A4 projections) and overview (integer
+ * GEMMs with per-token / per-channel scales); QuantWAMs sec. 4.2 (NVFP4
+ * W4A4 kernels, BF16 bypass).
+ *  fmt      W4A4_FMT_INT4: exact int32 accumulation of int4 x int4, then
+ *           y = fp32(fp32(acc) * a_scales[m]) * w_scales[n] * alpha.
+ *           W4A4_FMT_NVFP4: sum of E2M1*E4M3 products (exact operands,
+ *           fp32 accumulation), times alpha = fp32(g_a * g_w).
+ *  a_codes / a_scales   M rows from quantize_act; w_codes / w_scales N rows
+ *           from pack_weights (same fmt, same K).
+ *  br       NULL or a w4a4_branch (kind NONE or BF16).
+ *  y        M x N output, y_dtype F32 or BF16 (round to nearest even) with
+ *           row stride ldy >= N; y_dtype I32 writes the raw integer
+ *           accumulators (INT formats, no branch, alpha ignored).
+ *  workspace / workspace_bytes  optional device scratch for split-K
+ *           (size from w4a4_workspace_size, zero-filled once with
+ *           w4a4_workspace_init; every successful call leaves it zeroed).
+ *           NULL selects a configuration without split-K.  Calls that
+ *           share one workspace must be ordered on one stream.
+ * Shape rules: K % 64 == 0.  Alignment: codes 16-byte aligned.
+ */
+int w4a4_linear(const void* a_codes, const void* a_scales,
+                const void* w_codes, const void* w_scales,
+                int64_t M, int64_t N, int64_t K, int32_t fmt, float alpha,
+                const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* w8a8_linear -- INT8 W8A8 sibling (FoldQuantVLA contribution 3: INT8 at
+ * o_proj / down_proj).  Same arguments and semantics as w4a4_linear with
+ * W4A4_FMT_INT8 codes (exact int32 accumulation). */
+int w8a8_linear(const void* a_codes, const void* a_scales,
+                const void* w_codes, const void* w_scales,
+                int64_t M, int64_t N, int64_t K, float alpha,
+                const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* lowrank_add -- standalone 16-bit branch, y += (x L1) L2 or
+ * y += x[:, idx] W_idx^T (Q-WAM abstract: 16-bit low-rank branch as a dense
+ * product; QuantWAMs sec. 3.1 / 4.2: kept channels on a BF16 path).
+ *  x    M x K bf16, row stride ldx.
+ *  l1   bf16 K x r (row stride r) for the low-rank form, or NULL when idx
+ *       is given.
+ *  idx  int32[r] channel indices (0 <= idx < K) for the kept-channel form,
+ *       or NULL.  Exactly one of l1 / idx is non-NULL.
+ *  lw   bf16 N x r, row stride ldlw: L2 transposed, or W[:, idx].
+ *  y    M x N, F32 or BF16, row stride ldy; read, added to, written back.
+ *  Accumulation: x L1 in fp32, then the rank-r product in fp32, added to
+ *  y in fp32, one rounding to y_dtype.
+ */
+int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx,
+                const void* l1, const int32_t* idx, const void* lw, int64_t ldlw,
+                int64_t r, int64_t N, void* y, int32_t y_dtype, int64_t ldy,
+                void* stream);
+
+/* w4a4_lowrank_project -- first half of the branch, producing the
+ * w4a4_branch ``a`` operand: for l1 != NULL, t = x L1 in fp32 written as
+ * bf16 hi = bf16(t) and lo = bf16(t - hi) (out is M x 2r: columns [0, r)
+ * hi, [r, 2r) lo); for idx != NULL, out = x[:, idx] (M x r, exact).
+ *  x bf16 M x K (row stride ldx); out bf16 with row stride ldo. */
+int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx,
+                         const void* l1, const int32_t* idx, int64_t r,
+                         void* out, int64_t ldo, void* stream);
+
+/* w4a4_transform_amax -- max |transform(x)| over a whole R x K tensor,
+ * written to amax_out (device fp32[1]).  The calibration statistic of the
+ * static NVFP4 tensor scale g = amax / (6 * 448) (QuantWAMs sec. 4.2:
+ * statistics are collected after both transforms).  ``scale`` is 1/s for
+ * activations and s for weights; q->fmt is ignored. */
+int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, int64_t ldx,
+                        const float* scale, const w4a4_qdesc* q, float* amax_out,
+                        void* stream);
+
+/* Split-K scratch: bytes needed for (M, N, K, fmt); 0 if none is used. */
+size_t w4a4_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt);
+/* Zero-fill a workspace on ``stream`` (a kernel, no hipMemset). */
+int w4a4_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+const char* w4a4_status_string(int status);
+const char* w4a4_last_error(void);
+int w4a4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A4_H */

@@ -1,0 +1,76 @@
+"""Comparison helpers for the GPU-vs-oracle parity tests.
+
+Bars: packed codes and E4M3 scale bytes equal, where any mismatch is
+counted and admissible only if the oracle's pre-rounding value lies within
+1e-6 relative of a rounding boundary; fp32 steps equal; raw int32
+accumulators equal; outputs within ``rtol * (|y_ref| + rms(y_ref))``
+elementwise (rtol 1e-3 for fp32 output, 1e-2 for bf16).
+"""
+import numpy as np
+
+from oracle import w4a4_oracle as O
+
+BAND = 1e-6
+E2M1_BOUNDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+_E4 = O.e4m3_value(np.arange(0x7F))
+E4M3_BOUNDS = (_E4[1:] + _E4[:-1]) / 2
+
+
+def near_boundary(v, bounds):
+    v = np.abs(np.asarray(v, np.float64))
+    d = np.min(np.abs(v[..., None] - bounds), axis=-1)
+    return d <= BAND * np.maximum(v, 1e-30)
+
+
+def near_half_integer(v):
+    v = np.asarray(v, np.float64)
+    return np.abs(np.abs(v - np.floor(v)) - 0.5) <= BAND * np.maximum(np.abs(v), 1e-30)
+
+
+def unpack_codes(fmt, packed):
+    packed = np.asarray(packed)
+    if fmt == "int4":
+        return O.int4_from_nibbles(O.unpack_nibbles(packed.view(np.uint8)))
+    if fmt == "int8":
+        return packed.view(np.int8)
+    return O.unpack_nibbles(packed.view(np.uint8))
+
+
+def check_operand(fmt, gpu_codes, gpu_scales, ref, rows=None, what="operand"):
+    """Compare one quantized operand; returns the number of admissible mismatches."""
+    codes = unpack_codes(fmt, gpu_codes)
+    rc = ref["codes"] if rows is None else ref["codes"][rows]
+    rv = ref["v"] if rows is None else ref["v"][rows]
+    rs = ref["scales"] if rows is None else ref["scales"][rows]
+    if fmt == "nvfp4":
+        rc = rc.astype(np.uint8)
+        s_bad = np.asarray(gpu_scales).view(np.uint8) != rs
+        if s_bad.any():
+            sv = ref["sv"] if rows is None else ref["sv"][rows]
+            assert near_boundary(sv[s_bad], E4M3_BOUNDS).all(), f"{what}: E4M3 scale mismatch outside band"
+            rows_bad = np.repeat(s_bad, 16, axis=1)
+        else:
+            rows_bad = np.zeros_like(rc, dtype=bool)
+        bad = (codes != rc) & ~rows_bad
+        if bad.any():
+            assert near_boundary(rv[bad], E2M1_BOUNDS).all(), (
+                f"{what}: {int(bad.sum())} E2M1 code mismatches outside the band")
+        return int(bad.sum()) + int(s_bad.sum())
+    assert np.array_equal(np.asarray(gpu_scales, np.float32), rs), f"{what}: fp32 steps differ"
+    bad = codes != rc
+    if bad.any():
+        assert near_half_integer(rv[bad]).all(), f"{what}: {int(bad.sum())} code mismatches outside the band"
+    return int(bad.sum())
+
+
+def check_output(y, y_ref, rtol):
+    y = np.asarray(y, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    assert y.shape == y_ref.shape
+    assert np.all(np.isfinite(y))
+    rms = np.sqrt(np.mean(y_ref ** 2)) if y_ref.size else 0.0
+    err = np.abs(y - y_ref)
+    bound = rtol * (np.abs(y_ref) + rms)
+    worst = float(np.max(err / np.maximum(bound, 1e-30))) if y.size else 0.0
+    assert np.all(err <= bound), f"output outside tolerance: worst err/bound = {worst:.3g}"
+    return worst

@@ -1,0 +1,151 @@
+"""C-ABI library checks that need no GPU: the library loads, exports every
+symbol the header declares, and rejects bad arguments before any launch
+(so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a4.h")
+LIBPATH = os.path.join(ROOT, "w4a4_post_quantized_channel_amd", "libw4a4.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIBPATH), reason="libw4a4.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from w4a4_post_quantized_channel_amd import ops as _ops
+    return _ops
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "lowrank_add"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(ops):
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(LIBPATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ops.EXPORTS)
+    assert ops.LIB.w4a4_abi_version() == 1
+
+
+def test_status_strings(ops):
+    for code, text in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported shape"),
+                       (-3, "misaligned"), (-4, "unsupported format"), (-5, "workspace"),
+                       (-6, "launch")]:
+        assert text in ops.LIB.w4a4_status_string(code).decode()
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below is rejected
+FAKE2 = ctypes.c_void_p(0x20000)
+MISAL = ctypes.c_void_p(0x10008)
+
+
+def _q(ops, fmt=0, fwht=64, order=0, g=1.0):
+    return ctypes.byref(ops.QDesc(fmt, fwht, order, g))
+
+
+def test_quantize_act_rejects_bad_arguments(ops):
+    L = ops.LIB
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, None, FAKE2, FAKE2, None) == -1      # q NULL
+    assert L.quantize_act(FAKE, 1, -1, 128, 128, None, _q(ops), FAKE2, FAKE2, None) == -1  # M < 0
+    assert L.quantize_act(FAKE, 1, 4, 0, 128, None, _q(ops), FAKE2, FAKE2, None) == -1     # K == 0
+    assert L.quantize_act(FAKE, 1, 4, 96, 96, None, _q(ops), FAKE2, FAKE2, None) == -2     # K % 64 with FWHT
+    assert L.quantize_act(FAKE, 1, 4, 40, 40, None, _q(ops, fwht=0), FAKE2, FAKE2, None) == -2  # K % 16
+    assert L.quantize_act(FAKE, 1, 4, 128, 64, None, _q(ops), FAKE2, FAKE2, None) == -1    # ldx < K
+    assert L.quantize_act(MISAL, 1, 4, 128, 128, None, _q(ops), FAKE2, FAKE2, None) == -3  # x misaligned
+    assert L.quantize_act(FAKE, 1, 4, 128, 132, None, _q(ops), FAKE2, FAKE2, None) == -3   # row stride
+    assert L.quantize_act(FAKE, 7, 4, 128, 128, None, _q(ops), FAKE2, FAKE2, None) == -4   # dtype
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, _q(ops, fmt=9), FAKE2, FAKE2, None) == -4
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, _q(ops, fwht=32), FAKE2, FAKE2, None) == -4
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, _q(ops, order=5), FAKE2, FAKE2, None) == -4
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, _q(ops, fmt=2, g=0.0), FAKE2, FAKE2, None) == -1
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, _q(ops, fmt=2, g=float("inf")), FAKE2, FAKE2, None) == -1
+    assert L.quantize_act(None, 1, 4, 128, 128, None, _q(ops), FAKE2, FAKE2, None) == -1
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, _q(ops), None, FAKE2, None) == -1
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, _q(ops), MISAL, FAKE2, None) == -3
+    assert L.quantize_act(FAKE, 1, 4, 1 << 20, 1 << 20, None, _q(ops), FAKE2, FAKE2, None) == -2
+    assert "quantize_act" in L.w4a4_last_error().decode()
+    # M == 0 is a valid no-op (no pointers needed)
+    assert L.quantize_act(None, 1, 0, 128, 128, None, _q(ops), None, None, None) == 0
+    assert L.pack_weights(FAKE, 0, 4, 96, 96, None, _q(ops), FAKE2, FAKE2, None) == -2
+
+
+def _lin(ops, fn="w4a4_linear", M=8, N=8, K=128, fmt=0, alpha=1.0, br=None, y=FAKE, ydt=1, ldy=None,
+         ws=None, wsb=0, a=FAKE, sa=FAKE, w=FAKE, sw=FAKE):
+    ldy = N if ldy is None else ldy
+    brp = None if br is None else ctypes.byref(br)
+    if fn == "w8a8_linear":
+        return ops.LIB.w8a8_linear(a, sa, w, sw, M, N, K, alpha, brp, y, ydt, ldy, ws, wsb, None)
+    return ops.LIB.w4a4_linear(a, sa, w, sw, M, N, K, fmt, alpha, brp, y, ydt, ldy, ws, wsb, None)
+
+
+def test_linear_rejects_bad_arguments(ops):
+    assert _lin(ops, K=96) == -2
+    assert _lin(ops, K=0) == -1
+    assert _lin(ops, M=-1) == -1
+    assert _lin(ops, K=1 << 20) == -2
+    assert _lin(ops, fmt=1) == -4                 # int8 codes go through w8a8_linear
+    assert _lin(ops, fmt=2, ydt=2) == -4          # raw accumulators only for integer formats
+    assert _lin(ops, ydt=5) == -4
+    assert _lin(ops, ldy=4) == -1
+    assert _lin(ops, alpha=float("nan")) == -1
+    assert _lin(ops, a=None) == -1
+    assert _lin(ops, a=MISAL) == -3
+    assert _lin(ops, fn="w8a8_linear", w=MISAL) == -3
+    br = ops.BranchDesc(1, 12, 12, 0, 0x10000, 16, 0x20000, 16)
+    assert _lin(ops, br=br) == -1                 # r not a multiple of 8
+    br = ops.BranchDesc(1, 16, 24, 0, 0x10000, 32, 0x20000, 16)
+    assert _lin(ops, br=br) == -1                 # ra neither r nor 2r
+    br = ops.BranchDesc(1, 16, 32, 0, 0x10008, 32, 0x20000, 16)
+    assert _lin(ops, br=br) == -3                 # misaligned branch operand
+    br = ops.BranchDesc(3, 16, 16, 0, 0x10000, 16, 0x20000, 16)
+    assert _lin(ops, br=br) == -4
+    br = ops.BranchDesc(1, 16, 16, 0, 0x10000, 16, 0x20000, 16)
+    assert _lin(ops, br=br, ydt=2) == -4          # no raw accumulators with a branch
+    # workspace present but too small for a split-K shape
+    M, N, K = 512, 2048, 8192
+    need = ops.LIB.w4a4_workspace_size(M, N, K, 0)
+    assert need > M * N * 4
+    assert _lin(ops, M=M, N=N, K=K, ws=FAKE, wsb=need - 1) == -5
+    # empty problems are valid no-ops
+    assert _lin(ops, M=0, a=None, sa=None, y=None) == 0
+    assert _lin(ops, N=0, a=None, sa=None, w=None, sw=None, y=None) == 0
+
+
+def test_workspace_sizes(ops):
+    assert ops.LIB.w4a4_workspace_size(4096, 5120, 5120, 2) == 0        # NVFP4: no split-K
+    assert ops.LIB.w4a4_workspace_size(512, 16384, 2048, 0) == 0        # enough output tiles
+    assert ops.LIB.w4a4_workspace_size(64, 2048, 2048, 0) >= 64 * 2048 * 4
+    assert ops.LIB.w4a4_workspace_size(0, 2048, 2048, 0) == 0
+    assert ops.LIB.w4a4_workspace_init(None, 0, None) == 0
+    assert ops.LIB.w4a4_workspace_init(None, 64, None) == -1
+
+
+def test_lowrank_rejects_bad_arguments(ops):
+    L = ops.LIB
+    # both or neither of l1 / idx
+    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, FAKE, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -1
+    assert L.lowrank_add(FAKE, 4, 64, 64, None, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -1
+    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 8, 0, 16, FAKE2, 1, 16, None) == -1    # r
+    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 8, 200, 16, FAKE2, 1, 16, None) == -1  # r max
+    assert L.lowrank_add(FAKE, 4, 60, 60, FAKE, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -2    # K % 8
+    assert L.lowrank_add(MISAL, 4, 64, 64, FAKE, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -3
+    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 8, 8, 16, FAKE2, 2, 16, None) == -4    # y dtype
+    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 4, 8, 16, FAKE2, 1, 16, None) == -1    # ldlw
+    assert L.w4a4_lowrank_project(FAKE, 4, 64, 64, FAKE, None, 8, FAKE2, 8, None) == -1           # ldo < 2r
+    assert L.w4a4_transform_amax(FAKE, 1, 4, 96, 96, None, _q(ops), FAKE2, None) == -2
+    assert L.w4a4_transform_amax(FAKE, 1, 4, 128, 128, None, _q(ops), None, None) == -1

@@ -1,0 +1,60 @@
+// Internal launchers behind the C ABI (host side, C++ linkage).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a4 {
+
+// quantize.hip -------------------------------------------------------------
+// mode: 0 int4, 1 int8, 2 nvfp4, 3 transform-amax only.
+hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int64_t K,
+                           int64_t ldx, const float* scale, float g, int rot, int order,
+                           void* codes, void* scales, float* amax_out, hipStream_t st);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+int64_t quant_max_k();
+
+// gemm_int.hip / gemm_nvfp4.hip --------------------------------------------
+struct BranchArgs {
+  const uint16_t* a;  // bf16 M x ra
+  int64_t lda;
+  const uint16_t* b;  // bf16 N x r
+  int64_t ldb;
+  int r;
+  int ra;
+};
+
+struct GemmArgs {
+  const uint8_t* a;      // codes, M rows
+  const void* sa;        // fp32[M] or E4M3 M x K/16
+  const uint8_t* w;      // codes, N rows
+  const void* sw;
+  int M, N, K;
+  float alpha;
+  BranchArgs br;         // br.r == 0: no branch
+  void* y;
+  int y_dtype;           // 0 f32, 1 bf16, 2 i32
+  int64_t ldy;
+  int32_t* ws;           // split-K accumulators (zeroed) or null
+  uint32_t* counters;    // split-K tile arrival counters (zeroed)
+  int splits;
+};
+
+// fmt: 0 int4, 1 int8
+hipError_t launch_gemm_int(int fmt, GemmArgs g, hipStream_t st);
+size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
+int gemm_int_splits(int fmt, int64_t M, int64_t N, int64_t K, size_t ws_bytes);
+
+hipError_t launch_gemm_nvfp4(GemmArgs g, hipStream_t st);
+size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K);
+
+// branch.hip ----------------------------------------------------------------
+hipError_t launch_lowrank_project(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  const uint16_t* l1, const int32_t* idx, int r,
+                                  uint16_t* out, int64_t ldo, hipStream_t st);
+hipError_t launch_lowrank_add(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              const uint16_t* l1, const int32_t* idx, int r, const uint16_t* lw,
+                              int64_t ldlw, int64_t N, void* y, int y_dtype, int64_t ldy,
+                              hipStream_t st);
+
+}  // namespace w4a4

@@ -1,0 +1,265 @@
+"""Python binding of the C ABI in ``include/w4a4.h`` (ctypes).
+
+Argument marshalling only: every step of the quantized linear runs in the
+HIP kernels of ``libw4a4.so``.  PyTorch supplies device memory and the HIP
+stream.  If the library is missing this module raises at import: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a4.so")
+
+FMT_INT4, FMT_INT8, FMT_NVFP4 = 0, 1, 2
+DT_F32, DT_BF16, DT_I32 = 0, 1, 2
+ORDER_SMOOTH_THEN_ROTATE, ORDER_ROTATE_THEN_SMOOTH = 0, 1
+BRANCH_NONE, BRANCH_BF16 = 0, 1
+FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4}
+ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
+          "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
+ABI_VERSION = 1
+
+EXPORTS = ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "lowrank_add",
+           "w4a4_lowrank_project", "w4a4_transform_amax", "w4a4_workspace_size",
+           "w4a4_workspace_init", "w4a4_status_string", "w4a4_last_error", "w4a4_abi_version"]
+
+
+class QDesc(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("fwht_block", ctypes.c_int32),
+                ("order", ctypes.c_int32), ("tensor_scale", ctypes.c_float)]
+
+
+class BranchDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("r", ctypes.c_int32), ("ra", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("a", ctypes.c_void_p), ("lda", ctypes.c_int64),
+                ("b", ctypes.c_void_p), ("ldb", ctypes.c_int64)]
+
+
+class W4A4Error(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not built: run __graft_entry__.build() or "
+                          f"python -m w4a4_post_quantized_channel_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    qd, br = ctypes.POINTER(QDesc), ctypes.POINTER(BranchDesc)
+    sig = {
+        "quantize_act": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
+        "pack_weights": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
+        "w4a4_linear": [vp, vp, vp, vp, i64, i64, i64, i32, f32, br, vp, i32, i64, vp, sz, vp],
+        "w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
+        "lowrank_add": [vp, i64, i64, i64, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp],
+        "w4a4_lowrank_project": [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp],
+        "w4a4_transform_amax": [vp, i32, i64, i64, i64, vp, qd, vp, vp],
+        "w4a4_workspace_size": [i64, i64, i64, i32],
+        "w4a4_workspace_init": [vp, sz, vp],
+        "w4a4_status_string": [ctypes.c_int],
+        "w4a4_last_error": [],
+        "w4a4_abi_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.w4a4_workspace_size.restype = ctypes.c_size_t
+    lib.w4a4_status_string.restype = ctypes.c_char_p
+    lib.w4a4_last_error.restype = ctypes.c_char_p
+    if lib.w4a4_abi_version() != ABI_VERSION:
+        raise ImportError("libw4a4.so ABI version mismatch")
+    return lib
+
+
+LIB = load_library()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise W4A4Error(fn, status, LIB.w4a4_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_F32
+    if t.dtype == torch.int32:
+        return DT_I32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _rowmajor(t: torch.Tensor):
+    assert t.dim() == 2 and t.stride(1) == 1, "expect a 2-D row-major tensor"
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def qdesc(fmt, fwht_block: int = 64, order="smooth_then_rotate", tensor_scale: float = 1.0) -> QDesc:
+    f = FMTS[fmt] if isinstance(fmt, str) else int(fmt)
+    o = ORDERS[order] if isinstance(order, str) else int(order)
+    return QDesc(f, int(fwht_block), o, float(tensor_scale))
+
+
+def code_shapes(fmt: str, R: int, K: int):
+    """(codes shape, codes dtype, scales shape, scales dtype) of a packed operand."""
+    if fmt == "int4":
+        return (R, K // 2), torch.uint8, (R,), torch.float32
+    if fmt == "int8":
+        return (R, K), torch.int8, (R,), torch.float32
+    if fmt == "nvfp4":
+        return (R, K // 2), torch.uint8, (R, K // 16), torch.uint8
+    raise ValueError(fmt)
+
+
+def _alloc_codes(fmt, R, K, device):
+    cs, cd, ss, sd = code_shapes(fmt, R, K)
+    return torch.empty(cs, dtype=cd, device=device), torch.empty(ss, dtype=sd, device=device)
+
+
+def quantize_act(x: torch.Tensor, inv_smooth: Optional[torch.Tensor], fmt: str = "int4", *,
+                 fwht_block: int = 64, order="smooth_then_rotate", tensor_scale: float = 1.0,
+                 codes=None, scales=None, stream=None, M: Optional[int] = None):
+    """Per-token quantization of the transformed activations (see include/w4a4.h)."""
+    R, K, ld = _rowmajor(x)
+    if M is not None:
+        R = M
+    if codes is None:
+        codes, scales = _alloc_codes(fmt, R, K, x.device)
+    q = qdesc(fmt, fwht_block, order, tensor_scale)
+    _check("quantize_act", LIB.quantize_act(_ptr(x), _dtype_code(x), R, K, ld, _ptr(inv_smooth),
+                                            ctypes.byref(q), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def pack_weights(w: torch.Tensor, smooth: Optional[torch.Tensor], fmt: str = "int4", *,
+                 fwht_block: int = 64, order="smooth_then_rotate", tensor_scale: float = 1.0,
+                 codes=None, scales=None, stream=None):
+    """Per-output-channel quantization of W S R (inverse transform folded in)."""
+    R, K, ld = _rowmajor(w)
+    if codes is None:
+        codes, scales = _alloc_codes(fmt, R, K, w.device)
+    q = qdesc(fmt, fwht_block, order, tensor_scale)
+    _check("pack_weights", LIB.pack_weights(_ptr(w), _dtype_code(w), R, K, ld, _ptr(smooth),
+                                            ctypes.byref(q), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def transform_amax(x: torch.Tensor, scale: Optional[torch.Tensor], *, fwht_block: int = 64,
+                   order="smooth_then_rotate", out=None, stream=None) -> torch.Tensor:
+    R, K, ld = _rowmajor(x)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    q = qdesc("int4", fwht_block, order, 1.0)
+    _check("w4a4_transform_amax", LIB.w4a4_transform_amax(_ptr(x), _dtype_code(x), R, K, ld, _ptr(scale),
+                                                          ctypes.byref(q), _ptr(out), _stream(stream)))
+    return out
+
+
+def branch_desc(a: Optional[torch.Tensor], b: Optional[torch.Tensor], r: Optional[int] = None) -> BranchDesc:
+    """Fused-branch descriptor: a is bf16 M x ra (ra = r or 2r), b is bf16 N x r."""
+    if a is None:
+        return BranchDesc(BRANCH_NONE, 0, 0, 0, None, 0, None, 0)
+    r = b.shape[1] if r is None else r
+    return BranchDesc(BRANCH_BF16, r, a.shape[1], 0, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0))
+
+
+def workspace_size(M: int, N: int, K: int, fmt: str) -> int:
+    return int(LIB.w4a4_workspace_size(M, N, K, FMTS[fmt]))
+
+
+def workspace_init(ws: torch.Tensor, stream=None):
+    _check("w4a4_workspace_init", LIB.w4a4_workspace_init(_ptr(ws), ws.numel() * ws.element_size(),
+                                                          _stream(stream)))
+
+
+def make_workspace(M: int, N: int, K: int, fmt: str, device="cuda", stream=None) -> Optional[torch.Tensor]:
+    n = workspace_size(M, N, K, fmt)
+    if n == 0:
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    workspace_init(ws, stream)
+    return ws
+
+
+def _linear(fn: str, fmt: str, a_codes, a_scales, w_codes, w_scales, K: int, *, alpha=1.0,
+            branch: Optional[BranchDesc] = None, y=None, y_dtype=torch.bfloat16, workspace=None,
+            stream=None, M: Optional[int] = None):
+    M = a_codes.shape[0] if M is None else M
+    N = w_codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=a_codes.device)
+    br = branch if branch is not None else branch_desc(None, None)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K)
+    tail = (ctypes.byref(br), _ptr(y), _dtype_code(y), y.stride(0), _ptr(workspace), ws_bytes, _stream(stream))
+    if fn == "w8a8_linear":
+        st = LIB.w8a8_linear(*args, float(alpha), *tail)
+    else:
+        st = LIB.w4a4_linear(*args, FMTS[fmt], float(alpha), *tail)
+    _check(fn, st)
+    return y
+
+
+def w4a4_linear(a_codes, a_scales, w_codes, w_scales, K: int, fmt: str = "int4", **kw):
+    """y = alpha * dequant(A . W^T) (+ fused bf16 branch); fmt int4 or nvfp4."""
+    return _linear("w4a4_linear", fmt, a_codes, a_scales, w_codes, w_scales, K, **kw)
+
+
+def w8a8_linear(a_codes, a_scales, w_codes, w_scales, K: int, **kw):
+    """INT8 W8A8 sibling of w4a4_linear."""
+    return _linear("w8a8_linear", "int8", a_codes, a_scales, w_codes, w_scales, K, **kw)
+
+
+def _check_branch_inputs(x, l1, idx, lw=None):
+    if x.dtype != torch.bfloat16:
+        raise TypeError("the 16-bit branch takes bf16 activations")
+    if l1 is not None and l1.dtype != torch.bfloat16:
+        raise TypeError("l1 must be bf16")
+    if idx is not None and idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    if lw is not None and lw.dtype != torch.bfloat16:
+        raise TypeError("lw must be bf16")
+
+
+def lowrank_add(x: torch.Tensor, y: torch.Tensor, lw: torch.Tensor, *, l1: Optional[torch.Tensor] = None,
+                idx: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y += (x L1) lw^T  or  y += x[:, idx] lw^T, in place."""
+    _check_branch_inputs(x, l1, idx, lw)
+    M, K, ldx = _rowmajor(x)
+    N, r = lw.shape
+    _check("lowrank_add", LIB.lowrank_add(_ptr(x), M, K, ldx, _ptr(l1), _ptr(idx), _ptr(lw), lw.stride(0), r, N,
+                                          _ptr(y), _dtype_code(y), y.stride(0), _stream(stream)))
+    return y
+
+
+def lowrank_project(x: torch.Tensor, *, l1: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                    out=None, stream=None) -> torch.Tensor:
+    """The fused branch's ``a`` operand: [hi | lo] bf16 halves of x L1, or x[:, idx]."""
+    _check_branch_inputs(x, l1, idx)
+    M, K, ldx = _rowmajor(x)
+    r = l1.shape[1] if l1 is not None else idx.shape[0]
+    width = 2 * r if l1 is not None else r
+    if out is None:
+        out = torch.empty((M, width), dtype=torch.bfloat16, device=x.device)
+    _check("w4a4_lowrank_project", LIB.w4a4_lowrank_project(_ptr(x), M, K, ldx, _ptr(l1), _ptr(idx), r, _ptr(out),
+                                                            out.stride(0), _stream(stream)))
+    return out

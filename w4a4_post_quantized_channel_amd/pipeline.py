@@ -1,0 +1,139 @@
+"""A quantized linear layer assembled from the C-ABI calls.
+
+``QuantizedLinear`` packs a float weight once (``pack_weights``: smoothing
+and the block-64 rotation folded into the weight, FoldQuantVLA contribution
+1) and then runs, per call, ``quantize_act`` -> [``w4a4_lowrank_project``]
+-> ``w4a4_linear`` / ``w8a8_linear`` with the 16-bit branch fused into the
+GEMM epilogue.  Everything runs in the HIP library; this file only holds
+buffers and argument plumbing.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import ops
+
+E2M1_TIMES_E4M3_MAX = np.float32(6.0 * 448.0)
+
+
+def nvfp4_scale_from_amax(amax: float) -> float:
+    """Static NVFP4 tensor scale g = fp32(amax / (6 * 448)); 1 when amax is 0."""
+    a = np.float32(amax)
+    return float(np.float32(1.0) if a == 0 else np.float32(a / E2M1_TIMES_E4M3_MAX))
+
+
+class QuantizedLinear:
+    """y = x W^T computed as the quantized path (int4 / int8 / nvfp4).
+
+    w        N x K float weight (the part the quantized path carries), device.
+    s        K smoothing factors (weights multiplied by s, activations by
+             inv_s), device fp32, or None.
+    inv_s    K factors for the activations (fp32(1/s)), device, or None.
+    branch   None, {"kind": "lowrank", "l1": K x r bf16, "lw": N x r bf16}
+             or {"kind": "outlier", "idx": int32[r], "lw": N x r bf16}.
+    """
+
+    def __init__(self, w: torch.Tensor, s: Optional[torch.Tensor], inv_s: Optional[torch.Tensor],
+                 fmt: str = "int4", *, fwht_block: int = 64, order: str = "smooth_then_rotate",
+                 branch: Optional[dict] = None, y_dtype=torch.bfloat16, stream=None):
+        self.fmt, self.fwht_block, self.order = fmt, fwht_block, order
+        self.N, self.K = w.shape
+        self.inv_s = inv_s
+        self.y_dtype = y_dtype
+        self.branch = branch
+        self.g_w = 1.0
+        if fmt == "nvfp4":
+            amax = ops.transform_amax(w, s, fwht_block=fwht_block, order=order, stream=stream)
+            self.g_w = nvfp4_scale_from_amax(float(amax.item()))
+        self.w_codes, self.w_scales = ops.pack_weights(w, s, fmt, fwht_block=fwht_block, order=order,
+                                                       tensor_scale=self.g_w, stream=stream)
+        self.g_a = 1.0
+        self._bufs = {}
+
+    # NVFP4 activations use a static per-tensor scale from calibration data
+    # (statistics after both transforms, QuantWAMs sec. 4.2).
+    def calibrate(self, x_cal: torch.Tensor, stream=None) -> float:
+        if self.fmt == "nvfp4":
+            amax = ops.transform_amax(x_cal, self.inv_s, fwht_block=self.fwht_block, order=self.order,
+                                      stream=stream)
+            self.g_a = nvfp4_scale_from_amax(float(amax.item()))
+        return self.g_a
+
+    @property
+    def alpha(self) -> float:
+        if self.fmt == "nvfp4":
+            return float(np.float32(self.g_a) * np.float32(self.g_w))
+        return 1.0
+
+    def buffers(self, M: int, device):
+        b = self._bufs.get(M)
+        if b is None:
+            codes, scales = ops._alloc_codes(self.fmt, M, self.K, device)
+            br_a = None
+            if self.branch is not None:
+                r = self.branch["lw"].shape[1]
+                width = 2 * r if self.branch["kind"] == "lowrank" else r
+                br_a = torch.empty((M, width), dtype=torch.bfloat16, device=device)
+            ws = ops.make_workspace(M, self.N, self.K, self.fmt, device=device)
+            y = torch.empty((M, self.N), dtype=self.y_dtype, device=device)
+            b = {"codes": codes, "scales": scales, "br_a": br_a, "ws": ws, "y": y}
+            self._bufs[M] = b
+        return b
+
+    def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        M = x.shape[0]
+        b = self.buffers(M, x.device)
+        ops.quantize_act(x, self.inv_s, self.fmt, fwht_block=self.fwht_block, order=self.order,
+                         tensor_scale=self.g_a, codes=b["codes"], scales=b["scales"], stream=stream)
+        bd = None
+        if self.branch is not None:
+            if self.branch["kind"] == "lowrank":
+                ops.lowrank_project(x, l1=self.branch["l1"], out=b["br_a"], stream=stream)
+            else:
+                ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
+            bd = ops.branch_desc(b["br_a"], self.branch["lw"])
+        y = b["y"] if out is None else out
+        if self.fmt == "int8":
+            return ops.w8a8_linear(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K,
+                                   branch=bd, y=y, workspace=b["ws"], stream=stream)
+        return ops.w4a4_linear(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K, self.fmt,
+                               alpha=self.alpha, branch=bd, y=y, workspace=b["ws"], stream=stream)
+
+    __call__ = forward
+
+
+def case_to_device(case, device="cuda"):
+    """Upload a ``workloads.Case`` (numpy) as device tensors."""
+    from .workloads import bf16_bits
+
+    def bf16(a):
+        return torch.from_numpy(bf16_bits(np.ascontiguousarray(a)).view(np.int16)).view(torch.bfloat16).to(device)
+
+    t = {}
+    t["x"] = bf16(case.x) if case.x_dtype == "bf16" else torch.from_numpy(case.x).to(device)
+    t["w"] = torch.from_numpy(np.ascontiguousarray(case.w)).to(device)
+    t["s"] = None if case.s is None else torch.from_numpy(case.s).to(device)
+    t["inv_s"] = None if case.inv_s is None else torch.from_numpy(case.inv_s).to(device)
+    br = None
+    if case.branch is not None:
+        br = {"kind": case.branch["kind"], "lw": bf16(case.branch["lw"])}
+        if case.branch["kind"] == "lowrank":
+            br["l1"] = bf16(case.branch["l1"])
+        else:
+            br["idx"] = torch.from_numpy(case.branch["idx"].astype(np.int32)).to(device)
+    t["branch"] = br
+    return t
+
+
+def build_layer(case, device="cuda", order="smooth_then_rotate", calibrate=True) -> tuple:
+    """QuantizedLinear + device inputs for a ``workloads.Case``."""
+    t = case_to_device(case, device)
+    y_dtype = torch.float32 if case.y_dtype == "f32" else torch.bfloat16
+    layer = QuantizedLinear(t["w"], t["s"], t["inv_s"], case.fmt, fwht_block=case.fwht_block, order=order,
+                            branch=t["branch"], y_dtype=y_dtype)
+    if calibrate:
+        layer.calibrate(t["x"])
+    return layer, t
