@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--no-also", action="store_true", help="skip the secondary 4096-token measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample duration")
+    p.add_argument("--eager", action="store_true", help="launch every call from Python (no HIP graph)")
     return p.parse_args()
 
 
@@ -76,18 +77,45 @@ def gemm_bytes(case):
     return code * (M + N) * K + scales + out + br
 
 
-def time_region(torch, step, steps, warmup, kernel_events=None):
-    for _ in range(warmup):
+EAGER = False
+PER_GRAPH = 20
+
+
+def time_region(torch, step, steps, warmup):
+    """ms per call of ``step``.  Default: the calls are captured once into a
+    HIP graph of PER_GRAPH back-to-back calls and the graph is replayed, so
+    host launch cost is not what is measured; HIP events on the replay
+    stream bracket the timed replays.  With --eager every call is launched
+    from Python."""
+    for _ in range(3):
         step()
+    torch.cuda.synchronize()
+    if EAGER:
+        run, per = step, 1
+    else:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(PER_GRAPH):
+                step()
+        run, per = graph.replay, PER_GRAPH
+    reps = max(1, steps // per)
+    for _ in range(max(1, warmup // per)):
+        run()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(steps):
-        step()
+    for _ in range(reps):
+        run()
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    return t0.elapsed_time(t1) / (reps * per)
 
 
 def dominant_kernel_time(torch, case, layer, t, steps):
@@ -224,6 +252,8 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    global EAGER
+    EAGER = a.eager
     r = measure(torch, a.workload, a.steps, a.warmup)
     out = {
         "metric": "W4A4 linear effective TOPS + us/call (batch-1 64-token and 4096-token shapes)",
@@ -237,7 +267,8 @@ def main():
         "vs_baseline": None,
         "dtype": r["roofline"]["kernel"].startswith("w4a4_linear nvfp4") and "f16" or "i8",
         "data": "synthetic (seeded; shapes and outlier statistics of the workload descriptions)",
-        "config": {"workload": r["desc"], "projections": r["names"]},
+        "config": {"workload": r["desc"], "projections": r["names"],
+                   "launch": "eager" if a.eager else f"HIP graph of {PER_GRAPH} steps, replayed"},
         "roofline": r["roofline"],
         "quantize_kernel": r["quantize"],
     }

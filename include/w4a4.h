@@ -57,7 +57,7 @@ typedef enum w4a4_status {
   W4A4_ERR_UNSUPPORTED_SHAPE = -2, /* K not a multiple of the required block */
   W4A4_ERR_MISALIGNED = -3,        /* pointer / row stride not 16-byte aligned */
   W4A4_ERR_UNSUPPORTED_FORMAT = -4,/* format / dtype / option combination */
-  W4A4_ERR_WORKSPACE = -5,         /* workspace given but too small */
+  W4A4_ERR_WORKSPACE = -5,         /* workspace given but smaller than required */
   W4A4_ERR_LAUNCH_FAILED = -6      /* HIP launch error (see w4a4_last_error) */
 } w4a4_status;
 
@@ -156,11 +156,14 @@ int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t l
  *  y        M x N output, y_dtype F32 or BF16 (round to nearest even) with
  *           row stride ldy >= N; y_dtype I32 writes the raw integer
  *           accumulators (INT formats, no branch, alpha ignored).
- *  workspace / workspace_bytes  optional device scratch for split-K
- *           (size from w4a4_workspace_size, zero-filled once with
- *           w4a4_workspace_init; every successful call leaves it zeroed).
- *           NULL selects a configuration without split-K.  Calls that
- *           share one workspace must be ordered on one stream.
+ *  workspace / workspace_bytes  optional device scratch (NULL / 0 for
+ *           none).  Few-token shapes (M <= 64) split K over workgroups
+ *           when it is given: int32 partial tiles go to the workspace and a
+ *           second kernel adds them (exact) and runs the epilogue.  Size
+ *           from w4a4_workspace_size; no initialisation needed; contents
+ *           are overwritten.  Calls sharing one workspace must be ordered
+ *           on one stream.  A non-NULL workspace smaller than required is
+ *           W4A4_ERR_WORKSPACE.
  * Shape rules: K % 64 == 0.  Alignment: codes 16-byte aligned.
  */
 int w4a4_linear(const void* a_codes, const void* a_scales,
@@ -214,10 +217,9 @@ int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, in
                         const float* scale, const w4a4_qdesc* q, float* amax_out,
                         void* stream);
 
-/* Split-K scratch: bytes needed for (M, N, K, fmt); 0 if none is used. */
+/* Bytes of workspace w4a4_linear / w8a8_linear use for (M, N, K, fmt);
+ * 0 when the shape runs without one. */
 size_t w4a4_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt);
-/* Zero-fill a workspace on ``stream`` (a kernel, no hipMemset). */
-int w4a4_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 const char* w4a4_status_string(int status);
 const char* w4a4_last_error(void);

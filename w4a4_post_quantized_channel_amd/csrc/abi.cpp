@@ -140,21 +140,16 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
     g.br.r = br->r; g.br.ra = br->ra;
   }
   g.y = y; g.y_dtype = y_dtype; g.ldy = ldy;
-  g.splits = 1;
   hipError_t e;
   if (fmt == W4A4_FMT_NVFP4) {
     e = w4a4::launch_gemm_nvfp4(g, (hipStream_t)stream);
   } else {
     const size_t need = w4a4::gemm_int_workspace(fmt, M, N, K);
-    if (workspace && need > 0) {
-      if (ws_bytes < need)
-        return fail(W4A4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
-      if (!aligned(workspace, 16)) return fail(W4A4_ERR_MISALIGNED, "%s: workspace not 16-byte aligned", fn);
-      g.splits = w4a4::gemm_int_splits(fmt, M, N, K, ws_bytes);
-      g.ws = (int32_t*)workspace;
-      g.counters = (uint32_t*)((char*)workspace + (size_t)M * N * 4);
-    }
-    e = w4a4::launch_gemm_int(fmt, g, (hipStream_t)stream);
+    if (workspace && ws_bytes < need)
+      return fail(W4A4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+    if (workspace && !aligned(workspace, 16))
+      return fail(W4A4_ERR_MISALIGNED, "%s: workspace not 16-byte aligned", fn);
+    e = w4a4::launch_gemm_int(fmt, g, workspace, ws_bytes, (hipStream_t)stream);
   }
   return launch_status(e, fn);
 }
@@ -250,16 +245,9 @@ int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, in
 }
 
 size_t w4a4_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt) {
-  if (M <= 0 || N <= 0 || K <= 0) return 0;
-  if (fmt == W4A4_FMT_NVFP4) return w4a4::gemm_nvfp4_workspace(M, N, K);
+  if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0) return 0;
   if (fmt != W4A4_FMT_INT4 && fmt != W4A4_FMT_INT8) return 0;
   return w4a4::gemm_int_workspace(fmt, M, N, K);
-}
-
-int w4a4_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
-  if (workspace_bytes == 0) return ok();
-  if (!workspace || !aligned(workspace, 16)) return fail(W4A4_ERR_INVALID_ARG, "w4a4_workspace_init: bad pointer");
-  return launch_status(w4a4::launch_zero(workspace, workspace_bytes, (hipStream_t)stream), "w4a4_workspace_init");
 }
 
 const char* w4a4_status_string(int status) {

@@ -7,20 +7,26 @@
 // optional bf16 branch (Q-WAM 16-bit low-rank branch / QuantWAMs BF16
 // bypass) on the same fp32 accumulators.
 //
-// Design.  C = A . W^T with both operands K-contiguous.  A workgroup tile
-// BM x BN is split over four waves; each wave owns (WM/16) x (WN/16) tiles
-// of v_mfma_i32_16x16x64_i8.  K advances 128 elements per step through a
-// double-buffered LDS stage (16-byte global loads, one barrier per step).
-// int4 codes stay packed in HBM and LDS (half the bytes of int8) and are
-// widened in registers: for a packed dword d, (d << 4) & 0xF0F0F0F0 holds
-// the even-index codes and d & 0xF0F0F0F0 the odd-index codes, each as the
-// exact signed byte 16*q.  Both operands get the same lane permutation, so
-// the MFMA returns exactly 256 * sum(qa * qw); the epilogue shifts right
-// by 8.  Split-K (few output tiles, long K) adds int32 partials with
-// device-scope atomics into a workspace; the last workgroup of a tile
-// (arrival counter) reads the totals with atomic exchange (leaving the
-// workspace zeroed for the next call) and runs the epilogue, so the result
-// is bit-identical to the unsplit sum.
+// int4 codes stay packed in HBM (and LDS) and are widened in registers: for
+// a packed dword d, (d << 4) & 0xF0F0F0F0 holds the even-index codes and
+// d & 0xF0F0F0F0 the odd-index codes, each as the exact signed byte 16*q.
+// Both operands get the same lane permutation, so v_mfma_i32_16x16x64_i8
+// returns exactly 256 * sum(qa * qw); the epilogue shifts right by 8.
+//
+// Two kernels:
+//  * tile kernel (many tokens): BM x BN workgroup tile over four waves,
+//    K advanced 128 elements per step through a double-buffered LDS stage.
+//  * decode kernel (<= 64 tokens, weight streaming): 64 token rows x 64
+//    output channels per workgroup of four waves.  No LDS staging: each
+//    wave loads its MFMA operands straight from global memory with raw
+//    buffer loads (16 bytes per lane, whole 64-byte row segments per
+//    instruction, out-of-range rows read as zero) for an interleaved
+//    quarter of the workgroup's K range; the four partial tiles are summed
+//    in LDS.  K is split over workgroups when a workspace is given; a
+//    second kernel adds the int32 partial tiles (exact) and runs the
+//    epilogue.  Splits never hand off inside one kernel: on gfx950 a
+//    cross-workgroup handoff needs an agent-scope fence, which writes back
+//    and invalidates the XCD's L2.
 #include "device_common.h"
 #include "epilogue.h"
 #include "launch.h"
@@ -29,6 +35,64 @@ namespace w4a4 {
 
 constexpr int kBK = 128;  // K elements per main-loop step
 
+__device__ __forceinline__ v4i widen_int4(uint32_t lo, uint32_t hi) {
+  return v4i{(int)((lo << 4) & 0xF0F0F0F0u), (int)(lo & 0xF0F0F0F0u), (int)((hi << 4) & 0xF0F0F0F0u),
+             (int)(hi & 0xF0F0F0F0u)};
+}
+
+// Dequantise, add the branch, store.  acc[i][j] is the 16x16 tile whose
+// first row is m_base + 16 i and first column n_base + 16 j.
+template <bool INT4, int TI, int TJ>
+__device__ __forceinline__ void int_epilogue(v4i (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
+                                             int lane) {
+  const int lr = lane & 15, lq = lane >> 4;
+  if (g.y_dtype == 2) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m_base + i * 16 + lq * 4 + r, n = n_base + j * 16 + lr;
+          const int v = INT4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+          if (m < g.M && n < g.N) reinterpret_cast<int32_t*>(g.y)[(int64_t)m * g.ldy + n] = v;
+        }
+    return;
+  }
+  const float* sa = reinterpret_cast<const float*>(g.sa);
+  const float* sw = reinterpret_cast<const float*>(g.sw);
+  v4f accf[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n = n_base + j * 16 + lr;
+      const float swn = n < g.N ? sw[n] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m_base + i * 16 + lq * 4 + r;
+        const float sam = m < g.M ? sa[m] : 0.f;
+        const int q = INT4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+        float v = (float)q * sam;
+        v = v * swn;
+        accf[i][j][r] = v * g.alpha;
+      }
+    }
+  if (g.br.r > 0) branch_mfma<TI, TJ>(accf, g.br, g.M, g.N, m_base, n_base, lane);
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m_base + i * 16 + lq * 4 + r, n = n_base + j * 16 + lr;
+        if (m < g.M && n < g.N) store_out(g.y, g.y_dtype, g.ldy, m, n, accf[i][j][r]);
+      }
+}
+
+// ---------------------------------------------------------------------------
+// Tile kernel
+// ---------------------------------------------------------------------------
 template <bool INT4, int BM, int BN, int WM, int WN>
 struct IntTile {
   static constexpr int RB = INT4 ? kBK / 2 : kBK;   // bytes per row per step
@@ -43,20 +107,17 @@ struct IntTile {
 };
 
 template <bool INT4, int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(256) gemm_int_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(256) gemm_int_tile_kernel(GemmArgs g) {
   using T = IntTile<INT4, BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * T::PITCH];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * T::PITCH];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int wm0 = (wave / T::WAVES_N) * WM, wn0 = (wave % T::WAVES_N) * WN;
   const int64_t rowbytes = INT4 ? (g.K >> 1) : g.K;
-  const int nk_total = (g.K + kBK - 1) / kBK;
-  const int per = (nk_total + g.splits - 1) / g.splits;
-  const int ks0 = blockIdx.z * per;
-  const int ks1 = min(nk_total, ks0 + per);
+  const int ks0 = 0;
+  const int ks1 = (g.K + kBK - 1) / kBK;
 
   v4i acc[T::TI][T::TJ];
 #pragma unroll
@@ -64,6 +125,10 @@ __global__ void __launch_bounds__(256) gemm_int_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < T::TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(g.a + (int64_t)m0 * rowbytes,
+                                               (uint32_t)(min(BM, g.M - m0) * rowbytes));
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(g.w + (int64_t)n0 * rowbytes,
+                                               (uint32_t)(min(BN, g.N - n0) * rowbytes));
   uint4 ra[T::LA], rb[T::LB];
   auto gload = [&](int ks) {
     const int64_t kb0 = (int64_t)ks * T::RB;
@@ -71,19 +136,15 @@ __global__ void __launch_bounds__(256) gemm_int_kernel(GemmArgs g) {
     for (int t = 0; t < T::LA; ++t) {
       const int c = tid + t * 256;
       const int r = c / (T::RB / 16), col = (c % (T::RB / 16)) * 16;
-      uint4 d = make_uint4(0, 0, 0, 0);
-      if (c < T::CH_A && m0 + r < g.M && kb0 + col < rowbytes)
-        d = *reinterpret_cast<const uint4*>(g.a + (int64_t)(m0 + r) * rowbytes + kb0 + col);
-      ra[t] = d;
+      const bool ok = c < T::CH_A && kb0 + col < rowbytes;
+      ra[t] = buf_load16(rsA, ok ? (uint32_t)(r * rowbytes + kb0 + col) : kOOB);
     }
 #pragma unroll
     for (int t = 0; t < T::LB; ++t) {
       const int c = tid + t * 256;
       const int r = c / (T::RB / 16), col = (c % (T::RB / 16)) * 16;
-      uint4 d = make_uint4(0, 0, 0, 0);
-      if (c < T::CH_B && n0 + r < g.N && kb0 + col < rowbytes)
-        d = *reinterpret_cast<const uint4*>(g.w + (int64_t)(n0 + r) * rowbytes + kb0 + col);
-      rb[t] = d;
+      const bool ok = c < T::CH_B && kb0 + col < rowbytes;
+      rb[t] = buf_load16(rsB, ok ? (uint32_t)(r * rowbytes + kb0 + col) : kOOB);
     }
   };
   auto sstore = [&](int buf) {
@@ -121,15 +182,13 @@ __global__ void __launch_bounds__(256) gemm_int_kernel(GemmArgs g) {
           for (int i = 0; i < T::TI; ++i) {
             const uint2 d = *reinterpret_cast<const uint2*>(
                 &sA[buf][(wm0 + i * 16 + lr) * T::PITCH + sub * 32 + lq * 8]);
-            af[i] = v4i{(int)((d.x << 4) & 0xF0F0F0F0u), (int)(d.x & 0xF0F0F0F0u),
-                        (int)((d.y << 4) & 0xF0F0F0F0u), (int)(d.y & 0xF0F0F0F0u)};
+            af[i] = widen_int4(d.x, d.y);
           }
 #pragma unroll
           for (int j = 0; j < T::TJ; ++j) {
             const uint2 d = *reinterpret_cast<const uint2*>(
                 &sB[buf][(wn0 + j * 16 + lr) * T::PITCH + sub * 32 + lq * 8]);
-            bfr[j] = v4i{(int)((d.x << 4) & 0xF0F0F0F0u), (int)(d.x & 0xF0F0F0F0u),
-                         (int)((d.y << 4) & 0xF0F0F0F0u), (int)(d.y & 0xF0F0F0F0u)};
+            bfr[j] = widen_int4(d.x, d.y);
           }
         } else {
 #pragma unroll
@@ -152,133 +211,204 @@ __global__ void __launch_bounds__(256) gemm_int_kernel(GemmArgs g) {
     }
   }
 
-  // ---- split-K reduction --------------------------------------------------
-  if (g.splits > 1) {
+  int_epilogue<INT4, T::TI, T::TJ>(acc, g, m0 + wm0, n0 + wn0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernels: 64 token rows x 64 output channels per workgroup of four
+// waves.  Each wave takes an interleaved quarter of the workgroup's K range
+// and issues the buffer loads of a chunk of 128-deep steps before their
+// MFMAs.  With a workspace the K range is split over blockIdx.z: partial
+// tiles go to the workspace and a second kernel adds them and runs the
+// epilogue (the kernel boundary orders the writes; no fences).
+// ---------------------------------------------------------------------------
+constexpr int kDecTJ = 4;  // 64 output channels per workgroup when K is split
+
+template <bool INT4, int TJ>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
+  constexpr int TI = 4;
+  constexpr int LPR = INT4 ? 1 : 2;     // 16-byte loads per row and step
+  constexpr int CHUNK = INT4 ? 4 : 2;   // steps whose loads are in flight together
+  __shared__ int red[4][TI][TJ][4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int n0 = blockIdx.x * 16 * TJ, m0 = blockIdx.y * 64;
+  const int64_t rowbytes = INT4 ? (g.K >> 1) : g.K;
+  const int kz0 = blockIdx.z * kwg, kz1 = min(g.K, kz0 + kwg);
+  const int lofs = INT4 ? lq * 16 : lq * 32;  // this lane's bytes inside a 128-element step
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(g.a + (int64_t)m0 * rowbytes,
+                                               (uint32_t)(min(64, g.M - m0) * rowbytes));
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(g.w + (int64_t)n0 * rowbytes,
+                                               (uint32_t)(min(16 * TJ, g.N - n0) * rowbytes));
+
+  v4i acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < T::TI; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < T::TJ; ++j)
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  for (int kc = kz0 + wave * kBK; kc < kz1; kc += 4 * kBK * CHUNK) {
+    uint4 ra[CHUNK][TI][LPR], rb[CHUNK][TJ][LPR];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm0 + i * 16 + lq * 4 + r, n = n0 + wn0 + j * 16 + lr;
-          if (m < g.M && n < g.N) atomicAdd(&g.ws[(int64_t)m * g.N + n], acc[i][j][r]);
-        }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
-      const uint32_t prev = atomicAdd(&g.counters[tile], 1u);
-      const int last = prev == (uint32_t)(g.splits - 1);
-      if (last) g.counters[tile] = 0u;
-      s_last = last;
+    for (int s = 0; s < CHUNK; ++s) {
+      const int k = kc + s * 4 * kBK;
+      const int64_t kb = (INT4 ? (k >> 1) : k) + lofs;
+#pragma unroll
+      for (int l = 0; l < LPR; ++l) {
+        const bool kin = k < kz1 && kb + 16 * l < rowbytes;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+          ra[s][i][l] = buf_load16(rsA, kin ? (uint32_t)((i * 16 + lr) * rowbytes + kb + 16 * l) : kOOB);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          rb[s][j][l] = buf_load16(rsB, kin ? (uint32_t)((j * 16 + lr) * rowbytes + kb + 16 * l) : kOOB);
+      }
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk in flight before the MFMAs
 #pragma unroll
-    for (int i = 0; i < T::TI; ++i)
+    for (int s = 0; s < CHUNK; ++s)
 #pragma unroll
-      for (int j = 0; j < T::TJ; ++j)
+      for (int h = 0; h < 2; ++h) {
+        v4i a[TI], b[TJ];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm0 + i * 16 + lq * 4 + r, n = n0 + wn0 + j * 16 + lr;
-          acc[i][j][r] = (m < g.M && n < g.N) ? atomicExch(&g.ws[(int64_t)m * g.N + n], 0) : 0;
+        for (int i = 0; i < TI; ++i) {
+          if constexpr (INT4) a[i] = h ? widen_int4(ra[s][i][0].z, ra[s][i][0].w) : widen_int4(ra[s][i][0].x, ra[s][i][0].y);
+          else a[i] = __builtin_bit_cast(v4i, ra[s][i][h < LPR ? h : 0]);
         }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          if constexpr (INT4) b[j] = h ? widen_int4(rb[s][j][0].z, rb[s][j][0].w) : widen_int4(rb[s][j][0].x, rb[s][j][0].y);
+          else b[j] = __builtin_bit_cast(v4i, rb[s][j][h < LPR ? h : 0]);
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
   }
 
-  // ---- epilogue -----------------------------------------------------------
-  if (g.y_dtype == 2) {
+  // sum the four waves' partial tiles; wave w keeps row block w
 #pragma unroll
-    for (int i = 0; i < T::TI; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < T::TJ; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm0 + i * 16 + lq * 4 + r, n = n0 + wn0 + j * 16 + lr;
-          const int v = INT4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
-          if (m < g.M && n < g.N) reinterpret_cast<int32_t*>(g.y)[(int64_t)m * g.ldy + n] = v;
-        }
+      for (int r = 0; r < 4; ++r) red[wave][i][j][r][lane] = acc[i][j][r];
+  __syncthreads();
+  v4i tot[1][TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      tot[0][j][r] = red[0][wave][j][r][lane] + red[1][wave][j][r][lane] + red[2][wave][j][r][lane] +
+                     red[3][wave][j][r][lane];
+  if (part) {  // lane-contiguous partial tile: 16 ints (64 bytes) per lane
+    const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    uint4* p = reinterpret_cast<uint4*>(part + ((tile * gridDim.z + blockIdx.z) * 4 + wave) * (TJ * 256)) +
+               lane * TJ;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) p[j] = __builtin_bit_cast(uint4, tot[0][j]);
     return;
   }
-  const float* sa = reinterpret_cast<const float*>(g.sa);
-  const float* sw = reinterpret_cast<const float*>(g.sw);
-  v4f accf[T::TI][T::TJ];
+  int_epilogue<INT4, 1, TJ>(tot, g, m0 + wave * 16, n0, lane);
+}
+
+// One wave per (tile, row block): add the S partial tiles, then the epilogue.
+template <bool INT4>
+__global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, const int32_t* part) {
+  constexpr int TJ = kDecTJ;
+  const int lane = threadIdx.x;
+  const int nt = (g.N + 16 * TJ - 1) / (16 * TJ);
+  const int64_t tile = blockIdx.x >> 2;
+  const int rb = blockIdx.x & 3;
+  const int n0 = (int)(tile % nt) * 16 * TJ, m0 = (int)(tile / nt) * 64;
+  v4i tot[1][TJ];
 #pragma unroll
-  for (int i = 0; i < T::TI; ++i)
+  for (int j = 0; j < TJ; ++j) tot[0][j] = v4i{0, 0, 0, 0};
+  constexpr int ZB = 8;  // partial tiles whose loads are in flight together
+  for (int z0 = 0; z0 < S; z0 += ZB) {
+    uint4 v[ZB][TJ];
 #pragma unroll
-    for (int j = 0; j < T::TJ; ++j) {
-      const int n = n0 + wn0 + j * 16 + lr;
-      const float swn = n < g.N ? sw[n] : 0.f;
+    for (int dz = 0; dz < ZB; ++dz) {
+      const int z = z0 + dz < S ? z0 + dz : S - 1;
+      const uint4* p = reinterpret_cast<const uint4*>(part + ((tile * S + z) * 4 + rb) * (TJ * 256)) + lane * TJ;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm0 + i * 16 + lq * 4 + r;
-        const float sam = m < g.M ? sa[m] : 0.f;
-        const int q = INT4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
-        float v = (float)q * sam;
-        v = v * swn;
-        accf[i][j][r] = v * g.alpha;
-      }
+      for (int j = 0; j < TJ; ++j) v[dz][j] = p[j];
     }
-  if (g.br.r > 0) branch_mfma<T::TI, T::TJ>(accf, g.br, g.M, g.N, m0 + wm0, n0 + wn0, lane);
 #pragma unroll
-  for (int i = 0; i < T::TI; ++i)
+    for (int dz = 0; dz < ZB; ++dz)
+      if (z0 + dz < S)
 #pragma unroll
-    for (int j = 0; j < T::TJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm0 + i * 16 + lq * 4 + r, n = n0 + wn0 + j * 16 + lr;
-        if (m < g.M && n < g.N) store_out(g.y, g.y_dtype, g.ldy, m, n, accf[i][j][r]);
-      }
+        for (int j = 0; j < TJ; ++j) tot[0][j] += __builtin_bit_cast(v4i, v[dz][j]);
+  }
+  int_epilogue<INT4, 1, TJ>(tot, g, m0 + rb * 16, n0, lane);
 }
 
 // ---------------------------------------------------------------------------
-// Host-side configuration
+// Host-side dispatch
 // ---------------------------------------------------------------------------
-struct IntCfg {
-  int bm, bn;
+struct DecodePlan {
+  int splits;
+  int kwg;
+  int64_t tiles;
+  size_t ws_bytes;
 };
 
-static IntCfg pick_cfg(int64_t M, int64_t N) {
-  if (M <= 64) return {64, 64};
-  return {128, 128};
-}
-
-static int pick_splits(int64_t M, int64_t N, int64_t K, IntCfg c) {
-  const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-  const int64_t nk = (K + kBK - 1) / kBK;
-  int s = 1;
-  // Aim for about two workgroups per CU (256 CUs) while each split keeps
-  // at least two K steps.
-  while (tiles * s * 2 <= 512 && nk / (s * 2) >= 2) s *= 2;
-  const int64_t per = (nk + s - 1) / s;
-  return (int)((nk + per - 1) / per);
+// Split K so that about 256 workgroups stream the weights; each split is a
+// multiple of four 128-deep steps (one per wave).  Small weight matrices
+// are not split: the second kernel costs more than the split saves.
+static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, bool int4) {
+  DecodePlan p{};
+  p.tiles = ((N + 16 * kDecTJ - 1) / (16 * kDecTJ)) * ((M + 63) / 64);
+  const int64_t unit = 4 * kBK;
+  const int64_t nunits = (K + unit - 1) / unit;
+  const int64_t wbytes = N * K / (int4 ? 2 : 1);
+  int64_t s = wbytes < (8 << 20) ? 1 : 256 / p.tiles;
+  s = s < 1 ? 1 : (s > nunits ? nunits : s);
+  const int64_t per = (nunits + s - 1) / s;
+  p.kwg = (int)(per * unit);
+  p.splits = (int)((nunits + per - 1) / per);
+  p.ws_bytes = p.splits > 1 ? (size_t)(p.splits * p.tiles * 64 * 16 * kDecTJ * 4) : 0;
+  return p;
 }
 
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
-  (void)fmt;
-  IntCfg c = pick_cfg(M, N);
-  if (pick_splits(M, N, K, c) <= 1) return 0;
-  const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-  return (size_t)(M * N * 4 + ((tiles * 4 + 255) / 256) * 256);
+  return M <= 64 ? decode_plan(M, N, K, fmt == 0).ws_bytes : 0;
 }
 
-int gemm_int_splits(int fmt, int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
-  IntCfg c = pick_cfg(M, N);
-  const size_t need = gemm_int_workspace(fmt, M, N, K);
-  if (need == 0 || ws_bytes < need) return 1;
-  return pick_splits(M, N, K, c);
-}
-
-hipError_t launch_gemm_int(int fmt, GemmArgs g, hipStream_t st) {
-  IntCfg c = pick_cfg(g.M, g.N);
-  dim3 grid((g.N + c.bn - 1) / c.bn, (g.M + c.bm - 1) / c.bm, g.splits);
+hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st) {
   const bool int4 = fmt == 0;
-  if (c.bm == 64) {
-    if (int4) hipLaunchKernelGGL((gemm_int_kernel<true, 64, 64, 32, 32>), grid, dim3(256), 0, st, g);
-    else hipLaunchKernelGGL((gemm_int_kernel<false, 64, 64, 32, 32>), grid, dim3(256), 0, st, g);
+  if (g.M <= 64) {
+    DecodePlan p = decode_plan(g.M, g.N, g.K, int4);
+    const bool split = p.splits > 1 && workspace && ws_bytes >= p.ws_bytes;
+    int32_t* part = split ? reinterpret_cast<int32_t*>(workspace) : nullptr;
+    if (split) {
+      dim3 grid((g.N + 16 * kDecTJ - 1) / (16 * kDecTJ), (g.M + 63) / 64, p.splits);
+      if (int4) hipLaunchKernelGGL((gemm_int_decode_kernel<true, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
+      else hipLaunchKernelGGL((gemm_int_decode_kernel<false, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
+    } else {  // whole K per workgroup: 16 output channels each for more workgroups
+      dim3 grid((g.N + 15) / 16, (g.M + 63) / 64, 1);
+      if (int4) hipLaunchKernelGGL((gemm_int_decode_kernel<true, 1>), grid, dim3(256), 0, st, g, g.K, part);
+      else hipLaunchKernelGGL((gemm_int_decode_kernel<false, 1>), grid, dim3(256), 0, st, g, g.K, part);
+    }
+    if (split) {
+      dim3 rgrid((unsigned)(p.tiles * 4));
+      if (int4) hipLaunchKernelGGL((gemm_int_reduce_kernel<true>), rgrid, dim3(64), 0, st, g, p.splits, part);
+      else hipLaunchKernelGGL((gemm_int_reduce_kernel<false>), rgrid, dim3(64), 0, st, g, p.splits, part);
+    }
+    return hipGetLastError();
+  }
+  const int64_t tiles128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+  if (tiles128 >= 256) {
+    dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, 1);
+    if (int4) hipLaunchKernelGGL((gemm_int_tile_kernel<true, 128, 128, 64, 64>), grid, dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((gemm_int_tile_kernel<false, 128, 128, 64, 64>), grid, dim3(256), 0, st, g);
   } else {
-    if (int4) hipLaunchKernelGGL((gemm_int_kernel<true, 128, 128, 64, 64>), grid, dim3(256), 0, st, g);
-    else hipLaunchKernelGGL((gemm_int_kernel<false, 128, 128, 64, 64>), grid, dim3(256), 0, st, g);
+    dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, 1);
+    if (int4) hipLaunchKernelGGL((gemm_int_tile_kernel<true, 64, 64, 32, 32>), grid, dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((gemm_int_tile_kernel<false, 64, 64, 32, 32>), grid, dim3(256), 0, st, g);
   }
   return hipGetLastError();
 }

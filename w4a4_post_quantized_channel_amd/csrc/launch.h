@@ -11,7 +11,6 @@ namespace w4a4 {
 hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int64_t K,
                            int64_t ldx, const float* scale, float g, int rot, int order,
                            void* codes, void* scales, float* amax_out, hipStream_t st);
-hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 int64_t quant_max_k();
 
 // gemm_int.hip / gemm_nvfp4.hip --------------------------------------------
@@ -35,18 +34,13 @@ struct GemmArgs {
   void* y;
   int y_dtype;           // 0 f32, 1 bf16, 2 i32
   int64_t ldy;
-  int32_t* ws;           // split-K accumulators (zeroed) or null
-  uint32_t* counters;    // split-K tile arrival counters (zeroed)
-  int splits;
 };
 
-// fmt: 0 int4, 1 int8
-hipError_t launch_gemm_int(int fmt, GemmArgs g, hipStream_t st);
+// fmt: 0 int4, 1 int8.  workspace may be null (no split-K).
+hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st);
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
-int gemm_int_splits(int fmt, int64_t M, int64_t N, int64_t K, size_t ws_bytes);
 
 hipError_t launch_gemm_nvfp4(GemmArgs g, hipStream_t st);
-size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K);
 
 // branch.hip ----------------------------------------------------------------
 hipError_t launch_lowrank_project(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,

@@ -6,13 +6,23 @@
 // sees A R S^-1.  The same kernel packs weights (one row per output
 // channel, multiplying by s instead of 1/s: FoldQuantVLA contribution 1).
 //
-// Work mapping.  A row of K elements is cut into 16-byte slots of 8
-// consecutive elements; slot s of a row lives in lane (s mod 64) of the
-// row's wave group, chunk s / (64 * WPR).  A 64-element Hadamard block is
-// therefore 8 consecutive lanes: butterfly stages 1, 2, 4 run inside a
-// lane's registers and stages 8, 16, 32 across lanes (xor 1, 2, 4).  The
-// whole row stays in registers, so the per-row absolute maximum needs no
-// second read of HBM.  WPR (waves per row) is 1 for many rows, 4 for few.
+// Work mapping.  A row of K elements is cut into slots of 16 consecutive
+// elements; slot s of a row lives in lane (s mod 64) of the row's wave
+// group, chunk s / (64 * WPR).  A 64-element Hadamard block is one quad of
+// lanes: butterfly stages 1, 2, 4, 8 run inside a lane's registers, stages
+// 16 and 32 across the quad (DPP quad permutes, xor 1 and xor 2).  An
+// NVFP4 scale block (16 elements) is exactly one lane.  The whole row stays
+// in registers, so the per-row absolute maximum needs no second HBM read.
+// WPR (waves per row) is 1 for many rows, 4 for few.
+//
+// Exactness.  Every value the quantizer decides on is the one the fp32
+// definition gives: the butterflies are the same additions in the same
+// order (a cross-lane stage computes own + c * partner with c = +-1, an
+// exact negation, so the upper lane holds the negated sum; the sign is
+// tracked per lane and folded into the final 1/8).  Quotients y / step use
+// a correctly rounded reciprocal r = RN(1/step) per row or block and two
+// Markstein corrections, q <- q + (y - step*q) * r, which give RN(y / step)
+// for normal operands; steps below 2^-80 take the plain IEEE division.
 #include "device_common.h"
 #include "launch.h"
 
@@ -34,32 +44,46 @@ struct QuantArgs {
 
 enum { MODE_INT4 = 0, MODE_INT8 = 1, MODE_NVFP4 = 2, MODE_AMAX = 3 };
 
+constexpr float kTinyStep = 8.271806125530277e-25f;  // 2^-80
+
+// RN(a / b) given r = RN(1 / b), for b >= 2^-80 and finite a.
+__device__ __forceinline__ float div_rn(float a, float b, float r) {
+  float q = a * r;
+  float t = __builtin_fmaf(-b, q, a);
+  q = __builtin_fmaf(t, r, q);
+  t = __builtin_fmaf(-b, q, a);
+  return __builtin_fmaf(t, r, q);
+}
+
 template <bool BF16IN>
-__device__ __forceinline__ void load_slot(const void* rowp, int s, float (&v)[8]) {
+__device__ __forceinline__ void load_slot(const void* rowp, int s, float (&v)[16]) {
   if constexpr (BF16IN) {
-    uint4 d = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(rowp) + s * 8);
-    uint32_t w[4] = {d.x, d.y, d.z, d.w};
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(rowp) + s * 16);
+    const uint4 d0 = p[0], d1 = p[1];
+    const uint32_t w[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(rowp) + s * 8);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(rowp) + s * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = p[i];
+      v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+    }
   }
 }
 
-// Stages h = 1, 2, 4 inside the 8 registers of one slot.
-__device__ __forceinline__ void fwht8_local(float (&v)[8]) {
+// Stages h = 1, 2, 4, 8 inside the 16 registers of one slot.
+__device__ __forceinline__ void fwht16_local(float (&v)[16]) {
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
+  for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 16; ++j) {
       if ((j & h) == 0) {
-        float a = v[j], b = v[j + h];
+        const float a = v[j], b = v[j + h];
         v[j] = a + b;
         v[j + h] = a - b;
       }
@@ -67,18 +91,29 @@ __device__ __forceinline__ void fwht8_local(float (&v)[8]) {
   }
 }
 
-// Stages h = 8, 16, 32: partner slot is lane ^ m (m = 1, 2, 4).  The lane
-// holding index j keeps a + b, the lane holding j + h keeps a - b.
-__device__ __forceinline__ void fwht8_cross(float (&v)[8], int lane) {
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Stages h = 16 (partner lane ^ 1) and 32 (lane ^ 2).  Each lane computes
+// own + c * partner with c = -1 in the lane that holds the upper index, so
+// that lane stores the negated difference; the returned factor is the sign
+// every value of this lane now carries.
+__device__ __forceinline__ float fwht16_cross(float (&v)[16], int lane) {
+  const float c1 = (lane & 1) ? -1.f : 1.f;
+  const float c2 = (lane & 2) ? -1.f : 1.f;
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
-    const bool upper = (lane & m) != 0;
+  for (int j = 0; j < 16; ++j) v[j] = __builtin_fmaf(c1, quad_perm<0xB1>(v[j]), v[j]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float p = __shfl_xor(v[j], m);
-      v[j] = upper ? (p - v[j]) : (v[j] + p);
-    }
-  }
+  for (int j = 0; j < 16; ++j) v[j] = __builtin_fmaf(c2, quad_perm<0x4E>(v[j]), v[j]);
+  return c1 * c2;
+}
+
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
 }
 
 template <int MODE, bool BF16IN, int NC, int WPR>
@@ -86,33 +121,35 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
   constexpr int QMAX = MODE == MODE_INT4 ? 7 : 127;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int rows_per_block = 4 / WPR;
-  const int sub = WPR == 1 ? 0 : wave;            // wave index inside the row group
-  const int grp = WPR == 1 ? wave : 0;            // row group inside the block
-  const int nslots = a.K >> 3;
+  constexpr int RPB = 4 / WPR;                      // rows per block
+  const int sub = WPR == 1 ? 0 : wave;              // wave index inside the row group
+  const int grp = WPR == 1 ? wave : 0;              // row group inside the block
+  const int nslots = a.K >> 4;
   const bool has_scale = a.scale != nullptr;
   const size_t esz = BF16IN ? 2 : 4;
   __shared__ float red[4];
 
-  float sc[NC][8];
+  float sc[NC][16];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int s = (c * WPR + sub) * 64 + lane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sc[c][i] = 1.0f;
+    for (int i = 0; i < 16; ++i) sc[c][i] = 1.0f;
     if (has_scale && s < nslots) {
-      const float4* p = reinterpret_cast<const float4*>(a.scale + s * 8);
-      float4 u = p[0], w = p[1];
-      sc[c][0] = u.x; sc[c][1] = u.y; sc[c][2] = u.z; sc[c][3] = u.w;
-      sc[c][4] = w.x; sc[c][5] = w.y; sc[c][6] = w.z; sc[c][7] = w.w;
+      const float4* p = reinterpret_cast<const float4*>(a.scale + s * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 u = p[i];
+        sc[c][4 * i] = u.x; sc[c][4 * i + 1] = u.y; sc[c][4 * i + 2] = u.z; sc[c][4 * i + 3] = u.w;
+      }
     }
   }
+  const float rg = MODE == MODE_NVFP4 ? 1.0f / a.g : 1.0f;   // RN(1/g), IEEE division
 
   float tmax = 0.f;  // MODE_AMAX: running max over this wave's rows
-  for (int64_t row = (int64_t)blockIdx.x * rows_per_block + grp; row < a.R;
-       row += (int64_t)gridDim.x * rows_per_block) {
+  for (int64_t row = (int64_t)blockIdx.x * RPB + grp; row < a.R; row += (int64_t)gridDim.x * RPB) {
     const char* rowp = reinterpret_cast<const char*>(a.x) + (size_t)row * a.ldx * esz;
-    float v[NC][8];
+    float v[NC][16];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int s = (c * WPR + sub) * 64 + lane;
@@ -120,7 +157,7 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
         load_slot<BF16IN>(rowp, s, v[c]);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[c][i] = 0.f;
+        for (int i = 0; i < 16; ++i) v[c][i] = 0.f;
       }
     }
     // --- transform -------------------------------------------------------
@@ -128,17 +165,17 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
     for (int c = 0; c < NC; ++c) {
       if (a.order == 0 && has_scale) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[c][i] = v[c][i] * sc[c][i];
+        for (int i = 0; i < 16; ++i) v[c][i] = v[c][i] * sc[c][i];
       }
       if (a.rot) {
-        fwht8_local(v[c]);
-        fwht8_cross(v[c], lane);
+        fwht16_local(v[c]);
+        const float f = 0.125f * fwht16_cross(v[c], lane);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[c][i] = v[c][i] * 0.125f;
+        for (int i = 0; i < 16; ++i) v[c][i] = v[c][i] * f;
       }
       if (a.order == 1 && has_scale) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[c][i] = v[c][i] * sc[c][i];
+        for (int i = 0; i < 16; ++i) v[c][i] = v[c][i] * sc[c][i];
       }
     }
 
@@ -147,9 +184,8 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[c][i]));
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, __builtin_fabsf(v[c][i]));
+      m = wave_max(m);
       if constexpr (MODE == MODE_AMAX) {
         tmax = fmaxf(tmax, m);
         continue;
@@ -160,56 +196,86 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
           m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
           __syncthreads();
         }
-        const float step = m / (float)QMAX;
+        const float step = m / (float)QMAX;   // IEEE division
+        const bool fast = step >= kTinyStep;
+        const float rstep = fast ? 1.0f / step : 0.f;
         if (lane == 0 && sub == 0) reinterpret_cast<float*>(a.scales)[row] = step;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int s = (c * WPR + sub) * 64 + lane;
           if (s >= nslots) continue;
-          int q[8];
+          float t[16];
+          if (fast) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            float r = step > 0.f ? __builtin_rintf(v[c][i] / step) : 0.f;
-            r = fminf(fmaxf(r, (float)(-QMAX - 1)), (float)QMAX);
-            q[i] = (int)r;
-          }
-          if constexpr (MODE == MODE_INT4) {
-            uint32_t word = 0;
+            for (int i = 0; i < 16; ++i) t[i] = div_rn(v[c][i], step, rstep);
+          } else if (step > 0.f) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) word |= ((uint32_t)q[i] & 0xFu) << (4 * i);
-            *reinterpret_cast<uint32_t*>(a.codes + (size_t)row * (a.K >> 1) + s * 4) = word;
+            for (int i = 0; i < 16; ++i) t[i] = v[c][i] / step;
           } else {
-            uint32_t lo = 0, hi = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              lo |= ((uint32_t)q[i] & 0xFFu) << (8 * i);
-              hi |= ((uint32_t)q[i + 4] & 0xFFu) << (8 * i);
+            for (int i = 0; i < 16; ++i) t[i] = 0.f;
+          }
+          uint32_t q[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            q[i] = (uint32_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(t[i]), (float)(-QMAX - 1), (float)QMAX);
+          if constexpr (MODE == MODE_INT4) {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              w0 |= (q[i] & 0xFu) << (4 * i);
+              w1 |= (q[i + 8] & 0xFu) << (4 * i);
             }
-            *reinterpret_cast<uint2*>(a.codes + (size_t)row * a.K + s * 8) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = make_uint2(w0, w1);
+          } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              w[k] = (q[4 * k] & 0xFFu) | ((q[4 * k + 1] & 0xFFu) << 8) | ((q[4 * k + 2] & 0xFFu) << 16) |
+                     ((q[4 * k + 3] & 0xFFu) << 24);
+            *reinterpret_cast<uint4*>(a.codes + (size_t)row * a.K + s * 16) = make_uint4(w[0], w[1], w[2], w[3]);
           }
         }
       }
-    } else {  // NVFP4: one E4M3 scale per 16 elements = two neighbouring slots
+    } else {  // NVFP4: one E4M3 scale per slot (16 elements)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int s = (c * WPR + sub) * 64 + lane;
+        if (s >= nslots) continue;
         float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[c][i]));
-        m = fmaxf(m, __shfl_xor(m, 1));
-        if (s >= nslots) continue;
-        const float sb = m / 6.0f;
-        const uint32_t e = f32_to_e4m3_sat(sb / a.g);
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, __builtin_fabsf(v[c][i]));
+        const float sb = m / 6.0f;                                          // IEEE division
+        const float sv = a.g >= kTinyStep ? div_rn(sb, a.g, rg) : sb / a.g;  // RN(sb / g)
+        const uint32_t e = f32_to_e4m3_sat(sv);
         const float S = e4m3_to_f32(e) * a.g;
-        uint32_t word = 0;
+        uint32_t w[2] = {0u, 0u};
+        if (S > 0.f) {
+          const bool fast = S >= kTinyStep;
+          const float rS = 1.0f / S;                                         // IEEE division
+          float q[16];
+          if (fast) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t cd = S > 0.f ? f32_to_e2m1_sat(v[c][i] / S) : 0u;
-          word |= cd << (4 * i);
+            for (int i = 0; i < 16; ++i) q[i] = div_rn(v[c][i], S, rS);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) q[i] = v[c][i] / S;
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint32_t d = 0;
+            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 0], q[8 * h + 1], 1.0f, 0);
+            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 2], q[8 * h + 3], 1.0f, 1);
+            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 4], q[8 * h + 5], 1.0f, 2);
+            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 6], q[8 * h + 7], 1.0f, 3);
+            // the converter writes -0 as 0x8; the packed format uses +0
+            const uint32_t mag = d & 0x77777777u;
+            const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;
+            w[h] = mag | (d & nz);
+          }
         }
-        *reinterpret_cast<uint32_t*>(a.codes + (size_t)row * (a.K >> 1) + s * 4) = word;
-        if ((s & 1) == 0)
-          reinterpret_cast<uint8_t*>(a.scales)[(size_t)row * (a.K >> 4) + (s >> 1)] = (uint8_t)e;
+        *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = make_uint2(w[0], w[1]);
+        reinterpret_cast<uint8_t*>(a.scales)[(size_t)row * (a.K >> 4) + s] = (uint8_t)e;
       }
     }
   }
@@ -225,20 +291,18 @@ __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
 
 template <int MODE, bool BF16IN, int WPR>
 static hipError_t launch_nc(int nc, dim3 grid, hipStream_t st, const QuantArgs& a) {
-#define W4A4_NC_CASE(N)                                                              \
-  case N:                                                                           \
-    hipLaunchKernelGGL((quant_rows_kernel<MODE, BF16IN, N, WPR>), grid, dim3(256), 0, st, a); \
+#define W4A4_NC_CASE(N)                                                                         \
+  case N:                                                                                      \
+    hipLaunchKernelGGL((quant_rows_kernel<MODE, BF16IN, N, WPR>), grid, dim3(256), 0, st, a);  \
     break;
   switch (nc) {
     W4A4_NC_CASE(1)
     W4A4_NC_CASE(2)
     W4A4_NC_CASE(3)
     W4A4_NC_CASE(4)
+    W4A4_NC_CASE(5)
     W4A4_NC_CASE(6)
     W4A4_NC_CASE(8)
-    W4A4_NC_CASE(10)
-    W4A4_NC_CASE(12)
-    W4A4_NC_CASE(16)
     default:
       return hipErrorInvalidValue;
   }
@@ -247,27 +311,28 @@ static hipError_t launch_nc(int nc, dim3 grid, hipStream_t st, const QuantArgs& 
 }
 
 static int round_nc(int nc) {
-  const int allowed[] = {1, 2, 3, 4, 6, 8, 10, 12, 16};
+  const int allowed[] = {1, 2, 3, 4, 5, 6, 8};
   for (int v : allowed)
     if (nc <= v) return v;
   return -1;
 }
 
-// Largest K a single launch supports: 16 chunks x 64 lanes x 8 elements x 4 waves.
-int64_t quant_max_k() { return 16LL * 64 * 8 * 4; }
+// Largest K a single launch supports: 8 chunks x 64 lanes x 16 elements x 4 waves.
+int64_t quant_max_k() { return 8LL * 64 * 16 * 4; }
 
 hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int64_t K, int64_t ldx,
-                           const float* scale, float g, int rot, int order, void* codes,
-                           void* scales, float* amax_out, hipStream_t st) {
+                           const float* scale, float g, int rot, int order, void* codes, void* scales,
+                           float* amax_out, hipStream_t st) {
   QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, amax_out};
-  const int64_t nslots = K / 8;
-  // One wave per row when that already gives enough waves and fits in registers.
-  int wpr = (R >= 2048 && nslots <= 16 * 64) ? 1 : 4;
-  int nc = round_nc((int)((nslots + 64 * wpr - 1) / (64 * wpr)));
+  const int64_t nslots = K / 16;
+  // One wave per row when there are many rows and the row fits five chunks
+  // per lane (the factors then stay in registers); else four waves per row.
+  const int wpr = (R >= 1024 && nslots <= 5 * 64) ? 1 : 4;
+  const int nc = round_nc((int)((nslots + 64 * wpr - 1) / (64 * wpr)));
   if (nc < 0) return hipErrorInvalidValue;
   const int rows_per_block = 4 / wpr;
   int64_t blocks = (R + rows_per_block - 1) / rows_per_block;
-  const int64_t cap = 256 * 8;  // persistent-style cap: 8 blocks per CU
+  const int64_t cap = 256 * 8;  // grid-stride beyond 8 blocks per CU
   if (mode == MODE_AMAX) {
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, (uint32_t*)amax_out, (size_t)1);
   }
@@ -287,15 +352,6 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   W4A4_DISPATCH(MODE_AMAX)
 #undef W4A4_DISPATCH
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
-  size_t n = bytes / 4;
-  if (n == 0) return hipSuccess;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint32_t*)p, n);
-  return hipGetLastError();
 }
 
 }  // namespace w4a4

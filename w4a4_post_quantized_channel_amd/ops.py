@@ -26,8 +26,8 @@ ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
 ABI_VERSION = 1
 
 EXPORTS = ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "lowrank_add",
-           "w4a4_lowrank_project", "w4a4_transform_amax", "w4a4_workspace_size",
-           "w4a4_workspace_init", "w4a4_status_string", "w4a4_last_error", "w4a4_abi_version"]
+           "w4a4_lowrank_project", "w4a4_transform_amax", "w4a4_workspace_size", "w4a4_status_string",
+           "w4a4_last_error", "w4a4_abi_version"]
 
 
 class QDesc(ctypes.Structure):
@@ -59,11 +59,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pack_weights": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
         "w4a4_linear": [vp, vp, vp, vp, i64, i64, i64, i32, f32, br, vp, i32, i64, vp, sz, vp],
         "w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
+        "w4a4_workspace_size": [i64, i64, i64, i32],
         "lowrank_add": [vp, i64, i64, i64, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp],
         "w4a4_lowrank_project": [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp],
         "w4a4_transform_amax": [vp, i32, i64, i64, i64, vp, qd, vp, vp],
-        "w4a4_workspace_size": [i64, i64, i64, i32],
-        "w4a4_workspace_init": [vp, sz, vp],
         "w4a4_status_string": [ctypes.c_int],
         "w4a4_last_error": [],
         "w4a4_abi_version": [],
@@ -186,18 +185,9 @@ def workspace_size(M: int, N: int, K: int, fmt: str) -> int:
     return int(LIB.w4a4_workspace_size(M, N, K, FMTS[fmt]))
 
 
-def workspace_init(ws: torch.Tensor, stream=None):
-    _check("w4a4_workspace_init", LIB.w4a4_workspace_init(_ptr(ws), ws.numel() * ws.element_size(),
-                                                          _stream(stream)))
-
-
-def make_workspace(M: int, N: int, K: int, fmt: str, device="cuda", stream=None) -> Optional[torch.Tensor]:
+def make_workspace(M: int, N: int, K: int, fmt: str, device="cuda") -> Optional[torch.Tensor]:
     n = workspace_size(M, N, K, fmt)
-    if n == 0:
-        return None
-    ws = torch.empty(n, dtype=torch.uint8, device=device)
-    workspace_init(ws, stream)
-    return ws
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def _linear(fn: str, fmt: str, a_codes, a_scales, w_codes, w_scales, K: int, *, alpha=1.0,
@@ -208,8 +198,8 @@ def _linear(fn: str, fmt: str, a_codes, a_scales, w_codes, w_scales, K: int, *, 
     if y is None:
         y = torch.empty((M, N), dtype=y_dtype, device=a_codes.device)
     br = branch if branch is not None else branch_desc(None, None)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     tail = (ctypes.byref(br), _ptr(y), _dtype_code(y), y.stride(0), _ptr(workspace), ws_bytes, _stream(stream))
     if fn == "w8a8_linear":
         st = LIB.w8a8_linear(*args, float(alpha), *tail)

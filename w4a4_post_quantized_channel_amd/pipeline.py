@@ -38,8 +38,10 @@ class QuantizedLinear:
 
     def __init__(self, w: torch.Tensor, s: Optional[torch.Tensor], inv_s: Optional[torch.Tensor],
                  fmt: str = "int4", *, fwht_block: int = 64, order: str = "smooth_then_rotate",
-                 branch: Optional[dict] = None, y_dtype=torch.bfloat16, stream=None):
+                 branch: Optional[dict] = None, y_dtype=torch.bfloat16, use_workspace: bool = True,
+                 stream=None):
         self.fmt, self.fwht_block, self.order = fmt, fwht_block, order
+        self.use_workspace = use_workspace
         self.N, self.K = w.shape
         self.inv_s = inv_s
         self.y_dtype = y_dtype
@@ -77,9 +79,9 @@ class QuantizedLinear:
                 r = self.branch["lw"].shape[1]
                 width = 2 * r if self.branch["kind"] == "lowrank" else r
                 br_a = torch.empty((M, width), dtype=torch.bfloat16, device=device)
-            ws = ops.make_workspace(M, self.N, self.K, self.fmt, device=device)
             y = torch.empty((M, self.N), dtype=self.y_dtype, device=device)
-            b = {"codes": codes, "scales": scales, "br_a": br_a, "ws": ws, "y": y}
+            ws = ops.make_workspace(M, self.N, self.K, self.fmt, device=device) if self.use_workspace else None
+            b = {"codes": codes, "scales": scales, "br_a": br_a, "y": y, "ws": ws}
             self._bufs[M] = b
         return b
 
@@ -128,12 +130,12 @@ def case_to_device(case, device="cuda"):
     return t
 
 
-def build_layer(case, device="cuda", order="smooth_then_rotate", calibrate=True) -> tuple:
+def build_layer(case, device="cuda", order="smooth_then_rotate", calibrate=True, use_workspace=True) -> tuple:
     """QuantizedLinear + device inputs for a ``workloads.Case``."""
     t = case_to_device(case, device)
     y_dtype = torch.float32 if case.y_dtype == "f32" else torch.bfloat16
     layer = QuantizedLinear(t["w"], t["s"], t["inv_s"], case.fmt, fwht_block=case.fwht_block, order=order,
-                            branch=t["branch"], y_dtype=y_dtype)
+                            branch=t["branch"], y_dtype=y_dtype, use_workspace=use_workspace)
     if calibrate:
         layer.calibrate(t["x"])
     return layer, t
