@@ -185,8 +185,9 @@ int w8a8_linear(const void* a_codes, const void* a_scales,
  * y += x[:, idx] W_idx^T (Q-WAM abstract: 16-bit low-rank branch as a dense
  * product; QuantWAMs sec. 3.1 / 4.2: kept channels on a BF16 path).
  *  x    M x K bf16, row stride ldx.
- *  l1   bf16 K x r (row stride r) for the low-rank form, or NULL when idx
- *       is given.
+ *  l1t  bf16 r x K (row stride K, 16-byte aligned): L1 transposed, one
+ *       K-contiguous row per rank component, for the low-rank form; NULL
+ *       when idx is given.
  *  idx  int32[r] channel indices (0 <= idx < K) for the kept-channel form,
  *       or NULL.  Exactly one of l1 / idx is non-NULL.
  *  lw   bf16 N x r, row stride ldlw: L2 transposed, or W[:, idx].
@@ -195,17 +196,18 @@ int w8a8_linear(const void* a_codes, const void* a_scales,
  *  y in fp32, one rounding to y_dtype.
  */
 int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx,
-                const void* l1, const int32_t* idx, const void* lw, int64_t ldlw,
+                const void* l1t, const int32_t* idx, const void* lw, int64_t ldlw,
                 int64_t r, int64_t N, void* y, int32_t y_dtype, int64_t ldy,
                 void* stream);
 
 /* w4a4_lowrank_project -- first half of the branch, producing the
- * w4a4_branch ``a`` operand: for l1 != NULL, t = x L1 in fp32 written as
- * bf16 hi = bf16(t) and lo = bf16(t - hi) (out is M x 2r: columns [0, r)
- * hi, [r, 2r) lo); for idx != NULL, out = x[:, idx] (M x r, exact).
+ * w4a4_branch ``a`` operand: for l1t != NULL (L1 transposed, bf16 r x K),
+ * t = x L1 in fp32 written as bf16 hi = bf16(t) and lo = bf16(t - hi) (out
+ * is M x 2r: columns [0, r) hi, [r, 2r) lo); for idx != NULL,
+ * out = x[:, idx] (M x r, exact).
  *  x bf16 M x K (row stride ldx); out bf16 with row stride ldo. */
 int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx,
-                         const void* l1, const int32_t* idx, int64_t r,
+                         const void* l1t, const int32_t* idx, int64_t r,
                          void* out, int64_t ldo, void* stream);
 
 /* w4a4_transform_amax -- max |transform(x)| over a whole R x K tensor,

@@ -177,7 +177,7 @@ def test_lowrank_add_standalone(ops, pipe):
                 y0 = WL.bf16_round(y0)
             y = torch.from_numpy(y0).to("cuda", ydt)
             if kind == "lowrank":
-                ops.lowrank_add(t["x"], y, br["lw"], l1=br["l1"])
+                ops.lowrank_add(t["x"], y, br["lw"], l1t=br["l1t"])
                 add = O.lowrank_branch(case.x, case.branch["l1"], case.branch["lw"])
             else:
                 ops.lowrank_add(t["x"], y, br["lw"], idx=br["idx"])
@@ -188,7 +188,7 @@ def test_lowrank_add_standalone(ops, pipe):
 def test_lowrank_project(ops, pipe):
     case = WL.linear_case(50, 8, 512, seed=41, lowrank=24)
     t = pipe.case_to_device(case)
-    out = _np(ops.lowrank_project(t["x"], l1=t["branch"]["l1"]))
+    out = _np(ops.lowrank_project(t["x"], l1t=t["branch"]["l1t"]))
     T = case.x.astype(np.float64) @ case.branch["l1"].astype(np.float64)
     recon = out[:, :24].astype(np.float64) + out[:, 24:].astype(np.float64)
     assert np.max(np.abs(recon - T)) <= 2.0 ** -15 * np.max(np.abs(T))

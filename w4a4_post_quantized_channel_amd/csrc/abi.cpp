@@ -142,7 +142,7 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
   g.y = y; g.y_dtype = y_dtype; g.ldy = ldy;
   hipError_t e;
   if (fmt == W4A4_FMT_NVFP4) {
-    e = w4a4::launch_gemm_nvfp4(g, (hipStream_t)stream);
+    e = w4a4::launch_gemm_tile(2, g, (hipStream_t)stream);
   } else {
     const size_t need = w4a4::gemm_int_workspace(fmt, M, N, K);
     if (workspace && ws_bytes < need)
@@ -184,27 +184,27 @@ int w8a8_linear(const void* a_codes, const void* a_scales, const void* w_codes, 
                     y_dtype, ldy, workspace, workspace_bytes, stream);
 }
 
-static int check_lowrank(const char* fn, const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1,
+static int check_lowrank(const char* fn, const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t,
                          const int32_t* idx, int64_t r) {
   if (M < 0 || K <= 0) return fail(W4A4_ERR_INVALID_ARG, "%s: bad sizes", fn);
   if (r <= 0 || r > W4A4_MAX_BRANCH) return fail(W4A4_ERR_INVALID_ARG, "%s: r=%lld outside [1, %d]", fn, (long long)r, W4A4_MAX_BRANCH);
-  if ((l1 == nullptr) == (idx == nullptr)) return fail(W4A4_ERR_INVALID_ARG, "%s: exactly one of l1 / idx", fn);
+  if ((l1t == nullptr) == (idx == nullptr)) return fail(W4A4_ERR_INVALID_ARG, "%s: exactly one of l1t / idx", fn);
   if (K % 8 != 0) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K not a multiple of 8", fn);
   if (ldx < K) return fail(W4A4_ERR_INVALID_ARG, "%s: ldx < K", fn);
   if (M > 0) {
     if (!x) return fail(W4A4_ERR_INVALID_ARG, "%s: x is NULL", fn);
     if (!aligned(x, 16) || ldx % 8 != 0) return fail(W4A4_ERR_MISALIGNED, "%s: x / ldx not 16-byte aligned", fn);
     if (idx && !aligned(idx, 4)) return fail(W4A4_ERR_MISALIGNED, "%s: idx misaligned", fn);
-    if (l1 && !aligned(l1, 2)) return fail(W4A4_ERR_MISALIGNED, "%s: l1 misaligned", fn);
+    if (l1t && !aligned(l1t, 16)) return fail(W4A4_ERR_MISALIGNED, "%s: l1t not 16-byte aligned", fn);
   }
   return ok();
 }
 
-int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1, const int32_t* idx,
+int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t, const int32_t* idx,
                 const void* lw, int64_t ldlw, int64_t r, int64_t N, void* y, int32_t y_dtype, int64_t ldy,
                 void* stream) {
   const char* fn = "lowrank_add";
-  int st = check_lowrank(fn, x, M, K, ldx, l1, idx, r);
+  int st = check_lowrank(fn, x, M, K, ldx, l1t, idx, r);
   if (st != W4A4_OK) return st;
   if (N < 0) return fail(W4A4_ERR_INVALID_ARG, "%s: N < 0", fn);
   if (y_dtype != W4A4_DT_F32 && y_dtype != W4A4_DT_BF16)
@@ -214,21 +214,21 @@ int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1
   if (!lw || !y) return fail(W4A4_ERR_INVALID_ARG, "%s: NULL operand", fn);
   if (!aligned(lw, 2) || !aligned(y, dt_size(y_dtype))) return fail(W4A4_ERR_MISALIGNED, "%s: lw / y misaligned", fn);
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: too large", fn);
-  hipError_t e = w4a4::launch_lowrank_add((const uint16_t*)x, M, K, ldx, (const uint16_t*)l1, idx, (int)r,
+  hipError_t e = w4a4::launch_lowrank_add((const uint16_t*)x, M, K, ldx, (const uint16_t*)l1t, idx, (int)r,
                                           (const uint16_t*)lw, ldlw, N, y, y_dtype, ldy, (hipStream_t)stream);
   return launch_status(e, fn);
 }
 
-int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1, const int32_t* idx,
+int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t, const int32_t* idx,
                          int64_t r, void* out, int64_t ldo, void* stream) {
   const char* fn = "w4a4_lowrank_project";
-  int st = check_lowrank(fn, x, M, K, ldx, l1, idx, r);
+  int st = check_lowrank(fn, x, M, K, ldx, l1t, idx, r);
   if (st != W4A4_OK) return st;
-  if (ldo < (l1 ? 2 * r : r)) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo too small", fn);
+  if (ldo < (l1t ? 2 * r : r)) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo too small", fn);
   if (M == 0) return ok();
   if (!out || !aligned(out, 2)) return fail(W4A4_ERR_INVALID_ARG, "%s: out NULL or misaligned", fn);
   if (M > INT32_MAX || K > INT32_MAX) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: too large", fn);
-  hipError_t e = w4a4::launch_lowrank_project((const uint16_t*)x, M, K, ldx, (const uint16_t*)l1, idx, (int)r,
+  hipError_t e = w4a4::launch_lowrank_project((const uint16_t*)x, M, K, ldx, (const uint16_t*)l1t, idx, (int)r,
                                               (uint16_t*)out, ldo, (hipStream_t)stream);
   return launch_status(e, fn);
 }

@@ -4,8 +4,9 @@
 // product x[:, idx] W[:, idx]^T of the QuantWAMs BF16 bypass (sec. 3.1
 // top-K mask, sec. 4.2).
 //
-//  * project: t = x L1 (fp32, v_mfma_f32_16x16x32_bf16, K split over the
-//    four waves of a 16-row block and summed in LDS), emitted as the bf16
+//  * project: t = x L1 (fp32, v_mfma_f32_16x16x32_bf16 with L1 given
+//    transposed so both operands are K-contiguous, K split over the four
+//    waves of a 16-row block and summed in LDS), emitted as the bf16
 //    hi/lo pair the GEMM epilogue consumes; or the gather x[:, idx].
 //  * lowrank_add: the same projection kept in fp32 in LDS, then
 //    y[m, n] += sum_j t[m, j] lw[n, j] on the vector ALUs, one rounding to
@@ -18,10 +19,11 @@ namespace w4a4 {
 constexpr int kRows = 16;
 
 // Partial t[16 x r] over this wave's K range, r <= 128 (TJ = r/16 tiles).
+// l1t is L1 transposed (r rows of K), so both operands are K-contiguous.
 // Result left in `part` as 16x16 MFMA accumulators.
 template <int TJ>
 __device__ __forceinline__ void project_tile(const uint16_t* x, int64_t ldx, int M, int K,
-                                             const uint16_t* l1, int r, int m0, int k_begin,
+                                             const uint16_t* l1t, int r, int m0, int k_begin,
                                              int k_end, int lane, v4f (&part)[TJ]) {
   const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
@@ -35,12 +37,8 @@ __device__ __forceinline__ void project_tile(const uint16_t* x, int64_t ldx, int
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int col = j * 16 + lr;
-      uint16_t e[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        e[t] = (col < r && kc + t < K) ? l1[(int64_t)(kc + t) * r + col] : (uint16_t)0;
-      const uint4 bd = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                                  e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
+      uint4 bd = make_uint4(0, 0, 0, 0);
+      if (col < r && kc < K) bd = *reinterpret_cast<const uint4*>(l1t + (int64_t)col * K + kc);
       part[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(v8bf, bd), part[j], 0, 0, 0);
     }
   }
@@ -48,14 +46,14 @@ __device__ __forceinline__ void project_tile(const uint16_t* x, int64_t ldx, int
 
 // t (16 x r, fp32) into LDS: sum of the four waves' partials.
 template <int TJ>
-__device__ void project_block(const uint16_t* x, int64_t ldx, int M, int K, const uint16_t* l1,
+__device__ void project_block(const uint16_t* x, int64_t ldx, int M, int K, const uint16_t* l1t,
                               const int32_t* idx, int r, int m0, float* sT /*[4][16][128]*/) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  if (l1) {
+  if (l1t) {
     const int kq = ((K + 127) / 128) * 32;  // K range per wave, multiple of 32
     v4f part[TJ];
-    project_tile<TJ>(x, ldx, M, K, l1, r, m0, wave * kq, min(K, (wave + 1) * kq), lane, part);
+    project_tile<TJ>(x, ldx, M, K, l1t, r, m0, wave * kq, min(K, (wave + 1) * kq), lane, part);
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -80,16 +78,16 @@ __device__ void project_block(const uint16_t* x, int64_t ldx, int M, int K, cons
 
 template <int TJ>
 __global__ void __launch_bounds__(256) project_kernel(const uint16_t* x, int64_t ldx, int M, int K,
-                                                      const uint16_t* l1, const int32_t* idx, int r,
+                                                      const uint16_t* l1t, const int32_t* idx, int r,
                                                       uint16_t* out, int64_t ldo) {
   __shared__ float sT[64 * 128];
   const int m0 = blockIdx.x * kRows;
-  project_block<TJ>(x, ldx, M, K, l1, idx, r, m0, sT);
+  project_block<TJ>(x, ldx, M, K, l1t, idx, r, m0, sT);
   for (int e = threadIdx.x; e < 16 * r; e += 256) {
     const int row = e / r, col = e % r, m = m0 + row;
     if (m >= M) continue;
     const float t = sT[row * 128 + col];
-    if (l1) {
+    if (l1t) {
       const uint32_t hi = f32_to_bf16_bits(t);
       const float lo = t - bf16_bits_to_f32(hi);
       out[(int64_t)m * ldo + col] = (uint16_t)hi;
@@ -102,12 +100,12 @@ __global__ void __launch_bounds__(256) project_kernel(const uint16_t* x, int64_t
 
 template <int TJ>
 __global__ void __launch_bounds__(256) lowrank_add_kernel(const uint16_t* x, int64_t ldx, int M, int K,
-                                                          const uint16_t* l1, const int32_t* idx, int r,
+                                                          const uint16_t* l1t, const int32_t* idx, int r,
                                                           const uint16_t* lw, int64_t ldlw, int N,
                                                           void* y, int y_dtype, int64_t ldy) {
   __shared__ float sT[64 * 128];
   const int m0 = blockIdx.x * kRows;
-  project_block<TJ>(x, ldx, M, K, l1, idx, r, m0, sT);
+  project_block<TJ>(x, ldx, M, K, l1t, idx, r, m0, sT);
   const int rows = min(kRows, M - m0);
   for (int n = blockIdx.y * 256 + threadIdx.x; n < N; n += gridDim.y * 256) {
     float acc[kRows];
@@ -145,17 +143,17 @@ __global__ void __launch_bounds__(256) lowrank_add_kernel(const uint16_t* x, int
   }
 
 hipError_t launch_lowrank_project(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                  const uint16_t* l1, const int32_t* idx, int r, uint16_t* out,
+                                  const uint16_t* l1t, const int32_t* idx, int r, uint16_t* out,
                                   int64_t ldo, hipStream_t st) {
   dim3 grid((unsigned)((M + kRows - 1) / kRows));
 #define W4A4_PROJ(T) \
-  hipLaunchKernelGGL((project_kernel<T>), grid, dim3(256), 0, st, x, ldx, (int)M, (int)K, l1, idx, r, out, ldo)
+  hipLaunchKernelGGL((project_kernel<T>), grid, dim3(256), 0, st, x, ldx, (int)M, (int)K, l1t, idx, r, out, ldo)
   W4A4_TJ_SWITCH(r, W4A4_PROJ)
 #undef W4A4_PROJ
   return hipGetLastError();
 }
 
-hipError_t launch_lowrank_add(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* l1,
+hipError_t launch_lowrank_add(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* l1t,
                               const int32_t* idx, int r, const uint16_t* lw, int64_t ldlw, int64_t N,
                               void* y, int y_dtype, int64_t ldy, hipStream_t st) {
   const int64_t mb = (M + kRows - 1) / kRows;
@@ -164,7 +162,7 @@ hipError_t launch_lowrank_add(const uint16_t* x, int64_t M, int64_t K, int64_t l
   if (nb > 4) nb = mb >= 256 ? 1 : (nb < 8 ? nb : 8);
   dim3 grid((unsigned)mb, (unsigned)nb);
 #define W4A4_ADD(T)                                                                                  \
-  hipLaunchKernelGGL((lowrank_add_kernel<T>), grid, dim3(256), 0, st, x, ldx, (int)M, (int)K, l1, idx, r, \
+  hipLaunchKernelGGL((lowrank_add_kernel<T>), grid, dim3(256), 0, st, x, ldx, (int)M, (int)K, l1t, idx, r, \
                      lw, ldlw, (int)N, y, y_dtype, ldy)
   W4A4_TJ_SWITCH(r, W4A4_ADD)
 #undef W4A4_ADD

@@ -49,4 +49,74 @@ __device__ __forceinline__ void store_out(void* y, int y_dtype, int64_t ldy, int
   }
 }
 
+// Epilogue of a wave's TI x TJ grid of 16x16 accumulator tiles, one
+// 16-column block at a time (keeps the live register set small):
+// dequantise (integer: fp32(fp32(acc) * sa[m]) * sw[n] * alpha, with acc
+// shifted right by 8 for the x16-widened int4 operands; float: acc *
+// alpha), add the bf16 branch, store.  acc[i][j] covers rows
+// m_base + 16 i + [0, 16) and columns n_base + 16 j + [0, 16).
+// y_dtype 2 writes the raw integer accumulators.
+template <int KIND /*0 int4, 1 int8, 2 float*/, typename AccT, int TI, int TJ>
+__device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
+                                               int lane) {
+  const int lr = lane & 15, lq = lane >> 4;
+  if constexpr (KIND != 2) {
+    if (g.y_dtype == 2) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m_base + i * 16 + lq * 4 + r, n = n_base + j * 16 + lr;
+            const int v = KIND == 0 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+            if (m < g.M && n < g.N) reinterpret_cast<int32_t*>(g.y)[(int64_t)m * g.ldy + n] = v;
+          }
+      return;
+    }
+  }
+  const float* sa = reinterpret_cast<const float*>(g.sa);
+  const float* sw = reinterpret_cast<const float*>(g.sw);
+  float sam[TI][4];
+  if constexpr (KIND != 2) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m_base + i * 16 + lq * 4 + r;
+        sam[i][r] = m < g.M ? sa[m] : 0.f;
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int n = n_base + j * 16 + lr;
+    v4f col[TI][1];
+    if constexpr (KIND != 2) {
+      const float swn = n < g.N ? sw[n] : 0.f;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = KIND == 0 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+          float v = (float)q * sam[i][r];
+          v = v * swn;
+          col[i][0][r] = v * g.alpha;
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) col[i][0][r] = acc[i][j][r] * g.alpha;
+    }
+    if (g.br.r > 0) branch_mfma<TI, 1>(col, g.br, g.M, g.N, m_base, n_base + j * 16, lane);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m_base + i * 16 + lq * 4 + r;
+        if (m < g.M && n < g.N) store_out(g.y, g.y_dtype, g.ldy, m, n, col[i][0][r]);
+      }
+  }
+}
+
 }  // namespace w4a4

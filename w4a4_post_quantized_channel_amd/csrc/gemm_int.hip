@@ -13,9 +13,8 @@
 // Both operands get the same lane permutation, so v_mfma_i32_16x16x64_i8
 // returns exactly 256 * sum(qa * qw); the epilogue shifts right by 8.
 //
-// Two kernels:
-//  * tile kernel (many tokens): BM x BN workgroup tile over four waves,
-//    K advanced 128 elements per step through a double-buffered LDS stage.
+// This file holds the few-token path; many tokens go to the shared tile
+// kernel (gemm_mfma.hip).
 //  * decode kernel (<= 64 tokens, weight streaming): 64 token rows x 64
 //    output channels per workgroup of four waves.  No LDS staging: each
 //    wave loads its MFMA operands straight from global memory with raw
@@ -38,180 +37,6 @@ constexpr int kBK = 128;  // K elements per main-loop step
 __device__ __forceinline__ v4i widen_int4(uint32_t lo, uint32_t hi) {
   return v4i{(int)((lo << 4) & 0xF0F0F0F0u), (int)(lo & 0xF0F0F0F0u), (int)((hi << 4) & 0xF0F0F0F0u),
              (int)(hi & 0xF0F0F0F0u)};
-}
-
-// Dequantise, add the branch, store.  acc[i][j] is the 16x16 tile whose
-// first row is m_base + 16 i and first column n_base + 16 j.
-template <bool INT4, int TI, int TJ>
-__device__ __forceinline__ void int_epilogue(v4i (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
-                                             int lane) {
-  const int lr = lane & 15, lq = lane >> 4;
-  if (g.y_dtype == 2) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m_base + i * 16 + lq * 4 + r, n = n_base + j * 16 + lr;
-          const int v = INT4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
-          if (m < g.M && n < g.N) reinterpret_cast<int32_t*>(g.y)[(int64_t)m * g.ldy + n] = v;
-        }
-    return;
-  }
-  const float* sa = reinterpret_cast<const float*>(g.sa);
-  const float* sw = reinterpret_cast<const float*>(g.sw);
-  v4f accf[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = n_base + j * 16 + lr;
-      const float swn = n < g.N ? sw[n] : 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m_base + i * 16 + lq * 4 + r;
-        const float sam = m < g.M ? sa[m] : 0.f;
-        const int q = INT4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
-        float v = (float)q * sam;
-        v = v * swn;
-        accf[i][j][r] = v * g.alpha;
-      }
-    }
-  if (g.br.r > 0) branch_mfma<TI, TJ>(accf, g.br, g.M, g.N, m_base, n_base, lane);
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m_base + i * 16 + lq * 4 + r, n = n_base + j * 16 + lr;
-        if (m < g.M && n < g.N) store_out(g.y, g.y_dtype, g.ldy, m, n, accf[i][j][r]);
-      }
-}
-
-// ---------------------------------------------------------------------------
-// Tile kernel
-// ---------------------------------------------------------------------------
-template <bool INT4, int BM, int BN, int WM, int WN>
-struct IntTile {
-  static constexpr int RB = INT4 ? kBK / 2 : kBK;   // bytes per row per step
-  static constexpr int PITCH = RB + 16;             // padded LDS row pitch
-  static constexpr int TI = WM / 16, TJ = WN / 16;
-  static constexpr int WAVES_N = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves per workgroup");
-  static constexpr int CH_A = BM * RB / 16;         // 16-byte chunks per stage
-  static constexpr int CH_B = BN * RB / 16;
-  static constexpr int LA = (CH_A + 255) / 256;
-  static constexpr int LB = (CH_B + 255) / 256;
-};
-
-template <bool INT4, int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(256) gemm_int_tile_kernel(GemmArgs g) {
-  using T = IntTile<INT4, BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * T::PITCH];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * T::PITCH];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int wm0 = (wave / T::WAVES_N) * WM, wn0 = (wave % T::WAVES_N) * WN;
-  const int64_t rowbytes = INT4 ? (g.K >> 1) : g.K;
-  const int ks0 = 0;
-  const int ks1 = (g.K + kBK - 1) / kBK;
-
-  v4i acc[T::TI][T::TJ];
-#pragma unroll
-  for (int i = 0; i < T::TI; ++i)
-#pragma unroll
-    for (int j = 0; j < T::TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(g.a + (int64_t)m0 * rowbytes,
-                                               (uint32_t)(min(BM, g.M - m0) * rowbytes));
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(g.w + (int64_t)n0 * rowbytes,
-                                               (uint32_t)(min(BN, g.N - n0) * rowbytes));
-  uint4 ra[T::LA], rb[T::LB];
-  auto gload = [&](int ks) {
-    const int64_t kb0 = (int64_t)ks * T::RB;
-#pragma unroll
-    for (int t = 0; t < T::LA; ++t) {
-      const int c = tid + t * 256;
-      const int r = c / (T::RB / 16), col = (c % (T::RB / 16)) * 16;
-      const bool ok = c < T::CH_A && kb0 + col < rowbytes;
-      ra[t] = buf_load16(rsA, ok ? (uint32_t)(r * rowbytes + kb0 + col) : kOOB);
-    }
-#pragma unroll
-    for (int t = 0; t < T::LB; ++t) {
-      const int c = tid + t * 256;
-      const int r = c / (T::RB / 16), col = (c % (T::RB / 16)) * 16;
-      const bool ok = c < T::CH_B && kb0 + col < rowbytes;
-      rb[t] = buf_load16(rsB, ok ? (uint32_t)(r * rowbytes + kb0 + col) : kOOB);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < T::LA; ++t) {
-      const int c = tid + t * 256;
-      if (c < T::CH_A) {
-        const int r = c / (T::RB / 16), col = (c % (T::RB / 16)) * 16;
-        *reinterpret_cast<uint4*>(&sA[buf][r * T::PITCH + col]) = ra[t];
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < T::LB; ++t) {
-      const int c = tid + t * 256;
-      if (c < T::CH_B) {
-        const int r = c / (T::RB / 16), col = (c % (T::RB / 16)) * 16;
-        *reinterpret_cast<uint4*>(&sB[buf][r * T::PITCH + col]) = rb[t];
-      }
-    }
-  };
-
-  const int lr = lane & 15, lq = lane >> 4;
-  if (ks0 < ks1) {
-    gload(ks0);
-    sstore(0);
-    __syncthreads();
-    for (int ks = ks0; ks < ks1; ++ks) {
-      const int buf = (ks - ks0) & 1;
-      if (ks + 1 < ks1) gload(ks + 1);
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {  // two 64-deep MFMA steps per stage
-        v4i af[T::TI], bfr[T::TJ];
-        if constexpr (INT4) {
-#pragma unroll
-          for (int i = 0; i < T::TI; ++i) {
-            const uint2 d = *reinterpret_cast<const uint2*>(
-                &sA[buf][(wm0 + i * 16 + lr) * T::PITCH + sub * 32 + lq * 8]);
-            af[i] = widen_int4(d.x, d.y);
-          }
-#pragma unroll
-          for (int j = 0; j < T::TJ; ++j) {
-            const uint2 d = *reinterpret_cast<const uint2*>(
-                &sB[buf][(wn0 + j * 16 + lr) * T::PITCH + sub * 32 + lq * 8]);
-            bfr[j] = widen_int4(d.x, d.y);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < T::TI; ++i)
-            af[i] = *reinterpret_cast<const v4i*>(
-                &sA[buf][(wm0 + i * 16 + lr) * T::PITCH + sub * 64 + lq * 16]);
-#pragma unroll
-          for (int j = 0; j < T::TJ; ++j)
-            bfr[j] = *reinterpret_cast<const v4i*>(
-                &sB[buf][(wn0 + j * 16 + lr) * T::PITCH + sub * 64 + lq * 16]);
-        }
-#pragma unroll
-        for (int i = 0; i < T::TI; ++i)
-#pragma unroll
-          for (int j = 0; j < T::TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (ks + 1 < ks1) sstore(buf ^ 1);
-      __syncthreads();
-    }
-  }
-
-  int_epilogue<INT4, T::TI, T::TJ>(acc, g, m0 + wm0, n0 + wn0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -312,7 +137,7 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     for (int j = 0; j < TJ; ++j) p[j] = __builtin_bit_cast(uint4, tot[0][j]);
     return;
   }
-  int_epilogue<INT4, 1, TJ>(tot, g, m0 + wave * 16, n0, lane);
+  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0 + wave * 16, n0, lane);
 }
 
 // One wave per (tile, row block): add the S partial tiles, then the epilogue.
@@ -343,7 +168,7 @@ __global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, 
 #pragma unroll
         for (int j = 0; j < TJ; ++j) tot[0][j] += __builtin_bit_cast(v4i, v[dz][j]);
   }
-  int_epilogue<INT4, 1, TJ>(tot, g, m0 + rb * 16, n0, lane);
+  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0 + rb * 16, n0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -400,17 +225,7 @@ hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes
     }
     return hipGetLastError();
   }
-  const int64_t tiles128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
-  if (tiles128 >= 256) {
-    dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, 1);
-    if (int4) hipLaunchKernelGGL((gemm_int_tile_kernel<true, 128, 128, 64, 64>), grid, dim3(256), 0, st, g);
-    else hipLaunchKernelGGL((gemm_int_tile_kernel<false, 128, 128, 64, 64>), grid, dim3(256), 0, st, g);
-  } else {
-    dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, 1);
-    if (int4) hipLaunchKernelGGL((gemm_int_tile_kernel<true, 64, 64, 32, 32>), grid, dim3(256), 0, st, g);
-    else hipLaunchKernelGGL((gemm_int_tile_kernel<false, 64, 64, 32, 32>), grid, dim3(256), 0, st, g);
-  }
-  return hipGetLastError();
+  return launch_gemm_tile(fmt, g, st);
 }
 
 }  // namespace w4a4

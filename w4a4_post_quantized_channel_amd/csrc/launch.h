@@ -40,14 +40,15 @@ struct GemmArgs {
 hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st);
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 
-hipError_t launch_gemm_nvfp4(GemmArgs g, hipStream_t st);
+// gemm_mfma.hip: many-token tile kernel, fmt 0 int4, 1 int8, 2 nvfp4
+hipError_t launch_gemm_tile(int fmt, GemmArgs g, hipStream_t st);
 
 // branch.hip ----------------------------------------------------------------
 hipError_t launch_lowrank_project(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                  const uint16_t* l1, const int32_t* idx, int r,
+                                  const uint16_t* l1t, const int32_t* idx, int r,
                                   uint16_t* out, int64_t ldo, hipStream_t st);
 hipError_t launch_lowrank_add(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                              const uint16_t* l1, const int32_t* idx, int r, const uint16_t* lw,
+                              const uint16_t* l1t, const int32_t* idx, int r, const uint16_t* lw,
                               int64_t ldlw, int64_t N, void* y, int y_dtype, int64_t ldy,
                               hipStream_t st);
 

@@ -219,37 +219,38 @@ def w8a8_linear(a_codes, a_scales, w_codes, w_scales, K: int, **kw):
     return _linear("w8a8_linear", "int8", a_codes, a_scales, w_codes, w_scales, K, **kw)
 
 
-def _check_branch_inputs(x, l1, idx, lw=None):
+def _check_branch_inputs(x, l1t, idx, lw=None):
     if x.dtype != torch.bfloat16:
         raise TypeError("the 16-bit branch takes bf16 activations")
-    if l1 is not None and l1.dtype != torch.bfloat16:
-        raise TypeError("l1 must be bf16")
+    if l1t is not None and (l1t.dtype != torch.bfloat16 or not l1t.is_contiguous()
+                            or l1t.shape[1] != x.shape[1]):
+        raise TypeError("l1t must be a contiguous bf16 r x K tensor (L1 transposed)")
     if idx is not None and idx.dtype != torch.int32:
         raise TypeError("idx must be int32")
     if lw is not None and lw.dtype != torch.bfloat16:
         raise TypeError("lw must be bf16")
 
 
-def lowrank_add(x: torch.Tensor, y: torch.Tensor, lw: torch.Tensor, *, l1: Optional[torch.Tensor] = None,
+def lowrank_add(x: torch.Tensor, y: torch.Tensor, lw: torch.Tensor, *, l1t: Optional[torch.Tensor] = None,
                 idx: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """y += (x L1) lw^T  or  y += x[:, idx] lw^T, in place."""
-    _check_branch_inputs(x, l1, idx, lw)
+    """y += (x L1) lw^T  or  y += x[:, idx] lw^T, in place (l1t = L1 transposed, r x K)."""
+    _check_branch_inputs(x, l1t, idx, lw)
     M, K, ldx = _rowmajor(x)
     N, r = lw.shape
-    _check("lowrank_add", LIB.lowrank_add(_ptr(x), M, K, ldx, _ptr(l1), _ptr(idx), _ptr(lw), lw.stride(0), r, N,
+    _check("lowrank_add", LIB.lowrank_add(_ptr(x), M, K, ldx, _ptr(l1t), _ptr(idx), _ptr(lw), lw.stride(0), r, N,
                                           _ptr(y), _dtype_code(y), y.stride(0), _stream(stream)))
     return y
 
 
-def lowrank_project(x: torch.Tensor, *, l1: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+def lowrank_project(x: torch.Tensor, *, l1t: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
                     out=None, stream=None) -> torch.Tensor:
     """The fused branch's ``a`` operand: [hi | lo] bf16 halves of x L1, or x[:, idx]."""
-    _check_branch_inputs(x, l1, idx)
+    _check_branch_inputs(x, l1t, idx)
     M, K, ldx = _rowmajor(x)
-    r = l1.shape[1] if l1 is not None else idx.shape[0]
-    width = 2 * r if l1 is not None else r
+    r = l1t.shape[0] if l1t is not None else idx.shape[0]
+    width = 2 * r if l1t is not None else r
     if out is None:
         out = torch.empty((M, width), dtype=torch.bfloat16, device=x.device)
-    _check("w4a4_lowrank_project", LIB.w4a4_lowrank_project(_ptr(x), M, K, ldx, _ptr(l1), _ptr(idx), r, _ptr(out),
+    _check("w4a4_lowrank_project", LIB.w4a4_lowrank_project(_ptr(x), M, K, ldx, _ptr(l1t), _ptr(idx), r, _ptr(out),
                                                             out.stride(0), _stream(stream)))
     return out

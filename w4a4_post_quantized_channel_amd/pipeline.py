@@ -32,7 +32,7 @@ class QuantizedLinear:
     s        K smoothing factors (weights multiplied by s, activations by
              inv_s), device fp32, or None.
     inv_s    K factors for the activations (fp32(1/s)), device, or None.
-    branch   None, {"kind": "lowrank", "l1": K x r bf16, "lw": N x r bf16}
+    branch   None, {"kind": "lowrank", "l1t": r x K bf16 (L1 transposed), "lw": N x r bf16}
              or {"kind": "outlier", "idx": int32[r], "lw": N x r bf16}.
     """
 
@@ -93,7 +93,7 @@ class QuantizedLinear:
         bd = None
         if self.branch is not None:
             if self.branch["kind"] == "lowrank":
-                ops.lowrank_project(x, l1=self.branch["l1"], out=b["br_a"], stream=stream)
+                ops.lowrank_project(x, l1t=self.branch["l1t"], out=b["br_a"], stream=stream)
             else:
                 ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
             bd = ops.branch_desc(b["br_a"], self.branch["lw"])
@@ -123,7 +123,7 @@ def case_to_device(case, device="cuda"):
     if case.branch is not None:
         br = {"kind": case.branch["kind"], "lw": bf16(case.branch["lw"])}
         if case.branch["kind"] == "lowrank":
-            br["l1"] = bf16(case.branch["l1"])
+            br["l1t"] = bf16(np.ascontiguousarray(case.branch["l1"].T))
         else:
             br["idx"] = torch.from_numpy(case.branch["idx"].astype(np.int32)).to(device)
     t["branch"] = br
