@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample duration")
     p.add_argument("--eager", action="store_true", help="launch every call from Python (no HIP graph)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain elementwise copy of 256 MiB five times (hardware-counter scale)")
     return p.parse_args()
 
 
@@ -244,6 +246,20 @@ def measure(torch, wl, steps, warmup):
             "per_call_us": {n: None for n in names}}
 
 
+def copy_calibration(torch):
+    """Five launches of one elementwise kernel that reads and writes 256 MiB
+    each: the known-size reference for the HBM byte counters."""
+    n = 64 << 20                     # fp32 elements = 256 MiB
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "elementwise mul by 1.0 (fp32)", "read_bytes": 4 * n,
+                                           "write_bytes": 4 * n, "launches": 5}}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -254,6 +270,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     global EAGER
     EAGER = a.eager
+    if a.copy_calibration:
+        copy_calibration(torch)
+        return
     r = measure(torch, a.workload, a.steps, a.warmup)
     out = {
         "metric": "W4A4 linear effective TOPS + us/call (batch-1 64-token and 4096-token shapes)",

@@ -137,6 +137,38 @@ def test_extreme_codes_do_not_overflow(ops, fmt, val_a, val_w):
     assert np.all(_np(y) == val_a * val_w * K)
 
 
+@pytest.mark.parametrize("M", [20, 127])
+def test_nvfp4_every_scale_code(ops, M):
+    """Every finite non-negative E4M3 block scale (codes 0..126) through the
+    NVFP4 GEMM, on both operands: row m of A uses code m mod 127 for all
+    its blocks, row n of W code 7n mod 127.  Divided by the two scale
+    values, each output is a dot product of E2M1 codes (a multiple of 1/4),
+    so a wrong scale decode shows as a gross error on its own rows."""
+    N, K = 160, 2048
+    rng = np.random.default_rng(11)
+    ca = rng.integers(0, 16, (M, K))
+    cw = rng.integers(0, 16, (N, K))
+    ea = (np.arange(M) % 127).astype(np.uint8)
+    ew = ((7 * np.arange(N)) % 127).astype(np.uint8)
+    sa = np.repeat(ea[:, None], K // 16, axis=1)
+    sw = np.repeat(ew[:, None], K // 16, axis=1)
+    dot = O.e2m1_value(ca) @ O.e2m1_value(cw).T            # exact in fp64
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ops.w4a4_linear(torch.from_numpy(O.pack_nibbles(ca)).cuda(), torch.from_numpy(sa).cuda(),
+                    torch.from_numpy(O.pack_nibbles(cw)).cuda(), torch.from_numpy(sw).cuda(), K, "nvfp4",
+                    alpha=1.0, y=y)
+    got = _np(y).astype(np.float64)
+    va, vw = O.e4m3_value(ea), O.e4m3_value(ew)
+    prod = va[:, None] * vw[None, :]
+    assert np.all(got[prod == 0] == 0)
+    nz = prod != 0
+    # fp32 accumulation of exact products: error <= K * 2^-24 of the sum of
+    # |terms|; a wrong decode moves the whole row by at least 1/16 of |dot|
+    mag = np.abs(O.e2m1_value(ca)) @ np.abs(O.e2m1_value(cw)).T
+    err = np.abs(got[nz] / prod[nz] - dot[nz])
+    assert np.all(err <= K * 2.0 ** -24 * mag[nz] + 1e-9)
+
+
 def test_zero_rows_and_saturating_nvfp4(ops, pipe):
     case = WL.linear_case(40, 64, 256, seed=5, fmt="nvfp4", n_outliers=4, outlier_gain=30.0)
     case.x[3] = 0.0

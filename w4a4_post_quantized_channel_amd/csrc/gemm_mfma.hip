@@ -65,11 +65,11 @@ struct Fmt<F_NVFP4> {
 };
 
 __device__ __forceinline__ uint2 fp4_scale_pair(uint32_t e) {
-  float S = e4m3_to_f32(e);
-  S = S > 0.f ? S : 1.0f;  // a zero block scale only ever carries zero codes
+  // gfx950 converts OCP E4M3 in hardware (exact; code 0 gives 0.0, whose
+  // codes are all zero, so its scale pair never matters)
+  const float S = __builtin_amdgcn_cvt_f32_fp8((int)e, 0);
   const float mant = __uint_as_float((__float_as_uint(S) & 0x007FFFFFu) | 0x3F800000u);
-  const _Float16 mh = (_Float16)mant;
-  return make_uint2(__float_as_uint(S), __builtin_bit_cast(uint32_t, v2h{mh, mh}));
+  return make_uint2(__float_as_uint(S), __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(mant, mant)));
 }
 
 // 8 E2M1 codes (dword d) times scale pair -> 4 dwords of fp16
@@ -85,33 +85,35 @@ __device__ __forceinline__ uint4 fp4_widen8(uint32_t d, uint2 sp) {
 }
 
 // Global -> registers -> widened LDS rows, for one operand tile of ROWS rows
-// staged by NT threads.  Each thread owns 16-byte source chunks; chunk c
-// covers row c / CPR, source bytes (c % CPR) * 16 .. +16 of that row's
+// staged by NT threads.  The stage is cut into chunks of CB source bytes
+// (16, or 8 where 16-byte chunks would leave threads idle), so that every
+// thread stages the same number of chunks with straight-line code; chunk c
+// covers row c / CPR, source bytes (c % CPR) * CB .. +CB of that row's
 // stage.  StageMap holds the per-thread offsets (fixed for the kernel),
 // StageRegs one stage of loaded data.
 template <int FMT, int ROWS, int NT>
 struct StageMap {
   static constexpr int SRC = Fmt<FMT>::SRC_BYTES;
-  static constexpr int CPR = SRC / 16;                // chunks per row
+  static constexpr int CB = (ROWS * SRC / 16) % NT == 0 ? 16 : 8;
+  static constexpr int CPR = SRC / CB;                 // chunks per row
   static constexpr int CHUNKS = ROWS * CPR;
-  static constexpr int PER = (CHUNKS + NT - 1) / NT;  // chunks per thread
-  static constexpr bool ALL = CHUNKS % NT == 0;       // every thread owns PER chunks
+  static constexpr int PER = CHUNKS / NT;              // chunks per thread
+  static constexpr int WIDEN = FMT == F_INT4 ? 2 : (FMT == F_NVFP4 ? 4 : 1);
+  static_assert(CHUNKS % NT == 0 && PER > 0, "whole chunks per thread");
   uint32_t off[PER];    // source byte offset of the chunk in stage 0
   uint32_t soff[PER];   // NVFP4: scale byte offset in stage 0
   int col[PER];         // source column in bytes
   int lds[PER];         // LDS byte offset of the chunk's widened output
-  bool own[PER];        // the thread owns chunk t (always, when ALL)
 
   __device__ __forceinline__ void init(int tid, int64_t rowbytes, int64_t srow) {
 #pragma unroll
     for (int t = 0; t < PER; ++t) {
       const int c = tid + t * NT;
-      own[t] = ALL || c < CHUNKS;
-      const int r = own[t] ? c / CPR : 0, cc = c % CPR;
-      col[t] = cc * 16;
-      off[t] = (uint32_t)(r * rowbytes + cc * 16);
-      soff[t] = (uint32_t)(r * srow + cc * 2);
-      lds[t] = r * kPitch + cc * 16 * (FMT == F_INT4 ? 2 : (FMT == F_NVFP4 ? 4 : 1));
+      const int r = c / CPR, cc = c % CPR;
+      col[t] = cc * CB;
+      off[t] = (uint32_t)(r * rowbytes + cc * CB);
+      soff[t] = (uint32_t)(r * srow + cc * (CB / 8));
+      lds[t] = r * kPitch + cc * CB * WIDEN;
     }
   }
 };
@@ -119,8 +121,10 @@ struct StageMap {
 template <int FMT, int ROWS, int NT>
 struct StageRegs {
   typedef StageMap<FMT, ROWS, NT> Map;
-  uint4 raw[Map::PER];
-  uint32_t sc[Map::PER];  // NVFP4: the chunk's two scale bytes
+  static constexpr int CB = Map::CB;
+  typedef typename std::conditional<CB == 16, uint4, uint2>::type raw_t;
+  raw_t raw[Map::PER];
+  uint32_t sc[Map::PER];  // NVFP4: the chunk's scale bytes (one per 16 codes)
 
   // Loads are issued unconditionally (offsets past the resource read as
   // zeros), so the compiler can keep exact wait counts across the loop.
@@ -129,12 +133,18 @@ struct StageRegs {
     const int64_t kb0 = (int64_t)ks * Map::SRC;
 #pragma unroll
     for (int t = 0; t < Map::PER; ++t) {
-      const bool ok = valid && mp.own[t] && kb0 + mp.col[t] < rowbytes;
-      raw[t] = buf_load16(rs, ok ? mp.off[t] + (uint32_t)kb0 : kOOB);
+      const bool ok = valid && kb0 + mp.col[t] < rowbytes;
+      const int off = ok ? (int)(mp.off[t] + (uint32_t)kb0) : (int)kOOB;
+      if constexpr (CB == 16)
+        raw[t] = buf_load16(rs, (uint32_t)off);
+      else
+        raw[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
       if constexpr (FMT == F_NVFP4) {
-        // chunk = 32 codes = two 16-code scale blocks: 2 scale bytes
-        sc[t] = __builtin_amdgcn_raw_buffer_load_b16(rss, ok ? (int)(mp.soff[t] + (uint32_t)(kb0 / 8)) : (int)kOOB,
-                                                     0, 0);
+        const int soff = ok ? (int)(mp.soff[t] + (uint32_t)(kb0 / 8)) : (int)kOOB;
+        if constexpr (CB == 16)
+          sc[t] = __builtin_amdgcn_raw_buffer_load_b16(rss, soff, 0, 0);
+        else
+          sc[t] = __builtin_amdgcn_raw_buffer_load_b8(rss, soff, 0, 0);
       }
     }
   }
@@ -142,24 +152,27 @@ struct StageRegs {
   __device__ __forceinline__ void store(const Map& mp, uint8_t* lds) const {
 #pragma unroll
     for (int t = 0; t < Map::PER; ++t) {
-      if (!Map::ALL && !mp.own[t]) continue;
       uint4* dst = reinterpret_cast<uint4*>(lds + mp.lds[t]);
-      const uint4 d = raw[t];
+      const raw_t d = raw[t];
       if constexpr (FMT == F_INT8) {
-        dst[0] = d;
+        *reinterpret_cast<raw_t*>(dst) = d;
       } else if constexpr (FMT == F_INT4) {
-        // 32 codes -> 32 bytes: even codes of each dword, then odd codes
+        // 8 codes per dword -> 8 bytes: the even codes of the dword, then the odd ones
         dst[0] = make_uint4((d.x << 4) & 0xF0F0F0F0u, d.x & 0xF0F0F0F0u, (d.y << 4) & 0xF0F0F0F0u,
                             d.y & 0xF0F0F0F0u);
-        dst[1] = make_uint4((d.z << 4) & 0xF0F0F0F0u, d.z & 0xF0F0F0F0u, (d.w << 4) & 0xF0F0F0F0u,
-                            d.w & 0xF0F0F0F0u);
+        if constexpr (CB == 16)
+          dst[1] = make_uint4((d.z << 4) & 0xF0F0F0F0u, d.z & 0xF0F0F0F0u, (d.w << 4) & 0xF0F0F0F0u,
+                              d.w & 0xF0F0F0F0u);
       } else {
-        // 32 codes -> 64 bytes of fp16; codes 0..15 use the first scale, 16..31 the second
-        const uint2 s0 = fp4_scale_pair(sc[t] & 0xFFu), s1 = fp4_scale_pair((sc[t] >> 8) & 0xFFu);
+        // 16 codes per scale byte -> 32 bytes of fp16
+        const uint2 s0 = fp4_scale_pair(sc[t] & 0xFFu);
         dst[0] = fp4_widen8(d.x, s0);
         dst[1] = fp4_widen8(d.y, s0);
-        dst[2] = fp4_widen8(d.z, s1);
-        dst[3] = fp4_widen8(d.w, s1);
+        if constexpr (CB == 16) {
+          const uint2 s1 = fp4_scale_pair((sc[t] >> 8) & 0xFFu);
+          dst[2] = fp4_widen8(d.z, s1);
+          dst[3] = fp4_widen8(d.w, s1);
+        }
       }
     }
   }
@@ -174,6 +187,21 @@ __device__ __forceinline__ void mma(typename Fmt<FMT>::acc_t& c, uint4 a, uint4 
 }
 
 }  // namespace
+
+// Instruction-group pattern for one stage: global loads first, then each
+// MFMA followed by its share of VALU work and one LDS access.
+template <int FMT, int NMFMA>
+__device__ __forceinline__ void interleave() {
+  constexpr int V = FMT == F_NVFP4 ? 3 : (FMT == F_INT4 ? 1 : 0);
+  __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);   // VMEM reads
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // first fragment reads
+#pragma unroll
+  for (int k = 0; k < NMFMA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);  // one LDS read or write
+  }
+}
 
 template <int FMT, int BM, int BN, int WR, int WC>
 __global__ void __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(WR * WC / 4, WR * WC / 4)))
@@ -251,6 +279,10 @@ gemm_tile_kernel(GemmArgs g, int tiles_n) {
     constexpr int nx = (i + 1) % 3;
     stA[nx].store(mA, sA[buf ^ 1]);
     stB[nx].store(mB, sB[buf ^ 1]);
+    // Schedule: the widening (VALU) and LDS writes of the next stage, and
+    // the second half's fragment reads, go between this stage's MFMAs, so
+    // the matrix pipe keeps running while the wave does its staging work.
+    interleave<FMT, TI * TJ * (kRowBytes / 64)>();
     __syncthreads();
   };
   int ks = 0;

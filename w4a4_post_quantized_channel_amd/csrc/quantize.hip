@@ -18,11 +18,14 @@
 // Exactness.  Every value the quantizer decides on is the one the fp32
 // definition gives: the butterflies are the same additions in the same
 // order (a cross-lane stage computes own + c * partner with c = +-1, an
-// exact negation, so the upper lane holds the negated sum; the sign is
-// tracked per lane and folded into the final 1/8).  Quotients y / step use
-// a correctly rounded reciprocal r = RN(1/step) per row or block and two
-// Markstein corrections, q <- q + (y - step*q) * r, which give RN(y / step)
-// for normal operands; steps below 2^-80 take the plain IEEE division.
+// exact negation, so the upper lane holds the negated sum; that sign and
+// the final 1/8 are carried into the divisor, an exact power-of-two
+// rescaling).  A code is taken from the one-multiply quotient
+// RN(v * RN(1/D)) unless that quotient lies within a few representable
+// steps of a rounding boundary of the code grid; such slots are redone with
+// two Markstein corrections, q <- q + (v - D*q) * r, which give RN(v / D)
+// for normal operands.  Divisors outside [2^-80, 2^100] take the plain IEEE
+// division of the unscaled value.
 #include "device_common.h"
 #include "launch.h"
 
@@ -55,23 +58,38 @@ __device__ __forceinline__ float div_rn(float a, float b, float r) {
   return __builtin_fmaf(t, r, q);
 }
 
+// Raw bytes of slot s (16 elements) of a row: 32 bytes (bf16) or 64 bytes
+// (fp32).  Offsets past the row's resource read zeros.
 template <bool BF16IN>
-__device__ __forceinline__ void load_slot(const void* rowp, int s, float (&v)[16]) {
+struct SlotRaw {
+  uint4 d[BF16IN ? 2 : 4];
+};
+
+template <bool BF16IN>
+__device__ __forceinline__ SlotRaw<BF16IN> load_slot(__amdgpu_buffer_rsrc_t rs, int s) {
+  SlotRaw<BF16IN> r;
+  constexpr int B = BF16IN ? 32 : 64;
+#pragma unroll
+  for (int i = 0; i < B / 16; ++i) r.d[i] = buf_load16(rs, (uint32_t)(s * B + i * 16));
+  return r;
+}
+
+template <bool BF16IN>
+__device__ __forceinline__ void unpack_slot(const SlotRaw<BF16IN>& r, float (&v)[16]) {
   if constexpr (BF16IN) {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(rowp) + s * 16);
-    const uint4 d0 = p[0], d1 = p[1];
-    const uint32_t w[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    const uint32_t w[8] = {r.d[0].x, r.d[0].y, r.d[0].z, r.d[0].w, r.d[1].x, r.d[1].y, r.d[1].z, r.d[1].w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(rowp) + s * 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 a = p[i];
-      v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+      v[4 * i] = __uint_as_float(r.d[i].x);
+      v[4 * i + 1] = __uint_as_float(r.d[i].y);
+      v[4 * i + 2] = __uint_as_float(r.d[i].z);
+      v[4 * i + 3] = __uint_as_float(r.d[i].w);
     }
   }
 }
@@ -93,7 +111,8 @@ __device__ __forceinline__ void fwht16_local(float (&v)[16]) {
 
 template <int CTRL>
 __device__ __forceinline__ float quad_perm(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  // every lane of the quad is written, so no old value is needed
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Stages h = 16 (partner lane ^ 1) and 32 (lane ^ 2).  Each lane computes
@@ -116,6 +135,67 @@ __device__ __forceinline__ float wave_max(float m) {
   return m;
 }
 
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// Boundary screen for E2M1 quotients taken with one multiply,
+// q0 = RN(v * RN(1/D)), which is within three representable steps of
+// RN(v / D).  Every E2M1 rounding boundary (0.25, 0.75, 1.25, 1.75, 2.5,
+// 3.5, 5) has at most three significant bits, so its low 16 bits are zero.
+// If no q0 of a slot has its low 16 bits within 4 of a multiple of 2^16, no
+// boundary lies between q0 and RN(v / D) and both give the same code;
+// otherwise the slot is redone exactly.  Returns the minimum over the slot
+// of ((bits(q0) + 4) mod 2^16).
+__device__ __forceinline__ uint32_t near_boundary(const float (&q)[16]) {
+  us2 mn = (us2){0xFFFF, 0xFFFF};
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const uint32_t p = __builtin_amdgcn_perm(__float_as_uint(q[i + 1]), __float_as_uint(q[i]), 0x05040100u);
+    us2 t = __builtin_bit_cast(us2, p) + (us2){4, 4};
+    mn = __builtin_elementwise_min(mn, t);
+  }
+  return (uint32_t)__builtin_elementwise_min(mn.x, mn.y);
+}
+
+constexpr float kBig = 1.2676506002282294e30f;     // 2^100
+constexpr float kMinA = 8.077935669463161e-28f;    // 2^-90: dividends at or above keep residuals normal
+
+// Smoothing and rotation of one slot in place; returns the factor fl with
+// y = v * fl (see the kernel).
+template <bool BF16IN>
+__device__ __forceinline__ float transform_slot(const SlotRaw<BF16IN>& raw, float (&v)[16],
+                                                __amdgpu_buffer_rsrc_t rsc, bool has_scale, int rot, int order,
+                                                int s, int lane) {
+  unpack_slot<BF16IN>(raw, v);
+  float sc[16];
+  if (has_scale) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = buf_load16(rsc, (uint32_t)(s * 64 + i * 16));
+      sc[4 * i] = __uint_as_float(u.x); sc[4 * i + 1] = __uint_as_float(u.y);
+      sc[4 * i + 2] = __uint_as_float(u.z); sc[4 * i + 3] = __uint_as_float(u.w);
+    }
+  }
+  if (order == 0 && has_scale) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = v[i] * sc[i];
+  }
+  float fl = 1.0f;
+  if (rot) {
+    fwht16_local(v);
+    fl = 0.125f * fwht16_cross(v, lane);
+    if (order == 1) {  // rotate, then smooth: the factor must precede the smoothing product
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = v[i] * fl;
+      fl = 1.0f;
+    }
+  }
+  if (order == 1 && has_scale) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = v[i] * sc[i];
+  }
+  return fl;
+}
+
 template <int MODE, bool BF16IN, int NC, int WPR>
 __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
   constexpr int QMAX = MODE == MODE_INT4 ? 7 : 127;
@@ -126,66 +206,53 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
   const int grp = WPR == 1 ? wave : 0;              // row group inside the block
   const int nslots = a.K >> 4;
   const bool has_scale = a.scale != nullptr;
-  const size_t esz = BF16IN ? 2 : 4;
+  constexpr int ESZ = BF16IN ? 2 : 4;
   __shared__ float red[4];
-
-  float sc[NC][16];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int s = (c * WPR + sub) * 64 + lane;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc[c][i] = 1.0f;
-    if (has_scale && s < nslots) {
-      const float4* p = reinterpret_cast<const float4*>(a.scale + s * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 u = p[i];
-        sc[c][4 * i] = u.x; sc[c][4 * i + 1] = u.y; sc[c][4 * i + 2] = u.z; sc[c][4 * i + 3] = u.w;
-      }
+  // NVFP4: (S, RN(1/S)) for every E4M3 code e, S = fp32(value(e) * g).
+  __shared__ float2 stab[MODE == MODE_NVFP4 ? 128 : 1];
+  if constexpr (MODE == MODE_NVFP4) {
+    for (int e = threadIdx.x; e < 128; e += blockDim.x) {
+      const float S = e < 0x7F ? e4m3_to_f32((uint32_t)e) * a.g : 0.f;
+      stab[e] = make_float2(S, S > 0.f ? 1.0f / S : 0.f);  // IEEE division
     }
+    __syncthreads();
   }
+
+  // Smoothing factors: loaded per slot where they are used (every row
+  // reads the same K factors, so these hit in cache); past K they read 0.
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.scale, has_scale ? (uint32_t)(a.K * 4) : 0u);
   const float rg = MODE == MODE_NVFP4 ? 1.0f / a.g : 1.0f;   // RN(1/g), IEEE division
+  const bool g_fast = a.g >= kTinyStep && a.g <= kBig;
 
   float tmax = 0.f;  // MODE_AMAX: running max over this wave's rows
   for (int64_t row = (int64_t)blockIdx.x * RPB + grp; row < a.R; row += (int64_t)gridDim.x * RPB) {
-    const char* rowp = reinterpret_cast<const char*>(a.x) + (size_t)row * a.ldx * esz;
-    float v[NC][16];
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)row * a.ldx * ESZ, (uint32_t)(a.K * ESZ));
+    SlotRaw<BF16IN> raw[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int s = (c * WPR + sub) * 64 + lane;
-      if (s < nslots) {
-        load_slot<BF16IN>(rowp, s, v[c]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[c][i] = 0.f;
-      }
-    }
-    // --- transform -------------------------------------------------------
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (a.order == 0 && has_scale) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[c][i] = v[c][i] * sc[c][i];
-      }
-      if (a.rot) {
-        fwht16_local(v[c]);
-        const float f = 0.125f * fwht16_cross(v[c], lane);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[c][i] = v[c][i] * f;
-      }
-      if (a.order == 1 && has_scale) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[c][i] = v[c][i] * sc[c][i];
-      }
-    }
-
+    for (int c = 0; c < NC; ++c) raw[c] = load_slot<BF16IN>(rs, (c * WPR + sub) * 64 + lane);
+    // --- transform --------------------------------------------------------
+    // After this, the value the definition quantizes is y = v * fl exactly
+    // (fl = +-1/8 after a smoothing-then-rotation; the power-of-two factor
+    // and the lane's butterfly sign are carried into the divisor instead of
+    // being multiplied into every element).  Where v * fl would fall below
+    // the normal range, every decision is code 0 on both readings, or the
+    // slot takes the exact path, which forms y itself.
+    // Integer modes need the whole row for its maximum; NVFP4 transforms
+    // and quantizes one slot at a time.
     if constexpr (MODE == MODE_INT4 || MODE == MODE_INT8 || MODE == MODE_AMAX) {
-      float m = 0.f;
+      float v[NC][16];
+      float fl = 1.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) fl = transform_slot<BF16IN>(raw[c], v[c], rsc, has_scale, a.rot, a.order,
+                                                               (c * WPR + sub) * 64 + lane, lane);
+      const float afl = __builtin_fabsf(fl);
+      float mv = 0.f;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, __builtin_fabsf(v[c][i]));
-      m = wave_max(m);
+        for (int i = 0; i < 16; ++i) mv = fmaxf(mv, __builtin_fabsf(v[c][i]));
+      float m = wave_max(mv) * afl;   // = max |y| (rounding is monotone)
       if constexpr (MODE == MODE_AMAX) {
         tmax = fmaxf(tmax, m);
         continue;
@@ -197,28 +264,42 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
           __syncthreads();
         }
         const float step = m / (float)QMAX;   // IEEE division
-        const bool fast = step >= kTinyStep;
+        const bool fast = step >= kTinyStep && step <= kBig;
         const float rstep = fast ? 1.0f / step : 0.f;
+        const float D = step / fl, rD = rstep * fl;   // exact power-of-two rescaling
         if (lane == 0 && sub == 0) reinterpret_cast<float*>(a.scales)[row] = step;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int s = (c * WPR + sub) * 64 + lane;
-          if (s >= nslots) continue;
-          float t[16];
-          if (fast) {
+          // One-multiply quotients; a boundary k + 1/2 lies between t and
+          // RN(v / D) only if |t - rint(t)| is within three steps of 1/2.
+          float t[16], r[16], dmax = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) t[i] = div_rn(v[c][i], step, rstep);
-          } else if (step > 0.f) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) t[i] = v[c][i] / step;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) t[i] = 0.f;
+          for (int i = 0; i < 16; ++i) {
+            t[i] = v[c][i] * rD;
+            r[i] = __builtin_rintf(t[i]);
+            dmax = fmaxf(dmax, __builtin_fabsf(t[i] - r[i]));
           }
+          constexpr float kEdge = MODE == MODE_INT8 ? 0.5f - 3.0517578125e-05f : 0.5f - 1.9073486328125e-06f;
+          if (s < nslots && (!fast || dmax >= kEdge)) {
+            if (fast) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) t[i] = div_rn(v[c][i], D, rD);
+            } else if (step > 0.f) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) t[i] = (v[c][i] * fl) / step;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) t[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) r[i] = __builtin_rintf(t[i]);
+          }
+          if (s >= nslots) continue;
           uint32_t q[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            q[i] = (uint32_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(t[i]), (float)(-QMAX - 1), (float)QMAX);
+            q[i] = (uint32_t)(int)__builtin_amdgcn_fmed3f(r[i], (float)(-QMAX - 1), (float)QMAX);
           if constexpr (MODE == MODE_INT4) {
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -241,25 +322,31 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int s = (c * WPR + sub) * 64 + lane;
-        if (s >= nslots) continue;
-        float m = 0.f;
+        float vs[16];
+        const float fl = transform_slot<BF16IN>(raw[c], vs, rsc, has_scale, a.rot, a.order, s, lane);
+        float mv = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, __builtin_fabsf(v[c][i]));
-        const float sb = m / 6.0f;                                          // IEEE division
-        const float sv = a.g >= kTinyStep ? div_rn(sb, a.g, rg) : sb / a.g;  // RN(sb / g)
+        for (int i = 0; i < 16; ++i) mv = fmaxf(mv, __builtin_fabsf(vs[i]));
+        const float m = mv * __builtin_fabsf(fl);                                             // max |y| of the block
+        const float sb = m >= kMinA ? div_rn(m, 6.0f, 0.16666667163372040f) : m / 6.0f;  // RN(m / 6)
+        const float sv = (g_fast && sb >= kMinA) ? div_rn(sb, a.g, rg) : sb / a.g;   // RN(sb / g)
         const uint32_t e = f32_to_e4m3_sat(sv);
-        const float S = e4m3_to_f32(e) * a.g;
+        const float2 SR = stab[e];
         uint32_t w[2] = {0u, 0u};
-        if (S > 0.f) {
-          const bool fast = S >= kTinyStep;
-          const float rS = 1.0f / S;                                         // IEEE division
+        if (SR.x > 0.f) {
+          const bool fast = SR.x >= kTinyStep && SR.x <= kBig;
+          const float D = SR.x / fl, rD = SR.y * fl;   // exact power-of-two rescaling
           float q[16];
-          if (fast) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) q[i] = div_rn(v[c][i], S, rS);
-          } else {
+          for (int i = 0; i < 16; ++i) q[i] = vs[i] * rD;
+          if (s < nslots && (!fast || near_boundary(q) <= 8u)) {
+            if (fast) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) q[i] = v[c][i] / S;
+              for (int i = 0; i < 16; ++i) q[i] = div_rn(vs[i], D, rD);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) q[i] = (vs[i] * fl) / SR.x;
+            }
           }
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -274,8 +361,10 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
             w[h] = mag | (d & nz);
           }
         }
-        *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = make_uint2(w[0], w[1]);
-        reinterpret_cast<uint8_t*>(a.scales)[(size_t)row * (a.K >> 4) + s] = (uint8_t)e;
+        if (s < nslots) {
+          *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = make_uint2(w[0], w[1]);
+          reinterpret_cast<uint8_t*>(a.scales)[(size_t)row * (a.K >> 4) + s] = (uint8_t)e;
+        }
       }
     }
   }
