@@ -154,7 +154,7 @@ int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t l
  *           from pack_weights (same fmt, same K).
  *  br       NULL or a w4a4_branch (kind NONE or BF16).
  *  y        M x N output, y_dtype F32 or BF16 (round to nearest even) with
- *           row stride ldy >= N; y_dtype I32 writes the raw integer
+ *           row stride N <= ldy <= 2^22 elements; y_dtype I32 writes the raw integer
  *           accumulators (INT formats, no branch, alpha ignored).
  *  workspace / workspace_bytes  optional device scratch (NULL / 0 for
  *           none).  Few-token shapes (M <= 64) split K over workgroups

@@ -119,6 +119,7 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
   int st = check_branch(fn, br, M, N);
   if (st != W4A4_OK) return st;
   if (ldy < N) return fail(W4A4_ERR_INVALID_ARG, "%s: ldy < N", fn);
+  if (ldy > (1LL << 22)) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: ldy above 2^22 elements", fn);
   if (M == 0 || N == 0) return ok();
   if (!a_codes || !a_scales || !w_codes || !w_scales || !y)
     return fail(W4A4_ERR_INVALID_ARG, "%s: NULL operand", fn);
@@ -142,7 +143,7 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
   g.y = y; g.y_dtype = y_dtype; g.ldy = ldy;
   hipError_t e;
   if (fmt == W4A4_FMT_NVFP4) {
-    e = w4a4::launch_gemm_tile(2, g, (hipStream_t)stream);
+    e = w4a4::launch_gemm_wide(2, g, (hipStream_t)stream);
   } else {
     const size_t need = w4a4::gemm_int_workspace(fmt, M, N, K);
     if (workspace && ws_bytes < need)

@@ -40,38 +40,44 @@ __device__ __forceinline__ void branch_mfma(v4f (&acc)[TI][TJ], const BranchArgs
   }
 }
 
-// Store one fp32 value (f32 or bf16 output).
-__device__ __forceinline__ void store_out(void* y, int y_dtype, int64_t ldy, int m, int n, float v) {
-  if (y_dtype == 0) {
-    reinterpret_cast<float*>(y)[(int64_t)m * ldy + n] = v;
-  } else {
-    reinterpret_cast<uint16_t*>(y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16_bits(v);
-  }
-}
-
 // Epilogue of a wave's TI x TJ grid of 16x16 accumulator tiles, one
 // 16-column block at a time (keeps the live register set small):
 // dequantise (integer: fp32(fp32(acc) * sa[m]) * sw[n] * alpha, with acc
 // shifted right by 8 for the x16-widened int4 operands; float: acc *
 // alpha), add the bf16 branch, store.  acc[i][j] covers rows
 // m_base + 16 i + [0, 16) and columns n_base + 16 j + [0, 16).
-// y_dtype 2 writes the raw integer accumulators.
+// y_dtype 2 writes the raw integer accumulators.  Stores go through a
+// buffer resource over the tile's rows (rows past M fall outside it) with
+// 32-bit offsets; columns past N are sent past the resource.
 template <int KIND /*0 int4, 1 int8, 2 float*/, typename AccT, int TI, int TJ>
 __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
                                                int lane) {
   const int lr = lane & 15, lq = lane >> 4;
+  const int esz = g.y_dtype == 1 ? 2 : 4;
+  const int rows = max(0, min(TI * 16, g.M - m_base));
+  const uint32_t rstride = (uint32_t)(g.ldy * esz);
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc(reinterpret_cast<char*>(g.y) + (int64_t)m_base * g.ldy * esz, (uint32_t)rows * rstride);
+  uint32_t roff[TI][4];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) roff[i][r] = (uint32_t)(i * 16 + lq * 4 + r) * rstride;
+
   if constexpr (KIND != 2) {
     if (g.y_dtype == 2) {
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+      for (int j = 0; j < TJ; ++j) {
+        const int n = n_base + j * 16 + lr;
+        const uint32_t coff = n < g.N ? (uint32_t)n * 4u : kOOB;
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int m = m_base + i * 16 + lq * 4 + r, n = n_base + j * 16 + lr;
             const int v = KIND == 0 ? (acc[i][j][r] >> 8) : acc[i][j][r];
-            if (m < g.M && n < g.N) reinterpret_cast<int32_t*>(g.y)[(int64_t)m * g.ldy + n] = v;
+            __builtin_amdgcn_raw_buffer_store_b32(v, ry, (int)(roff[i][r] + coff), 0, 0);
           }
+      }
       return;
     }
   }
@@ -90,6 +96,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int n = n_base + j * 16 + lr;
+    const uint32_t coff = n < g.N ? (uint32_t)n * (uint32_t)esz : kOOB;
     v4f col[TI][1];
     if constexpr (KIND != 2) {
       const float swn = n < g.N ? sw[n] : 0.f;
@@ -109,13 +116,20 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
         for (int r = 0; r < 4; ++r) col[i][0][r] = acc[i][j][r] * g.alpha;
     }
     if (g.br.r > 0) branch_mfma<TI, 1>(col, g.br, g.M, g.N, m_base, n_base + j * 16, lane);
+    if (g.y_dtype == 0) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m_base + i * 16 + lq * 4 + r;
-        if (m < g.M && n < g.N) store_out(g.y, g.y_dtype, g.ldy, m, n, col[i][0][r]);
-      }
+        for (int r = 0; r < 4; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(col[i][0][r]), ry, (int)(roff[i][r] + coff), 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(col[i][0][r]), ry,
+                                                (int)(roff[i][r] + coff), 0, 0);
+    }
   }
 }
 

@@ -225,7 +225,7 @@ hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes
     }
     return hipGetLastError();
   }
-  return launch_gemm_tile(fmt, g, st);
+  return launch_gemm_wide(fmt, g, st);
 }
 
 }  // namespace w4a4

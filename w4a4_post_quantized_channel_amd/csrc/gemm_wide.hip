@@ -1,0 +1,568 @@
+// Many-token GEMM for gfx950 with packed operands in LDS: W4A4 (int4),
+// W8A8 (int8) and NVFP4.
+//
+// FoldQuantVLA overview / contributions 3-4 (integer GEMMs with per-token
+// and per-channel scales, W4A4 and INT8 W8A8 projections); LatentQuant
+// abstract and QuantWAMs sec. 4.2 (NVFP4 W4A4, BF16 bypass).
+//
+// Design.
+// * Each K stage of the A and W tiles is copied global -> LDS still packed
+//   (0.5 byte per int4 / E2M1 code), by 16-byte buffer loads that write LDS
+//   directly; NVFP4 block-scale bytes follow in 4-byte pieces.  Two LDS
+//   buffers: the copy of stage s + 1 runs while stage s is multiplied.
+// * Operands are widened in registers as fragments are read:
+//     int4  -> bytes 16*q ((d << 4) & 0xF0F0F0F0: even codes, d & 0xF0F0F0F0:
+//              odd codes); v_mfma_i32_16x16x64_i8 returns 256 * sum(qa*qw);
+//     int8  -> used as loaded;
+//     NVFP4 -> exact fp16 value(c) * value(e): v_cvt_scalef32_pk_f16_fp4 by
+//              the power of two of the E4M3 scale, then one exact packed fp16
+//              multiply by its mantissa; v_mfma_f32_16x16x32_f16.
+//   The widening of one MFMA step is interleaved with the MFMAs of the
+//   previous one.
+// * K order.  A stage holds 128 packed bytes per row for each of the WK
+//   K-groups of waves.  Lane group q (lanes 16q..16q+15) of a wave owns the
+//   contiguous quarter q of its group's 128 bytes (two 16-byte slots) and
+//   walks it over the stage's MFMA steps; both operands use the same order,
+//   so every MFMA multiplies matching K elements and the sum over a stage
+//   covers each K element once.
+// * LDS rows are XOR-swizzled in 16-byte slots (slot ^ f(row)), so the 16
+//   rows read by one MFMA fragment fall on distinct banks.
+// * Waves: WR x WC x WK = 4.  WK > 1 splits each stage's K among wave
+//   groups; their partial tiles are summed through LDS at the end (exact for
+//   the integer formats).
+// * Tiles are ordered so that each XCD (workgroup id mod 8) walks a compact
+//   block of the tile grid, four row tiles per column step.
+#include <type_traits>
+
+#include "device_common.h"
+#include "epilogue.h"
+#include "launch.h"
+
+namespace w4a4 {
+
+namespace {
+
+enum { W_INT4 = 0, W_INT8 = 1, W_NVFP4 = 2 };
+
+template <int FMT>
+struct WFmt;
+template <>
+struct WFmt<W_INT4> {
+  static constexpr int KSEG = 128;   // K elements per 64-byte segment
+  static constexpr int STEPS = 2;    // MFMA K steps per segment
+  typedef v4i acc_t;
+};
+template <>
+struct WFmt<W_INT8> {
+  static constexpr int KSEG = 64;
+  static constexpr int STEPS = 1;
+  typedef v4i acc_t;
+};
+template <>
+struct WFmt<W_NVFP4> {
+  static constexpr int KSEG = 128;
+  static constexpr int STEPS = 4;
+  typedef v4f acc_t;
+};
+
+constexpr int kSeg = 64;     // packed bytes per row per K-group per stage
+constexpr int kNBuf = 4;     // LDS stage buffers (three stages in flight)
+
+// Global -> LDS copies (buffer loads with the LDS flag: lane l writes its
+// bytes at M0 + size * l).  Issued as inline assembly so that the compiler
+// does not track them: it would otherwise wait for every copy in flight
+// before any LDS read.  The kernel orders them itself (explicit vmcnt wait
+// and barrier before a stage's buffer is read).  No register is written.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4u rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4u{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+// off: per-lane byte offset; soff: wave-uniform byte offset added to it.
+__device__ __forceinline__ void dma16(const v4u& rs, uint8_t* lds, uint32_t off, uint32_t soff) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds));   // lds is wave-uniform
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m), "v"(off), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const v4u& rs, uint8_t* lds, uint32_t off, uint32_t soff) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds));   // lds is wave-uniform
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(m), "v"(off), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
+// XOR swizzle of the 16-byte slots of an LDS row of P bytes: the 16 rows
+// of one MFMA fragment, read at the same logical slot, land in 16
+// distinct 16-byte bank groups.
+template <int P>
+__device__ __forceinline__ int swz(int row) {
+  constexpr int S = P / 16;   // slots per row
+  return S >= 16 ? (row & 15) : ((row / (16 / S)) & (S - 1));
+}
+
+__device__ __forceinline__ uint2 scale_pair(uint32_t e) {
+  const float S = __builtin_amdgcn_cvt_f32_fp8((int)e, 0);   // OCP E4M3, exact
+  const float mant = __uint_as_float((__float_as_uint(S) & 0x007FFFFFu) | 0x3F800000u);
+  return make_uint2(__float_as_uint(S), __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(mant, mant)));
+}
+
+// 8 E2M1 codes times one scale pair -> 8 fp16 (exact)
+__device__ __forceinline__ uint4 widen_fp4(uint32_t d, uint2 sp) {
+  const float S = __uint_as_float(sp.x);
+  const v2h m2 = __builtin_bit_cast(v2h, sp.y);
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, S, 0) * m2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, S, 1) * m2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, S, 2) * m2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, S, 3) * m2;
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
+// 16 int4 codes (two dwords) -> 16 bytes holding 16*q
+__device__ __forceinline__ uint4 widen_i4(uint32_t d0, uint32_t d1) {
+  return make_uint4((d0 << 4) & 0xF0F0F0F0u, d0 & 0xF0F0F0F0u, (d1 << 4) & 0xF0F0F0F0u, d1 & 0xF0F0F0F0u);
+}
+
+__device__ __forceinline__ uint32_t dw(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+template <int FMT>
+__device__ __forceinline__ void mfma_w(typename WFmt<FMT>::acc_t& c, const uint4& a, const uint4& b) {
+  if constexpr (FMT == W_NVFP4)
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  else
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a), __builtin_bit_cast(v4i, b), c, 0, 0, 0);
+}
+
+// Operand fragment for MFMA step t of a stage, from the lane's packed
+// 16-byte slot p (and, for NVFP4, the 2 scale bytes of its 32 codes).
+template <int FMT>
+__device__ __forceinline__ uint4 operand(const uint4& p, int t, uint32_t sc) {
+  if constexpr (FMT == W_INT8) {
+    return p;
+  } else if constexpr (FMT == W_INT4) {
+    return (t & 1) ? widen_i4(p.z, p.w) : widen_i4(p.x, p.y);
+  } else {
+    return widen_fp4(dw(p, t), scale_pair((sc >> (8 * (t >> 1))) & 0xFFu));
+  }
+}
+
+// Instruction-group pattern of one stage: the fragment reads first, then
+// each MFMA followed by its share of the widening work.
+template <int NDS, int NMFMA, int NVALU>
+__device__ __forceinline__ void interleave_steps() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+#pragma unroll
+  for (int k = 0; k < NMFMA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (NVALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);
+  }
+}
+
+template <int FMT, int TI, int TJ, int WR, int WC, int WK>
+struct WCfg {
+  static constexpr int BM = WR * TI * 16, BN = WC * TJ * 16;
+  static constexpr int P = kSeg * WK;                // packed bytes per row per stage
+  static constexpr int KST = WFmt<FMT>::KSEG * WK;   // K elements per stage
+  static constexpr int SP = (kSeg / 8) * WK;         // NVFP4 scale bytes per row per stage
+  static constexpr int A_BYTES = BM * P, B_BYTES = BN * P;
+  static constexpr int SA_BYTES = FMT == W_NVFP4 ? BM * SP : 0;
+  static constexpr int SB_BYTES = FMT == W_NVFP4 ? BN * SP : 0;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+  static constexpr int NW = WR * WC * WK;            // waves per workgroup (4 or 8)
+  static constexpr int RED = WK > 1 ? NW * TI * TJ * 4 * 64 * 4 : 0;   // every wave's partial tile
+  static constexpr int PIPE = kNBuf * STAGE + 1024;                    // + DMA pad target
+  static constexpr int LDS = PIPE > RED ? PIPE : RED;
+  static constexpr int NA = A_BYTES / 1024, NB = B_BYTES / 1024;       // 16-byte DMA wave-instructions
+  static constexpr int NSA = SA_BYTES / 256, NSB = SB_BYTES / 256;     // 4-byte DMA wave-instructions
+  // every wave issues the same number per stage (the last round padded)
+  static constexpr int DPS = (NA + NW - 1) / NW + (NB + NW - 1) / NW + (NSA + NW - 1) / NW + (NSB + NW - 1) / NW;
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole DMA instructions");
+  static_assert(SA_BYTES % 256 == 0 && SB_BYTES % 256 == 0, "whole scale DMA instructions");
+  static_assert(TJ % WK == 0, "split-K epilogue splits the columns");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(DPS * (kNBuf - 2) <= 63, "vmcnt range");
+};
+
+// s_waitcnt with vmcnt <= n and no wait on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Copy of one operand region (rows x P packed bytes) per stage.  Wave w of
+// NW issues instructions w, w + NW, ...; instruction n covers region bytes
+// [1024 n, 1024 n + 1024), lane l the 16 bytes at 1024 n + 16 l (logical
+// slot = physical slot ^ swizzle).  The last round is padded so every wave
+// issues the same count; padding instructions load out of range into the
+// pad area.  Per-lane offsets are fixed; a stage adds s * P through the
+// instruction's scalar offset, and only a stage that crosses the end of K
+// checks columns per lane.
+template <int P, int NI, int NW>
+struct CodeCopy {
+  static constexpr int PW = (NI + NW - 1) / NW;
+  uint32_t off[PW];   // row * rowbytes + logical column (stage 0), kOOB for padding
+  uint32_t col[PW];   // logical column within the stage (bytes)
+
+  __device__ __forceinline__ void init(int wave, int lane, int64_t rowbytes) {
+#pragma unroll
+    for (int t = 0; t < PW; ++t) {
+      const int n = NW * t + wave;
+      const int p = n * 1024 + lane * 16;
+      const int row = p / P, q = (p % P) / 16;
+      const int L = q ^ swz<P>(row);
+      col[t] = (uint32_t)(L * 16);
+      off[t] = (NI % NW == 0 || n < NI) ? (uint32_t)(row * rowbytes) + col[t] : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(const v4u& rs, uint8_t* region, uint8_t* pad, int64_t rowbytes, int s,
+                                        int wave) const {
+    const int64_t k0 = (int64_t)s * P;
+    const bool full = k0 + P <= rowbytes;   // wave-uniform
+#pragma unroll
+    for (int t = 0; t < PW; ++t) {
+      const int n = NW * t + wave;
+      uint8_t* dst = (NI % NW == 0 || n < NI) ? region + n * 1024 : pad;
+      if (full) {
+        dma16(rs, dst, off[t], (uint32_t)k0);
+      } else {
+        const bool ok = k0 + col[t] < rowbytes;
+        dma16(rs, dst, ok ? off[t] + (uint32_t)k0 : kOOB, 0u);
+      }
+    }
+  }
+};
+
+// NVFP4 scales per stage: rows x SP bytes, 4-byte pieces (256 bytes per
+// wave-instruction), unswizzled; same scheme.
+template <int SP, int NI, int NW>
+struct ScaleCopy {
+  static constexpr int PW = (NI + NW - 1) / NW;
+  uint32_t off[PW];
+  uint32_t col[PW];
+
+  __device__ __forceinline__ void init(int wave, int lane, int64_t srow) {
+#pragma unroll
+    for (int t = 0; t < PW; ++t) {
+      const int n = NW * t + wave;
+      const int p = n * 256 + lane * 4;
+      const int row = p / SP, c = p % SP;
+      col[t] = (uint32_t)c;
+      off[t] = (NI % NW == 0 || n < NI) ? (uint32_t)(row * srow + c) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(const v4u& rs, uint8_t* region, uint8_t* pad, int64_t srow, int s,
+                                        int wave) const {
+    const int64_t k0 = (int64_t)s * SP;
+    const bool full = k0 + SP <= srow;
+#pragma unroll
+    for (int t = 0; t < PW; ++t) {
+      const int n = NW * t + wave;
+      uint8_t* dst = (NI % NW == 0 || n < NI) ? region + n * 256 : pad;
+      if (full) {
+        dma4(rs, dst, off[t], (uint32_t)k0);
+      } else {
+        const bool ok = k0 + col[t] < srow;
+        dma4(rs, dst, ok ? off[t] + (uint32_t)k0 : kOOB, 0u);
+      }
+    }
+  }
+};
+
+}  // namespace
+
+template <int FMT, int TI, int TJ, int WR, int WC, int WK>
+__global__ void __launch_bounds__(64 * WR * WC * WK)
+    __attribute__((amdgpu_waves_per_eu(WR * WC * WK / 4, WR * WC * WK / 4)))
+    gemm_wide_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  typedef WCfg<FMT, TI, TJ, WR, WC, WK> C;
+  typedef typename WFmt<FMT>::acc_t acc_t;
+  constexpr int STEPS = WFmt<FMT>::STEPS;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+
+  // Tile order: workgroup id -> XCD-contiguous index t -> groups of four
+  // row tiles walked column by column.
+  const int nwg = gridDim.x, wid = blockIdx.x;
+  const int t = (nwg % 8 == 0) ? (wid % 8) * (nwg / 8) + wid / 8 : wid;
+  constexpr int GM = 4;
+  const int gsz = GM * tiles_n;
+  const int grp = t / gsz, gm0 = grp * GM;
+  const int gh = min(GM, tiles_m - gm0);
+  const int tm = gm0 + (t % gsz) % gh, tn = (t % gsz) / gh;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int lr = lane & 15, lq = lane >> 4;
+  const int kw = wave / (WR * WC), wrc = wave % (WR * WC);
+  const int wm0 = (wrc / WC) * TI * 16, wn0 = (wrc % WC) * TJ * 16;
+
+  const int64_t rowbytes = FMT == W_INT8 ? g.K : (g.K >> 1);
+  const int64_t srow = g.K >> 4;
+  const int nk = (int)((g.K + C::KST - 1) / C::KST);
+  const v4u rsA = rsrc_words(g.a + (int64_t)m0 * rowbytes, (uint32_t)(min(C::BM, g.M - m0) * rowbytes));
+  const v4u rsB = rsrc_words(g.w + (int64_t)n0 * rowbytes, (uint32_t)(min(C::BN, g.N - n0) * rowbytes));
+  v4u rsSA = rsA, rsSB = rsB;
+  if constexpr (FMT == W_NVFP4) {
+    rsSA = rsrc_words(reinterpret_cast<const uint8_t*>(g.sa) + (int64_t)m0 * srow, (uint32_t)(min(C::BM, g.M - m0) * srow));
+    rsSB = rsrc_words(reinterpret_cast<const uint8_t*>(g.sw) + (int64_t)n0 * srow, (uint32_t)(min(C::BN, g.N - n0) * srow));
+  }
+
+  uint8_t* pad = smem + kNBuf * C::STAGE;
+  CodeCopy<C::P, C::NA, C::NW> cpA;
+  CodeCopy<C::P, C::NB, C::NW> cpB;
+  ScaleCopy<C::SP, (C::NSA > 0 ? C::NSA : 1), C::NW> cpSA;
+  ScaleCopy<C::SP, (C::NSB > 0 ? C::NSB : 1), C::NW> cpSB;
+  cpA.init(wave, lane, rowbytes);
+  cpB.init(wave, lane, rowbytes);
+  if constexpr (FMT == W_NVFP4) {
+    cpSA.init(wave, lane, srow);
+    cpSB.init(wave, lane, srow);
+  }
+  auto copy_stage = [&](int s) {
+    uint8_t* base = smem + (s % kNBuf) * C::STAGE;
+    cpA.issue(rsA, base, pad, rowbytes, s, wave);
+    cpB.issue(rsB, base + C::A_BYTES, pad, rowbytes, s, wave);
+    if constexpr (FMT == W_NVFP4) {
+      cpSA.issue(rsSA, base + C::A_BYTES + C::B_BYTES, pad, srow, s, wave);
+      cpSB.issue(rsSB, base + C::A_BYTES + C::B_BYTES + C::SA_BYTES, pad, srow, s, wave);
+    }
+  };
+
+  acc_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+
+  // Per-lane LDS offsets of the fragment rows (the swizzle term does not
+  // depend on the fragment index: fragments are 16 rows apart).  Lane
+  // group lq of K-group kw owns logical slot 4 kw + lq of each row.
+  const int L = kw * (kSeg / 16) + lq;
+  const int aoff = (wm0 + lr) * C::P + ((L ^ swz<C::P>(wm0 + lr)) * 16);
+  const int boff = C::A_BYTES + (wn0 + lr) * C::P + ((L ^ swz<C::P>(wn0 + lr)) * 16);
+  const int saoff = C::A_BYTES + C::B_BYTES + (wm0 + lr) * C::SP + kw * (kSeg / 8) + lq * 2;
+  const int sboff = C::A_BYTES + C::B_BYTES + C::SA_BYTES + (wn0 + lr) * C::SP + kw * (kSeg / 8) + lq * 2;
+
+  // Pipeline.  Copies run three stages ahead of the MFMAs, and the
+  // fragments of stage s + 1 are read from LDS into registers while stage
+  // s is widened and multiplied from the registers read one iteration
+  // earlier.  Iteration s: wait until stage s + 1 has landed (one later
+  // stage may still be in flight), barrier, copy stage s + 3 into the
+  // buffer of stage s - 1 (read two iterations ago), read stage s + 1,
+  // compute stage s.  Stages past the end are still copied (zeros) and
+  // read, so every iteration waits on the same count and has no branches.
+  struct Frags {
+    uint4 a[TI], b[TJ];
+    uint32_t sa[TI], sb[TJ];
+  };
+  auto read_frags = [&](int s, Frags& f) {
+    const uint8_t* base = smem + (s % kNBuf) * C::STAGE;
+    if constexpr (FMT == W_NVFP4) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) f.sa[i] = *reinterpret_cast<const uint16_t*>(base + saoff + i * 16 * C::SP);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) f.sb[j] = *reinterpret_cast<const uint16_t*>(base + sboff + j * 16 * C::SP);
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const uint4*>(base + aoff + i * 16 * C::P);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) f.b[j] = *reinterpret_cast<const uint4*>(base + boff + j * 16 * C::P);
+  };
+  struct Ops {
+    uint4 a[TI], b[TJ];
+  };
+  auto widen = [&](const Frags& f, int st, Ops& o) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) o.a[i] = operand<FMT>(f.a[i], st, FMT == W_NVFP4 ? f.sa[i] : 0u);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) o.b[j] = operand<FMT>(f.b[j], st, FMT == W_NVFP4 ? f.sb[j] : 0u);
+  };
+  auto mma_step = [&](const Ops& o) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) mfma_w<FMT>(acc[i][j], o.a[i], o.b[j]);
+  };
+  constexpr int NV = FMT == W_NVFP4 ? 3 : (FMT == W_INT4 ? 2 : 0);
+  auto sync_stage = [&](int wait_stages) {
+    if (wait_stages == 1) wait_vmcnt<C::DPS>(); else wait_vmcnt<C::DPS * (kNBuf - 2)>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+#pragma unroll
+  for (int p = 0; p < kNBuf - 1; ++p) copy_stage(p);
+  if constexpr (FMT != W_NVFP4) {
+    // Two fragment sets and two widened operand sets.  The operands of an
+    // MFMA step are widened during the previous step's MFMAs; step 0 of
+    // stage s + 1 is widened from the fragments read in iteration s.
+    // Iteration s: wait for stage s + 1, barrier, copy stage s + 3 (into
+    // the buffer of stage s - 1, read two iterations ago), read stage s + 1,
+    // then the MFMA steps of stage s.
+    sync_stage(2);   // stage 0 landed
+    Frags f0, f1;
+    read_frags(0, f0);
+    Ops w, x;
+    widen(f0, 0, w);
+    auto iter = [&](int s, const Frags& cur, Frags& nxt) {
+      sync_stage(1);
+      copy_stage(s + kNBuf - 1);
+      read_frags(s + 1, nxt);
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        Ops& now = (st & 1) ? x : w;
+        Ops& next = (st & 1) ? w : x;
+        if (st + 1 < STEPS) widen(cur, st + 1, next); else widen(nxt, 0, next);
+        mma_step(now);
+      }
+      interleave_steps<TI + TJ, TI * TJ * STEPS, NV>();
+    };
+    static_assert(STEPS % 2 == 0 || STEPS == 1, "operand sets alternate per step");
+    int s = 0;
+    if constexpr (STEPS == 1) {
+      // one step per stage: the widened sets alternate per stage
+      auto iter1 = [&](int s1, const Frags& cur, Frags& nxt, Ops& now, Ops& next) {
+        (void)cur;
+        sync_stage(1);
+        copy_stage(s1 + kNBuf - 1);
+        read_frags(s1 + 1, nxt);
+        widen(nxt, 0, next);
+        mma_step(now);
+        interleave_steps<TI + TJ, TI * TJ, NV>();
+      };
+      for (; s + 1 < nk; s += 2) {
+        iter1(s, f0, f1, w, x);
+        iter1(s + 1, f1, f0, x, w);
+      }
+      if (s < nk) iter1(s, f0, f1, w, x);
+    } else {
+      for (; s + 1 < nk; s += 2) {
+        iter(s, f0, f1);
+        iter(s + 1, f1, f0);
+      }
+      if (s < nk) iter(s, f0, f1);
+    }
+  } else {
+    // NVFP4 keeps one fragment set (its widened operands and scales leave
+    // no registers for a second): read stage s, then widen each MFMA step
+    // during the previous step's MFMAs.
+    for (int s = 0; s < nk; ++s) {
+      sync_stage(2);   // stage s landed
+      copy_stage(s + kNBuf - 1);
+      Frags f;
+      read_frags(s, f);
+      Ops w, x;
+      widen(f, 0, w);
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        Ops& now = (st & 1) ? x : w;
+        Ops& next = (st & 1) ? w : x;
+        if (st + 1 < STEPS) widen(f, st + 1, next);
+        mma_step(now);
+      }
+      interleave_steps<(TI + TJ) * 2, TI * TJ * STEPS, NV>();
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();   // all copies landed and all waves are done with the stage buffers
+
+  constexpr int KIND = FMT == W_NVFP4 ? 2 : (FMT == W_INT4 ? 0 : 1);
+  if constexpr (WK == 1) {
+    epilogue_tiles<KIND>(acc, g, m0 + wm0, n0 + wn0, lane);
+  } else {
+    // Sum the WK partial tiles: every wave stores its tile, then wave group
+    // kw adds up columns [kw * TJ / WK, (kw + 1) * TJ / WK) and runs the
+    // epilogue on them.
+    constexpr int TJW = TJ / WK;
+    typedef typename std::conditional<FMT == W_NVFP4, float, int32_t>::type el_t;
+    el_t* red = reinterpret_cast<el_t*>(smem);
+    auto slot = [&](int k, int i, int j, int r) {   // element index of (group k, wave wrc, tile i j, r, lane)
+      return ((((k * (WR * WC) + wrc) * TI + i) * TJ + j) * 4 + r) * 64 + lane;
+    };
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[slot(kw, i, j, r)] = acc[i][j][r];
+    __syncthreads();
+    acc_t part[TI][TJW];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TJW; ++jj) {
+        const int j = kw * TJW + jj;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          el_t v = red[slot(0, i, j, r)];
+#pragma unroll
+          for (int k = 1; k < WK; ++k) v += red[slot(k, i, j, r)];
+          part[i][jj][r] = v;
+        }
+      }
+    epilogue_tiles<KIND>(part, g, m0 + wm0, n0 + wn0 + kw * TJW * 16, lane);
+  }
+}
+
+namespace {
+
+struct WideChoice {
+  int cfg;
+  int64_t tm, tn;
+};
+
+// Candidate tilings (tile rows, tile columns, relative efficiency of the
+// wave tile); the cost is rounds of 256 workgroups times tile work.
+constexpr int kNumCfg = 4;
+constexpr int kCfgBM[kNumCfg] = {256, 128, 128, 64};
+constexpr int kCfgBN[kNumCfg] = {160, 256, 96, 64};
+constexpr double kCfgEff[kNumCfg] = {0.95, 0.9, 0.8, 0.7};
+
+WideChoice choose(int64_t M, int64_t N) {
+  WideChoice best{-1, 0, 0};
+  double best_cost = 0;
+  for (int c = 0; c < kNumCfg; ++c) {
+    const int64_t tm = (M + kCfgBM[c] - 1) / kCfgBM[c], tn = (N + kCfgBN[c] - 1) / kCfgBN[c];
+    const int64_t rounds = (tm * tn + 255) / 256;
+    const double cost = (double)rounds * kCfgBM[c] * kCfgBN[c] / kCfgEff[c];
+    if (best.cfg < 0 || cost < best_cost) {
+      best = {c, tm, tn};
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <int FMT>
+hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
+  const WideChoice c = choose(g.M, g.N);
+  const dim3 grid((unsigned)(c.tm * c.tn));
+  const int tm = (int)c.tm, tn = (int)c.tn;
+  switch (c.cfg) {
+    case 0: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 5, 4, 2, 1>), grid, dim3(512), 0, st, g, tm, tn); break;
+    case 1: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 2, 4, 1>), grid, dim3(512), 0, st, g, tm, tn); break;
+    case 2: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 6, 2, 1, 2>), grid, dim3(256), 0, st, g, tm, tn); break;
+    default: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 1, 1, 4>), grid, dim3(256), 0, st, g, tm, tn); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st) {
+  if (fmt == 0) return launch_wide_fmt<W_INT4>(g, st);
+  if (fmt == 1) return launch_wide_fmt<W_INT8>(g, st);
+  return launch_wide_fmt<W_NVFP4>(g, st);
+}
+
+}  // namespace w4a4
