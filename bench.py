@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--eager", action="store_true", help="launch every call from Python (no HIP graph)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain elementwise copy of 256 MiB five times (hardware-counter scale)")
+    p.add_argument("--summarize-profiles", metavar="DIR",
+                   help="turn rocprofv3 outputs under DIR (kt_<workload>, pmc_<workload>_<counter>, "
+                        "pmc_copy_<counter>) into the text summaries under profiles/ and exit (no GPU)")
     return p.parse_args()
 
 
@@ -234,7 +237,7 @@ def measure(torch, wl, steps, warmup):
         roof = {"bound": "mfma", "achieved": flop_k / (k_ms * 1e-3) / 1e12, "peak": PEAK_TFLOPS[mtype],
                 "unit": "TFLOP/s" if mtype != "i8" else "TOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(wl)
     roof["kernel"] = f"{'w8a8_linear' if c.fmt == 'int8' else 'w4a4_linear'} {c.fmt} {c.M}x{c.N}x{c.K}"
     roof["kernel_us"] = k_ms * 1e3
     roof["algorithmic_bytes"] = bytes_k
@@ -260,8 +263,122 @@ def copy_calibration(torch):
                                            "write_bytes": 4 * n, "launches": 5}}), flush=True)
 
 
+
+# ---------------------------------------------------------------------------
+# Profile summaries (rocprofv3 outputs -> profiles/*.txt, profiles/traffic.json)
+# ---------------------------------------------------------------------------
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["quantize.hip", "gemm_int.hip", "gemm_wide.hip", "branch.hip", "epilogue.h", "device_common.h"]
+
+# The dominant call of each workload: the kernels one linear call launches.
+DOMINANT = {
+    "batch1": ("w8a8_linear int8 64x2048x8192", ["gemm_int_decode_kernel<false, 4>", "gemm_int_reduce_kernel<false>"]),
+    "video4096": ("w4a4_linear nvfp4 4096x5120x5120", ["gemm_wide_kernel<2,"]),
+    "prefill": ("w4a4_linear int4 512x16384x2048", ["gemm_wide_kernel<0, 4, 4, 2, 4, 1>"]),
+    "lowrank": ("w4a4_linear int4 1024x3072x3072", ["gemm_wide_kernel<0, 4, 6, 2, 1, 2>"]),
+}
+
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/kt_{w} -o run -- "
+             "python3 bench.py --workload {w} --steps 100 --warmup 10 --no-cpu-baseline --no-also",
+    "pmc": "rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_{w}_{c} -o run -- "
+           "python3 bench.py --workload {w} --steps 5 --warmup 1 --eager --no-cpu-baseline --no-also",
+    "copy": "rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_copy_{c} -o run -- python3 bench.py --copy-calibration",
+}
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "w4a4_post_quantized_channel_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(wl):
+    """HBM bytes per dominant call from the committed counter summary, or
+    None when there is none or the kernel sources changed since."""
+    try:
+        with open(os.path.join(PROFILES, "traffic.json")) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = rec.get("workloads", {}).get(wl)
+    if not e or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return {"fetch_bytes": e["fetch_bytes"], "write_bytes": e["write_bytes"],
+            "total_bytes": e["fetch_bytes"] + e["write_bytes"]}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_profiles(d):
+    """Write profiles/<kernel>_<workload>.txt (kernel-trace statistics) and
+    profiles/traffic.json (FETCH_SIZE / WRITE_SIZE per dominant call, scaled
+    by the same counters read on a plain copy of known size)."""
+    import re
+    os.makedirs(PROFILES, exist_ok=True)
+    factor = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = [r for r in _csv_rows(os.path.join(d, f"pmc_copy_{c}", "run_counter_collection.csv"))
+                if "MulFunctor" in r["Kernel_Name"]]
+        kib = sum(float(r["Counter_Value"]) for r in rows) / len(rows)
+        factor[c] = (256 * 1024) / kib          # known KiB per launch / counter KiB
+    traffic = {"source_hash": kernel_source_hash(), "copy_scale": factor,
+               "commands": {k: v for k, v in PROFILE_CMDS.items()}, "workloads": {}}
+    for wl, (label, kernels) in DOMINANT.items():
+        kt = os.path.join(d, f"kt_{wl}", "run_kernel_stats.csv")
+        if not os.path.exists(kt):
+            continue
+        stats = _csv_rows(kt)
+        lines = [f"rocprofv3 kernel-trace statistics, workload {wl} ({WORKLOADS[wl][1]})",
+                 "command: " + PROFILE_CMDS["trace"].format(w=wl), "",
+                 f"{'kernel':72s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}"]
+        for r in stats:
+            name = re.sub(r"\(.*", "", r["Name"])[:72]
+            lines.append(f"{name:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                         f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+        dom_us = sum(float(r["AverageNs"]) / 1e3 for r in stats if any(k in r["Name"] for k in kernels))
+        lines += ["", f"dominant call: {label} = {' + '.join(kernels)}; sum of average durations {dom_us:.2f} us"]
+        per = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            f = os.path.join(d, f"pmc_{wl}_{c}", "run_counter_collection.csv")
+            if not os.path.exists(f):
+                continue
+            tot, found = 0.0, True
+            for k in kernels:
+                vals = [float(r["Counter_Value"]) for r in _csv_rows(f) if k in r["Kernel_Name"]]
+                if not vals:
+                    found = False
+                    break
+                tot += sum(vals) / len(vals)
+            if not found:
+                continue
+            per[c] = tot * factor[c] * 1024.0
+            lines.append(f"{c}: {tot:.1f} KiB per call (counter) x {factor[c]:.4f} (copy scale) = "
+                         f"{per[c] / 1e6:.3f} MB   [" + PROFILE_CMDS["pmc"].format(w=wl, c=c) + "]")
+        if len(per) == 2:
+            traffic["workloads"][wl] = {"call": label, "fetch_bytes": per["FETCH_SIZE"],
+                                        "write_bytes": per["WRITE_SIZE"], "avg_us": dom_us}
+        slug = re.sub(r"[^a-z0-9]+", "_", label.lower()).strip("_")
+        with open(os.path.join(PROFILES, f"{slug}_{wl}.txt"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+    traffic["copy_commands"] = [PROFILE_CMDS["copy"].format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as fh:
+        json.dump(traffic, fh, indent=1)
+    print(f"wrote summaries for {sorted(traffic['workloads'])} into {PROFILES}")
+
+
 def main():
     a = parse()
+    if a.summarize_profiles:
+        summarize_profiles(a.summarize_profiles)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (every box here has one GPU)",
               file=sys.stderr)

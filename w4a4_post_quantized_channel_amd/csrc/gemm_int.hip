@@ -129,46 +129,41 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     for (int r = 0; r < 4; ++r)
       tot[0][j][r] = red[0][wave][j][r][lane] + red[1][wave][j][r][lane] + red[2][wave][j][r][lane] +
                      red[3][wave][j][r][lane];
-  if (part) {  // lane-contiguous partial tile: 16 ints (64 bytes) per lane
+  if (part) {  // one contiguous 1 KB block per (tile, row block, 16-column block, split)
     const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    uint4* p = reinterpret_cast<uint4*>(part + ((tile * gridDim.z + blockIdx.z) * 4 + wave) * (TJ * 256)) +
-               lane * TJ;
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) p[j] = __builtin_bit_cast(uint4, tot[0][j]);
+    for (int j = 0; j < TJ; ++j) {
+      uint4* p = reinterpret_cast<uint4*>(part + (((tile * 4 + wave) * TJ + j) * gridDim.z + blockIdx.z) * 256);
+      p[lane] = __builtin_bit_cast(uint4, tot[0][j]);
+    }
     return;
   }
   epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0 + wave * 16, n0, lane);
 }
 
-// One wave per (tile, row block): add the S partial tiles, then the epilogue.
+// One wave per 16 x 16 output tile (tile, row block, column block): add its
+// S partial blocks (coalesced 1 KB reads, all in flight), then the epilogue.
 template <bool INT4>
 __global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, const int32_t* part) {
   constexpr int TJ = kDecTJ;
+  constexpr int ZB = 16;  // partial blocks whose loads are in flight together
   const int lane = threadIdx.x;
   const int nt = (g.N + 16 * TJ - 1) / (16 * TJ);
-  const int64_t tile = blockIdx.x >> 2;
-  const int rb = blockIdx.x & 3;
-  const int n0 = (int)(tile % nt) * 16 * TJ, m0 = (int)(tile / nt) * 64;
-  v4i tot[1][TJ];
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) tot[0][j] = v4i{0, 0, 0, 0};
-  constexpr int ZB = 8;  // partial tiles whose loads are in flight together
+  const int64_t blk = blockIdx.x;              // (tile * 4 + rb) * TJ + j
+  const int j = (int)(blk % TJ), rb = (int)((blk / TJ) & 3);
+  const int64_t tile = blk / (4 * TJ);
+  const int n0 = (int)(tile % nt) * 16 * TJ + j * 16, m0 = (int)(tile / nt) * 64 + rb * 16;
+  const uint4* p = reinterpret_cast<const uint4*>(part + blk * S * 256) + lane;
+  v4i tot[1][1] = {{v4i{0, 0, 0, 0}}};
   for (int z0 = 0; z0 < S; z0 += ZB) {
-    uint4 v[ZB][TJ];
+    uint4 v[ZB];
 #pragma unroll
-    for (int dz = 0; dz < ZB; ++dz) {
-      const int z = z0 + dz < S ? z0 + dz : S - 1;
-      const uint4* p = reinterpret_cast<const uint4*>(part + ((tile * S + z) * 4 + rb) * (TJ * 256)) + lane * TJ;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) v[dz][j] = p[j];
-    }
+    for (int dz = 0; dz < ZB; ++dz) v[dz] = p[(z0 + dz < S ? z0 + dz : S - 1) * 64];
 #pragma unroll
     for (int dz = 0; dz < ZB; ++dz)
-      if (z0 + dz < S)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) tot[0][j] += __builtin_bit_cast(v4i, v[dz][j]);
+      if (z0 + dz < S) tot[0][0] += __builtin_bit_cast(v4i, v[dz]);
   }
-  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0 + rb * 16, n0, lane);
+  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0, n0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -219,7 +214,7 @@ hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes
       else hipLaunchKernelGGL((gemm_int_decode_kernel<false, 1>), grid, dim3(256), 0, st, g, g.K, part);
     }
     if (split) {
-      dim3 rgrid((unsigned)(p.tiles * 4));
+      dim3 rgrid((unsigned)(p.tiles * 4 * kDecTJ));
       if (int4) hipLaunchKernelGGL((gemm_int_reduce_kernel<true>), rgrid, dim3(64), 0, st, g, p.splits, part);
       else hipLaunchKernelGGL((gemm_int_reduce_kernel<false>), rgrid, dim3(64), 0, st, g, p.splits, part);
     }
