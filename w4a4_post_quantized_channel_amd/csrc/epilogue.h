@@ -49,9 +49,15 @@ __device__ __forceinline__ void branch_mfma(v4f (&acc)[TI][TJ], const BranchArgs
 // y_dtype 2 writes the raw integer accumulators.  Stores go through a
 // buffer resource over the tile's rows (rows past M fall outside it) with
 // 32-bit offsets; columns past N are sent past the resource.
+// LDS bytes a wave needs to stage a TI x TJ tile of bf16 output.
+template <int TI, int TJ>
+constexpr int epilogue_stage_bytes() {
+  return TI * 16 * (TJ * 32 + 16);
+}
+
 template <int KIND /*0 int4, 1 int8, 2 float*/, typename AccT, int TI, int TJ>
 __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
-                                               int lane) {
+                                               int lane, uint8_t* stage = nullptr) {
   const int lr = lane & 15, lq = lane >> 4;
   const int esz = g.y_dtype == 1 ? 2 : 4;
   const int rows = max(0, min(TI * 16, g.M - m_base));
@@ -116,6 +122,16 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
         for (int r = 0; r < 4; ++r) col[i][0][r] = acc[i][j][r] * g.alpha;
     }
     if (g.br.r > 0) branch_mfma<TI, 1>(col, g.br, g.M, g.N, m_base, n_base + j * 16, lane);
+    if (stage != nullptr && g.y_dtype == 1) {
+      // bf16 into the wave's LDS tile (row pitch TJ * 32 + 16 bytes)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<uint16_t*>(stage + (i * 16 + lq * 4 + r) * (TJ * 32 + 16) + (j * 16 + lr) * 2) =
+              (uint16_t)f32_to_bf16_bits(col[i][0][r]);
+      continue;
+    }
     if (g.y_dtype == 0) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
@@ -129,6 +145,32 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
         for (int r = 0; r < 4; ++r)
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(col[i][0][r]), ry,
                                                 (int)(roff[i][r] + coff), 0, 0);
+    }
+  }
+  if (stage != nullptr && g.y_dtype == 1) {
+    // Rows back out of LDS, 16 bytes (8 columns) per lane: every row of the
+    // tile leaves as whole contiguous segments.
+    constexpr int CPR = TJ * 2;                  // 16-byte chunks per row
+    constexpr int NCH = TI * 16 * CPR;           // chunks in the tile
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c0 = 0; c0 < NCH; c0 += 64) {
+      const int c = c0 + lane;
+      if (NCH % 64 != 0 && c >= NCH) break;
+      const int row = c / CPR, ch = c % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (TJ * 32 + 16) + ch * 16);
+      const int n = n_base + ch * 8;
+      const uint32_t off = (uint32_t)row * rstride + (uint32_t)n * 2u;
+      if (n + 8 <= g.N) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), ry, (int)off, 0, 0);
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < g.N)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[e >> 1] >> (16 * (e & 1))), ry, (int)(off + 2 * e),
+                                                  0, 0);
+      }
     }
   }
 }

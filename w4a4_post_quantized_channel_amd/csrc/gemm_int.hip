@@ -13,8 +13,7 @@
 // Both operands get the same lane permutation, so v_mfma_i32_16x16x64_i8
 // returns exactly 256 * sum(qa * qw); the epilogue shifts right by 8.
 //
-// This file holds the few-token path; many tokens go to the shared tile
-// kernel (gemm_mfma.hip).
+// This file holds the few-token path; many tokens go to gemm_wide.hip.
 //  * decode kernel (<= 64 tokens, weight streaming): 64 token rows x 64
 //    output channels per workgroup of four waves.  No LDS staging: each
 //    wave loads its MFMA operands straight from global memory with raw

@@ -478,7 +478,9 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 
   constexpr int KIND = FMT == W_NVFP4 ? 2 : (FMT == W_INT4 ? 0 : 1);
   if constexpr (WK == 1) {
-    epilogue_tiles<KIND>(acc, g, m0 + wm0, n0 + wn0, lane);
+    // bf16 output is staged through this wave's slice of the (now idle) LDS
+    static_assert(C::NW * epilogue_stage_bytes<TI, TJ>() <= C::LDS, "epilogue staging fits");
+    epilogue_tiles<KIND>(acc, g, m0 + wm0, n0 + wn0, lane, smem + wave * epilogue_stage_bytes<TI, TJ>());
   } else {
     // Sum the WK partial tiles: every wave stores its tile, then wave group
     // kw adds up columns [kw * TJ / WK, (kw + 1) * TJ / WK) and runs the

@@ -40,9 +40,7 @@ struct GemmArgs {
 hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st);
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 
-// gemm_mfma.hip: many-token tile kernel (widened operands in LDS), fmt 0 int4, 1 int8, 2 nvfp4
-hipError_t launch_gemm_tile(int fmt, GemmArgs g, hipStream_t st);
-// gemm_wide.hip: many-token kernel with packed operands in LDS (same formats)
+// gemm_wide.hip: many-token kernel with packed operands in LDS, fmt 0 int4, 1 int8, 2 nvfp4
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st);
 
 // branch.hip ----------------------------------------------------------------
