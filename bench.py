@@ -130,7 +130,7 @@ def dominant_kernel_time(torch, case, layer, t, steps):
     from w4a4_post_quantized_channel_amd import ops
     br = None
     if layer.branch is not None:
-        br = ops.branch_desc(b["br_a"], layer.branch["lw"])
+        br = ops.branch_desc(layer.branch_operand(case.M, t["x"].device), layer.branch["lw"])
 
     def gemm():
         if case.fmt == "int8":

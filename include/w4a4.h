@@ -50,6 +50,7 @@ extern "C" {
 
 #define W4A4_ABI_VERSION 1
 #define W4A4_MAX_BRANCH 128 /* largest branch width (rank or kept channels) */
+#define W4A4_LOWRANK_MAX_PARTS 4 /* K parts of a low-rank projection (see w4a4_lowrank_width) */
 
 typedef enum w4a4_status {
   W4A4_OK = 0,
@@ -92,11 +93,12 @@ typedef struct w4a4_qdesc {
  * bypass of kept channels).  Adds  sum_j a[m, j] * b[n, j mod r]  for
  * j < ra to every output, in fp32 after the dequantised main product.
  *  a   bf16, M x ra, row stride lda (elements).  For a rank-r factor product
- *      (x L1) L2 it holds the hi and lo bf16 halves of x L1 (ra = 2r,
- *      produced by w4a4_lowrank_project); for kept channels it holds
- *      x[:, idx] (ra = r).
+ *      (x L1) L2 it holds the hi and lo bf16 halves of x L1 (ra = 2r, as
+ *      produced by w4a4_lowrank_project), or P such pairs whose sum is
+ *      x L1 (ra = 2 P r); for kept channels it holds x[:, idx] (ra = r).
  *  b   bf16, N x r, row stride ldb: L2 transposed, or W[:, idx].
- *  r   1..W4A4_MAX_BRANCH; ra is r or 2r.
+ *  r   8..W4A4_MAX_BRANCH, a multiple of 8; ra is r or 2 P r with
+ *      1 <= P <= W4A4_LOWRANK_MAX_PARTS.
  */
 typedef struct w4a4_branch {
   int32_t kind;
@@ -201,14 +203,25 @@ int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx,
                 void* stream);
 
 /* w4a4_lowrank_project -- first half of the branch, producing the
- * w4a4_branch ``a`` operand: for l1t != NULL (L1 transposed, bf16 r x K),
- * t = x L1 in fp32 written as bf16 hi = bf16(t) and lo = bf16(t - hi) (out
- * is M x 2r: columns [0, r) hi, [r, 2r) lo); for idx != NULL,
+ * w4a4_branch ``a`` operand.  For l1t != NULL (L1 transposed, bf16 r x K):
+ * t = x L1 in fp32, written as bf16 hi = bf16(t) and lo = bf16(t - hi) in
+ * columns [0, r) and [r, 2r) of out (the branch's ra = 2r).  For few rows K
+ * is cut into P parts computed by separate workgroups (P is a function of
+ * M and K); their fp32 partial products are staged in the rest of the row
+ * and added in part order, so out needs w4a4_lowrank_width(M, K, r) = 2 P r
+ * columns, of which the first 2r hold the result.  For idx != NULL,
  * out = x[:, idx] (M x r, exact).
- *  x bf16 M x K (row stride ldx); out bf16 with row stride ldo. */
+ *  x bf16 M x K (row stride ldx); out bf16 with row stride
+ *  ldo >= w4a4_lowrank_width(M, K, l1t ? r : -r). */
 int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx,
                          const void* l1t, const int32_t* idx, int64_t r,
                          void* out, int64_t ldo, void* stream);
+
+/* w4a4_lowrank_width -- columns w4a4_lowrank_project needs in its output:
+ * 2 P r for a rank-r projection of an M x K input (r > 0; the result is in
+ * the first 2r), or |r| for a gather of |r| kept channels (r < 0).
+ * Host-only, no device access. */
+int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r);
 
 /* w4a4_transform_amax -- max |transform(x)| over a whole R x K tensor,
  * written to amax_out (device fp32[1]).  The calibration statistic of the

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIBPATH), reason="libw4a4.so 
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^(?:int|int64_t|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
 
 
 @pytest.fixture(scope="module")
@@ -40,6 +40,16 @@ def test_library_exports_every_declared_symbol(ops):
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
     assert ops.LIB.w4a4_abi_version() == 1
+
+
+def test_lowrank_width_host_query(ops):
+    L = ops.LIB
+    # gather: |r| columns; projection: 2 P r with 1 <= P <= 4, P*64 <= K, more parts for fewer rows
+    assert L.w4a4_lowrank_width(1024, 3072, -64) == 64
+    assert L.w4a4_lowrank_width(4096, 5120, 32) == 64           # 256 row blocks: no split
+    assert L.w4a4_lowrank_width(1024, 3072, 32) == 2 * 4 * 32   # 64 row blocks: four parts
+    assert L.w4a4_lowrank_width(50, 128, 24) == 2 * 2 * 24      # parts capped by K / 64
+    assert L.w4a4_lowrank_width(50, 64, 8) == 16
 
 
 def test_status_strings(ops):

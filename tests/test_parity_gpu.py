@@ -61,6 +61,9 @@ SMALL = [
     ("nvfp4_plain", 66, 72, 256, "nvfp4", "bf16", dict(n_outliers=4, outlier_gain=10.0)),
     ("int4_single_row", 1, 64, 64, "int4", "bf16", dict()),
     ("int8_lowrank", 33, 48, 192, "int8", "bf16", dict(lowrank=8)),
+    # >= 256 rows: the row-per-lane NVFP4 quantizer (ragged last group of 64 rows)
+    ("nvfp4_rows", 300, 96, 320, "nvfp4", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=8)),
+    ("nvfp4_rows_f32", 260, 64, 256, "nvfp4", "f32", dict(n_outliers=4, outlier_gain=20.0)),
 ]
 
 
@@ -220,8 +223,10 @@ def test_lowrank_add_standalone(ops, pipe):
 def test_lowrank_project(ops, pipe):
     case = WL.linear_case(50, 8, 512, seed=41, lowrank=24)
     t = pipe.case_to_device(case)
+    assert ops.lowrank_width(50, 512, 24) >= 96          # few rows: K split in parts
     out = _np(ops.lowrank_project(t["x"], l1t=t["branch"]["l1t"]))
     T = case.x.astype(np.float64) @ case.branch["l1"].astype(np.float64)
+    assert out.shape == (50, 48)
     recon = out[:, :24].astype(np.float64) + out[:, 24:].astype(np.float64)
     assert np.max(np.abs(recon - T)) <= 2.0 ** -15 * np.max(np.abs(T))
     idx = torch.tensor([0, 5, 511, 100, 7, 8, 9, 300], dtype=torch.int32, device="cuda")

@@ -91,8 +91,8 @@ int check_branch(const char* fn, const w4a4_branch* br, int64_t M, int64_t N) {
   if (br->kind != W4A4_BRANCH_BF16) return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: unknown branch kind %d", fn, br->kind);
   if (br->r <= 0 || br->r > W4A4_MAX_BRANCH || br->r % 8 != 0)
     return fail(W4A4_ERR_INVALID_ARG, "%s: branch r=%d must be a multiple of 8 in [8, %d]", fn, br->r, W4A4_MAX_BRANCH);
-  if (br->ra != br->r && br->ra != 2 * br->r)
-    return fail(W4A4_ERR_INVALID_ARG, "%s: branch ra must be r or 2r", fn);
+  if (br->ra != br->r && !(br->ra % (2 * br->r) == 0 && br->ra / (2 * br->r) <= W4A4_LOWRANK_MAX_PARTS))
+    return fail(W4A4_ERR_INVALID_ARG, "%s: branch ra must be r or 2 p r with p <= %d", fn, W4A4_LOWRANK_MAX_PARTS);
   if (br->lda < br->ra || br->ldb < br->r || br->lda % 8 != 0 || br->ldb % 8 != 0)
     return fail(W4A4_ERR_INVALID_ARG, "%s: branch strides must be >= width and multiples of 8", fn);
   if (M > 0 && N > 0) {
@@ -220,12 +220,18 @@ int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1
   return launch_status(e, fn);
 }
 
+int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r) {
+  if (r < 0) return -r;   // gather: r kept channels
+  if (M <= 0 || K <= 0 || r <= 0) return 2 * (r > 0 ? r : 0);
+  return 2 * (int64_t)w4a4::lowrank_parts(M, K) * r;
+}
+
 int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t, const int32_t* idx,
                          int64_t r, void* out, int64_t ldo, void* stream) {
   const char* fn = "w4a4_lowrank_project";
   int st = check_lowrank(fn, x, M, K, ldx, l1t, idx, r);
   if (st != W4A4_OK) return st;
-  if (ldo < (l1t ? 2 * r : r)) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo too small", fn);
+  if (ldo < w4a4_lowrank_width(M, K, l1t ? r : -r)) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo too small", fn);
   if (M == 0) return ok();
   if (!out || !aligned(out, 2)) return fail(W4A4_ERR_INVALID_ARG, "%s: out NULL or misaligned", fn);
   if (M > INT32_MAX || K > INT32_MAX) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: too large", fn);

@@ -5,9 +5,11 @@
 // top-K mask, sec. 4.2).
 //
 //  * project: t = x L1 (fp32, v_mfma_f32_16x16x32_bf16 with L1 given
-//    transposed so both operands are K-contiguous, K split over the four
-//    waves of a 16-row block and summed in LDS), emitted as the bf16
-//    hi/lo pair the GEMM epilogue consumes; or the gather x[:, idx].
+//    transposed so both operands are K-contiguous).  K is cut into P parts
+//    (enough 16-row x part workgroups to fill the chip); each part's
+//    product is summed over its four waves in LDS and stored in fp32 in the
+//    output row, and a second kernel adds the P parts in order and writes
+//    the bf16 hi/lo pair the GEMM epilogue consumes; or the gather x[:, idx].
 //  * lowrank_add: the same projection kept in fp32 in LDS, then
 //    y[m, n] += sum_j t[m, j] lw[n, j] on the vector ALUs, one rounding to
 //    the output type.
@@ -76,25 +78,121 @@ __device__ void project_block(const uint16_t* x, int64_t ldx, int M, int K, cons
   }
 }
 
+// Number of K parts the projection is split into for M rows: enough
+// 16-row x part workgroups to fill the chip, each part at least 64 deep.
+int lowrank_parts(int64_t M, int64_t K) {
+  const int64_t rb = (M + kRows - 1) / kRows;
+  int64_t p = rb >= 256 ? 1 : (256 + rb - 1) / rb;
+  p = p > 4 ? 4 : p;
+  const int64_t pk = K / 64;
+  p = p > pk ? pk : p;
+  return (int)(p < 1 ? 1 : p);
+}
+
+// t_p = x[:, Kp] L1[Kp, :] for one 16-row block and one K part p, the part
+// split over the four waves (every load of a wave issued before its MFMAs;
+// out-of-range rows and columns read as zeros), summed in LDS, written as
+// bf16 hi/lo into columns [2 p r, 2 p r + 2r) of out.
 template <int TJ>
-__global__ void __launch_bounds__(256) project_kernel(const uint16_t* x, int64_t ldx, int M, int K,
-                                                      const uint16_t* l1t, const int32_t* idx, int r,
-                                                      uint16_t* out, int64_t ldo) {
-  __shared__ float sT[64 * 128];
-  const int m0 = blockIdx.x * kRows;
-  project_block<TJ>(x, ldx, M, K, l1t, idx, r, m0, sT);
-  for (int e = threadIdx.x; e < 16 * r; e += 256) {
+__global__ void __launch_bounds__(256) project_parts_kernel(const uint16_t* x, int64_t ldx, int M, int K,
+                                                            const uint16_t* l1t, int r, int parts,
+                                                            uint16_t* out, int64_t ldo) {
+  __shared__ float sT[4][16][TJ * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int m0 = blockIdx.x * kRows, part = blockIdx.y;
+  const int kp = ((K + parts * 64 - 1) / (parts * 64)) * 64;   // K per part, multiple of 64
+  const int kb = part * kp, ke = min(K, kb + kp);
+  const int kw = kp / 4;                                       // K per wave, multiple of 16
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m0 * ldx, (uint32_t)(max(0, min(kRows, M - m0)) * ldx * 2));
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(l1t, (uint32_t)((int64_t)r * K * 2));
+  v4f acc[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int k0 = kb + wave * kw, k1 = min(ke, k0 + kw);
+  constexpr int U = 4;   // 32-deep steps whose loads are in flight together
+  for (int k = k0; k < k1; k += 32 * U) {
+    uint4 xa[U], lb[U][TJ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kc = k + u * 32 + lq * 8;
+      const bool ok = kc < k1;
+      xa[u] = buf_load16(rx, ok ? (uint32_t)((lr * ldx + kc) * 2) : kOOB);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = j * 16 + lr;
+        lb[u][j] = buf_load16(rl, (ok && col < r) ? (uint32_t)(((int64_t)col * K + kc) * 2) : kOOB);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xa[u]), __builtin_bit_cast(v8bf, lb[u][j]),
+                                                         acc[j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sT[wave][lq * 4 + q][j * 16 + lr] = acc[j][q];
+  __syncthreads();
+  for (int e = tid; e < 16 * r; e += 256) {
     const int row = e / r, col = e % r, m = m0 + row;
     if (m >= M) continue;
-    const float t = sT[row * 128 + col];
-    if (l1t) {
+    const float t = sT[0][row][col] + sT[1][row][col] + sT[2][row][col] + sT[3][row][col];
+    if (parts == 1) {
       const uint32_t hi = f32_to_bf16_bits(t);
       const float lo = t - bf16_bits_to_f32(hi);
-      out[(int64_t)m * ldo + col] = (uint16_t)hi;
-      out[(int64_t)m * ldo + r + col] = (uint16_t)f32_to_bf16_bits(lo);
-    } else {
-      out[(int64_t)m * ldo + col] = (uint16_t)f32_to_bf16_bits(t);  // exact: t is a bf16 value
+      uint16_t* o = out + (int64_t)m * ldo;
+      o[col] = (uint16_t)hi;
+      o[r + col] = (uint16_t)f32_to_bf16_bits(lo);
+    } else {  // fp32 partial p at element p r + col of the row (the row holds 2 P r bf16 = P r fp32)
+      reinterpret_cast<float*>(out + (int64_t)m * ldo)[part * r + col] = t;
     }
+  }
+}
+
+// Sum of the P fp32 partial products of each row (in part order), written
+// in place as the bf16 hi/lo pair in columns [0, 2r): one wave per row; every
+// lane reads its partials before any lane of the wave writes.
+__global__ void __launch_bounds__(64) project_sum_kernel(int M, int r, int parts, uint16_t* out, int64_t ldo) {
+  const int64_t m = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* pr = reinterpret_cast<const float*>(out + m * ldo);
+  float t[2] = {0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = lane + 64 * h;
+    if (col < r) {
+      float acc = pr[col];
+      for (int p = 1; p < parts; ++p) acc = acc + pr[p * r + col];
+      t[h] = acc;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);      // all of this wave's reads returned
+  __builtin_amdgcn_wave_barrier();
+  uint16_t* o = out + m * ldo;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = lane + 64 * h;
+    if (col < r) {
+      const uint32_t hi = f32_to_bf16_bits(t[h]);
+      const float lo = t[h] - bf16_bits_to_f32(hi);
+      o[col] = (uint16_t)hi;
+      o[r + col] = (uint16_t)f32_to_bf16_bits(lo);
+    }
+  }
+}
+
+// Gather of kept channels: out[m, j] = x[m, idx[j]] (exact).
+__global__ void __launch_bounds__(256) gather_kernel(const uint16_t* x, int64_t ldx, int M, int K,
+                                                     const int32_t* idx, int r, uint16_t* out, int64_t ldo) {
+  const int64_t total = (int64_t)M * r;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t m = e / r;
+    const int j = (int)(e - m * r);
+    const int c = idx[j];
+    out[m * ldo + j] = (c >= 0 && c < K) ? x[m * ldx + c] : (uint16_t)0;
   }
 }
 
@@ -145,11 +243,22 @@ __global__ void __launch_bounds__(256) lowrank_add_kernel(const uint16_t* x, int
 hipError_t launch_lowrank_project(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   const uint16_t* l1t, const int32_t* idx, int r, uint16_t* out,
                                   int64_t ldo, hipStream_t st) {
-  dim3 grid((unsigned)((M + kRows - 1) / kRows));
-#define W4A4_PROJ(T) \
-  hipLaunchKernelGGL((project_kernel<T>), grid, dim3(256), 0, st, x, ldx, (int)M, (int)K, l1t, idx, r, out, ldo)
+  if (!l1t) {
+    int64_t blocks = (M * r + 255) / 256;
+    blocks = blocks > 2048 ? 2048 : (blocks < 1 ? 1 : blocks);
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, ldx, (int)M, (int)K, idx, r,
+                       out, ldo);
+    return hipGetLastError();
+  }
+  const int parts = lowrank_parts(M, K);
+  dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)parts);
+#define W4A4_PROJ(T)                                                                                       \
+  hipLaunchKernelGGL((project_parts_kernel<T>), grid, dim3(256), 0, st, x, ldx, (int)M, (int)K, l1t, r, parts, \
+                     out, ldo)
   W4A4_TJ_SWITCH(r, W4A4_PROJ)
 #undef W4A4_PROJ
+  if (parts > 1)
+    hipLaunchKernelGGL(project_sum_kernel, dim3((unsigned)M), dim3(64), 0, st, (int)M, r, parts, out, ldo);
   return hipGetLastError();
 }
 

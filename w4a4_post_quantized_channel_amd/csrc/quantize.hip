@@ -159,6 +159,54 @@ __device__ __forceinline__ uint32_t near_boundary(const float (&q)[16]) {
 constexpr float kBig = 1.2676506002282294e30f;     // 2^100
 constexpr float kMinA = 8.077935669463161e-28f;    // 2^-90: dividends at or above keep residuals normal
 
+// One NVFP4 block of 16 transformed values y = v * fl (fl a power of two,
+// possibly negative): E4M3 block scale e and the 16 E2M1 codes packed in two
+// dwords (low nibble first).  stab holds (S, RN(1/S)) per E4M3 code; live
+// says whether the block exists (a screened slot past the end of a row must
+// not take the exact path).
+__device__ __forceinline__ uint32_t nvfp4_block16(const float (&v)[16], float fl, float g, float rg, bool g_fast,
+                                                  const float2* stab, bool live, uint2& codes) {
+  float mv = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mv = fmaxf(mv, __builtin_fabsf(v[i]));
+  const float m = mv * __builtin_fabsf(fl);                                             // max |y| of the block
+  const float sb = m >= kMinA ? div_rn(m, 6.0f, 0.16666667163372040f) : m / 6.0f;      // RN(m / 6)
+  const float sv = (g_fast && sb >= kMinA) ? div_rn(sb, g, rg) : sb / g;                // RN(sb / g)
+  const uint32_t e = f32_to_e4m3_sat(sv);
+  const float2 SR = stab[e];
+  uint32_t w[2] = {0u, 0u};
+  if (SR.x > 0.f) {
+    const bool fast = SR.x >= kTinyStep && SR.x <= kBig;
+    const float D = SR.x / fl, rD = SR.y * fl;   // exact power-of-two rescaling
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = v[i] * rD;
+    if (live && (!fast || near_boundary(q) <= 8u)) {
+      if (fast) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = div_rn(v[i], D, rD);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = (v[i] * fl) / SR.x;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t d = 0;
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 0], q[8 * h + 1], 1.0f, 0);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 2], q[8 * h + 3], 1.0f, 1);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 4], q[8 * h + 5], 1.0f, 2);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 6], q[8 * h + 7], 1.0f, 3);
+      // the converter writes -0 as 0x8; the packed format uses +0
+      const uint32_t mag = d & 0x77777777u;
+      const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;
+      w[h] = mag | (d & nz);
+    }
+  }
+  codes = make_uint2(w[0], w[1]);
+  return e;
+}
+
 // Smoothing and rotation of one slot in place; returns the factor fl with
 // y = v * fl (see the kernel).
 template <bool BF16IN>
@@ -324,45 +372,10 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
         const int s = (c * WPR + sub) * 64 + lane;
         float vs[16];
         const float fl = transform_slot<BF16IN>(raw[c], vs, rsc, has_scale, a.rot, a.order, s, lane);
-        float mv = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mv = fmaxf(mv, __builtin_fabsf(vs[i]));
-        const float m = mv * __builtin_fabsf(fl);                                             // max |y| of the block
-        const float sb = m >= kMinA ? div_rn(m, 6.0f, 0.16666667163372040f) : m / 6.0f;  // RN(m / 6)
-        const float sv = (g_fast && sb >= kMinA) ? div_rn(sb, a.g, rg) : sb / a.g;   // RN(sb / g)
-        const uint32_t e = f32_to_e4m3_sat(sv);
-        const float2 SR = stab[e];
-        uint32_t w[2] = {0u, 0u};
-        if (SR.x > 0.f) {
-          const bool fast = SR.x >= kTinyStep && SR.x <= kBig;
-          const float D = SR.x / fl, rD = SR.y * fl;   // exact power-of-two rescaling
-          float q[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) q[i] = vs[i] * rD;
-          if (s < nslots && (!fast || near_boundary(q) <= 8u)) {
-            if (fast) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) q[i] = div_rn(vs[i], D, rD);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) q[i] = (vs[i] * fl) / SR.x;
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            uint32_t d = 0;
-            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 0], q[8 * h + 1], 1.0f, 0);
-            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 2], q[8 * h + 3], 1.0f, 1);
-            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 4], q[8 * h + 5], 1.0f, 2);
-            d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[8 * h + 6], q[8 * h + 7], 1.0f, 3);
-            // the converter writes -0 as 0x8; the packed format uses +0
-            const uint32_t mag = d & 0x77777777u;
-            const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;
-            w[h] = mag | (d & nz);
-          }
-        }
+        uint2 w;
+        const uint32_t e = nvfp4_block16(vs, fl, a.g, rg, g_fast, stab, s < nslots, w);
         if (s < nslots) {
-          *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = make_uint2(w[0], w[1]);
+          *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = w;
           reinterpret_cast<uint8_t*>(a.scales)[(size_t)row * (a.K >> 4) + s] = (uint8_t)e;
         }
       }
@@ -370,6 +383,122 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
   }
   if constexpr (MODE == MODE_AMAX) {
     if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(a.amax_out), __float_as_uint(tmax));
+  }
+}
+
+// NVFP4 quantizer for many rows, K a multiple of 64: lane = row.  A wave
+// takes 64 consecutive rows and one 64-channel Hadamard block; every
+// butterfly stage then runs inside one lane's registers, and the block's 64
+// smoothing factors are the same for the whole wave (scalar loads).  NVFP4
+// needs no row-wide reduction (its scales are per 16 elements and the tensor
+// scale is fixed), so every (rows, block) pair is independent.
+template <bool BF16IN, bool ROT>
+__global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
+  constexpr int ESZ = BF16IN ? 2 : 4;
+  constexpr int RB = 64 * ESZ;              // bytes of one row's 64-element block
+  constexpr int TILE = 64 * RB;             // one wave's 64 x 64 tile
+  __shared__ float2 stab[128];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][TILE];
+  for (int e = threadIdx.x; e < 128; e += blockDim.x) {
+    const float S = e < 0x7F ? e4m3_to_f32((uint32_t)e) * a.g : 0.f;
+    stab[e] = make_float2(S, S > 0.f ? 1.0f / S : 0.f);  // IEEE division
+  }
+  __syncthreads();
+  const float rg = 1.0f / a.g;   // RN(1/g)
+  const bool g_fast = a.g >= kTinyStep && a.g <= kBig;
+  const bool has_scale = a.scale != nullptr;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* tile = tiles[wave];
+  const int nblk = a.K >> 6;
+  const int64_t ngrp = (a.R + 63) >> 6;
+  const int64_t ntask = ngrp * nblk;
+  constexpr int CPR = RB / 16;              // 16-byte chunks per row of the tile
+  for (int64_t task = (int64_t)blockIdx.x * 4 + wave; task < ntask; task += (int64_t)gridDim.x * 4) {
+    const int64_t grp = task / nblk;
+    const int b = (int)(task - grp * nblk);
+    const int64_t row = grp * 64 + lane;
+    const bool live = row < a.R;
+    // Coalesced copy of the 64 x 64 tile into this wave's LDS slice: load
+    // instruction i covers tile bytes [1024 i, 1024 i + 1024); the chunk at
+    // slot q of tile row r holds logical chunk q ^ (r & 7) (so that the 64
+    // rows read back by the 64 lanes spread over the banks).  Rows past R
+    // read zeros.
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)(grp * 64) * a.ldx * ESZ,
+                  (uint32_t)(min((int64_t)64, a.R - grp * 64) * a.ldx * ESZ));
+#pragma unroll
+    for (int i = 0; i < TILE / 1024; ++i) {
+      const int p = i * 1024 + lane * 16;
+      const int r = p / RB, q = (p % RB) / 16;
+      const int L = q ^ (r & 7 & (CPR - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + i * 1024), 16,
+                                               r * (int)(a.ldx * ESZ) + b * RB + L * 16, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);   // vmcnt(0): this wave's copies are in LDS
+    float v[64];
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) {
+      const uint4 d = *reinterpret_cast<const uint4*>(tile + lane * RB + ((c ^ (lane & 7 & (CPR - 1))) * 16));
+      if constexpr (BF16IN) {
+        const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
+          v[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+      } else {
+        v[4 * c] = __uint_as_float(d.x); v[4 * c + 1] = __uint_as_float(d.y);
+        v[4 * c + 2] = __uint_as_float(d.z); v[4 * c + 3] = __uint_as_float(d.w);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();   // the next task's copies overwrite the slice only after these reads
+    // the block's 64 factors are the same for the whole wave: scalar loads
+    const __attribute__((address_space(4))) float* sc =
+        (const __attribute__((address_space(4))) float*)(a.scale + (has_scale ? b * 64 : 0));
+    if (has_scale && a.order == 0) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] = v[i] * sc[i];
+    }
+    float fl = 1.0f;
+    if constexpr (ROT) {
+#pragma unroll
+      for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+          if ((j & h) == 0) {
+            const float x0 = v[j], x1 = v[j + h];
+            v[j] = x0 + x1;
+            v[j + h] = x0 - x1;
+          }
+        }
+      }
+      fl = 0.125f;
+      if (a.order == 1) {  // rotate, then smooth: the factor must precede the smoothing product
+#pragma unroll
+        for (int i = 0; i < 64; ++i) v[i] = v[i] * 0.125f;
+        fl = 1.0f;
+      }
+    }
+    if (has_scale && a.order == 1) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] = v[i] * sc[i];
+    }
+    uint2 c[4];
+    uint32_t e4 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float vb[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vb[i] = v[16 * q + i];
+      e4 |= nvfp4_block16(vb, fl, a.g, rg, g_fast, stab, live, c[q]) << (8 * q);
+    }
+    if (live) {
+      uint4* cp = reinterpret_cast<uint4*>(a.codes + (size_t)row * (a.K >> 1) + b * 32);
+      cp[0] = make_uint4(c[0].x, c[0].y, c[1].x, c[1].y);
+      cp[1] = make_uint4(c[2].x, c[2].y, c[3].x, c[3].y);
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.scales) + (size_t)row * (a.K >> 4) + b * 4) = e4;
+    }
   }
 }
 
@@ -413,6 +542,20 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
                            const float* scale, float g, int rot, int order, void* codes, void* scales,
                            float* amax_out, hipStream_t st) {
   QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, amax_out};
+  if (mode == MODE_NVFP4 && R >= 256 && K % 64 == 0 && (rot == 0 || rot == 64)) {
+    const int64_t tasks = ((R + 63) / 64) * (K / 64);
+    int64_t blocks = (tasks + 3) / 4;
+    if (blocks > 256 * 8) blocks = 256 * 8;
+    const dim3 grid((unsigned)blocks);
+    if (bf16in) {
+      if (rot) hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<true, true>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<true, false>), grid, dim3(256), 0, st, a);
+    } else {
+      if (rot) hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<false, true>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<false, false>), grid, dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+  }
   const int64_t nslots = K / 16;
   // One wave per row when there are many rows and the row fits five chunks
   // per lane (the factors then stay in registers); else four waves per row.

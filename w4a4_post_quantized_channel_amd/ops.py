@@ -26,7 +26,7 @@ ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
 ABI_VERSION = 1
 
 EXPORTS = ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "lowrank_add",
-           "w4a4_lowrank_project", "w4a4_transform_amax", "w4a4_workspace_size", "w4a4_status_string",
+           "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_workspace_size", "w4a4_status_string",
            "w4a4_last_error", "w4a4_abi_version"]
 
 
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "w4a4_workspace_size": [i64, i64, i64, i32],
         "lowrank_add": [vp, i64, i64, i64, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp],
         "w4a4_lowrank_project": [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp],
+        "w4a4_lowrank_width": [i64, i64, i64],
         "w4a4_transform_amax": [vp, i32, i64, i64, i64, vp, qd, vp, vp],
         "w4a4_status_string": [ctypes.c_int],
         "w4a4_last_error": [],
@@ -72,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = ctypes.c_int
     lib.w4a4_workspace_size.restype = ctypes.c_size_t
+    lib.w4a4_lowrank_width.restype = ctypes.c_int64
     lib.w4a4_status_string.restype = ctypes.c_char_p
     lib.w4a4_last_error.restype = ctypes.c_char_p
     if lib.w4a4_abi_version() != ABI_VERSION:
@@ -174,7 +176,7 @@ def transform_amax(x: torch.Tensor, scale: Optional[torch.Tensor], *, fwht_block
 
 
 def branch_desc(a: Optional[torch.Tensor], b: Optional[torch.Tensor], r: Optional[int] = None) -> BranchDesc:
-    """Fused-branch descriptor: a is bf16 M x ra (ra = r or 2r), b is bf16 N x r."""
+    """Fused-branch descriptor: a is bf16 M x ra (ra = r, or 2 P r from lowrank_project), b is bf16 N x r."""
     if a is None:
         return BranchDesc(BRANCH_NONE, 0, 0, 0, None, 0, None, 0)
     r = b.shape[1] if r is None else r
@@ -242,15 +244,23 @@ def lowrank_add(x: torch.Tensor, y: torch.Tensor, lw: torch.Tensor, *, l1t: Opti
     return y
 
 
+def lowrank_width(M: int, K: int, r: int) -> int:
+    """Columns lowrank_project needs in its output: 2 P r for a rank-r
+    projection (r > 0; the result is the first 2r), or |r| for a gather of
+    |r| kept channels (r < 0)."""
+    return int(LIB.w4a4_lowrank_width(M, K, r))
+
+
 def lowrank_project(x: torch.Tensor, *, l1t: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
                     out=None, stream=None) -> torch.Tensor:
-    """The fused branch's ``a`` operand: [hi | lo] bf16 halves of x L1, or x[:, idx]."""
+    """The fused branch's ``a`` operand: [hi | lo] bf16 halves of x L1 (a view of
+    the first 2r columns of ``out``), or x[:, idx]."""
     _check_branch_inputs(x, l1t, idx)
     M, K, ldx = _rowmajor(x)
     r = l1t.shape[0] if l1t is not None else idx.shape[0]
-    width = 2 * r if l1t is not None else r
+    width = lowrank_width(M, K, r if l1t is not None else -r)
     if out is None:
         out = torch.empty((M, width), dtype=torch.bfloat16, device=x.device)
     _check("w4a4_lowrank_project", LIB.w4a4_lowrank_project(_ptr(x), M, K, ldx, _ptr(l1t), _ptr(idx), r, _ptr(out),
                                                             out.stride(0), _stream(stream)))
-    return out
+    return out[:, :2 * r] if l1t is not None else out

@@ -77,7 +77,7 @@ class QuantizedLinear:
             br_a = None
             if self.branch is not None:
                 r = self.branch["lw"].shape[1]
-                width = 2 * r if self.branch["kind"] == "lowrank" else r
+                width = ops.lowrank_width(M, self.K, r if self.branch["kind"] == "lowrank" else -r)
                 br_a = torch.empty((M, width), dtype=torch.bfloat16, device=device)
             y = torch.empty((M, self.N), dtype=self.y_dtype, device=device)
             ws = ops.make_workspace(M, self.N, self.K, self.fmt, device=device) if self.use_workspace else None
@@ -93,10 +93,10 @@ class QuantizedLinear:
         bd = None
         if self.branch is not None:
             if self.branch["kind"] == "lowrank":
-                ops.lowrank_project(x, l1t=self.branch["l1t"], out=b["br_a"], stream=stream)
+                a = ops.lowrank_project(x, l1t=self.branch["l1t"], out=b["br_a"], stream=stream)
             else:
-                ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
-            bd = ops.branch_desc(b["br_a"], self.branch["lw"])
+                a = ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
+            bd = ops.branch_desc(a, self.branch["lw"])
         y = b["y"] if out is None else out
         if self.fmt == "int8":
             return ops.w8a8_linear(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K,
@@ -105,6 +105,14 @@ class QuantizedLinear:
                                alpha=self.alpha, branch=bd, y=y, workspace=b["ws"], stream=stream)
 
     __call__ = forward
+
+    def branch_operand(self, M: int, device):
+        """The branch ``a`` operand inside the M-row buffers (after forward)."""
+        b = self.buffers(M, device)
+        if self.branch is None:
+            return None
+        r = self.branch["lw"].shape[1]
+        return b["br_a"][:, :2 * r] if self.branch["kind"] == "lowrank" else b["br_a"]
 
 
 def case_to_device(case, device="cuda"):
