@@ -40,6 +40,36 @@ __device__ __forceinline__ void branch_mfma(v4f (&acc)[TI][TJ], const BranchArgs
   }
 }
 
+// Dequantisation scales of a wave's TI x TJ tile grid as the lane uses them:
+// sa for its rows 4*(lane/16)+0..3 of each row block, sw for its column
+// lane%16 of each 16-column block (0 past M / N).  A kernel that loads
+// them before its main loop hides their latency behind it.
+template <int TI, int TJ>
+struct EpiScales {
+  float sa[TI][4];
+  float sw[TJ];
+};
+
+template <int TI, int TJ>
+__device__ __forceinline__ void load_epi_scales(EpiScales<TI, TJ>& s, const GemmArgs& g, int m_base, int n_base,
+                                                int lane) {
+  const int lr = lane & 15, lq = lane >> 4;
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(g.sa, g.sa ? (uint32_t)g.M * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(g.sw, g.sw ? (uint32_t)g.N * 4u : 0u);
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m_base + i * 16 + lq * 4 + r;
+      s.sa[i][r] = __uint_as_float(buf_load4(rsa, m < g.M ? (uint32_t)m * 4u : kOOB));
+    }
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int n = n_base + j * 16 + lr;
+    s.sw[j] = __uint_as_float(buf_load4(rsw, n < g.N ? (uint32_t)n * 4u : kOOB));
+  }
+}
+
 // Epilogue of a wave's TI x TJ grid of 16x16 accumulator tiles, one
 // 16-column block at a time (keeps the live register set small):
 // dequantise (integer: fp32(fp32(acc) * sa[m]) * sw[n] * alpha, with acc
@@ -55,9 +85,11 @@ constexpr int epilogue_stage_bytes() {
   return TI * 16 * (TJ * 32 + 16);
 }
 
+// `pre`, when given, holds the scales already loaded (load_epi_scales).
 template <int KIND /*0 int4, 1 int8, 2 float*/, typename AccT, int TI, int TJ>
 __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
-                                               int lane, uint8_t* stage = nullptr) {
+                                               int lane, uint8_t* stage = nullptr,
+                                               const EpiScales<TI, TJ>* pre = nullptr) {
   const int lr = lane & 15, lq = lane >> 4;
   const int esz = g.y_dtype == 1 ? 2 : 4;
   const int rows = max(0, min(TI * 16, g.M - m_base));
@@ -96,7 +128,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m_base + i * 16 + lq * 4 + r;
-        sam[i][r] = m < g.M ? sa[m] : 0.f;
+        sam[i][r] = pre ? pre->sa[i][r] : (m < g.M ? sa[m] : 0.f);
       }
   }
 #pragma unroll
@@ -105,7 +137,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
     const uint32_t coff = n < g.N ? (uint32_t)n * (uint32_t)esz : kOOB;
     v4f col[TI][1];
     if constexpr (KIND != 2) {
-      const float swn = n < g.N ? sw[n] : 0.f;
+      const float swn = pre ? pre->sw[j] : (n < g.N ? sw[n] : 0.f);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll

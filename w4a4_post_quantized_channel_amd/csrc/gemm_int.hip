@@ -39,32 +39,45 @@ __device__ __forceinline__ v4i widen_int4(uint32_t lo, uint32_t hi) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernels: 64 token rows x 64 output channels per workgroup of four
-// waves.  Each wave takes an interleaved quarter of the workgroup's K range
-// and issues the buffer loads of a chunk of 128-deep steps before their
-// MFMAs.  With a workspace the K range is split over blockIdx.z: partial
-// tiles go to the workspace and a second kernel adds them and runs the
-// epilogue (the kernel boundary orders the writes; no fences).
+// Decode kernels: 16*TI token rows x 16*TJ output channels per workgroup of
+// four waves.  Each wave takes an interleaved quarter of the workgroup's K
+// range and issues the buffer loads of a chunk of 128-deep steps before
+// their MFMAs.  With a workspace the K range is split over blockIdx.z:
+// partial tiles go to the workspace and a second kernel adds them and runs
+// the epilogue (the kernel boundary orders the writes; no fences).
 // ---------------------------------------------------------------------------
 constexpr int kDecTJ = 4;  // 64 output channels per workgroup when K is split
 
-template <bool INT4, int TJ>
+// Row blocks of 16 tokens per workgroup: with a split, one row tile covers
+// all M <= 64 rows; without one, tiles of 32 rows (16 for M <= 32) give
+// twice the workgroups of a 64-row tile.
+static int decode_ti(int64_t M, bool split) {
+  if (split) return M > 32 ? 4 : (M > 16 ? 2 : 1);
+  return M > 32 ? 2 : 1;
+}
+
+template <bool INT4, int TI, int TJ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
-  constexpr int TI = 4;
+  static_assert(TI == 1 || TI == 2 || TI == 4, "row blocks per workgroup");
   constexpr int LPR = INT4 ? 1 : 2;     // 16-byte loads per row and step
   constexpr int CHUNK = INT4 ? 4 : 2;   // steps whose loads are in flight together
   __shared__ int red[4][TI][TJ][4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const int n0 = blockIdx.x * 16 * TJ, m0 = blockIdx.y * 64;
+  const int n0 = blockIdx.x * 16 * TJ, m0 = blockIdx.y * 16 * TI;
   const int64_t rowbytes = INT4 ? (g.K >> 1) : g.K;
   const int kz0 = blockIdx.z * kwg, kz1 = min(g.K, kz0 + kwg);
-  const int lofs = INT4 ? lq * 16 : lq * 32;  // this lane's bytes inside a 128-element step
+  const int lofs = lq * 16;  // this lane's 16 bytes inside each 64-byte segment of a step
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(g.a + (int64_t)m0 * rowbytes,
-                                               (uint32_t)(min(64, g.M - m0) * rowbytes));
+                                               (uint32_t)(min(16 * TI, g.M - m0) * rowbytes));
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(g.w + (int64_t)n0 * rowbytes,
                                                (uint32_t)(min(16 * TJ, g.N - n0) * rowbytes));
+
+  // Without a split this kernel runs the epilogue: its scales load now, so
+  // their latency hides behind the main loop.
+  EpiScales<1, TJ> es;
+  if (!part && wave < TI) load_epi_scales(es, g, m0 + wave * 16, n0, lane);
 
   v4i acc[TI][TJ];
 #pragma unroll
@@ -80,13 +93,13 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
       const int64_t kb = (INT4 ? (k >> 1) : k) + lofs;
 #pragma unroll
       for (int l = 0; l < LPR; ++l) {
-        const bool kin = k < kz1 && kb + 16 * l < rowbytes;
+        const bool kin = k < kz1 && kb + 64 * l < rowbytes;
 #pragma unroll
         for (int i = 0; i < TI; ++i)
-          ra[s][i][l] = buf_load16(rsA, kin ? (uint32_t)((i * 16 + lr) * rowbytes + kb + 16 * l) : kOOB);
+          ra[s][i][l] = buf_load16(rsA, kin ? (uint32_t)((i * 16 + lr) * rowbytes + kb + 64 * l) : kOOB);
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          rb[s][j][l] = buf_load16(rsB, kin ? (uint32_t)((j * 16 + lr) * rowbytes + kb + 16 * l) : kOOB);
+          rb[s][j][l] = buf_load16(rsB, kin ? (uint32_t)((j * 16 + lr) * rowbytes + kb + 64 * l) : kOOB);
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk in flight before the MFMAs
@@ -113,7 +126,7 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
       }
   }
 
-  // sum the four waves' partial tiles; wave w keeps row block w
+  // sum the four waves' partial tiles; wave w < TI keeps row block w
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -121,6 +134,7 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave][i][j][r][lane] = acc[i][j][r];
   __syncthreads();
+  if (wave >= TI) return;
   v4i tot[1][TJ];
 #pragma unroll
   for (int j = 0; j < TJ; ++j)
@@ -132,37 +146,41 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      uint4* p = reinterpret_cast<uint4*>(part + (((tile * 4 + wave) * TJ + j) * gridDim.z + blockIdx.z) * 256);
+      uint4* p = reinterpret_cast<uint4*>(part + (((tile * TI + wave) * TJ + j) * gridDim.z + blockIdx.z) * 256);
       p[lane] = __builtin_bit_cast(uint4, tot[0][j]);
     }
     return;
   }
-  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0 + wave * 16, n0, lane);
+  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0 + wave * 16, n0, lane, nullptr, &es);
 }
 
 // One wave per 16 x 16 output tile (tile, row block, column block): add its
-// S partial blocks (coalesced 1 KB reads, all in flight), then the epilogue.
-template <bool INT4>
+// S partial blocks (coalesced 1 KB reads, up to eight in flight; the
+// epilogue's scales load alongside the first ones), then the epilogue.
+template <bool INT4, int TI>
 __global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, const int32_t* part) {
   constexpr int TJ = kDecTJ;
-  constexpr int ZB = 16;  // partial blocks whose loads are in flight together
+  constexpr int ZB = 8;  // partial blocks whose loads are in flight together
   const int lane = threadIdx.x;
   const int nt = (g.N + 16 * TJ - 1) / (16 * TJ);
-  const int64_t blk = blockIdx.x;              // (tile * 4 + rb) * TJ + j
-  const int j = (int)(blk % TJ), rb = (int)((blk / TJ) & 3);
-  const int64_t tile = blk / (4 * TJ);
-  const int n0 = (int)(tile % nt) * 16 * TJ + j * 16, m0 = (int)(tile / nt) * 64 + rb * 16;
+  const int64_t blk = blockIdx.x;              // (tile * TI + rb) * TJ + j
+  const int j = (int)(blk % TJ), rb = (int)((blk / TJ) % TI);
+  const int64_t tile = blk / (TI * TJ);
+  const int n0 = (int)(tile % nt) * 16 * TJ + j * 16, m0 = (int)(tile / nt) * 16 * TI + rb * 16;
+  EpiScales<1, 1> es;
+  load_epi_scales(es, g, m0, n0, lane);
   const uint4* p = reinterpret_cast<const uint4*>(part + blk * S * 256) + lane;
   v4i tot[1][1] = {{v4i{0, 0, 0, 0}}};
   for (int z0 = 0; z0 < S; z0 += ZB) {
     uint4 v[ZB];
 #pragma unroll
-    for (int dz = 0; dz < ZB; ++dz) v[dz] = p[(z0 + dz < S ? z0 + dz : S - 1) * 64];
+    for (int dz = 0; dz < ZB; ++dz)
+      if (z0 + dz < S) v[dz] = p[(z0 + dz) * 64];
 #pragma unroll
     for (int dz = 0; dz < ZB; ++dz)
       if (z0 + dz < S) tot[0][0] += __builtin_bit_cast(v4i, v[dz]);
   }
-  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0, n0, lane);
+  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0, n0, lane, nullptr, &es);
 }
 
 // ---------------------------------------------------------------------------
@@ -171,6 +189,7 @@ __global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, 
 struct DecodePlan {
   int splits;
   int kwg;
+  int ti;          // row blocks per workgroup of the split kernel (one row tile)
   int64_t tiles;
   size_t ws_bytes;
 };
@@ -180,7 +199,8 @@ struct DecodePlan {
 // are not split: the second kernel costs more than the split saves.
 static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, bool int4) {
   DecodePlan p{};
-  p.tiles = ((N + 16 * kDecTJ - 1) / (16 * kDecTJ)) * ((M + 63) / 64);
+  p.ti = decode_ti(M, true);
+  p.tiles = (N + 16 * kDecTJ - 1) / (16 * kDecTJ);  // M <= 64: one row tile
   const int64_t unit = 4 * kBK;
   const int64_t nunits = (K + unit - 1) / unit;
   const int64_t wbytes = N * K / (int4 ? 2 : 1);
@@ -189,7 +209,7 @@ static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, bool int4) {
   const int64_t per = (nunits + s - 1) / s;
   p.kwg = (int)(per * unit);
   p.splits = (int)((nunits + per - 1) / per);
-  p.ws_bytes = p.splits > 1 ? (size_t)(p.splits * p.tiles * 64 * 16 * kDecTJ * 4) : 0;
+  p.ws_bytes = p.splits > 1 ? (size_t)(p.splits * p.tiles * 16 * p.ti * 16 * kDecTJ * 4) : 0;
   return p;
 }
 
@@ -197,26 +217,42 @@ size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
   return M <= 64 ? decode_plan(M, N, K, fmt == 0).ws_bytes : 0;
 }
 
+template <bool INT4>
+static void launch_decode(const GemmArgs& g, const DecodePlan& p, int32_t* part, hipStream_t st) {
+  if (part) {
+    const dim3 grid((unsigned)p.tiles, 1, p.splits);
+    const dim3 rgrid((unsigned)(p.tiles * p.ti * kDecTJ));
+    switch (p.ti) {
+      case 1:
+        hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 1, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
+        hipLaunchKernelGGL((gemm_int_reduce_kernel<INT4, 1>), rgrid, dim3(64), 0, st, g, p.splits, part);
+        break;
+      case 2:
+        hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 2, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
+        hipLaunchKernelGGL((gemm_int_reduce_kernel<INT4, 2>), rgrid, dim3(64), 0, st, g, p.splits, part);
+        break;
+      default:
+        hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 4, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
+        hipLaunchKernelGGL((gemm_int_reduce_kernel<INT4, 4>), rgrid, dim3(64), 0, st, g, p.splits, part);
+        break;
+    }
+    return;
+  }
+  // whole K per workgroup: 16 output channels and 16 or 32 rows each, for more workgroups
+  const int ti = decode_ti(g.M, false);
+  const dim3 grid((g.N + 15) / 16, (g.M + 16 * ti - 1) / (16 * ti), 1);
+  if (ti == 1) hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 1, 1>), grid, dim3(256), 0, st, g, g.K, part);
+  else hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 2, 1>), grid, dim3(256), 0, st, g, g.K, part);
+}
+
 hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st) {
   const bool int4 = fmt == 0;
   if (g.M <= 64) {
-    DecodePlan p = decode_plan(g.M, g.N, g.K, int4);
+    const DecodePlan p = decode_plan(g.M, g.N, g.K, int4);
     const bool split = p.splits > 1 && workspace && ws_bytes >= p.ws_bytes;
     int32_t* part = split ? reinterpret_cast<int32_t*>(workspace) : nullptr;
-    if (split) {
-      dim3 grid((g.N + 16 * kDecTJ - 1) / (16 * kDecTJ), (g.M + 63) / 64, p.splits);
-      if (int4) hipLaunchKernelGGL((gemm_int_decode_kernel<true, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
-      else hipLaunchKernelGGL((gemm_int_decode_kernel<false, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
-    } else {  // whole K per workgroup: 16 output channels each for more workgroups
-      dim3 grid((g.N + 15) / 16, (g.M + 63) / 64, 1);
-      if (int4) hipLaunchKernelGGL((gemm_int_decode_kernel<true, 1>), grid, dim3(256), 0, st, g, g.K, part);
-      else hipLaunchKernelGGL((gemm_int_decode_kernel<false, 1>), grid, dim3(256), 0, st, g, g.K, part);
-    }
-    if (split) {
-      dim3 rgrid((unsigned)(p.tiles * 4 * kDecTJ));
-      if (int4) hipLaunchKernelGGL((gemm_int_reduce_kernel<true>), rgrid, dim3(64), 0, st, g, p.splits, part);
-      else hipLaunchKernelGGL((gemm_int_reduce_kernel<false>), rgrid, dim3(64), 0, st, g, p.splits, part);
-    }
+    if (int4) launch_decode<true>(g, p, part, st);
+    else launch_decode<false>(g, p, part, st);
     return hipGetLastError();
   }
   return launch_gemm_wide(fmt, g, st);
