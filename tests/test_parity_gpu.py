@@ -61,6 +61,9 @@ SMALL = [
     ("nvfp4_plain", 66, 72, 256, "nvfp4", "bf16", dict(n_outliers=4, outlier_gain=10.0)),
     ("int4_single_row", 1, 64, 64, "int4", "bf16", dict()),
     ("int8_lowrank", 33, 48, 192, "int8", "bf16", dict(lowrank=8)),
+    # rows longer than 4096: eight waves per row in the integer quantizer (ragged chunks)
+    ("int8_long_rows", 5, 40, 4160, "int8", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
+    ("int4_long_rows", 3, 24, 8256, "int4", "f32", dict(n_outliers=6, outlier_gain=20.0)),
     # >= 256 rows: the row-per-lane NVFP4 quantizer (ragged last group of 64 rows)
     ("nvfp4_rows", 300, 96, 320, "nvfp4", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=8)),
     ("nvfp4_rows_f32", 260, 64, 256, "nvfp4", "f32", dict(n_outliers=4, outlier_gain=20.0)),

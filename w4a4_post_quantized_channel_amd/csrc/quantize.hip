@@ -13,7 +13,7 @@
 // 16 and 32 across the quad (DPP quad permutes, xor 1 and xor 2).  An
 // NVFP4 scale block (16 elements) is exactly one lane.  The whole row stays
 // in registers, so the per-row absolute maximum needs no second HBM read.
-// WPR (waves per row) is 1 for many rows, 4 for few.
+// WPR (waves per row) is 1 for many rows, 4 or 8 for few (8 for long rows).
 //
 // Exactness.  Every value the quantizer decides on is the one the fp32
 // definition gives: the butterflies are the same additions in the same
@@ -245,17 +245,19 @@ __device__ __forceinline__ float transform_slot(const SlotRaw<BF16IN>& raw, floa
 }
 
 template <int MODE, bool BF16IN, int NC, int WPR>
-__global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
+__global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(QuantArgs a) {
   constexpr int QMAX = MODE == MODE_INT4 ? 7 : 127;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  constexpr int RPB = 4 / WPR;                      // rows per block
+  static_assert(WPR == 1 || WPR == 4 || WPR == 8, "waves per row");
+  constexpr int NWB = WPR > 4 ? WPR : 4;            // waves per block
+  constexpr int RPB = NWB / WPR;                    // rows per block
   const int sub = WPR == 1 ? 0 : wave;              // wave index inside the row group
   const int grp = WPR == 1 ? wave : 0;              // row group inside the block
   const int nslots = a.K >> 4;
   const bool has_scale = a.scale != nullptr;
   constexpr int ESZ = BF16IN ? 2 : 4;
-  __shared__ float red[4];
+  __shared__ float red[NWB];
   // NVFP4: (S, RN(1/S)) for every E4M3 code e, S = fp32(value(e) * g).
   __shared__ float2 stab[MODE == MODE_NVFP4 ? 128 : 1];
   if constexpr (MODE == MODE_NVFP4) {
@@ -309,6 +311,7 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QuantArgs a) {
           if (lane == 0) red[wave] = m;
           __syncthreads();
           m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+          if constexpr (WPR == 8) m = fmaxf(m, fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
           __syncthreads();
         }
         const float step = m / (float)QMAX;   // IEEE division
@@ -511,7 +514,7 @@ template <int MODE, bool BF16IN, int WPR>
 static hipError_t launch_nc(int nc, dim3 grid, hipStream_t st, const QuantArgs& a) {
 #define W4A4_NC_CASE(N)                                                                         \
   case N:                                                                                      \
-    hipLaunchKernelGGL((quant_rows_kernel<MODE, BF16IN, N, WPR>), grid, dim3(256), 0, st, a);  \
+    hipLaunchKernelGGL((quant_rows_kernel<MODE, BF16IN, N, WPR>), grid, dim3(WPR > 4 ? 64 * WPR : 256), 0, st, a); \
     break;
   switch (nc) {
     W4A4_NC_CASE(1)
@@ -558,11 +561,14 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   }
   const int64_t nslots = K / 16;
   // One wave per row when there are many rows and the row fits five chunks
-  // per lane (the factors then stay in registers); else four waves per row.
-  const int wpr = (R >= 1024 && nslots <= 5 * 64) ? 1 : 4;
+  // per lane (the factors then stay in registers); else four waves per row,
+  // eight for integer codes of rows longer than 4096.
+  const bool intmode = mode == MODE_INT4 || mode == MODE_INT8;
+  int wpr = (R >= 1024 && nslots <= 5 * 64) ? 1 : 4;
+  if (wpr == 4 && intmode && nslots > 4 * 64) wpr = 8;
   const int nc = round_nc((int)((nslots + 64 * wpr - 1) / (64 * wpr)));
   if (nc < 0) return hipErrorInvalidValue;
-  const int rows_per_block = 4 / wpr;
+  const int rows_per_block = wpr == 1 ? 4 : 1;
   int64_t blocks = (R + rows_per_block - 1) / rows_per_block;
   const int64_t cap = 256 * 8;  // grid-stride beyond 8 blocks per CU
   if (mode == MODE_AMAX) {
@@ -571,6 +577,11 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   dim3 grid((unsigned)blocks);
+  if (wpr == 8) {
+    if (mode == MODE_INT4) return bf16in ? launch_nc<MODE_INT4, true, 8>(nc, grid, st, a)
+                                         : launch_nc<MODE_INT4, false, 8>(nc, grid, st, a);
+    return bf16in ? launch_nc<MODE_INT8, true, 8>(nc, grid, st, a) : launch_nc<MODE_INT8, false, 8>(nc, grid, st, a);
+  }
 #define W4A4_DISPATCH(MODE)                                                          \
   if (mode == MODE) {                                                                \
     if (bf16in) return wpr == 1 ? launch_nc<MODE, true, 1>(nc, grid, st, a)          \
