@@ -14,12 +14,18 @@
 // returns exactly 256 * sum(qa * qw); the epilogue shifts right by 8.
 //
 // This file holds the few-token path; many tokens go to gemm_wide.hip.
-//  * decode kernel (<= 64 tokens, weight streaming): 64 token rows x 64
-//    output channels per workgroup of four waves.  No LDS staging: each
-//    wave loads its MFMA operands straight from global memory with raw
-//    buffer loads (16 bytes per lane, whole 64-byte row segments per
-//    instruction, out-of-range rows read as zero) for an interleaved
-//    quarter of the workgroup's K range; the four partial tiles are summed
+//  * decode kernel (<= 64 tokens, weight streaming): 16*TI token rows x
+//    16*TJ output channels per workgroup of four waves, each wave on an
+//    interleaved quarter of the workgroup's K range.  A wave copies its
+//    operand rows into its own LDS area with buffer loads to LDS: one
+//    instruction moves whole 128-byte (int8) or 64-byte (int4) row segments
+//    of 8 or 16 rows, every 16-byte chunk placed at position
+//    chunk XOR (row mod chunks-per-row) so that the MFMA-layout reads
+//    (ds_read_b128, 16 rows per instruction) spread over the LDS banks.
+//    Loading the MFMA layout straight from global memory instead touches 16
+//    half-used cache lines per instruction and streams the weights about a
+//    third slower.  Chunks past K or past the last row fall outside the
+//    buffer resource and arrive as zeros.  The four partial tiles are summed
 //    in LDS.  K is split over workgroups when a workspace is given; a
 //    second kernel adds the int32 partial tiles (exact) and runs the
 //    epilogue.  Splits never hand off inside one kernel: on gfx950 a
@@ -28,6 +34,7 @@
 #include "device_common.h"
 #include "epilogue.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace w4a4 {
 
@@ -56,23 +63,44 @@ static int decode_ti(int64_t M, bool split) {
   return M > 32 ? 2 : 1;
 }
 
+// A wave's wait before reading step s of a chunk: the copies of the later
+// steps may still be in flight (copies complete in issue order).
+template <int PER_STEP, int CHUNK>
+__device__ __forceinline__ void wait_step(int s) {
+  switch (CHUNK - 1 - s) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER_STEP>(); break;
+    case 2: wait_vmcnt<2 * PER_STEP>(); break;
+    default: wait_vmcnt<3 * PER_STEP>(); break;
+  }
+}
+
 template <bool INT4, int TI, int TJ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
   static_assert(TI == 1 || TI == 2 || TI == 4, "row blocks per workgroup");
-  constexpr int LPR = INT4 ? 1 : 2;     // 16-byte loads per row and step
-  constexpr int CHUNK = INT4 ? 4 : 2;   // steps whose loads are in flight together
-  __shared__ int red[4][TI][TJ][4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int CHUNK = INT4 ? 4 : 2;             // steps whose copies are in flight together
+  constexpr int SB = INT4 ? 64 : 128;             // bytes of a row in one 128-element step
+  constexpr int CPR = SB / 16;                    // 16-byte chunks per row and step
+  constexpr int RPI = 64 / CPR;                   // rows per copy instruction
+  constexpr int ROWS = 16 * (TI + TJ);            // A rows, then W rows
+  constexpr int PER_STEP = ROWS / RPI;            // copy instructions per step
+  constexpr int WAVE_BYTES = CHUNK * ROWS * SB;
+  constexpr int RED_BYTES = 4 * TI * TJ * 1024;
+  constexpr int LDS_BYTES = 4 * WAVE_BYTES > RED_BYTES ? 4 * WAVE_BYTES : RED_BYTES;
+  static_assert(CHUNK <= 4 && (CHUNK - 1) * PER_STEP <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int lr = lane & 15, lq = lane >> 4;
   const int n0 = blockIdx.x * 16 * TJ, m0 = blockIdx.y * 16 * TI;
   const int64_t rowbytes = INT4 ? (g.K >> 1) : g.K;
   const int kz0 = blockIdx.z * kwg, kz1 = min(g.K, kz0 + kwg);
-  const int lofs = lq * 16;  // this lane's 16 bytes inside each 64-byte segment of a step
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(g.a + (int64_t)m0 * rowbytes,
-                                               (uint32_t)(min(16 * TI, g.M - m0) * rowbytes));
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(g.w + (int64_t)n0 * rowbytes,
-                                               (uint32_t)(min(16 * TJ, g.N - n0) * rowbytes));
+  const v4u rsA = rsrc_words(g.a + (int64_t)m0 * rowbytes, (uint32_t)(min(16 * TI, g.M - m0) * rowbytes));
+  const v4u rsB = rsrc_words(g.w + (int64_t)n0 * rowbytes, (uint32_t)(min(16 * TJ, g.N - n0) * rowbytes));
+  uint8_t* const area = smem + wave * WAVE_BYTES;
+  // copy instruction d: lane -> row d*RPI + lane/CPR, LDS chunk position lane%CPR
+  const int dr = lane / CPR, dp = lane % CPR;
 
   // Without a split this kernel runs the epilogue: its scales load now, so
   // their latency hides behind the main loop.
@@ -86,45 +114,72 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
   for (int kc = kz0 + wave * kBK; kc < kz1; kc += 4 * kBK * CHUNK) {
-    uint4 ra[CHUNK][TI][LPR], rb[CHUNK][TJ][LPR];
 #pragma unroll
     for (int s = 0; s < CHUNK; ++s) {
       const int k = kc + s * 4 * kBK;
-      const int64_t kb = (INT4 ? (k >> 1) : k) + lofs;
+      const int64_t kb = INT4 ? (k >> 1) : k;
+      uint8_t* st = area + s * ROWS * SB;
 #pragma unroll
-      for (int l = 0; l < LPR; ++l) {
-        const bool kin = k < kz1 && kb + 64 * l < rowbytes;
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-          ra[s][i][l] = buf_load16(rsA, kin ? (uint32_t)((i * 16 + lr) * rowbytes + kb + 64 * l) : kOOB);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          rb[s][j][l] = buf_load16(rsB, kin ? (uint32_t)((j * 16 + lr) * rowbytes + kb + 64 * l) : kOOB);
+      for (int d = 0; d < PER_STEP; ++d) {
+        const bool isa = d * RPI < 16 * TI;       // uniform per instruction
+        const int r = d * RPI + dr - (isa ? 0 : 16 * TI);
+        const int64_t cb = kb + 16 * (dp ^ (r & (CPR - 1)));
+        const bool ok = k < kz1 && cb < rowbytes;
+        dma16(isa ? rsA : rsB, st + d * 1024, ok ? (uint32_t)(r * rowbytes + cb) : kOOB, 0u);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk in flight before the MFMAs
 #pragma unroll
-    for (int s = 0; s < CHUNK; ++s)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        v4i a[TI], b[TJ];
+    for (int s = 0; s < CHUNK; ++s) {
+      wait_step<PER_STEP, CHUNK>(s);
+      asm volatile("" ::: "memory");
+      const uint8_t* st = area + s * ROWS * SB;
+      if constexpr (INT4) {
+        uint4 ra[TI], rb[TJ];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-          if constexpr (INT4) a[i] = h ? widen_int4(ra[s][i][0].z, ra[s][i][0].w) : widen_int4(ra[s][i][0].x, ra[s][i][0].y);
-          else a[i] = __builtin_bit_cast(v4i, ra[s][i][h < LPR ? h : 0]);
+          const int R = i * 16 + lr;
+          ra[i] = *reinterpret_cast<const uint4*>(st + R * SB + 16 * (lq ^ (R & 3)));
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          if constexpr (INT4) b[j] = h ? widen_int4(rb[s][j][0].z, rb[s][j][0].w) : widen_int4(rb[s][j][0].x, rb[s][j][0].y);
-          else b[j] = __builtin_bit_cast(v4i, rb[s][j][h < LPR ? h : 0]);
+          const int R = j * 16 + lr;
+          rb[j] = *reinterpret_cast<const uint4*>(st + (16 * TI + R) * SB + 16 * (lq ^ (R & 3)));
         }
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+              const v4i a = h ? widen_int4(ra[i].z, ra[i].w) : widen_int4(ra[i].x, ra[i].y);
+              const v4i b = h ? widen_int4(rb[j].z, rb[j].w) : widen_int4(rb[j].x, rb[j].y);
+              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i][j], 0, 0, 0);
+            }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          v4i a[TI], b[TJ];
+#pragma unroll
+          for (int i = 0; i < TI; ++i) {
+            const int R = i * 16 + lr;
+            a[i] = *reinterpret_cast<const v4i*>(st + R * SB + 16 * ((h * 4 + lq) ^ (R & 7)));
+          }
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const int R = j * 16 + lr;
+            b[j] = *reinterpret_cast<const v4i*>(st + (16 * TI + R) * SB + 16 * ((h * 4 + lq) ^ (R & 7)));
+          }
+#pragma unroll
+          for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
       }
+    }
   }
+  __syncthreads();   // every wave is done with its copy area; LDS now holds the partial tiles
+  int (*red)[TI][TJ][4][64] = reinterpret_cast<int (*)[TI][TJ][4][64]>(smem);
 
   // sum the four waves' partial tiles; wave w < TI keeps row block w
 #pragma unroll

@@ -36,6 +36,7 @@
 
 #include "device_common.h"
 #include "epilogue.h"
+#include "lds_dma.h"
 #include "launch.h"
 
 namespace w4a4 {
@@ -68,35 +69,6 @@ struct WFmt<W_NVFP4> {
 constexpr int kSeg = 64;     // packed bytes per row per K-group per stage
 constexpr int kNBuf = 4;     // LDS stage buffers (three stages in flight)
 
-// Global -> LDS copies (buffer loads with the LDS flag: lane l writes its
-// bytes at M0 + size * l).  Issued as inline assembly so that the compiler
-// does not track them: it would otherwise wait for every copy in flight
-// before any LDS read.  The kernel orders them itself (explicit vmcnt wait
-// and barrier before a stage's buffer is read).  No register is written.
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ v4u rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return v4u{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
-}
-// off: per-lane byte offset; soff: wave-uniform byte offset added to it.
-__device__ __forceinline__ void dma16(const v4u& rs, uint8_t* lds, uint32_t off, uint32_t soff) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds));   // lds is wave-uniform
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(m), "v"(off), "s"(rs), "s"(soff)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const v4u& rs, uint8_t* lds, uint32_t off, uint32_t soff) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds));   // lds is wave-uniform
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :
-               : "s"(m), "v"(off), "s"(rs), "s"(soff)
-               : "memory", "m0");
-}
 
 // XOR swizzle of the 16-byte slots of an LDS row of P bytes: the 16 rows
 // of one MFMA fragment, read at the same logical slot, land in 16
@@ -192,11 +164,6 @@ struct WCfg {
   static_assert(DPS * (kNBuf - 2) <= 63, "vmcnt range");
 };
 
-// s_waitcnt with vmcnt <= n and no wait on the other counters.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // Copy of one operand region (rows x P packed bytes) per stage.  Wave w of
 // NW issues instructions w, w + NW, ...; instruction n covers region bytes
