@@ -90,7 +90,8 @@ def test_small_cases(ops, pipe, name, M, N, K, fmt, xdt, kw, order):
 @pytest.mark.parametrize("fmt", ["int4", "int8"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (17, 33, 192), (100, 200, 384), (130, 260, 320),
                                    (64, 2048, 2048), (64, 512, 8192), (512, 512, 4096), (300, 100, 64),
-                                   (64, 2048, 8192), (40, 4096, 4160), (3, 8200, 2048), (30, 8192, 2048)])
+                                   (64, 2048, 8192), (40, 4096, 4160), (3, 8200, 2048), (30, 8192, 2048),
+                                   (20, 512, 4096), (9, 768, 8192), (50, 640, 8256)])
 @pytest.mark.parametrize("split", [False, True])
 def test_raw_accumulators_exact(ops, fmt, M, N, K, split):
     """Integer GEMM on random codes: bit-exact int32 accumulators (decode kernel with and

@@ -31,6 +31,8 @@
 //    epilogue.  Splits never hand off inside one kernel: on gfx950 a
 //    cross-workgroup handoff needs an agent-scope fence, which writes back
 //    and invalidates the XCD's L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "epilogue.h"
 #include "launch.h"
@@ -63,15 +65,17 @@ static int decode_ti(int64_t M, bool split) {
   return M > 32 ? 2 : 1;
 }
 
-// A wave's wait before reading step s of a chunk: the copies of the later
-// steps may still be in flight (copies complete in issue order).
-template <int PER_STEP, int CHUNK>
-__device__ __forceinline__ void wait_step(int s) {
-  switch (CHUNK - 1 - s) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<PER_STEP>(); break;
-    case 2: wait_vmcnt<2 * PER_STEP>(); break;
-    default: wait_vmcnt<3 * PER_STEP>(); break;
+// LDS bytes a decode wave keeps in flight (its ring of step slots): int4
+// rows are half as long per step, and a smaller ring measured faster there.
+template <bool INT4>
+constexpr int dec_ring_bytes() { return INT4 ? 12 * 1024 : 36 * 1024; }
+
+// f(integral_constant<int, J>) for J = J0 .. J1 - 1, in order.
+template <int J0, int J1, typename F>
+__device__ __forceinline__ void drain_ring(F&& f) {
+  if constexpr (J0 < J1) {
+    f(std::integral_constant<int, J0>{});
+    drain_ring<J0 + 1, J1>(f);
   }
 }
 
@@ -79,16 +83,18 @@ template <bool INT4, int TI, int TJ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
   static_assert(TI == 1 || TI == 2 || TI == 4, "row blocks per workgroup");
-  constexpr int CHUNK = INT4 ? 4 : 2;             // steps whose copies are in flight together
   constexpr int SB = INT4 ? 64 : 128;             // bytes of a row in one 128-element step
   constexpr int CPR = SB / 16;                    // 16-byte chunks per row and step
   constexpr int RPI = 64 / CPR;                   // rows per copy instruction
   constexpr int ROWS = 16 * (TI + TJ);            // A rows, then W rows
   constexpr int PER_STEP = ROWS / RPI;            // copy instructions per step
-  constexpr int WAVE_BYTES = CHUNK * ROWS * SB;
+  constexpr int STEP_BYTES = ROWS * SB;
+  constexpr int NBUF0 = dec_ring_bytes<INT4>() / STEP_BYTES;
+  constexpr int NBUF = NBUF0 > 8 ? 8 : (NBUF0 < 2 ? 2 : NBUF0);   // ring slots per wave
+  constexpr int WAVE_BYTES = NBUF * STEP_BYTES;
   constexpr int RED_BYTES = 4 * TI * TJ * 1024;
   constexpr int LDS_BYTES = 4 * WAVE_BYTES > RED_BYTES ? 4 * WAVE_BYTES : RED_BYTES;
-  static_assert(CHUNK <= 4 && (CHUNK - 1) * PER_STEP <= 63, "vmcnt range");
+  static_assert((NBUF - 1) * PER_STEP <= 63 && NBUF <= 8, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -101,11 +107,28 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
   uint8_t* const area = smem + wave * WAVE_BYTES;
   // copy instruction d: lane -> row d*RPI + lane/CPR, LDS chunk position lane%CPR
   const int dr = lane / CPR, dp = lane % CPR;
+  // this wave's steps: k = kz0 + 128 * (wave + 4 t), t < nsteps
+  const int kw = kz0 + wave * kBK;
+  const int nsteps = kw < kz1 ? (kz1 - kw + 4 * kBK - 1) / (4 * kBK) : 0;
 
   // Without a split this kernel runs the epilogue: its scales load now, so
   // their latency hides behind the main loop.
   EpiScales<1, TJ> es;
   if (!part && wave < TI) load_epi_scales(es, g, m0 + wave * 16, n0, lane);
+
+  auto issue = [&](int t, int slot) {   // copies of step t into ring slot `slot`
+    const int k = kw + t * 4 * kBK;
+    const int64_t kb = INT4 ? (k >> 1) : k;
+    uint8_t* st = area + slot * STEP_BYTES;
+#pragma unroll
+    for (int d = 0; d < PER_STEP; ++d) {
+      const bool isa = d * RPI < 16 * TI;         // uniform per instruction
+      const int r = d * RPI + dr - (isa ? 0 : 16 * TI);
+      const int64_t cb = kb + 16 * (dp ^ (r & (CPR - 1)));
+      const bool ok = k < kz1 && cb < rowbytes;
+      dma16(isa ? rsA : rsB, st + d * 1024, ok ? (uint32_t)(r * rowbytes + cb) : kOOB, 0u);
+    }
+  };
 
   v4i acc[TI][TJ];
 #pragma unroll
@@ -113,71 +136,78 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  for (int kc = kz0 + wave * kBK; kc < kz1; kc += 4 * kBK * CHUNK) {
+  auto compute = [&](const uint8_t* st) {   // the MFMAs of one step from its ring slot
+    if constexpr (INT4) {
+      uint4 ra[TI], rb[TJ];
 #pragma unroll
-    for (int s = 0; s < CHUNK; ++s) {
-      const int k = kc + s * 4 * kBK;
-      const int64_t kb = INT4 ? (k >> 1) : k;
-      uint8_t* st = area + s * ROWS * SB;
-#pragma unroll
-      for (int d = 0; d < PER_STEP; ++d) {
-        const bool isa = d * RPI < 16 * TI;       // uniform per instruction
-        const int r = d * RPI + dr - (isa ? 0 : 16 * TI);
-        const int64_t cb = kb + 16 * (dp ^ (r & (CPR - 1)));
-        const bool ok = k < kz1 && cb < rowbytes;
-        dma16(isa ? rsA : rsB, st + d * 1024, ok ? (uint32_t)(r * rowbytes + cb) : kOOB, 0u);
+      for (int i = 0; i < TI; ++i) {
+        const int R = i * 16 + lr;
+        ra[i] = *reinterpret_cast<const uint4*>(st + R * SB + 16 * (lq ^ (R & 3)));
       }
-    }
 #pragma unroll
-    for (int s = 0; s < CHUNK; ++s) {
-      wait_step<PER_STEP, CHUNK>(s);
-      asm volatile("" ::: "memory");
-      const uint8_t* st = area + s * ROWS * SB;
-      if constexpr (INT4) {
-        uint4 ra[TI], rb[TJ];
+      for (int j = 0; j < TJ; ++j) {
+        const int R = j * 16 + lr;
+        rb[j] = *reinterpret_cast<const uint4*>(st + (16 * TI + R) * SB + 16 * (lq ^ (R & 3)));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const v4i a = h ? widen_int4(ra[i].z, ra[i].w) : widen_int4(ra[i].x, ra[i].y);
+            const v4i b = h ? widen_int4(rb[j].z, rb[j].w) : widen_int4(rb[j].x, rb[j].y);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i][j], 0, 0, 0);
+          }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4i a[TI], b[TJ];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
           const int R = i * 16 + lr;
-          ra[i] = *reinterpret_cast<const uint4*>(st + R * SB + 16 * (lq ^ (R & 3)));
+          a[i] = *reinterpret_cast<const v4i*>(st + R * SB + 16 * ((h * 4 + lq) ^ (R & 7)));
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int R = j * 16 + lr;
-          rb[j] = *reinterpret_cast<const uint4*>(st + (16 * TI + R) * SB + 16 * (lq ^ (R & 3)));
+          b[j] = *reinterpret_cast<const v4i*>(st + (16 * TI + R) * SB + 16 * ((h * 4 + lq) ^ (R & 7)));
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-          for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-              const v4i a = h ? widen_int4(ra[i].z, ra[i].w) : widen_int4(ra[i].x, ra[i].y);
-              const v4i b = h ? widen_int4(rb[j].z, rb[j].w) : widen_int4(rb[j].x, rb[j].y);
-              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i][j], 0, 0, 0);
-            }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          v4i a[TI], b[TJ];
-#pragma unroll
-          for (int i = 0; i < TI; ++i) {
-            const int R = i * 16 + lr;
-            a[i] = *reinterpret_cast<const v4i*>(st + R * SB + 16 * ((h * 4 + lq) ^ (R & 7)));
-          }
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            const int R = j * 16 + lr;
-            b[j] = *reinterpret_cast<const v4i*>(st + (16 * TI + R) * SB + 16 * ((h * 4 + lq) ^ (R & 7)));
-          }
-#pragma unroll
-          for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
       }
     }
+  };
+
+  // Ring of NBUF step slots per wave: the copies of step t + NBUF - 1 are
+  // issued before step t is read.  A slot is refilled only after the reads
+  // of its previous step have returned (their MFMAs consumed them).  The
+  // last NBUF - 1 steps drain the ring with no further copies; each drain
+  // position has a fixed number of younger steps, so every wait is exact.
+  // A wave with fewer than NBUF - 1 steps runs the missing ones on copies
+  // past kz1, which read as zeros and add nothing: the code stays free of
+  // branches around the waits.
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p) issue(p, p);
+  int rslot = 0, wslot = NBUF - 1;
+  for (int t = 0; t < nsteps - (NBUF - 1); ++t) {
+    issue(t + NBUF - 1, wslot);
+    wslot = wslot == NBUF - 1 ? 0 : wslot + 1;
+    wait_vmcnt<(NBUF - 1) * PER_STEP>();
+    asm volatile("" ::: "memory");
+    compute(area + rslot * STEP_BYTES);
+    rslot = rslot == NBUF - 1 ? 0 : rslot + 1;
   }
+  drain_ring<0, NBUF - 1>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    wait_vmcnt<(NBUF - 2 - j) * PER_STEP>();
+    asm volatile("" ::: "memory");
+    compute(area + rslot * STEP_BYTES);
+    rslot = rslot == NBUF - 1 ? 0 : rslot + 1;
+  });
   __syncthreads();   // every wave is done with its copy area; LDS now holds the partial tiles
   int (*red)[TI][TJ][4][64] = reinterpret_cast<int (*)[TI][TJ][4][64]>(smem);
 
@@ -249,9 +279,11 @@ struct DecodePlan {
   size_t ws_bytes;
 };
 
-// Split K so that about 256 workgroups stream the weights; each split is a
-// multiple of four 128-deep steps (one per wave).  Small weight matrices
-// are not split: the second kernel costs more than the split saves.
+// K is split only when the unsplit grid (16 channels x 16 or 32 rows per
+// workgroup) has fewer than 128 workgroups: then about 256 workgroups
+// stream the weights, each split a multiple of four 128-deep steps (one per
+// wave).  Small weight matrices and short K are not split: the second
+// kernel costs more than the split saves.
 static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, bool int4) {
   DecodePlan p{};
   p.ti = decode_ti(M, true);
@@ -259,7 +291,9 @@ static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, bool int4) {
   const int64_t unit = 4 * kBK;
   const int64_t nunits = (K + unit - 1) / unit;
   const int64_t wbytes = N * K / (int4 ? 2 : 1);
-  int64_t s = wbytes < (8 << 20) ? 1 : 256 / p.tiles;
+  const int ti_ns = decode_ti(M, false);
+  const int64_t wg_unsplit = ((N + 15) / 16) * ((M + 16 * ti_ns - 1) / (16 * ti_ns));
+  int64_t s = (wg_unsplit >= 128 || wbytes < (1 << 20) || nunits < 4) ? 1 : 256 / p.tiles;
   s = s < 1 ? 1 : (s > nunits ? nunits : s);
   const int64_t per = (nunits + s - 1) / s;
   p.kwg = (int)(per * unit);
