@@ -159,7 +159,8 @@ int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t l
  *           row stride N <= ldy <= 2^22 elements; y_dtype I32 writes the raw integer
  *           accumulators (INT formats, no branch, alpha ignored).
  *  workspace / workspace_bytes  optional device scratch (NULL / 0 for
- *           none).  Few-token shapes (M <= 64) split K over workgroups
+ *           none).  Few-token shapes (M <= 64) whose unsplit grid would be
+ *           small (few output channels, long K) split K over workgroups
  *           when it is given: int32 partial tiles go to the workspace and a
  *           second kernel adds them (exact) and runs the epilogue.  Size
  *           from w4a4_workspace_size; no initialisation needed; contents

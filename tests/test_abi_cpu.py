@@ -127,7 +127,7 @@ def test_linear_rejects_bad_arguments(ops):
     br = ops.BranchDesc(1, 16, 16, 0, 0x10000, 16, 0x20000, 16)
     assert _lin(ops, br=br, ydt=2) == -4          # no raw accumulators with a branch
     # workspace present but smaller than the split-K plan needs
-    M, N, K = 64, 2048, 8192
+    M, N, K = 64, 512, 8192
     need = ops.LIB.w4a4_workspace_size(M, N, K, 1)
     assert need > 0
     assert _lin(ops, fn="w8a8_linear", M=M, N=N, K=K, ws=FAKE2, wsb=need - 1) == -5
@@ -140,8 +140,11 @@ def test_workspace_sizes(ops):
     L = ops.LIB
     assert L.w4a4_workspace_size(4096, 5120, 5120, 2) == 0        # NVFP4: no split-K
     assert L.w4a4_workspace_size(512, 16384, 2048, 0) == 0        # many tokens: tile kernel
-    assert L.w4a4_workspace_size(64, 2048, 8192, 1) > 0           # few tokens, big weight: split-K
-    assert L.w4a4_workspace_size(64, 2048, 2048, 0) == 0          # small weight: no split
+    assert L.w4a4_workspace_size(64, 512, 8192, 1) > 0            # few tokens, few channels, long K: split-K
+    assert L.w4a4_workspace_size(9, 768, 8192, 0) > 0
+    assert L.w4a4_workspace_size(64, 2048, 8192, 1) == 0          # 256 workgroups unsplit: no split
+    assert L.w4a4_workspace_size(64, 2048, 2048, 0) == 0
+    assert L.w4a4_workspace_size(64, 256, 1024, 0) == 0           # small weight: no split
     assert L.w4a4_workspace_size(16, 256, 256, 0) == 0            # a single K split
     assert L.w4a4_workspace_size(0, 2048, 2048, 0) == 0
 
