@@ -129,10 +129,20 @@ __device__ __forceinline__ float fwht16_cross(float (&v)[16], int lane) {
   return c1 * c2;
 }
 
+// Maximum over the wave (exact in any order): DPP within each 16-lane row
+// (quad swaps, then the half-row and row mirrors leave the row maximum in
+// every lane of the row), then the four row maxima read as scalars.
 __device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  return m;
+  m = fmaxf(m, quad_perm<0xB1>(m));    // lane ^ 1
+  m = fmaxf(m, quad_perm<0x4E>(m));    // lane ^ 2
+  m = fmaxf(m, quad_perm<0x141>(m));   // row_half_mirror: quad q <-> 1 - q in each half row
+  m = fmaxf(m, quad_perm<0x140>(m));   // row_mirror: half rows swap
+  const int b = __float_as_int(m);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
