@@ -272,7 +272,7 @@ KERNEL_SOURCES = ["quantize.hip", "gemm_int.hip", "gemm_wide.hip", "branch.hip",
 
 # The dominant call of each workload: the kernels one linear call launches.
 DOMINANT = {
-    "batch1": ("w8a8_linear int8 64x2048x8192", ["gemm_int_decode_kernel<false, 4>", "gemm_int_reduce_kernel<false>"]),
+    "batch1": ("w8a8_linear int8 64x2048x8192", ["gemm_int_decode_kernel<false, 2, 1>"]),
     "video4096": ("w4a4_linear nvfp4 4096x5120x5120", ["gemm_wide_kernel<2,"]),
     "prefill": ("w4a4_linear int4 512x16384x2048", ["gemm_wide_kernel<0, 4, 4, 2, 4, 1>"]),
     "lowrank": ("w4a4_linear int4 1024x3072x3072", ["gemm_wide_kernel<0, 4, 6, 2, 1, 2>"]),

@@ -68,7 +68,7 @@ static int decode_ti(int64_t M, bool split) {
 // LDS bytes a decode wave keeps in flight (its ring of step slots): int4
 // rows are half as long per step, and a smaller ring measured faster there.
 template <bool INT4>
-constexpr int dec_ring_bytes() { return INT4 ? 12 * 1024 : 36 * 1024; }
+constexpr int dec_ring_bytes() { return INT4 ? 12 * 1024 : 18 * 1024; }
 
 // f(integral_constant<int, J>) for J = J0 .. J1 - 1, in order.
 template <int J0, int J1, typename F>
