@@ -40,6 +40,47 @@ __device__ __forceinline__ void branch_mfma(v4f (&acc)[TI][TJ], const BranchArgs
   }
 }
 
+// Epilogue operands a kernel has already staged in LDS for its whole tile:
+// the scales of the tile's rows and columns and, for a branch with r and ra
+// at most kBrLdsMax, the tile's rows of A_br and B_br.  A branch row holds
+// 128 bytes whose 16-byte chunk c sits at position c XOR (row mod 8); chunks
+// past ra (A) or r (B) hold zeros.
+constexpr int kBrLdsMax = 64;
+struct EpiLds {
+  const float* sa;       // sa[m - m_tile]
+  const float* sw;       // sw[n - n_tile]
+  const uint8_t* bra;    // A_br rows of the tile, or null (branch read from global memory)
+  const uint8_t* brb;    // B_br rows of the tile
+  int m_tile, n_tile;
+};
+
+// acc[i][j] += A_br . B_br^T over ra (B_br index k mod r), operands from the
+// LDS-staged branch rows.  m_loc / n_loc: tile-relative first row / column.
+template <int TI, int TJ>
+__device__ __forceinline__ void branch_mfma_lds(v4f (&acc)[TI][TJ], const EpiLds& el, int ra, int r, int m_loc,
+                                                int n_loc, int lane) {
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  for (int kk = 0; kk < ra; kk += 32) {
+    const int ka = kk + lk, kb = ka % r;
+    v8bf af[TI], bfr[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = m_loc + i * 16 + lr;
+      af[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(el.bra + row * 128 + (((ka >> 3) ^ (row & 7)) << 4)));
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = n_loc + j * 16 + lr;
+      bfr[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(el.brb + row * 128 + (((kb >> 3) ^ (row & 7)) << 4)));
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+}
+
 // Dequantisation scales of a wave's TI x TJ tile grid as the lane uses them:
 // sa for its rows 4*(lane/16)+0..3 of each row block, sw for its column
 // lane%16 of each 16-column block (0 past M / N).  A kernel that loads
@@ -85,11 +126,12 @@ constexpr int epilogue_stage_bytes() {
   return TI * 16 * (TJ * 32 + 16);
 }
 
-// `pre`, when given, holds the scales already loaded (load_epi_scales).
+// `pre`, when given, holds the scales already loaded (load_epi_scales);
+// `el`, when given, the LDS-staged scales and branch rows of the tile.
 template <int KIND /*0 int4, 1 int8, 2 float*/, typename AccT, int TI, int TJ>
 __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
                                                int lane, uint8_t* stage = nullptr,
-                                               const EpiScales<TI, TJ>* pre = nullptr) {
+                                               const EpiScales<TI, TJ>* pre = nullptr, const EpiLds* el = nullptr) {
   const int lr = lane & 15, lq = lane >> 4;
   const int esz = g.y_dtype == 1 ? 2 : 4;
   const int rows = max(0, min(TI * 16, g.M - m_base));
@@ -128,7 +170,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m_base + i * 16 + lq * 4 + r;
-        sam[i][r] = pre ? pre->sa[i][r] : (m < g.M ? sa[m] : 0.f);
+        sam[i][r] = pre ? pre->sa[i][r] : el ? el->sa[m - el->m_tile] : (m < g.M ? sa[m] : 0.f);
       }
   }
 #pragma unroll
@@ -137,7 +179,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
     const uint32_t coff = n < g.N ? (uint32_t)n * (uint32_t)esz : kOOB;
     v4f col[TI][1];
     if constexpr (KIND != 2) {
-      const float swn = pre ? pre->sw[j] : (n < g.N ? sw[n] : 0.f);
+      const float swn = pre ? pre->sw[j] : el ? el->sw[n - el->n_tile] : (n < g.N ? sw[n] : 0.f);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -153,7 +195,12 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
 #pragma unroll
         for (int r = 0; r < 4; ++r) col[i][0][r] = acc[i][j][r] * g.alpha;
     }
-    if (g.br.r > 0) branch_mfma<TI, 1>(col, g.br, g.M, g.N, m_base, n_base + j * 16, lane);
+    if (g.br.r > 0) {
+      if (el && el->bra)
+        branch_mfma_lds<TI, 1>(col, *el, g.br.ra, g.br.r, m_base - el->m_tile, n_base + j * 16 - el->n_tile, lane);
+      else
+        branch_mfma<TI, 1>(col, g.br, g.M, g.N, m_base, n_base + j * 16, lane);
+    }
     if (stage != nullptr && g.y_dtype == 1) {
       // bf16 into the wave's LDS tile (row pitch TJ * 32 + 16 bytes)
 #pragma unroll

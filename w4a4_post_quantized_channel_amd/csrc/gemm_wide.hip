@@ -152,7 +152,15 @@ struct WCfg {
   static constexpr int NW = WR * WC * WK;            // waves per workgroup (4 or 8)
   static constexpr int RED = WK > 1 ? NW * TI * TJ * 4 * 64 * 4 : 0;   // every wave's partial tile
   static constexpr int PIPE = kNBuf * STAGE + 1024;                    // + DMA pad target
-  static constexpr int LDS = PIPE > RED ? PIPE : RED;
+  // After the main loop: the epilogue's own LDS use (bf16 staging, or the
+  // split-K partial tiles), then the tile's branch rows (kBrLdsMax bf16 =
+  // 128 bytes each), then the tile's scales (one float per row and column).
+  static constexpr int EPI = WK == 1 ? NW * epilogue_stage_bytes<TI, TJ>() : RED;
+  static constexpr int BR_OFF = (EPI + 1023) / 1024 * 1024;
+  static constexpr int BR_BYTES = (BM + BN) * 2 * kBrLdsMax;
+  static constexpr int MAIN = PIPE > BR_OFF + BR_BYTES ? PIPE : BR_OFF + BR_BYTES;
+  static constexpr int SC_OFF = (MAIN + 255) / 256 * 256;
+  static constexpr int LDS = SC_OFF + (BM + BN) * 4;
   static constexpr int NA = A_BYTES / 1024, NB = B_BYTES / 1024;       // 16-byte DMA wave-instructions
   static constexpr int NSA = SA_BYTES / 256, NSB = SB_BYTES / 256;     // 4-byte DMA wave-instructions
   // every wave issues the same number per stage (the last round padded)
@@ -162,6 +170,8 @@ struct WCfg {
   static_assert(TJ % WK == 0, "split-K epilogue splits the columns");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(DPS * (kNBuf - 2) <= 63, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(BM + BN <= 64 * NW, "one scale per thread");
 };
 
 
@@ -310,6 +320,19 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
+  // The epilogue's scales: one per thread (tile rows, then tile columns),
+  // loaded now and written to LDS after the main loop.
+  float scv = 0.f;
+  if constexpr (FMT != W_NVFP4) {
+    if (tid < C::BM) {
+      const int m = m0 + tid;
+      scv = m < g.M ? reinterpret_cast<const float*>(g.sa)[m] : 0.f;
+    } else if (tid < C::BM + C::BN) {
+      const int n = n0 + tid - C::BM;
+      scv = n < g.N ? reinterpret_cast<const float*>(g.sw)[n] : 0.f;
+    }
+  }
+
   // Per-lane LDS offsets of the fragment rows (the swizzle term does not
   // depend on the fragment index: fragments are 16 rows apart).  Lane
   // group lq of K-group kw owns logical slot 4 kw + lq of each row.
@@ -443,11 +466,41 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   wait_vmcnt<0>();
   __syncthreads();   // all copies landed and all waves are done with the stage buffers
 
+  // Epilogue operands into LDS in one batch: the scales, and for a branch
+  // with r and ra at most kBrLdsMax, the tile's rows of A_br and B_br (8
+  // rows of 128 bytes per copy instruction, chunk c of a row at position
+  // c XOR (row mod 8), chunks past ra or r and rows past M or N as zeros).
+  float* lsc = reinterpret_cast<float*>(smem + C::SC_OFF);
+  if (tid < C::BM + C::BN) lsc[tid] = scv;
+  const bool br_lds = g.br.r > 0 && g.br.ra <= kBrLdsMax && g.br.r <= kBrLdsMax && g.br.lda <= (1 << 20) &&
+                      g.br.ldb <= (1 << 20);
+  uint8_t* bra = smem + C::BR_OFF;
+  uint8_t* brb = bra + C::BM * 2 * kBrLdsMax;
+  if (br_lds) {
+    constexpr int NIA = C::BM / 8, NIB = C::BN / 8;
+    const v4u rbA = rsrc_words(g.br.a + (int64_t)m0 * g.br.lda, (uint32_t)(max(0, min(C::BM, g.M - m0)) * g.br.lda * 2));
+    const v4u rbB = rsrc_words(g.br.b + (int64_t)n0 * g.br.ldb, (uint32_t)(max(0, min(C::BN, g.N - n0)) * g.br.ldb * 2));
+    const int rl = lane >> 3, pos = lane & 7, chunk = pos ^ rl;
+    for (int n = wave; n < NIA + NIB; n += C::NW) {   // wave-uniform
+      const bool isa = n < NIA;
+      const int row = (isa ? n : n - NIA) * 8 + rl;
+      const int64_t ld = isa ? g.br.lda : g.br.ldb;
+      const int klen = isa ? g.br.ra : g.br.r;
+      const uint32_t off = chunk * 8 < klen ? (uint32_t)(row * ld * 2 + chunk * 16) : kOOB;
+      dma16(isa ? rbA : rbB, (isa ? bra : brb) + (isa ? n : n - NIA) * 1024, off, 0u);
+    }
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  const EpiLds el{FMT == W_NVFP4 ? nullptr : lsc, FMT == W_NVFP4 ? nullptr : lsc + C::BM,
+                  br_lds ? bra : nullptr, brb, m0, n0};
+
   constexpr int KIND = FMT == W_NVFP4 ? 2 : (FMT == W_INT4 ? 0 : 1);
   if constexpr (WK == 1) {
     // bf16 output is staged through this wave's slice of the (now idle) LDS
-    static_assert(C::NW * epilogue_stage_bytes<TI, TJ>() <= C::LDS, "epilogue staging fits");
-    epilogue_tiles<KIND>(acc, g, m0 + wm0, n0 + wn0, lane, smem + wave * epilogue_stage_bytes<TI, TJ>());
+    static_assert(C::NW * epilogue_stage_bytes<TI, TJ>() <= C::BR_OFF, "epilogue staging fits");
+    epilogue_tiles<KIND>(acc, g, m0 + wm0, n0 + wn0, lane, smem + wave * epilogue_stage_bytes<TI, TJ>(),
+                         static_cast<const EpiScales<TI, TJ>*>(nullptr), &el);
   } else {
     // Sum the WK partial tiles: every wave stores its tile, then wave group
     // kw adds up columns [kw * TJ / WK, (kw + 1) * TJ / WK) and runs the
@@ -479,7 +532,8 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
           part[i][jj][r] = v;
         }
       }
-    epilogue_tiles<KIND>(part, g, m0 + wm0, n0 + wn0 + kw * TJW * 16, lane);
+    epilogue_tiles<KIND>(part, g, m0 + wm0, n0 + wn0 + kw * TJW * 16, lane, nullptr,
+                         static_cast<const EpiScales<TI, TJW>*>(nullptr), &el);
   }
 }
 
