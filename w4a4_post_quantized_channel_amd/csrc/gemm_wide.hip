@@ -460,7 +460,8 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
         if (st + 1 < STEPS) widen(f, st + 1, next);
         mma_step(now);
       }
-      interleave_steps<(TI + TJ) * 2, TI * TJ * STEPS, NV>();
+      // no instruction-group pattern here: the compiler's own order of the
+      // widening (4.5 VALU per MFMA) measured faster than a fixed one
     }
   }
   wait_vmcnt<0>();
