@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="batch1", choices=["batch1", "video4096", "prefill", "lowrank", "tiny"])
+    p.add_argument("--workload", default="batch1", choices=["batch1", "video4096", "prefill", "lowrank", "tiny", "batch1_a8", "video4096_a8"])
     p.add_argument("--no-also", action="store_true", help="skip the secondary 4096-token measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample duration")
@@ -68,7 +68,8 @@ def gemm_bytes(case):
     """Algorithmic HBM bytes of one GEMM launch: packed weight and activation
     codes, their scales, the output and the branch operands."""
     M, N, K = case.M, case.N, case.K
-    code = {"int4": 0.5, "int8": 1.0, "nvfp4": 0.5}[case.fmt]
+    code_a = {"int4": 0.5, "int8": 1.0, "nvfp4": 0.5, "w4a8": 1.0}[case.fmt]
+    code_w = {"int4": 0.5, "int8": 1.0, "nvfp4": 0.5, "w4a8": 0.5}[case.fmt]
     if case.fmt == "nvfp4":
         scales = (M + N) * K / 16
     else:
@@ -79,7 +80,7 @@ def gemm_bytes(case):
         r = case.branch["lw"].shape[1]
         ra = 2 * r if case.branch["kind"] == "lowrank" else r
         br = 2 * (M * ra + N * r)
-    return code * (M + N) * K + scales + out + br
+    return code_a * M * K + code_w * N * K + scales + out + br
 
 
 EAGER = False
@@ -133,9 +134,10 @@ def dominant_kernel_time(torch, case, layer, t, steps):
         br = ops.branch_desc(layer.branch_operand(case.M, t["x"].device), layer.branch["lw"])
 
     def gemm():
-        if case.fmt == "int8":
-            ops.w8a8_linear(b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K, branch=br,
-                            y=b["y"], workspace=b["ws"])
+        if case.fmt in ("int8", "w4a8"):
+            fn = ops.w8a8_linear if case.fmt == "int8" else ops.w4a8_linear
+            fn(b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K, branch=br,
+               y=b["y"], workspace=b["ws"])
         else:
             ops.w4a4_linear(b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K, case.fmt,
                             alpha=layer.alpha, branch=br, y=b["y"], workspace=b["ws"])
@@ -147,7 +149,7 @@ def quant_kernel_time(torch, case, layer, t, steps):
     b = layer.buffers(case.M, t["x"].device)
 
     def q():
-        ops.quantize_act(t["x"], layer.inv_s, case.fmt, fwht_block=layer.fwht_block, order=layer.order,
+        ops.quantize_act(t["x"], layer.inv_s, layer.a_fmt, fwht_block=layer.fwht_block, order=layer.order,
                          tensor_scale=layer.g_a, codes=b["codes"], scales=b["scales"])
     return time_region(torch, q, steps, max(5, steps // 10))
 
@@ -167,15 +169,15 @@ def cpu_baseline(names, target_s):
     prepared = []
     for n in names:
         c = WL.workload(n)
-        W = O.quantize_operand(c.w, c.s, c.fmt)
+        W = O.quantize_operand(c.w, c.s, O.OPERAND_FORMATS[c.fmt][1])
         g_a = None
         if c.fmt == "nvfp4":
             g_a = O.nvfp4_tensor_scale(O.transformed_amax(c.x, c.inv_s))
         prepared.append((c, W, g_a))
 
     def one_call(c, W, g_a):
-        A = O.quantize_operand(c.x, c.inv_s, c.fmt, g=g_a)
-        if c.fmt in ("int4", "int8"):
+        A = O.quantize_operand(c.x, c.inv_s, O.OPERAND_FORMATS[c.fmt][0], g=g_a)
+        if c.fmt in ("int4", "int8", "w4a8"):
             y = O.dequant_epilogue(O.int_gemm(A["codes"], W["codes"]), A["scales"], W["scales"])
         else:
             y = O.dequantize_nvfp4(A["codes"], A["scales"], A["g"]) @ O.dequantize_nvfp4(
@@ -213,6 +215,11 @@ WORKLOADS = {
                                                      "512x16384x2048 + down W4A4 512x2048x8192"),
     "lowrank": (["lowrank"], "1024-token low-rank-protected W4A4 1024x3072x3072 + rank-32 bf16 branch"),
     "tiny": (["tiny"], "tiny W4A4 16x256x256 (fp32 in/out)"),
+    "batch1_a8": (["decode_w4a8", "decode_w4a8_down"],
+                  "batch-1 64-token action step at 8-bit activations (protected denoising step): "
+                  "W4A8 64x2048x2048 + W4A8 64x2048x8192, smoothing + FWHT-64 + per-token int8"),
+    "video4096_a8": (["video_w4a8"], "4096-token video-latent projection at 8-bit activations "
+                                     "(protected denoising step), W4A8 4096x5120x5120 + 64 kept bf16 channels"),
 }
 
 
@@ -228,7 +235,7 @@ def measure(torch, wl, steps, warmup):
     q_ms = quant_kernel_time(torch, c, layer, t, ksteps)
     flop_k = 2.0 * c.M * c.N * c.K
     bytes_k = gemm_bytes(c)
-    mtype = {"int4": "i8", "int8": "i8", "nvfp4": "f16"}[c.fmt]
+    mtype = {"int4": "i8", "int8": "i8", "nvfp4": "f16", "w4a8": "i8"}[c.fmt]
     intensity = flop_k / bytes_k
     ridge = PEAK_TFLOPS[mtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
     if intensity < ridge:
@@ -238,12 +245,13 @@ def measure(torch, wl, steps, warmup):
                 "unit": "TFLOP/s" if mtype != "i8" else "TOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = recorded_traffic(wl)
-    roof["kernel"] = f"{'w8a8_linear' if c.fmt == 'int8' else 'w4a4_linear'} {c.fmt} {c.M}x{c.N}x{c.K}"
+    entry = {"int8": "w8a8_linear", "w4a8": "w4a8_linear"}.get(c.fmt, "w4a4_linear")
+    roof["kernel"] = f"{entry} {c.fmt} {c.M}x{c.N}x{c.K}"
     roof["kernel_us"] = k_ms * 1e3
     roof["algorithmic_bytes"] = bytes_k
-    qbytes = c.M * c.K * (2 if c.x_dtype == "bf16" else 4) + c.M * c.K * (1 if c.fmt == "int8" else 0.5) + (
+    qbytes = c.M * c.K * (2 if c.x_dtype == "bf16" else 4) + c.M * c.K * (1 if c.fmt in ("int8", "w4a8") else 0.5) + (
         c.M * c.K / 16 if c.fmt == "nvfp4" else 4 * c.M)
-    quant = {"kernel": f"quantize_act {c.fmt} {c.M}x{c.K}", "us": q_ms * 1e3,
+    quant = {"kernel": f"quantize_act {layer.a_fmt} {c.M}x{c.K}", "us": q_ms * 1e3,
              "achieved_GBs": qbytes / (q_ms * 1e-3) / 1e9, "frac_hbm": qbytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     return {"names": names, "desc": desc, "ms": ms, "flops": flops, "roofline": roof, "quantize": quant,
             "per_call_us": {n: None for n in names}}
@@ -272,7 +280,9 @@ KERNEL_SOURCES = ["quantize.hip", "gemm_int.hip", "gemm_wide.hip", "branch.hip",
 
 # The dominant call of each workload: the kernels one linear call launches.
 DOMINANT = {
-    "batch1": ("w8a8_linear int8 64x2048x8192", ["gemm_int_decode_kernel<false, 2, 1>"]),
+    "batch1": ("w8a8_linear int8 64x2048x8192", ["gemm_int_decode_kernel<1, 2, 1>"]),
+    "batch1_a8": ("w4a8_linear w4a8 64x2048x8192", ["gemm_int_decode_kernel<2, 2, 1>"]),
+    "video4096_a8": ("w4a8_linear w4a8 4096x5120x5120", ["gemm_wide_kernel<3,"]),
     "video4096": ("w4a4_linear nvfp4 4096x5120x5120", ["gemm_wide_kernel<2,"]),
     "prefill": ("w4a4_linear int4 512x16384x2048", ["gemm_wide_kernel<0, 4, 4, 2, 4, 1>"]),
     "lowrank": ("w4a4_linear int4 1024x3072x3072", ["gemm_wide_kernel<0, 4, 6, 2, 1, 2>"]),

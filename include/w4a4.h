@@ -63,7 +63,10 @@ typedef enum w4a4_status {
 } w4a4_status;
 
 /* Code formats. */
-enum { W4A4_FMT_INT4 = 0, W4A4_FMT_INT8 = 1, W4A4_FMT_NVFP4 = 2 };
+enum { W4A4_FMT_INT4 = 0, W4A4_FMT_INT8 = 1, W4A4_FMT_NVFP4 = 2, W4A4_FMT_W4A8 = 3 };
+/* W4A4_FMT_W4A8 names the GEMM pairing of INT8 activation codes with INT4
+ * weight codes (w4a8_linear, w4a4_workspace_size); quantize_act and
+ * pack_weights take INT8 and INT4 for its two sides. */
 /* Element types of float inputs / outputs.  I32 = raw integer accumulators. */
 enum { W4A4_DT_F32 = 0, W4A4_DT_BF16 = 1, W4A4_DT_I32 = 2 };
 /* Order of the two transforms applied before quantization. */
@@ -229,12 +232,31 @@ int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r);
  * static NVFP4 tensor scale g = amax / (6 * 448) (QuantWAMs sec. 4.2:
  * statistics are collected after both transforms).  ``scale`` is 1/s for
  * activations and s for weights; q->fmt is ignored. */
+/* w4a8_linear -- W4A8: INT8 activation codes x INT4 weight codes, the GEMM
+ * of the denoising steps whose activations stay at 8 bits while the weights
+ * keep their 4-bit codes (QuantWAMs, Experimental Details, quantization
+ * configuration; sec. 4.4.3, fixed-intervention rollout scheduling).
+ *  a_codes / a_scales   M rows from quantize_act with W4A4_FMT_INT8
+ *           (int8 M x K, fp32[M]).
+ *  w_codes / w_scales   N rows from pack_weights with W4A4_FMT_INT4
+ *           (packed int4 N x K/2, fp32[N]).
+ *  Exact int32 accumulation of int8 x int4 products, then
+ *  y = fp32(fp32(acc) * a_scales[m]) * w_scales[n] * alpha, as for INT4.
+ *  br, y, y_dtype (I32 = raw accumulators), ldy, workspace and the shape
+ *  and alignment rules are those of w4a4_linear; size a workspace with
+ *  w4a4_workspace_size(M, N, K, W4A4_FMT_W4A8). */
+int w4a8_linear(const void* a_codes, const void* a_scales,
+                const void* w_codes, const void* w_scales,
+                int64_t M, int64_t N, int64_t K, float alpha,
+                const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
+                void* workspace, size_t workspace_bytes, void* stream);
+
 int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, int64_t ldx,
                         const float* scale, const w4a4_qdesc* q, float* amax_out,
                         void* stream);
 
-/* Bytes of workspace w4a4_linear / w8a8_linear use for (M, N, K, fmt);
- * 0 when the shape runs without one. */
+/* Bytes of workspace w4a4_linear / w8a8_linear / w4a8_linear use for
+ * (M, N, K, fmt); 0 when the shape runs without one. */
 size_t w4a4_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt);
 
 const char* w4a4_status_string(int status);

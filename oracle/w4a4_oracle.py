@@ -23,6 +23,9 @@ Sources (the pages this restates; no text is quoted):
 * LatentQuant abstract: NVFP4 W4A4 and activation quantize-dequantize.
 * Q-WAM abstract: a 16-bit low-rank branch plus 4-bit complement, both as
   dense matrix products.
+* QuantWAMs, Experimental Details (quantization configuration) and
+  sec. 4.4.3: some denoising steps keep their activations at 8 bits while
+  the weights stay at 4 bits (W4A8).
 
 Readings where the pages are silent (each also listed in the design notes):
 
@@ -331,15 +334,23 @@ def transformed_amax(x, scale, fwht_block=FWHT_BLOCK, order="smooth_then_rotate"
     return F32(np.abs(y).max()) if y.size else F32(0)
 
 
+# Activation and weight formats of each linear: W4A8 is the 8-bit-activation
+# step of the QuantWAMs schedule (Experimental Details, quantization
+# configuration; sec. 4.4.3), with the same 4-bit weight codes as W4A4.
+OPERAND_FORMATS = {"int4": ("int4", "int4"), "int8": ("int8", "int8"),
+                   "nvfp4": ("nvfp4", "nvfp4"), "w4a8": ("int8", "int4")}
+
+
 def linear(case, order="smooth_then_rotate", g_a=None, g_w=None) -> dict:
     """Full quantized linear for a ``workloads.Case``: quantize activations
     and weights, integer (or NVFP4) GEMM, dequant epilogue, 16-bit branch.
     Returns the intermediate codes, scales and accumulators and y (float64)."""
     fb = case.fwht_block
-    A = quantize_operand(case.x, case.inv_s, case.fmt, fb, order, g_a)
-    W = quantize_operand(case.w, case.s, case.fmt, fb, order, g_w)
+    fa, fw = OPERAND_FORMATS[case.fmt]
+    A = quantize_operand(case.x, case.inv_s, fa, fb, order, g_a)
+    W = quantize_operand(case.w, case.s, fw, fb, order, g_w)
     out = {"a": A, "w": W}
-    if case.fmt in ("int4", "int8"):
+    if case.fmt in ("int4", "int8", "w4a8"):
         acc = int_gemm(A["codes"], W["codes"])
         y = dequant_epilogue(acc, A["scales"], W["scales"])
         out["acc"] = acc

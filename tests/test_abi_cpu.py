@@ -28,7 +28,7 @@ def ops():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "lowrank_add"]:
+    for n in ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "lowrank_add"]:
         assert n in names
 
 
@@ -98,8 +98,8 @@ def _lin(ops, fn="w4a4_linear", M=8, N=8, K=128, fmt=0, alpha=1.0, br=None, y=FA
          ws=None, wsb=0, a=FAKE, sa=FAKE, w=FAKE, sw=FAKE):
     ldy = N if ldy is None else ldy
     brp = None if br is None else ctypes.byref(br)
-    if fn == "w8a8_linear":
-        return ops.LIB.w8a8_linear(a, sa, w, sw, M, N, K, alpha, brp, y, ydt, ldy, ws, wsb, None)
+    if fn in ("w8a8_linear", "w4a8_linear"):
+        return getattr(ops.LIB, fn)(a, sa, w, sw, M, N, K, alpha, brp, y, ydt, ldy, ws, wsb, None)
     return ops.LIB.w4a4_linear(a, sa, w, sw, M, N, K, fmt, alpha, brp, y, ydt, ldy, ws, wsb, None)
 
 
@@ -109,6 +109,10 @@ def test_linear_rejects_bad_arguments(ops):
     assert _lin(ops, M=-1) == -1
     assert _lin(ops, K=1 << 20) == -2
     assert _lin(ops, fmt=1) == -4                 # int8 codes go through w8a8_linear
+    assert _lin(ops, fmt=3) == -4                 # int8 x int4 goes through w4a8_linear
+    assert _lin(ops, fn="w4a8_linear", K=96) == -2
+    assert _lin(ops, fn="w4a8_linear", a=MISAL) == -3
+    assert _lin(ops, fn="w4a8_linear", ydt=5) == -4
     assert _lin(ops, fmt=2, ydt=2) == -4          # raw accumulators only for integer formats
     assert _lin(ops, ydt=5) == -4
     assert _lin(ops, ldy=4) == -1
@@ -131,6 +135,10 @@ def test_linear_rejects_bad_arguments(ops):
     need = ops.LIB.w4a4_workspace_size(M, N, K, 1)
     assert need > 0
     assert _lin(ops, fn="w8a8_linear", M=M, N=N, K=K, ws=FAKE2, wsb=need - 1) == -5
+    need = ops.LIB.w4a4_workspace_size(M, N, K, 3)
+    assert need > 0
+    assert _lin(ops, fn="w4a8_linear", M=M, N=N, K=K, ws=FAKE2, wsb=need - 1) == -5
+    assert _lin(ops, fn="w4a8_linear", M=0, a=None, sa=None, y=None) == 0
     # empty problems are valid no-ops
     assert _lin(ops, M=0, a=None, sa=None, y=None) == 0
     assert _lin(ops, N=0, a=None, sa=None, w=None, sw=None, y=None) == 0
@@ -144,6 +152,10 @@ def test_workspace_sizes(ops):
     assert L.w4a4_workspace_size(9, 768, 8192, 0) > 0
     assert L.w4a4_workspace_size(64, 2048, 8192, 1) == 0          # 256 workgroups unsplit: no split
     assert L.w4a4_workspace_size(64, 2048, 2048, 0) == 0
+    assert L.w4a4_workspace_size(9, 768, 8192, 3) > 0             # W4A8 decode splits like INT4
+    assert L.w4a4_workspace_size(64, 2048, 8192, 3) == 0
+    assert L.w4a4_workspace_size(512, 5120, 5120, 3) == 0         # many tokens: tile kernel
+    assert L.w4a4_workspace_size(9, 768, 8192, 4) == 0            # unknown format
     assert L.w4a4_workspace_size(64, 256, 1024, 0) == 0           # small weight: no split
     assert L.w4a4_workspace_size(16, 256, 256, 0) == 0            # a single K split
     assert L.w4a4_workspace_size(0, 2048, 2048, 0) == 0

@@ -398,3 +398,62 @@ def test_whole_path_nvfp4_and_branch_small():
     # branch contribution is exactly the kept-channel product
     assert np.allclose(out["y"] - out["y_main"],
                        c.x[:, c.branch["idx"]].astype(np.float64) @ c.branch["lw"].astype(np.float64).T)
+
+
+# ------------------------------------------------------------------- W4A8
+def _plain_case(x, w, fmt):
+    """A case without smoothing or rotation: the quantizers see x and w."""
+    x = np.asarray(x, np.float32)
+    w = np.asarray(w, np.float32)
+    return WL.Case(name="pin", M=x.shape[0], N=w.shape[0], K=x.shape[1], fmt=fmt,
+                   x_dtype="f32", y_dtype="f32", x=x, w=w, s=None, inv_s=None,
+                   fwht_block=0, w_full=w)
+
+
+def test_w4a8_exact_on_grid_values():
+    """Integer activations whose rows peak at 127 and integer weights whose
+    rows peak at 7 lie on the int8 and int4 grids with step 1, so W4A8 gives
+    x w^T exactly.  A 4-bit activation grid, an 8-bit weight grid or a
+    transposed product breaks the equality."""
+    rng = np.random.default_rng(7)
+    M, N, K = 5, 6, 128
+    x = rng.integers(-127, 128, size=(M, K))
+    x[np.arange(M), rng.integers(0, K, M)] = 127
+    w = rng.integers(-7, 8, size=(N, K))
+    w[np.arange(N), rng.integers(0, K, N)] = -7
+    out = O.linear(_plain_case(x, w, "w4a8"))
+    assert np.array_equal(out["a"]["codes"], x)
+    assert np.array_equal(out["w"]["codes"], w)
+    assert np.all(out["a"]["scales"] == 1) and np.all(out["w"]["scales"] == 1)
+    assert np.array_equal(out["acc"], x @ w.T)
+    assert np.array_equal(out["y"], (x @ w.T).astype(np.float64))
+    # weights go through the nibble packing of the 4-bit format
+    assert out["w"]["packed"].shape == (N, K // 2)
+    assert out["a"]["packed"].shape == (M, K)
+    # the same inputs as W4A4 lose the activation grid
+    assert not np.array_equal(O.linear(_plain_case(x, w, "int4"))["y"], out["y"])
+
+
+def test_w4a8_error_bound_with_transforms():
+    """With smoothing and the 64-point rotation (orthonormal, folded into the
+    weights), |y - x w^T| <= sum_k (d_a |w^_k| + d_w |a_k|) with half-steps
+    d_a = step_a / 2 and d_w = step_w / 2, up to fp32 rounding of the
+    transforms; W4A8 error is below W4A4 error on the same layer."""
+    c = WL.linear_case(24, 40, 256, seed=31, fmt="w4a8", x_dtype="f32",
+                       n_outliers=6, outlier_gain=20.0)
+    out = O.linear(c)
+    A, W = out["a"], out["w"]
+    assert A["codes"].min() >= -128 and np.abs(A["codes"]).max(axis=1).min() == 127
+    assert W["codes"].min() >= -8 and np.abs(W["codes"]).max(axis=1).min() == 7
+    ref = c.x.astype(np.float64) @ c.w.astype(np.float64).T
+    w_hat = W["codes"].astype(np.float64) * W["scales"].astype(np.float64)[:, None]
+    a_t = A["y"].astype(np.float64)
+    bound = (A["scales"].astype(np.float64)[:, None] / 2 * np.abs(w_hat).sum(axis=1)[None, :]
+             + W["scales"].astype(np.float64)[None, :] / 2 * np.abs(a_t).sum(axis=1)[:, None])
+    slack = 1e-5 * (np.abs(c.x.astype(np.float64)) @ np.abs(c.w.astype(np.float64)).T)
+    err = np.abs(out["y"] - ref)
+    assert np.all(err <= bound * (1 + 1e-6) + slack)
+    c4 = WL.linear_case(24, 40, 256, seed=31, fmt="int4", x_dtype="f32",
+                        n_outliers=6, outlier_gain=20.0)
+    err4 = np.abs(O.linear(c4)["y"] - ref)
+    assert np.sum(err ** 2) < 0.8 * np.sum(err4 ** 2)

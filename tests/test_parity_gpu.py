@@ -46,6 +46,24 @@ def _oracle(case, order="smooth_then_rotate"):
     return O.linear(case, order=order)
 
 
+def _sides(fmt):
+    return O.OPERAND_FORMATS[fmt]
+
+
+def _raw_linear(ops, fmt, a, sa, w, sw, K, **kw):
+    """The integer linear entry point for ``fmt`` (int4, int8, w4a8)."""
+    if fmt == "int4":
+        return ops.w4a4_linear(a, sa, w, sw, K, "int4", **kw)
+    fn = ops.w8a8_linear if fmt == "int8" else ops.w4a8_linear
+    return fn(a, sa, w, sw, K, **kw)
+
+
+def _random_codes(rng, fmt, R, K):
+    if fmt == "int4":
+        return rng.integers(0, 256, size=(R, K // 2), dtype=np.uint8)
+    return rng.integers(-128, 128, size=(R, K), dtype=np.int8)
+
+
 def _report(name, **kw):
     print(f"[parity] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
 
@@ -67,6 +85,13 @@ SMALL = [
     # >= 256 rows: the row-per-lane NVFP4 quantizer (ragged last group of 64 rows)
     ("nvfp4_rows", 300, 96, 320, "nvfp4", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=8)),
     ("nvfp4_rows_f32", 260, 64, 256, "nvfp4", "f32", dict(n_outliers=4, outlier_gain=20.0)),
+    # W4A8: int8 activation codes x int4 weight codes
+    ("w4a8_ragged", 70, 96, 448, "w4a8", "bf16", dict(n_outliers=6, outlier_gain=15.0)),
+    ("w4a8_tiles", 160, 256, 512, "w4a8", "bf16", dict(n_outliers=8, outlier_gain=15.0, row_gain_sigma=0.5)),
+    ("w4a8_f32", 16, 256, 256, "w4a8", "f32", dict(n_outliers=4, outlier_gain=20.0)),
+    ("w4a8_lowrank", 90, 200, 384, "w4a8", "bf16", dict(n_outliers=6, outlier_gain=25.0, lowrank=16)),
+    ("w4a8_outlier", 33, 130, 320, "w4a8", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=8)),
+    ("w4a8_long_rows", 5, 40, 4160, "w4a8", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
 ]
 
 
@@ -80,14 +105,15 @@ def test_small_cases(ops, pipe, name, M, N, K, fmt, xdt, kw, order):
     if fmt == "nvfp4":
         assert np.float32(layer.g_a) == ref["a"]["g"] and np.float32(layer.g_w) == ref["w"]["g"]
     b = layer.buffers(M, t["x"].device)
-    na = check_operand(fmt, _np(b["codes"]), _np(b["scales"]), ref["a"], what="activations")
-    nw = check_operand(fmt, _np(layer.w_codes), _np(layer.w_scales), ref["w"], what="weights")
+    fa, fw = _sides(fmt)
+    na = check_operand(fa, _np(b["codes"]), _np(b["scales"]), ref["a"], what="activations")
+    nw = check_operand(fw, _np(layer.w_codes), _np(layer.w_scales), ref["w"], what="weights")
     rtol = 1e-3 if case.y_dtype == "f32" else 1e-2
     worst = check_output(_np(y), ref["y"], rtol)
     _report(name, band_mismatch_a=na, band_mismatch_w=nw, worst=f"{worst:.3g}")
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8"])
+@pytest.mark.parametrize("fmt", ["int4", "int8", "w4a8"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (17, 33, 192), (100, 200, 384), (130, 260, 320),
                                    (64, 2048, 2048), (64, 512, 8192), (512, 512, 4096), (300, 100, 64),
                                    (64, 2048, 8192), (40, 4096, 4160), (3, 8200, 2048), (30, 8192, 2048),
@@ -97,50 +123,42 @@ def test_raw_accumulators_exact(ops, fmt, M, N, K, split):
     """Integer GEMM on random codes: bit-exact int32 accumulators (decode kernel with and
     without the split-K workspace, tile kernels)."""
     rng = np.random.default_rng(M * 7 + N * 13 + K)
-    if fmt == "int4":
-        a_b = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
-        w_b = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
-    else:
-        a_b = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
-        w_b = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
-    ref = O.int_gemm(unpack_codes(fmt, a_b), unpack_codes(fmt, w_b))
+    fa, fw = _sides(fmt)
+    a_b = _random_codes(rng, fa, M, K)
+    w_b = _random_codes(rng, fw, N, K)
+    ref = O.int_gemm(unpack_codes(fa, a_b), unpack_codes(fw, w_b))
     dev = "cuda"
     a = torch.from_numpy(a_b).to(dev)
     w = torch.from_numpy(w_b).to(dev)
     sa = torch.ones(M, dtype=torch.float32, device=dev)
     sw = torch.ones(N, dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.int32, device=dev)
-    fn = ops.w4a4_linear if fmt == "int4" else ops.w8a8_linear
     ws = ops.make_workspace(M, N, K, fmt) if split else None
     if split and ws is None:
         pytest.skip("shape runs without a workspace")
-    kw = dict(y=y, workspace=ws)
-    if fmt == "int4":
-        fn(a, sa, w, sw, K, "int4", **kw)
-    else:
-        fn(a, sa, w, sw, K, **kw)
+    _raw_linear(ops, fmt, a, sa, w, sw, K, y=y, workspace=ws)
     got = _np(y).astype(np.int64)
     assert np.array_equal(got, ref)
 
 
 @pytest.mark.parametrize("fmt,val_a,val_w", [("int4", 7, 7), ("int4", -8, -8), ("int4", -8, 7),
-                                            ("int8", -128, -128), ("int8", 127, -128)])
+                                            ("int8", -128, -128), ("int8", 127, -128),
+                                            ("w4a8", -128, -8), ("w4a8", 127, -8), ("w4a8", -128, 7)])
 def test_extreme_codes_do_not_overflow(ops, fmt, val_a, val_w):
     M, N, K = 32, 48, 65536
-    if fmt == "int4":
-        a_b = np.full((M, K // 2), (val_a & 0xF) | ((val_a & 0xF) << 4), np.uint8)
-        w_b = np.full((N, K // 2), (val_w & 0xF) | ((val_w & 0xF) << 4), np.uint8)
-    else:
-        a_b = np.full((M, K), val_a, np.int8)
-        w_b = np.full((N, K), val_w, np.int8)
+    fa, fw = _sides(fmt)
+
+    def fill(f, R, v):
+        if f == "int4":
+            return np.full((R, K // 2), (v & 0xF) | ((v & 0xF) << 4), np.uint8)
+        return np.full((R, K), v, np.int8)
+
+    a_b, w_b = fill(fa, M, val_a), fill(fw, N, val_w)
     a, w = torch.from_numpy(a_b).cuda(), torch.from_numpy(w_b).cuda()
     ones_m, ones_n = torch.ones(M, device="cuda"), torch.ones(N, device="cuda")
     y = torch.empty((M, N), dtype=torch.int32, device="cuda")
     ws = ops.make_workspace(M, N, K, fmt)
-    if fmt == "int4":
-        ops.w4a4_linear(a, ones_m, w, ones_n, K, "int4", y=y, workspace=ws)
-    else:
-        ops.w8a8_linear(a, ones_m, w, ones_n, K, y=y, workspace=ws)
+    _raw_linear(ops, fmt, a, ones_m, w, ones_n, K, y=y, workspace=ws)
     assert np.all(_np(y) == val_a * val_w * K)
 
 
@@ -296,17 +314,14 @@ def test_full_workloads(ops, pipe, name):
     layer, t, y = _run(pipe, case)
     ref = _oracle(case)
     b = layer.buffers(case.M, t["x"].device)
-    na = check_operand(case.fmt, _np(b["codes"]), _np(b["scales"]), ref["a"], what="activations")
-    nw = check_operand(case.fmt, _np(layer.w_codes), _np(layer.w_scales), ref["w"], what="weights")
+    fa, fw = _sides(case.fmt)
+    na = check_operand(fa, _np(b["codes"]), _np(b["scales"]), ref["a"], what="activations")
+    nw = check_operand(fw, _np(layer.w_codes), _np(layer.w_scales), ref["w"], what="weights")
     worst = check_output(_np(y), ref["y"], 1e-3 if case.y_dtype == "f32" else 1e-2)
-    if case.fmt in ("int4", "int8"):
+    if case.fmt in ("int4", "int8", "w4a8"):
         yi = torch.empty((case.M, case.N), dtype=torch.int32, device="cuda")
-        fn = ops.w8a8_linear if case.fmt == "int8" else ops.w4a4_linear
-        args = (b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K)
-        if case.fmt == "int4":
-            fn(*args, "int4", y=yi, workspace=b["ws"])
-        else:
-            fn(*args, y=yi, workspace=b["ws"])
-        acc = O.int_gemm(unpack_codes(case.fmt, _np(b["codes"])), unpack_codes(case.fmt, _np(layer.w_codes)))
+        _raw_linear(ops, case.fmt, b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K,
+                    y=yi, workspace=b["ws"])
+        acc = O.int_gemm(unpack_codes(fa, _np(b["codes"])), unpack_codes(fw, _np(layer.w_codes)))
         assert np.array_equal(_np(yi).astype(np.int64), acc)
     _report(name, band_mismatch_a=na, band_mismatch_w=nw, worst=f"{worst:.3g}")

@@ -185,6 +185,13 @@ int w8a8_linear(const void* a_codes, const void* a_scales, const void* w_codes, 
                     y_dtype, ldy, workspace, workspace_bytes, stream);
 }
 
+int w4a8_linear(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                int64_t M, int64_t N, int64_t K, float alpha, const w4a4_branch* br, void* y, int32_t y_dtype,
+                int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_linear("w4a8_linear", W4A4_FMT_W4A8, a_codes, a_scales, w_codes, w_scales, M, N, K, alpha, br, y,
+                    y_dtype, ldy, workspace, workspace_bytes, stream);
+}
+
 static int check_lowrank(const char* fn, const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t,
                          const int32_t* idx, int64_t r) {
   if (M < 0 || K <= 0) return fail(W4A4_ERR_INVALID_ARG, "%s: bad sizes", fn);
@@ -253,7 +260,7 @@ int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, in
 
 size_t w4a4_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0) return 0;
-  if (fmt != W4A4_FMT_INT4 && fmt != W4A4_FMT_INT8) return 0;
+  if (fmt != W4A4_FMT_INT4 && fmt != W4A4_FMT_INT8 && fmt != W4A4_FMT_W4A8) return 0;
   return w4a4::gemm_int_workspace(fmt, M, N, K);
 }
 

@@ -114,7 +114,8 @@ __device__ __forceinline__ void load_epi_scales(EpiScales<TI, TJ>& s, const Gemm
 // Epilogue of a wave's TI x TJ grid of 16x16 accumulator tiles, one
 // 16-column block at a time (keeps the live register set small):
 // dequantise (integer: fp32(fp32(acc) * sa[m]) * sw[n] * alpha, with acc
-// shifted right by 8 for the x16-widened int4 operands; float: acc *
+// shifted right by 8 when both operands are x16-widened int4 and by 4 when
+// one is (int8 x int4); float: acc *
 // alpha), add the bf16 branch, store.  acc[i][j] covers rows
 // m_base + 16 i + [0, 16) and columns n_base + 16 j + [0, 16).
 // y_dtype 2 writes the raw integer accumulators.  Stores go through a
@@ -128,7 +129,7 @@ constexpr int epilogue_stage_bytes() {
 
 // `pre`, when given, holds the scales already loaded (load_epi_scales);
 // `el`, when given, the LDS-staged scales and branch rows of the tile.
-template <int KIND /*0 int4, 1 int8, 2 float*/, typename AccT, int TI, int TJ>
+template <int KIND /*0 int4, 1 int8, 2 float, 3 int8 x int4*/, typename AccT, int TI, int TJ>
 __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
                                                int lane, uint8_t* stage = nullptr,
                                                const EpiScales<TI, TJ>* pre = nullptr, const EpiLds* el = nullptr) {
@@ -154,7 +155,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
         for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int v = KIND == 0 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+            const int v = KIND == 0 ? (acc[i][j][r] >> 8) : KIND == 3 ? (acc[i][j][r] >> 4) : acc[i][j][r];
             __builtin_amdgcn_raw_buffer_store_b32(v, ry, (int)(roff[i][r] + coff), 0, 0);
           }
       }
@@ -184,7 +185,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int q = KIND == 0 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+          const int q = KIND == 0 ? (acc[i][j][r] >> 8) : KIND == 3 ? (acc[i][j][r] >> 4) : acc[i][j][r];
           float v = (float)q * sam[i][r];
           v = v * swn;
           col[i][0][r] = v * g.alpha;

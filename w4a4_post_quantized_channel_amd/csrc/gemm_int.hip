@@ -67,8 +67,8 @@ static int decode_ti(int64_t M, bool split) {
 
 // LDS bytes a decode wave keeps in flight (its ring of step slots): int4
 // rows are half as long per step, and a smaller ring measured faster there.
-template <bool INT4>
-constexpr int dec_ring_bytes() { return INT4 ? 12 * 1024 : 18 * 1024; }
+template <bool BOTH_INT4>
+constexpr int dec_ring_bytes() { return BOTH_INT4 ? 12 * 1024 : 18 * 1024; }
 
 // f(integral_constant<int, J>) for J = J0 .. J1 - 1, in order.
 template <int J0, int J1, typename F>
@@ -79,34 +79,55 @@ __device__ __forceinline__ void drain_ring(F&& f) {
   }
 }
 
-template <bool INT4, int TI, int TJ>
+// Operand formats of the decode kernel: both int4, both int8, or int8
+// activations with int4 weights (W4A8).  int4 codes are widened to 16*q,
+// so the MFMA sum carries a factor 256 (both int4) or 16 (W4A8) that the
+// epilogue shifts out (KIND 0 / 3).
+enum { DF_I4 = 0, DF_I8 = 1, DF_W4A8 = 2 };
+template <int DF>
+struct DecFmt {
+  static constexpr bool A4 = DF == DF_I4, W4 = DF != DF_I8;   // operand packed as int4
+  static constexpr int SBA = A4 ? 64 : 128, SBB = W4 ? 64 : 128;   // bytes of a row per 128-element step
+  static constexpr int KIND = DF == DF_I4 ? 0 : (DF == DF_I8 ? 1 : 3);
+};
+
+// 16 int8 codes (bytes, K order 0..15) -> the K order of a widened int4
+// fragment: even K of the first 8, odd K of the first 8, even, odd of the
+// last 8 (the order widen_int4 produces for 16 packed codes).
+__device__ __forceinline__ v4i order_like_int4(const uint4& v) {
+  return v4i{(int)__builtin_amdgcn_perm(v.y, v.x, 0x06040200u), (int)__builtin_amdgcn_perm(v.y, v.x, 0x07050301u),
+             (int)__builtin_amdgcn_perm(v.w, v.z, 0x06040200u), (int)__builtin_amdgcn_perm(v.w, v.z, 0x07050301u)};
+}
+
+template <int DF, int TI, int TJ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
   static_assert(TI == 1 || TI == 2 || TI == 4, "row blocks per workgroup");
-  constexpr int SB = INT4 ? 64 : 128;             // bytes of a row in one 128-element step
-  constexpr int CPR = SB / 16;                    // 16-byte chunks per row and step
-  constexpr int RPI = 64 / CPR;                   // rows per copy instruction
-  constexpr int ROWS = 16 * (TI + TJ);            // A rows, then W rows
-  constexpr int PER_STEP = ROWS / RPI;            // copy instructions per step
-  constexpr int STEP_BYTES = ROWS * SB;
-  constexpr int NBUF0 = dec_ring_bytes<INT4>() / STEP_BYTES;
+  typedef DecFmt<DF> F;
+  constexpr int SBA = F::SBA, SBB = F::SBB;
+  constexpr int CPRA = SBA / 16, CPRB = SBB / 16;          // 16-byte chunks per row and step
+  constexpr int RPIA = 64 / CPRA, RPIB = 64 / CPRB;        // rows per copy instruction
+  constexpr int NIA = 16 * TI / RPIA, NIB = 16 * TJ / RPIB;
+  constexpr int PER_STEP = NIA + NIB;                      // copy instructions per step (A first)
+  constexpr int AREG = 16 * TI * SBA;                      // A rows' bytes in a slot; W rows follow
+  constexpr int STEP_BYTES = AREG + 16 * TJ * SBB;
+  constexpr int NBUF0 = dec_ring_bytes<DF == DF_I4>() / STEP_BYTES;
   constexpr int NBUF = NBUF0 > 8 ? 8 : (NBUF0 < 2 ? 2 : NBUF0);   // ring slots per wave
   constexpr int WAVE_BYTES = NBUF * STEP_BYTES;
   constexpr int RED_BYTES = 4 * TI * TJ * 1024;
   constexpr int LDS_BYTES = 4 * WAVE_BYTES > RED_BYTES ? 4 * WAVE_BYTES : RED_BYTES;
   static_assert((NBUF - 1) * PER_STEP <= 63 && NBUF <= 8, "vmcnt range");
+  static_assert(AREG == NIA * 1024, "A copies fill whole instructions");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int lr = lane & 15, lq = lane >> 4;
   const int n0 = blockIdx.x * 16 * TJ, m0 = blockIdx.y * 16 * TI;
-  const int64_t rowbytes = INT4 ? (g.K >> 1) : g.K;
+  const int64_t rbA = F::A4 ? (g.K >> 1) : g.K, rbB = F::W4 ? (g.K >> 1) : g.K;   // row bytes
   const int kz0 = blockIdx.z * kwg, kz1 = min(g.K, kz0 + kwg);
-  const v4u rsA = rsrc_words(g.a + (int64_t)m0 * rowbytes, (uint32_t)(min(16 * TI, g.M - m0) * rowbytes));
-  const v4u rsB = rsrc_words(g.w + (int64_t)n0 * rowbytes, (uint32_t)(min(16 * TJ, g.N - n0) * rowbytes));
+  const v4u rsA = rsrc_words(g.a + (int64_t)m0 * rbA, (uint32_t)(min(16 * TI, g.M - m0) * rbA));
+  const v4u rsB = rsrc_words(g.w + (int64_t)n0 * rbB, (uint32_t)(min(16 * TJ, g.N - n0) * rbB));
   uint8_t* const area = smem + wave * WAVE_BYTES;
-  // copy instruction d: lane -> row d*RPI + lane/CPR, LDS chunk position lane%CPR
-  const int dr = lane / CPR, dp = lane % CPR;
   // this wave's steps: k = kz0 + 128 * (wave + 4 t), t < nsteps
   const int kw = kz0 + wave * kBK;
   const int nsteps = kw < kz1 ? (kz1 - kw + 4 * kBK - 1) / (4 * kBK) : 0;
@@ -116,17 +137,21 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
   EpiScales<1, TJ> es;
   if (!part && wave < TI) load_epi_scales(es, g, m0 + wave * 16, n0, lane);
 
+  // copy instruction d: lane -> row d*RPI + lane/CPR of its operand, LDS
+  // chunk position lane%CPR holding chunk position^(row mod CPR)
   auto issue = [&](int t, int slot) {   // copies of step t into ring slot `slot`
     const int k = kw + t * 4 * kBK;
-    const int64_t kb = INT4 ? (k >> 1) : k;
     uint8_t* st = area + slot * STEP_BYTES;
 #pragma unroll
     for (int d = 0; d < PER_STEP; ++d) {
-      const bool isa = d * RPI < 16 * TI;         // uniform per instruction
-      const int r = d * RPI + dr - (isa ? 0 : 16 * TI);
-      const int64_t cb = kb + 16 * (dp ^ (r & (CPR - 1)));
-      const bool ok = k < kz1 && cb < rowbytes;
-      dma16(isa ? rsA : rsB, st + d * 1024, ok ? (uint32_t)(r * rowbytes + cb) : kOOB, 0u);
+      const bool isa = d < NIA;                   // compile-time per instruction
+      const int cpr = isa ? CPRA : CPRB, rpi = isa ? RPIA : RPIB;
+      const int64_t rb = isa ? rbA : rbB;
+      const int r = (isa ? d : d - NIA) * rpi + lane / cpr;
+      const int64_t kb = (isa ? F::A4 : F::W4) ? (k >> 1) : k;
+      const int64_t cb = kb + 16 * ((lane % cpr) ^ (r & (cpr - 1)));
+      const bool ok = k < kz1 && cb < rb;
+      dma16(isa ? rsA : rsB, st + d * 1024, ok ? (uint32_t)(r * rb + cb) : kOOB, 0u);
     }
   };
 
@@ -137,17 +162,17 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
   auto compute = [&](const uint8_t* st) {   // the MFMAs of one step from its ring slot
-    if constexpr (INT4) {
+    if constexpr (DF == DF_I4) {
       uint4 ra[TI], rb[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const int R = i * 16 + lr;
-        ra[i] = *reinterpret_cast<const uint4*>(st + R * SB + 16 * (lq ^ (R & 3)));
+        ra[i] = *reinterpret_cast<const uint4*>(st + R * SBA + 16 * (lq ^ (R & 3)));
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int R = j * 16 + lr;
-        rb[j] = *reinterpret_cast<const uint4*>(st + (16 * TI + R) * SB + 16 * (lq ^ (R & 3)));
+        rb[j] = *reinterpret_cast<const uint4*>(st + AREG + R * SBB + 16 * (lq ^ (R & 3)));
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -159,25 +184,51 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
             const v4i b = h ? widen_int4(rb[j].z, rb[j].w) : widen_int4(rb[j].x, rb[j].y);
             acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i][j], 0, 0, 0);
           }
-    } else {
+    } else if constexpr (DF == DF_I8) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         v4i a[TI], b[TJ];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
           const int R = i * 16 + lr;
-          a[i] = *reinterpret_cast<const v4i*>(st + R * SB + 16 * ((h * 4 + lq) ^ (R & 7)));
+          a[i] = *reinterpret_cast<const v4i*>(st + R * SBA + 16 * ((h * 4 + lq) ^ (R & 7)));
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int R = j * 16 + lr;
-          b[j] = *reinterpret_cast<const v4i*>(st + (16 * TI + R) * SB + 16 * ((h * 4 + lq) ^ (R & 7)));
+          b[j] = *reinterpret_cast<const v4i*>(st + AREG + R * SBB + 16 * ((h * 4 + lq) ^ (R & 7)));
         }
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    } else {
+      // W4A8: lane group lq owns K [32 lq, 32 lq + 32) of the step, half h
+      // its 16 K from 16 h.  The weight chunk lq is widened as in the int4
+      // case; the activation bytes (chunk 2 lq + h) are put in the same order.
+      uint4 rb[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int R = j * 16 + lr;
+        rb[j] = *reinterpret_cast<const uint4*>(st + AREG + R * SBB + 16 * (lq ^ (R & 3)));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4i a[TI];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const int R = i * 16 + lr;
+          a[i] = order_like_int4(*reinterpret_cast<const uint4*>(st + R * SBA + 16 * ((2 * lq + h) ^ (R & 7))));
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const v4i b = h ? widen_int4(rb[j].z, rb[j].w) : widen_int4(rb[j].x, rb[j].y);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b, acc[i][j], 0, 0, 0);
+          }
       }
     }
   };
@@ -236,13 +287,13 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     }
     return;
   }
-  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0 + wave * 16, n0, lane, nullptr, &es);
+  epilogue_tiles<F::KIND>(tot, g, m0 + wave * 16, n0, lane, nullptr, &es);
 }
 
 // One wave per 16 x 16 output tile (tile, row block, column block): add its
 // S partial blocks (coalesced 1 KB reads, up to eight in flight; the
 // epilogue's scales load alongside the first ones), then the epilogue.
-template <bool INT4, int TI>
+template <int KIND, int TI>
 __global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, const int32_t* part) {
   constexpr int TJ = kDecTJ;
   constexpr int ZB = 8;  // partial blocks whose loads are in flight together
@@ -265,7 +316,7 @@ __global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, 
     for (int dz = 0; dz < ZB; ++dz)
       if (z0 + dz < S) tot[0][0] += __builtin_bit_cast(v4i, v[dz]);
   }
-  epilogue_tiles<INT4 ? 0 : 1>(tot, g, m0, n0, lane, nullptr, &es);
+  epilogue_tiles<KIND>(tot, g, m0, n0, lane, nullptr, &es);
 }
 
 // ---------------------------------------------------------------------------
@@ -302,27 +353,29 @@ static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, bool int4) {
   return p;
 }
 
+// fmt: 0 int4 x int4, 1 int8 x int8, 3 int8 activations x int4 weights
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
-  return M <= 64 ? decode_plan(M, N, K, fmt == 0).ws_bytes : 0;
+  return M <= 64 ? decode_plan(M, N, K, fmt != 1).ws_bytes : 0;
 }
 
-template <bool INT4>
+template <int DF>
 static void launch_decode(const GemmArgs& g, const DecodePlan& p, int32_t* part, hipStream_t st) {
+  constexpr int KIND = DecFmt<DF>::KIND;
   if (part) {
     const dim3 grid((unsigned)p.tiles, 1, p.splits);
     const dim3 rgrid((unsigned)(p.tiles * p.ti * kDecTJ));
     switch (p.ti) {
       case 1:
-        hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 1, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
-        hipLaunchKernelGGL((gemm_int_reduce_kernel<INT4, 1>), rgrid, dim3(64), 0, st, g, p.splits, part);
+        hipLaunchKernelGGL((gemm_int_decode_kernel<DF, 1, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
+        hipLaunchKernelGGL((gemm_int_reduce_kernel<KIND, 1>), rgrid, dim3(64), 0, st, g, p.splits, part);
         break;
       case 2:
-        hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 2, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
-        hipLaunchKernelGGL((gemm_int_reduce_kernel<INT4, 2>), rgrid, dim3(64), 0, st, g, p.splits, part);
+        hipLaunchKernelGGL((gemm_int_decode_kernel<DF, 2, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
+        hipLaunchKernelGGL((gemm_int_reduce_kernel<KIND, 2>), rgrid, dim3(64), 0, st, g, p.splits, part);
         break;
       default:
-        hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 4, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
-        hipLaunchKernelGGL((gemm_int_reduce_kernel<INT4, 4>), rgrid, dim3(64), 0, st, g, p.splits, part);
+        hipLaunchKernelGGL((gemm_int_decode_kernel<DF, 4, kDecTJ>), grid, dim3(256), 0, st, g, p.kwg, part);
+        hipLaunchKernelGGL((gemm_int_reduce_kernel<KIND, 4>), rgrid, dim3(64), 0, st, g, p.splits, part);
         break;
     }
     return;
@@ -330,18 +383,18 @@ static void launch_decode(const GemmArgs& g, const DecodePlan& p, int32_t* part,
   // whole K per workgroup: 16 output channels and 16 or 32 rows each, for more workgroups
   const int ti = decode_ti(g.M, false);
   const dim3 grid((g.N + 15) / 16, (g.M + 16 * ti - 1) / (16 * ti), 1);
-  if (ti == 1) hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 1, 1>), grid, dim3(256), 0, st, g, g.K, part);
-  else hipLaunchKernelGGL((gemm_int_decode_kernel<INT4, 2, 1>), grid, dim3(256), 0, st, g, g.K, part);
+  if (ti == 1) hipLaunchKernelGGL((gemm_int_decode_kernel<DF, 1, 1>), grid, dim3(256), 0, st, g, g.K, part);
+  else hipLaunchKernelGGL((gemm_int_decode_kernel<DF, 2, 1>), grid, dim3(256), 0, st, g, g.K, part);
 }
 
 hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st) {
-  const bool int4 = fmt == 0;
   if (g.M <= 64) {
-    const DecodePlan p = decode_plan(g.M, g.N, g.K, int4);
+    const DecodePlan p = decode_plan(g.M, g.N, g.K, fmt != 1);   // weights int4 unless W8A8
     const bool split = p.splits > 1 && workspace && ws_bytes >= p.ws_bytes;
     int32_t* part = split ? reinterpret_cast<int32_t*>(workspace) : nullptr;
-    if (int4) launch_decode<true>(g, p, part, st);
-    else launch_decode<false>(g, p, part, st);
+    if (fmt == 0) launch_decode<DF_I4>(g, p, part, st);
+    else if (fmt == 1) launch_decode<DF_I8>(g, p, part, st);
+    else launch_decode<DF_W4A8>(g, p, part, st);
     return hipGetLastError();
   }
   return launch_gemm_wide(fmt, g, st);

@@ -43,7 +43,7 @@ namespace w4a4 {
 
 namespace {
 
-enum { W_INT4 = 0, W_INT8 = 1, W_NVFP4 = 2 };
+enum { W_INT4 = 0, W_INT8 = 1, W_NVFP4 = 2, W_W4A8 = 3 };   // W4A8: int8 activations, int4 weights
 
 template <int FMT>
 struct WFmt;
@@ -65,9 +65,14 @@ struct WFmt<W_NVFP4> {
   static constexpr int STEPS = 4;
   typedef v4f acc_t;
 };
+template <>
+struct WFmt<W_W4A8> {               // per 64-byte weight segment; activations take 128 bytes
+  static constexpr int KSEG = 128;
+  static constexpr int STEPS = 2;
+  typedef v4i acc_t;
+};
 
-constexpr int kSeg = 64;     // packed bytes per row per K-group per stage
-constexpr int kNBuf = 4;     // LDS stage buffers (three stages in flight)
+constexpr int kSeg = 64;     // packed weight bytes per row per K-group per stage
 
 
 // XOR swizzle of the 16-byte slots of an LDS row of P bytes: the 16 rows
@@ -114,13 +119,23 @@ __device__ __forceinline__ void mfma_w(typename WFmt<FMT>::acc_t& c, const uint4
     c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a), __builtin_bit_cast(v4i, b), c, 0, 0, 0);
 }
 
+// 16 int8 codes (bytes, K order 0..15) -> the K order widen_i4 gives 16
+// packed int4 codes: even K of the first 8, odd K of the first 8, then the
+// same for the last 8.
+__device__ __forceinline__ uint4 order_like_i4(const uint4& v) {
+  return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u), __builtin_amdgcn_perm(v.y, v.x, 0x07050301u),
+                    __builtin_amdgcn_perm(v.w, v.z, 0x06040200u), __builtin_amdgcn_perm(v.w, v.z, 0x07050301u));
+}
+
 // Operand fragment for MFMA step t of a stage, from the lane's packed
 // 16-byte slot p (and, for NVFP4, the 2 scale bytes of its 32 codes).
+// W4A8 weights widen like int4; its activation fragments go through
+// order_like_i4 at the read instead.
 template <int FMT>
 __device__ __forceinline__ uint4 operand(const uint4& p, int t, uint32_t sc) {
   if constexpr (FMT == W_INT8) {
     return p;
-  } else if constexpr (FMT == W_INT4) {
+  } else if constexpr (FMT == W_INT4 || FMT == W_W4A8) {
     return (t & 1) ? widen_i4(p.z, p.w) : widen_i4(p.x, p.y);
   } else {
     return widen_fp4(dw(p, t), scale_pair((sc >> (8 * (t >> 1))) & 0xFFu));
@@ -142,16 +157,18 @@ __device__ __forceinline__ void interleave_steps() {
 template <int FMT, int TI, int TJ, int WR, int WC, int WK>
 struct WCfg {
   static constexpr int BM = WR * TI * 16, BN = WC * TJ * 16;
-  static constexpr int P = kSeg * WK;                // packed bytes per row per stage
+  static constexpr int P = kSeg * WK;                // packed weight bytes per row per stage
+  static constexpr int PA = FMT == W_W4A8 ? 2 * P : P;   // activation bytes per row per stage
   static constexpr int KST = WFmt<FMT>::KSEG * WK;   // K elements per stage
   static constexpr int SP = (kSeg / 8) * WK;         // NVFP4 scale bytes per row per stage
-  static constexpr int A_BYTES = BM * P, B_BYTES = BN * P;
+  static constexpr int A_BYTES = BM * PA, B_BYTES = BN * P;
   static constexpr int SA_BYTES = FMT == W_NVFP4 ? BM * SP : 0;
   static constexpr int SB_BYTES = FMT == W_NVFP4 ? BN * SP : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
   static constexpr int NW = WR * WC * WK;            // waves per workgroup (4 or 8)
   static constexpr int RED = WK > 1 ? NW * TI * TJ * 4 * 64 * 4 : 0;   // every wave's partial tile
-  static constexpr int PIPE = kNBuf * STAGE + 1024;                    // + DMA pad target
+  static constexpr int NBUF = 4 * STAGE + 1024 <= 152 * 1024 ? 4 : 3;   // LDS stage buffers
+  static constexpr int PIPE = NBUF * STAGE + 1024;                     // + DMA pad target
   // After the main loop: the epilogue's own LDS use (bf16 staging, or the
   // split-K partial tiles), then the tile's branch rows (kBrLdsMax bf16 =
   // 128 bytes each), then the tile's scales (one float per row and column).
@@ -169,7 +186,7 @@ struct WCfg {
   static_assert(SA_BYTES % 256 == 0 && SB_BYTES % 256 == 0, "whole scale DMA instructions");
   static_assert(TJ % WK == 0, "split-K epilogue splits the columns");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
-  static_assert(DPS * (kNBuf - 2) <= 63, "vmcnt range");
+  static_assert(DPS * (NBUF - 2) <= 63, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(BM + BN <= 64 * NW, "one scale per thread");
 };
@@ -282,10 +299,11 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   const int kw = wave / (WR * WC), wrc = wave % (WR * WC);
   const int wm0 = (wrc / WC) * TI * 16, wn0 = (wrc % WC) * TJ * 16;
 
-  const int64_t rowbytes = FMT == W_INT8 ? g.K : (g.K >> 1);
+  const int64_t rowbytes = FMT == W_INT8 ? g.K : (g.K >> 1);   // weight rows
+  const int64_t rbA = (FMT == W_INT8 || FMT == W_W4A8) ? g.K : (g.K >> 1);   // activation rows
   const int64_t srow = g.K >> 4;
   const int nk = (int)((g.K + C::KST - 1) / C::KST);
-  const v4u rsA = rsrc_words(g.a + (int64_t)m0 * rowbytes, (uint32_t)(min(C::BM, g.M - m0) * rowbytes));
+  const v4u rsA = rsrc_words(g.a + (int64_t)m0 * rbA, (uint32_t)(min(C::BM, g.M - m0) * rbA));
   const v4u rsB = rsrc_words(g.w + (int64_t)n0 * rowbytes, (uint32_t)(min(C::BN, g.N - n0) * rowbytes));
   v4u rsSA = rsA, rsSB = rsB;
   if constexpr (FMT == W_NVFP4) {
@@ -293,20 +311,20 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
     rsSB = rsrc_words(reinterpret_cast<const uint8_t*>(g.sw) + (int64_t)n0 * srow, (uint32_t)(min(C::BN, g.N - n0) * srow));
   }
 
-  uint8_t* pad = smem + kNBuf * C::STAGE;
-  CodeCopy<C::P, C::NA, C::NW> cpA;
+  uint8_t* pad = smem + C::NBUF * C::STAGE;
+  CodeCopy<C::PA, C::NA, C::NW> cpA;
   CodeCopy<C::P, C::NB, C::NW> cpB;
   ScaleCopy<C::SP, (C::NSA > 0 ? C::NSA : 1), C::NW> cpSA;
   ScaleCopy<C::SP, (C::NSB > 0 ? C::NSB : 1), C::NW> cpSB;
-  cpA.init(wave, lane, rowbytes);
+  cpA.init(wave, lane, rbA);
   cpB.init(wave, lane, rowbytes);
   if constexpr (FMT == W_NVFP4) {
     cpSA.init(wave, lane, srow);
     cpSB.init(wave, lane, srow);
   }
   auto copy_stage = [&](int s) {
-    uint8_t* base = smem + (s % kNBuf) * C::STAGE;
-    cpA.issue(rsA, base, pad, rowbytes, s, wave);
+    uint8_t* base = smem + (s % C::NBUF) * C::STAGE;
+    cpA.issue(rsA, base, pad, rbA, s, wave);
     cpB.issue(rsB, base + C::A_BYTES, pad, rowbytes, s, wave);
     if constexpr (FMT == W_NVFP4) {
       cpSA.issue(rsSA, base + C::A_BYTES + C::B_BYTES, pad, srow, s, wave);
@@ -336,8 +354,16 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   // Per-lane LDS offsets of the fragment rows (the swizzle term does not
   // depend on the fragment index: fragments are 16 rows apart).  Lane
   // group lq of K-group kw owns logical slot 4 kw + lq of each row.
+  // W4A8 activations: lane group lq of K-group kw reads slot 8 kw + 2 lq + h
+  // for MFMA step h (the 16 int8 codes of the same K as the weight's half h).
+  constexpr int NSA = FMT == W_W4A8 ? 2 : 1;   // activation slots per fragment row and stage
   const int L = kw * (kSeg / 16) + lq;
-  const int aoff = (wm0 + lr) * C::P + ((L ^ swz<C::P>(wm0 + lr)) * 16);
+  int aoff[NSA];
+#pragma unroll
+  for (int h = 0; h < NSA; ++h) {
+    const int La = FMT == W_W4A8 ? kw * 8 + 2 * lq + h : L;
+    aoff[h] = (wm0 + lr) * C::PA + ((La ^ swz<C::PA>(wm0 + lr)) * 16);
+  }
   const int boff = C::A_BYTES + (wn0 + lr) * C::P + ((L ^ swz<C::P>(wn0 + lr)) * 16);
   const int saoff = C::A_BYTES + C::B_BYTES + (wm0 + lr) * C::SP + kw * (kSeg / 8) + lq * 2;
   const int sboff = C::A_BYTES + C::B_BYTES + C::SA_BYTES + (wn0 + lr) * C::SP + kw * (kSeg / 8) + lq * 2;
@@ -351,11 +377,11 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   // compute stage s.  Stages past the end are still copied (zeros) and
   // read, so every iteration waits on the same count and has no branches.
   struct Frags {
-    uint4 a[TI], b[TJ];
+    uint4 a[TI][NSA], b[TJ];
     uint32_t sa[TI], sb[TJ];
   };
   auto read_frags = [&](int s, Frags& f) {
-    const uint8_t* base = smem + (s % kNBuf) * C::STAGE;
+    const uint8_t* base = smem + (s % C::NBUF) * C::STAGE;
     if constexpr (FMT == W_NVFP4) {
 #pragma unroll
       for (int i = 0; i < TI; ++i) f.sa[i] = *reinterpret_cast<const uint16_t*>(base + saoff + i * 16 * C::SP);
@@ -363,7 +389,9 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
       for (int j = 0; j < TJ; ++j) f.sb[j] = *reinterpret_cast<const uint16_t*>(base + sboff + j * 16 * C::SP);
     }
 #pragma unroll
-    for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const uint4*>(base + aoff + i * 16 * C::P);
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int h = 0; h < NSA; ++h) f.a[i][h] = *reinterpret_cast<const uint4*>(base + aoff[h] + i * 16 * C::PA);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) f.b[j] = *reinterpret_cast<const uint4*>(base + boff + j * 16 * C::P);
   };
@@ -372,7 +400,10 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   };
   auto widen = [&](const Frags& f, int st, Ops& o) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i) o.a[i] = operand<FMT>(f.a[i], st, FMT == W_NVFP4 ? f.sa[i] : 0u);
+    for (int i = 0; i < TI; ++i) {
+      if constexpr (FMT == W_W4A8) o.a[i] = order_like_i4(f.a[i][st]);
+      else o.a[i] = operand<FMT>(f.a[i][0], st, FMT == W_NVFP4 ? f.sa[i] : 0u);
+    }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) o.b[j] = operand<FMT>(f.b[j], st, FMT == W_NVFP4 ? f.sb[j] : 0u);
   };
@@ -382,23 +413,26 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 #pragma unroll
       for (int j = 0; j < TJ; ++j) mfma_w<FMT>(acc[i][j], o.a[i], o.b[j]);
   };
-  constexpr int NV = FMT == W_NVFP4 ? 3 : (FMT == W_INT4 ? 2 : 0);
+  constexpr int NV = FMT == W_NVFP4 ? 3 : (FMT == W_INT4 || FMT == W_W4A8 ? 2 : 0);
+  // wait_stages 1: stage s + 1 landed, with stages after it still in flight
+  // (the integer path's iteration); 2: stage s landed (before the integer
+  // loop, and every NVFP4 iteration).
   auto sync_stage = [&](int wait_stages) {
-    if (wait_stages == 1) wait_vmcnt<C::DPS>(); else wait_vmcnt<C::DPS * (kNBuf - 2)>();
+    if (wait_stages == 1) wait_vmcnt<C::DPS * (C::NBUF - 3)>(); else wait_vmcnt<C::DPS * (C::NBUF - 2)>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
 
 #pragma unroll
-  for (int p = 0; p < kNBuf - 1; ++p) copy_stage(p);
+  for (int p = 0; p < C::NBUF - 1; ++p) copy_stage(p);
   if constexpr (FMT != W_NVFP4) {
     // Two fragment sets and two widened operand sets.  The operands of an
     // MFMA step are widened during the previous step's MFMAs; step 0 of
     // stage s + 1 is widened from the fragments read in iteration s.
-    // Iteration s: wait for stage s + 1, barrier, copy stage s + 3 (into
-    // the buffer of stage s - 1, read two iterations ago), read stage s + 1,
-    // then the MFMA steps of stage s.
+    // Iteration s: wait for stage s + 1, barrier, copy stage s + NBUF - 1
+    // (into the buffer of stage s - 1, read two iterations ago), read stage
+    // s + 1, then the MFMA steps of stage s.
     sync_stage(2);   // stage 0 landed
     Frags f0, f1;
     read_frags(0, f0);
@@ -406,7 +440,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
     widen(f0, 0, w);
     auto iter = [&](int s, const Frags& cur, Frags& nxt) {
       sync_stage(1);
-      copy_stage(s + kNBuf - 1);
+      copy_stage(s + C::NBUF - 1);
       read_frags(s + 1, nxt);
 #pragma unroll
       for (int st = 0; st < STEPS; ++st) {
@@ -415,7 +449,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
         if (st + 1 < STEPS) widen(cur, st + 1, next); else widen(nxt, 0, next);
         mma_step(now);
       }
-      interleave_steps<TI + TJ, TI * TJ * STEPS, NV>();
+      interleave_steps<TI * NSA + TJ, TI * TJ * STEPS, NV>();
     };
     static_assert(STEPS % 2 == 0 || STEPS == 1, "operand sets alternate per step");
     int s = 0;
@@ -424,7 +458,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
       auto iter1 = [&](int s1, const Frags& cur, Frags& nxt, Ops& now, Ops& next) {
         (void)cur;
         sync_stage(1);
-        copy_stage(s1 + kNBuf - 1);
+        copy_stage(s1 + C::NBUF - 1);
         read_frags(s1 + 1, nxt);
         widen(nxt, 0, next);
         mma_step(now);
@@ -448,7 +482,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
     // during the previous step's MFMAs.
     for (int s = 0; s < nk; ++s) {
       sync_stage(2);   // stage s landed
-      copy_stage(s + kNBuf - 1);
+      copy_stage(s + C::NBUF - 1);
       Frags f;
       read_frags(s, f);
       Ops w, x;
@@ -496,7 +530,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   const EpiLds el{FMT == W_NVFP4 ? nullptr : lsc, FMT == W_NVFP4 ? nullptr : lsc + C::BM,
                   br_lds ? bra : nullptr, brb, m0, n0};
 
-  constexpr int KIND = FMT == W_NVFP4 ? 2 : (FMT == W_INT4 ? 0 : 1);
+  constexpr int KIND = FMT == W_NVFP4 ? 2 : (FMT == W_INT4 ? 0 : (FMT == W_W4A8 ? 3 : 1));
   if constexpr (WK == 1) {
     // bf16 output is staged through this wave's slice of the (now idle) LDS
     static_assert(C::NW * epilogue_stage_bytes<TI, TJ>() <= C::BR_OFF, "epilogue staging fits");
@@ -552,10 +586,12 @@ constexpr int kCfgBM[kNumCfg] = {256, 128, 128, 64};
 constexpr int kCfgBN[kNumCfg] = {160, 256, 96, 64};
 constexpr double kCfgEff[kNumCfg] = {0.95, 0.9, 0.8, 0.7};
 
-WideChoice choose(int64_t M, int64_t N) {
+// skip0: the 256x160 shape is not offered (W4A8: its two activation
+// fragments per row block do not fit the register budget of eight waves).
+WideChoice choose(int64_t M, int64_t N, bool skip0) {
   WideChoice best{-1, 0, 0};
   double best_cost = 0;
-  for (int c = 0; c < kNumCfg; ++c) {
+  for (int c = skip0 ? 1 : 0; c < kNumCfg; ++c) {
     const int64_t tm = (M + kCfgBM[c] - 1) / kCfgBM[c], tn = (N + kCfgBN[c] - 1) / kCfgBN[c];
     const int64_t rounds = (tm * tn + 255) / 256;
     const double cost = (double)rounds * kCfgBM[c] * kCfgBN[c] / kCfgEff[c];
@@ -569,11 +605,14 @@ WideChoice choose(int64_t M, int64_t N) {
 
 template <int FMT>
 hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
-  const WideChoice c = choose(g.M, g.N);
+  const WideChoice c = choose(g.M, g.N, FMT == W_W4A8);
   const dim3 grid((unsigned)(c.tm * c.tn));
   const int tm = (int)c.tm, tn = (int)c.tn;
   switch (c.cfg) {
-    case 0: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 5, 4, 2, 1>), grid, dim3(512), 0, st, g, tm, tn); break;
+    case 0:
+      if constexpr (FMT != W_W4A8)
+        hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 5, 4, 2, 1>), grid, dim3(512), 0, st, g, tm, tn);
+      break;
     case 1: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 2, 4, 1>), grid, dim3(512), 0, st, g, tm, tn); break;
     case 2: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 6, 2, 1, 2>), grid, dim3(256), 0, st, g, tm, tn); break;
     default: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 1, 1, 4>), grid, dim3(256), 0, st, g, tm, tn); break;
@@ -586,6 +625,7 @@ hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st) {
   if (fmt == 0) return launch_wide_fmt<W_INT4>(g, st);
   if (fmt == 1) return launch_wide_fmt<W_INT8>(g, st);
+  if (fmt == 3) return launch_wide_fmt<W_W4A8>(g, st);
   return launch_wide_fmt<W_NVFP4>(g, st);
 }
 

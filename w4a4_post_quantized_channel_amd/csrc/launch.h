@@ -36,11 +36,12 @@ struct GemmArgs {
   int64_t ldy;
 };
 
-// fmt: 0 int4, 1 int8.  workspace may be null (no split-K).
+// fmt: 0 int4, 1 int8, 3 int8 activations x int4 weights (W4A8).
+// workspace may be null (no split-K).
 hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st);
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 
-// gemm_wide.hip: many-token kernel with packed operands in LDS, fmt 0 int4, 1 int8, 2 nvfp4
+// gemm_wide.hip: many-token kernel with packed operands in LDS, fmt 0 int4, 1 int8, 2 nvfp4, 3 W4A8
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st);
 
 // branch.hip ----------------------------------------------------------------

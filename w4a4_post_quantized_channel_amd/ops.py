@@ -16,16 +16,16 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a4.so")
 
-FMT_INT4, FMT_INT8, FMT_NVFP4 = 0, 1, 2
+FMT_INT4, FMT_INT8, FMT_NVFP4, FMT_W4A8 = 0, 1, 2, 3
 DT_F32, DT_BF16, DT_I32 = 0, 1, 2
 ORDER_SMOOTH_THEN_ROTATE, ORDER_ROTATE_THEN_SMOOTH = 0, 1
 BRANCH_NONE, BRANCH_BF16 = 0, 1
-FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4}
+FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4, "w4a8": FMT_W4A8}  # w4a8: GEMM only
 ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
           "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
 ABI_VERSION = 1
 
-EXPORTS = ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "lowrank_add",
+EXPORTS = ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "lowrank_add",
            "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_workspace_size", "w4a4_status_string",
            "w4a4_last_error", "w4a4_abi_version"]
 
@@ -59,6 +59,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pack_weights": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
         "w4a4_linear": [vp, vp, vp, vp, i64, i64, i64, i32, f32, br, vp, i32, i64, vp, sz, vp],
         "w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
+        "w4a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
         "w4a4_workspace_size": [i64, i64, i64, i32],
         "lowrank_add": [vp, i64, i64, i64, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp],
         "w4a4_lowrank_project": [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp],
@@ -203,8 +204,8 @@ def _linear(fn: str, fmt: str, a_codes, a_scales, w_codes, w_scales, K: int, *, 
     args = (_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     tail = (ctypes.byref(br), _ptr(y), _dtype_code(y), y.stride(0), _ptr(workspace), ws_bytes, _stream(stream))
-    if fn == "w8a8_linear":
-        st = LIB.w8a8_linear(*args, float(alpha), *tail)
+    if fn in ("w8a8_linear", "w4a8_linear"):
+        st = getattr(LIB, fn)(*args, float(alpha), *tail)
     else:
         st = LIB.w4a4_linear(*args, FMTS[fmt], float(alpha), *tail)
     _check(fn, st)
@@ -219,6 +220,11 @@ def w4a4_linear(a_codes, a_scales, w_codes, w_scales, K: int, fmt: str = "int4",
 def w8a8_linear(a_codes, a_scales, w_codes, w_scales, K: int, **kw):
     """INT8 W8A8 sibling of w4a4_linear."""
     return _linear("w8a8_linear", "int8", a_codes, a_scales, w_codes, w_scales, K, **kw)
+
+
+def w4a8_linear(a_codes, a_scales, w_codes, w_scales, K: int, **kw):
+    """INT8 activation codes x packed INT4 weight codes (W4A8)."""
+    return _linear("w4a8_linear", "w4a8", a_codes, a_scales, w_codes, w_scales, K, **kw)
 
 
 def _check_branch_inputs(x, l1t, idx, lw=None):

@@ -41,6 +41,8 @@ class QuantizedLinear:
                  branch: Optional[dict] = None, y_dtype=torch.bfloat16, use_workspace: bool = True,
                  stream=None):
         self.fmt, self.fwht_block, self.order = fmt, fwht_block, order
+        # W4A8 (the 8-bit-activation denoising steps) keeps 4-bit weight codes
+        self.a_fmt, w_fmt = {"w4a8": ("int8", "int4")}.get(fmt, (fmt, fmt))
         self.use_workspace = use_workspace
         self.N, self.K = w.shape
         self.inv_s = inv_s
@@ -50,7 +52,7 @@ class QuantizedLinear:
         if fmt == "nvfp4":
             amax = ops.transform_amax(w, s, fwht_block=fwht_block, order=order, stream=stream)
             self.g_w = nvfp4_scale_from_amax(float(amax.item()))
-        self.w_codes, self.w_scales = ops.pack_weights(w, s, fmt, fwht_block=fwht_block, order=order,
+        self.w_codes, self.w_scales = ops.pack_weights(w, s, w_fmt, fwht_block=fwht_block, order=order,
                                                        tensor_scale=self.g_w, stream=stream)
         self.g_a = 1.0
         self._bufs = {}
@@ -73,7 +75,7 @@ class QuantizedLinear:
     def buffers(self, M: int, device):
         b = self._bufs.get(M)
         if b is None:
-            codes, scales = ops._alloc_codes(self.fmt, M, self.K, device)
+            codes, scales = ops._alloc_codes(self.a_fmt, M, self.K, device)
             br_a = None
             if self.branch is not None:
                 r = self.branch["lw"].shape[1]
@@ -88,7 +90,7 @@ class QuantizedLinear:
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
         M = x.shape[0]
         b = self.buffers(M, x.device)
-        ops.quantize_act(x, self.inv_s, self.fmt, fwht_block=self.fwht_block, order=self.order,
+        ops.quantize_act(x, self.inv_s, self.a_fmt, fwht_block=self.fwht_block, order=self.order,
                          tensor_scale=self.g_a, codes=b["codes"], scales=b["scales"], stream=stream)
         bd = None
         if self.branch is not None:
@@ -98,9 +100,10 @@ class QuantizedLinear:
                 a = ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
             bd = ops.branch_desc(a, self.branch["lw"])
         y = b["y"] if out is None else out
-        if self.fmt == "int8":
-            return ops.w8a8_linear(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K,
-                                   branch=bd, y=y, workspace=b["ws"], stream=stream)
+        if self.fmt in ("int8", "w4a8"):
+            fn = ops.w8a8_linear if self.fmt == "int8" else ops.w4a8_linear
+            return fn(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K,
+                      branch=bd, y=y, workspace=b["ws"], stream=stream)
         return ops.w4a4_linear(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K, self.fmt,
                                alpha=self.alpha, branch=bd, y=y, workspace=b["ws"], stream=stream)
 

@@ -65,7 +65,7 @@ class Case:
     M: int
     N: int
     K: int
-    fmt: str                 # "int4" | "int8" | "nvfp4"
+    fmt: str                 # "int4" | "int8" | "nvfp4" | "w4a8" (int8 x, int4 w)
     x_dtype: str             # "bf16" | "f32"
     y_dtype: str             # "bf16" | "f32"
     x: np.ndarray            # M x K fp32 values
@@ -213,8 +213,19 @@ def workload(name: str) -> Case:
     if name == "video_nvfp4":
         return linear_case(4096, 5120, 5120, seed=4, fmt="nvfp4", n_outliers=64,
                            outlier_gain=30.0, keep_channels=64, name=name)
+    # W4A8: the 8-bit-activation denoising steps (QuantWAMs, Experimental
+    # Details, quantization configuration; sec. 4.4.3) on the same shapes
+    if name == "decode_w4a8":   # protected batch-1 action step, projection (a)
+        return linear_case(64, 2048, 2048, seed=11, fmt="w4a8", n_outliers=16,
+                           outlier_gain=15.0, name=name)
+    if name == "decode_w4a8_down":   # protected batch-1 action step, 4-bit-weight down projection
+        return linear_case(64, 2048, 8192, seed=111, fmt="w4a8", n_outliers=16,
+                           outlier_gain=15.0, name=name)
+    if name == "video_w4a8":    # protected video-denoising step, integer codes
+        return linear_case(4096, 5120, 5120, seed=44, fmt="w4a8", n_outliers=64,
+                           outlier_gain=30.0, keep_channels=64, name=name)
     raise KeyError(name)
 
 
 WORKLOADS = ["tiny", "decode_w4a4", "decode_w8a8", "prefill_gate_up", "prefill_down",
-             "lowrank", "video_nvfp4"]
+             "lowrank", "video_nvfp4", "decode_w4a8", "decode_w4a8_down", "video_w4a8"]
