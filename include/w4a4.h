@@ -32,6 +32,12 @@
  *           low nibble and code 2j+1 in its high nibble, two's complement
  *           (-8..7).  scales: fp32[R], one step per row.
  *  - INT8 : R x K bytes (int8 codes).  scales: fp32[R].
+ *  - W4A8 activations (quantize_act with W4A4_FMT_W4A8): the INT8
+ *           quantization, R x K bytes, with every aligned group of 8 codes
+ *           k0..k0+7 stored as k0, k0+2, k0+4, k0+6, k0+1, k0+3, k0+5, k0+7
+ *           (the order in which INT4 weight codes unpack to bytes, so the
+ *           matrix cores take both operands without reordering).
+ *           scales: fp32[R].  W4A8 weights are INT4.
  *  - NVFP4: R x K/2 bytes of E2M1 nibbles (same nibble order; sign bit 3,
  *           exponent bits 2..1 with bias 1, mantissa bit 0).  scales:
  *           R x K/16 bytes of OCP E4M3 (E4M3FN, bias 7, max 448), one per 16
@@ -64,9 +70,10 @@ typedef enum w4a4_status {
 
 /* Code formats. */
 enum { W4A4_FMT_INT4 = 0, W4A4_FMT_INT8 = 1, W4A4_FMT_NVFP4 = 2, W4A4_FMT_W4A8 = 3 };
-/* W4A4_FMT_W4A8 names the GEMM pairing of INT8 activation codes with INT4
- * weight codes (w4a8_linear, w4a4_workspace_size); quantize_act and
- * pack_weights take INT8 and INT4 for its two sides. */
+/* W4A4_FMT_W4A8 names the pairing of INT8 activation codes with INT4 weight
+ * codes: quantize_act writes the activations in the W4A8 layout, the
+ * weights come from pack_weights with W4A4_FMT_INT4 (pack_weights rejects
+ * W4A4_FMT_W4A8), and w4a8_linear / w4a4_workspace_size take the pair. */
 /* Element types of float inputs / outputs.  I32 = raw integer accumulators. */
 enum { W4A4_DT_F32 = 0, W4A4_DT_BF16 = 1, W4A4_DT_I32 = 2 };
 /* Order of the two transforms applied before quantization. */
@@ -236,8 +243,8 @@ int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r);
  * of the denoising steps whose activations stay at 8 bits while the weights
  * keep their 4-bit codes (QuantWAMs, Experimental Details, quantization
  * configuration; sec. 4.4.3, fixed-intervention rollout scheduling).
- *  a_codes / a_scales   M rows from quantize_act with W4A4_FMT_INT8
- *           (int8 M x K, fp32[M]).
+ *  a_codes / a_scales   M rows from quantize_act with W4A4_FMT_W4A8
+ *           (int8 M x K in the W4A8 layout, fp32[M]).
  *  w_codes / w_scales   N rows from pack_weights with W4A4_FMT_INT4
  *           (packed int4 N x K/2, fp32[N]).
  *  Exact int32 accumulation of int8 x int4 products, then

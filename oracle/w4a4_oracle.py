@@ -270,6 +270,28 @@ def int4_from_nibbles(n: np.ndarray) -> np.ndarray:
     return np.where(n >= 8, n - 16, n).astype(np.int8)
 
 
+# W4A8 activation layout (a storage convention of this library, not of the
+# pages): the int8 codes of each aligned group of 8 K indices are stored
+# with the even indices first, then the odd ones -- the order in which the
+# nibbles of packed int4 weight codes come apart when unpacked to bytes.
+W4A8_GROUP_ORDER = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+
+
+def pack_w4a8_activations(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int8)
+    R, K = c.shape
+    assert K % 8 == 0
+    return np.ascontiguousarray(c.reshape(R, K // 8, 8)[:, :, W4A8_GROUP_ORDER]).reshape(R, K).view(np.uint8)
+
+
+def unpack_w4a8_activations(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed).view(np.int8)
+    R, K = p.shape
+    out = np.empty((R, K // 8, 8), dtype=np.int8)
+    out[:, :, W4A8_GROUP_ORDER] = p.reshape(R, K // 8, 8)
+    return out.reshape(R, K)
+
+
 # ----------------------------------------------------------------------------
 # GEMM, epilogue, 16-bit branch
 # ----------------------------------------------------------------------------
@@ -313,10 +335,12 @@ def quantize_operand(x, scale, fmt: str, fwht_block=FWHT_BLOCK,
     Activations pass inv_s (per-token scales), weights pass s (per-output-
     channel scales): the arithmetic is the same."""
     y = transform(x, scale, fwht_block, order)
-    if fmt in ("int4", "int8"):
+    if fmt in ("int4", "int8", "w4a8"):
+        # "w4a8": the activation side of W4A8, int8 codes in the W4A8 layout
         qmax = INT4_QMAX if fmt == "int4" else INT8_QMAX
         codes, step, v = quantize_int(y, qmax)
-        packed = pack_nibbles(codes) if fmt == "int4" else codes.view(np.uint8)
+        packed = {"int4": pack_nibbles, "int8": lambda c: c.view(np.uint8),
+                  "w4a8": pack_w4a8_activations}[fmt](codes)
         return {"y": y, "codes": codes, "scales": step, "v": v, "packed": packed}
     if fmt == "nvfp4":
         if g is None:
@@ -336,9 +360,10 @@ def transformed_amax(x, scale, fwht_block=FWHT_BLOCK, order="smooth_then_rotate"
 
 # Activation and weight formats of each linear: W4A8 is the 8-bit-activation
 # step of the QuantWAMs schedule (Experimental Details, quantization
-# configuration; sec. 4.4.3), with the same 4-bit weight codes as W4A4.
+# configuration; sec. 4.4.3), with the same 4-bit weight codes as W4A4; its
+# activations are the int8 quantization, stored in the W4A8 layout.
 OPERAND_FORMATS = {"int4": ("int4", "int4"), "int8": ("int8", "int8"),
-                   "nvfp4": ("nvfp4", "nvfp4"), "w4a8": ("int8", "int4")}
+                   "nvfp4": ("nvfp4", "nvfp4"), "w4a8": ("w4a8", "int4")}
 
 
 def linear(case, order="smooth_then_rotate", g_a=None, g_w=None) -> dict:

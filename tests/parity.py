@@ -33,6 +33,8 @@ def unpack_codes(fmt, packed):
         return O.int4_from_nibbles(O.unpack_nibbles(packed.view(np.uint8)))
     if fmt == "int8":
         return packed.view(np.int8)
+    if fmt == "w4a8":
+        return O.unpack_w4a8_activations(packed)
     return O.unpack_nibbles(packed.view(np.uint8))
 
 

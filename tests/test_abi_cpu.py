@@ -92,6 +92,10 @@ def test_quantize_act_rejects_bad_arguments(ops):
     # M == 0 is a valid no-op (no pointers needed)
     assert L.quantize_act(None, 1, 0, 128, 128, None, _q(ops), None, None, None) == 0
     assert L.pack_weights(FAKE, 0, 4, 96, 96, None, _q(ops), FAKE2, FAKE2, None) == -2
+    # W4A8: activations only (int8 in the W4A8 layout); weights are packed as INT4
+    assert L.pack_weights(FAKE, 1, 4, 128, 128, None, _q(ops, fmt=3), FAKE2, FAKE2, None) == -4
+    assert L.quantize_act(FAKE, 1, 4, 96, 96, None, _q(ops, fmt=3), FAKE2, FAKE2, None) == -2
+    assert L.quantize_act(None, 1, 0, 128, 128, None, _q(ops, fmt=3), None, None, None) == 0
 
 
 def _lin(ops, fn="w4a4_linear", M=8, N=8, K=128, fmt=0, alpha=1.0, br=None, y=FAKE, ydt=1, ldy=None,

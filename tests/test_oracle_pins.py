@@ -457,3 +457,25 @@ def test_w4a8_error_bound_with_transforms():
                         n_outliers=6, outlier_gain=20.0)
     err4 = np.abs(O.linear(c4)["y"] - ref)
     assert np.sum(err ** 2) < 0.8 * np.sum(err4 ** 2)
+
+
+def test_w4a8_activation_layout_example_and_roundtrip():
+    codes = np.arange(16, dtype=np.int8)[None, :] - 8
+    packed = O.pack_w4a8_activations(codes).view(np.int8)[0] + 8
+    assert packed.tolist() == [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]
+    rng = np.random.default_rng(3)
+    c = rng.integers(-128, 128, size=(7, 192)).astype(np.int8)
+    assert np.array_equal(O.unpack_w4a8_activations(O.pack_w4a8_activations(c)), c)
+
+
+def test_w4a8_activation_layout_is_the_int4_unpack_order():
+    """Unpacking a packed int4 word d to bytes as (d << 4) & 0xF0F0F0F0 (even
+    codes, times 16) then d & 0xF0F0F0F0 (odd codes, times 16) yields the
+    codes in exactly the W4A8 activation order."""
+    rng = np.random.default_rng(4)
+    c = rng.integers(-8, 8, size=(5, 128)).astype(np.int8)
+    words = O.pack_nibbles(c).view("<u4")                      # R x K/8 little-endian words
+    ev = ((words << np.uint32(4)) & np.uint32(0xF0F0F0F0)).astype("<u4")
+    od = (words & np.uint32(0xF0F0F0F0)).astype("<u4")
+    seq = np.stack([ev, od], axis=-1).reshape(5, -1).view(np.int8).astype(np.int64) // 16
+    assert np.array_equal(seq, O.pack_w4a8_activations(c).view(np.int8))

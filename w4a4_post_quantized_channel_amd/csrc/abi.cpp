@@ -46,7 +46,8 @@ int check_quant(const char* fn, const void* x, int32_t dt, int64_t R, int64_t K,
   if (R < 0 || K <= 0) return fail(W4A4_ERR_INVALID_ARG, "%s: bad sizes R=%lld K=%lld", fn, (long long)R, (long long)K);
   if (dt != W4A4_DT_F32 && dt != W4A4_DT_BF16)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: input dtype %d not F32/BF16", fn, dt);
-  if (q->fmt != W4A4_FMT_INT4 && q->fmt != W4A4_FMT_INT8 && q->fmt != W4A4_FMT_NVFP4)
+  if (q->fmt != W4A4_FMT_INT4 && q->fmt != W4A4_FMT_INT8 && q->fmt != W4A4_FMT_NVFP4 &&
+      q->fmt != W4A4_FMT_W4A8)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: unknown fmt %d", fn, q->fmt);
   if (q->fwht_block != 0 && q->fwht_block != 64)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: fwht_block must be 0 or 64", fn);
@@ -79,7 +80,7 @@ int run_quant(const char* fn, const void* x, int32_t dt, int64_t R, int64_t K, i
               const float* scale, const w4a4_qdesc* q, void* codes, void* scales, void* stream) {
   int st = check_quant(fn, x, dt, R, K, ldx, scale, q, true, codes, scales);
   if (st != W4A4_OK || R == 0) return st;
-  const int mode = q->fmt;  // 0 int4, 1 int8, 2 nvfp4
+  const int mode = q->fmt == W4A4_FMT_W4A8 ? 4 : q->fmt;  // 0 int4, 1 int8, 2 nvfp4, 4 W4A8 int8
   hipError_t e = w4a4::launch_quantize(mode, dt == W4A4_DT_BF16, x, R, K, ldx, scale, q->tensor_scale,
                                        q->fwht_block, q->order, codes, scales, nullptr,
                                        (hipStream_t)stream);
@@ -166,6 +167,8 @@ int quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t l
 
 int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const float* smooth,
                  const w4a4_qdesc* q, void* codes, void* scales, void* stream) {
+  if (q && q->fmt == W4A4_FMT_W4A8)
+    return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "pack_weights: W4A8 weights are packed with W4A4_FMT_INT4");
   return run_quant("pack_weights", w, w_dtype, N, K, ldw, smooth, q, codes, scales, stream);
 }
 

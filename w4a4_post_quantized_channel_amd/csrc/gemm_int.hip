@@ -91,14 +91,6 @@ struct DecFmt {
   static constexpr int KIND = DF == DF_I4 ? 0 : (DF == DF_I8 ? 1 : 3);
 };
 
-// 16 int8 codes (bytes, K order 0..15) -> the K order of a widened int4
-// fragment: even K of the first 8, odd K of the first 8, even, odd of the
-// last 8 (the order widen_int4 produces for 16 packed codes).
-__device__ __forceinline__ v4i order_like_int4(const uint4& v) {
-  return v4i{(int)__builtin_amdgcn_perm(v.y, v.x, 0x06040200u), (int)__builtin_amdgcn_perm(v.y, v.x, 0x07050301u),
-             (int)__builtin_amdgcn_perm(v.w, v.z, 0x06040200u), (int)__builtin_amdgcn_perm(v.w, v.z, 0x07050301u)};
-}
-
 template <int DF, int TI, int TJ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
@@ -207,7 +199,8 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     } else {
       // W4A8: lane group lq owns K [32 lq, 32 lq + 32) of the step, half h
       // its 16 K from 16 h.  The weight chunk lq is widened as in the int4
-      // case; the activation bytes (chunk 2 lq + h) are put in the same order.
+      // case; the activation chunk 2 lq + h already holds its codes in the
+      // widened order (even K, then odd K, of each group of 8).
       uint4 rb[TJ];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
@@ -220,7 +213,7 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
           const int R = i * 16 + lr;
-          a[i] = order_like_int4(*reinterpret_cast<const uint4*>(st + R * SBA + 16 * ((2 * lq + h) ^ (R & 7))));
+          a[i] = *reinterpret_cast<const v4i*>(st + R * SBA + 16 * ((2 * lq + h) ^ (R & 7)));
         }
 #pragma unroll
         for (int i = 0; i < TI; ++i)

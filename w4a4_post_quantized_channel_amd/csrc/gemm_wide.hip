@@ -119,18 +119,10 @@ __device__ __forceinline__ void mfma_w(typename WFmt<FMT>::acc_t& c, const uint4
     c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a), __builtin_bit_cast(v4i, b), c, 0, 0, 0);
 }
 
-// 16 int8 codes (bytes, K order 0..15) -> the K order widen_i4 gives 16
-// packed int4 codes: even K of the first 8, odd K of the first 8, then the
-// same for the last 8.
-__device__ __forceinline__ uint4 order_like_i4(const uint4& v) {
-  return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u), __builtin_amdgcn_perm(v.y, v.x, 0x07050301u),
-                    __builtin_amdgcn_perm(v.w, v.z, 0x06040200u), __builtin_amdgcn_perm(v.w, v.z, 0x07050301u));
-}
-
 // Operand fragment for MFMA step t of a stage, from the lane's packed
 // 16-byte slot p (and, for NVFP4, the 2 scale bytes of its 32 codes).
-// W4A8 weights widen like int4; its activation fragments go through
-// order_like_i4 at the read instead.
+// W4A8 weights widen like int4; its int8 activation codes arrive in the
+// widened order (even K, then odd K, of each group of 8) and go in as read.
 template <int FMT>
 __device__ __forceinline__ uint4 operand(const uint4& p, int t, uint32_t sc) {
   if constexpr (FMT == W_INT8) {
@@ -401,7 +393,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   auto widen = [&](const Frags& f, int st, Ops& o) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      if constexpr (FMT == W_W4A8) o.a[i] = order_like_i4(f.a[i][st]);
+      if constexpr (FMT == W_W4A8) o.a[i] = f.a[i][st];
       else o.a[i] = operand<FMT>(f.a[i][0], st, FMT == W_NVFP4 ? f.sa[i] : 0u);
     }
 #pragma unroll

@@ -7,7 +7,8 @@
 namespace w4a4 {
 
 // quantize.hip -------------------------------------------------------------
-// mode: 0 int4, 1 int8, 2 nvfp4, 3 transform-amax only.
+// mode: 0 int4, 1 int8, 2 nvfp4, 3 transform-amax only, 4 int8 in the W4A8 order
+// (each aligned group of 8 codes stored even-K codes first, then odd-K codes).
 hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int64_t K,
                            int64_t ldx, const float* scale, float g, int rot, int order,
                            void* codes, void* scales, float* amax_out, hipStream_t st);

@@ -45,7 +45,10 @@ struct QuantArgs {
   float* amax_out;      // transform_amax mode
 };
 
-enum { MODE_INT4 = 0, MODE_INT8 = 1, MODE_NVFP4 = 2, MODE_AMAX = 3 };
+// MODE_INT8W: int8 codes for the W4A8 GEMM, every aligned group of 8 codes
+// stored as its even-K codes then its odd-K codes (the order packed int4
+// weight codes take when widened to bytes).
+enum { MODE_INT4 = 0, MODE_INT8 = 1, MODE_NVFP4 = 2, MODE_AMAX = 3, MODE_INT8W = 4 };
 
 constexpr float kTinyStep = 8.271806125530277e-25f;  // 2^-80
 
@@ -257,6 +260,7 @@ __device__ __forceinline__ float transform_slot(const SlotRaw<BF16IN>& raw, floa
 template <int MODE, bool BF16IN, int NC, int WPR>
 __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(QuantArgs a) {
   constexpr int QMAX = MODE == MODE_INT4 ? 7 : 127;
+  constexpr bool I8 = MODE == MODE_INT8 || MODE == MODE_INT8W;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   static_assert(WPR == 1 || WPR == 4 || WPR == 8, "waves per row");
@@ -300,7 +304,7 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
     // slot takes the exact path, which forms y itself.
     // Integer modes need the whole row for its maximum; NVFP4 transforms
     // and quantizes one slot at a time.
-    if constexpr (MODE == MODE_INT4 || MODE == MODE_INT8 || MODE == MODE_AMAX) {
+    if constexpr (MODE == MODE_INT4 || I8 || MODE == MODE_AMAX) {
       float v[NC][16];
       float fl = 1.0f;
 #pragma unroll
@@ -341,7 +345,7 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
             r[i] = __builtin_rintf(t[i]);
             dmax = fmaxf(dmax, __builtin_fabsf(t[i] - r[i]));
           }
-          constexpr float kEdge = MODE == MODE_INT8 ? 0.5f - 3.0517578125e-05f : 0.5f - 1.9073486328125e-06f;
+          constexpr float kEdge = I8 ? 0.5f - 3.0517578125e-05f : 0.5f - 1.9073486328125e-06f;
           if (s < nslots && (!fast || dmax >= kEdge)) {
             if (fast) {
 #pragma unroll
@@ -372,9 +376,14 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
           } else {
             uint32_t w[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-              w[k] = (q[4 * k] & 0xFFu) | ((q[4 * k + 1] & 0xFFu) << 8) | ((q[4 * k + 2] & 0xFFu) << 16) |
-                     ((q[4 * k + 3] & 0xFFu) << 24);
+            for (int k = 0; k < 4; ++k) {
+              // natural order: dword k holds codes 4k .. 4k+3; W4A8 order: dword k
+              // holds the even (k even) or odd (k odd) codes of group k / 2
+              const int b = MODE == MODE_INT8W ? 8 * (k >> 1) + (k & 1) : 4 * k;
+              const int d = MODE == MODE_INT8W ? 2 : 1;
+              w[k] = (q[b] & 0xFFu) | ((q[b + d] & 0xFFu) << 8) | ((q[b + 2 * d] & 0xFFu) << 16) |
+                     ((q[b + 3 * d] & 0xFFu) << 24);
+            }
             *reinterpret_cast<uint4*>(a.codes + (size_t)row * a.K + s * 16) = make_uint4(w[0], w[1], w[2], w[3]);
           }
         }
@@ -573,7 +582,7 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   // One wave per row when there are many rows and the row fits five chunks
   // per lane (the factors then stay in registers); else four waves per row,
   // eight for integer codes of rows longer than 4096.
-  const bool intmode = mode == MODE_INT4 || mode == MODE_INT8;
+  const bool intmode = mode == MODE_INT4 || mode == MODE_INT8 || mode == MODE_INT8W;
   int wpr = (R >= 1024 && nslots <= 5 * 64) ? 1 : 4;
   if (wpr == 4 && intmode && nslots > 4 * 64) wpr = 8;
   const int nc = round_nc((int)((nslots + 64 * wpr - 1) / (64 * wpr)));
@@ -590,6 +599,8 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   if (wpr == 8) {
     if (mode == MODE_INT4) return bf16in ? launch_nc<MODE_INT4, true, 8>(nc, grid, st, a)
                                          : launch_nc<MODE_INT4, false, 8>(nc, grid, st, a);
+    if (mode == MODE_INT8W) return bf16in ? launch_nc<MODE_INT8W, true, 8>(nc, grid, st, a)
+                                          : launch_nc<MODE_INT8W, false, 8>(nc, grid, st, a);
     return bf16in ? launch_nc<MODE_INT8, true, 8>(nc, grid, st, a) : launch_nc<MODE_INT8, false, 8>(nc, grid, st, a);
   }
 #define W4A4_DISPATCH(MODE)                                                          \
@@ -601,6 +612,7 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   }
   W4A4_DISPATCH(MODE_INT4)
   W4A4_DISPATCH(MODE_INT8)
+  W4A4_DISPATCH(MODE_INT8W)
   W4A4_DISPATCH(MODE_NVFP4)
   W4A4_DISPATCH(MODE_AMAX)
 #undef W4A4_DISPATCH

@@ -20,7 +20,8 @@ FMT_INT4, FMT_INT8, FMT_NVFP4, FMT_W4A8 = 0, 1, 2, 3
 DT_F32, DT_BF16, DT_I32 = 0, 1, 2
 ORDER_SMOOTH_THEN_ROTATE, ORDER_ROTATE_THEN_SMOOTH = 0, 1
 BRANCH_NONE, BRANCH_BF16 = 0, 1
-FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4, "w4a8": FMT_W4A8}  # w4a8: GEMM only
+# w4a8: quantize_act writes W4A8-layout int8 activations; the weights are int4
+FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4, "w4a8": FMT_W4A8}
 ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
           "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
 ABI_VERSION = 1
@@ -125,7 +126,7 @@ def code_shapes(fmt: str, R: int, K: int):
     """(codes shape, codes dtype, scales shape, scales dtype) of a packed operand."""
     if fmt == "int4":
         return (R, K // 2), torch.uint8, (R,), torch.float32
-    if fmt == "int8":
+    if fmt in ("int8", "w4a8"):   # w4a8: activation side, int8 in the W4A8 layout
         return (R, K), torch.int8, (R,), torch.float32
     if fmt == "nvfp4":
         return (R, K // 2), torch.uint8, (R, K // 16), torch.uint8

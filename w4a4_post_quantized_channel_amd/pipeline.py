@@ -41,8 +41,9 @@ class QuantizedLinear:
                  branch: Optional[dict] = None, y_dtype=torch.bfloat16, use_workspace: bool = True,
                  stream=None):
         self.fmt, self.fwht_block, self.order = fmt, fwht_block, order
-        # W4A8 (the 8-bit-activation denoising steps) keeps 4-bit weight codes
-        self.a_fmt, w_fmt = {"w4a8": ("int8", "int4")}.get(fmt, (fmt, fmt))
+        # W4A8 (the 8-bit-activation denoising steps) keeps 4-bit weight codes;
+        # its activations are int8 codes in the W4A8 layout
+        self.a_fmt, w_fmt = {"w4a8": ("w4a8", "int4")}.get(fmt, (fmt, fmt))
         self.use_workspace = use_workspace
         self.N, self.K = w.shape
         self.inv_s = inv_s
