@@ -65,10 +65,13 @@ static int decode_ti(int64_t M, bool split) {
   return M > 32 ? 2 : 1;
 }
 
-// LDS bytes a decode wave keeps in flight (its ring of step slots): int4
-// rows are half as long per step, and a smaller ring measured faster there.
-template <bool BOTH_INT4>
-constexpr int dec_ring_bytes() { return BOTH_INT4 ? 12 * 1024 : 18 * 1024; }
+// LDS bytes of a decode wave's ring of step slots: int4 rows are half as
+// long per step, and a smaller ring measured faster there; int8 activation
+// rows take a deeper ring (the register prefetch below holds one slot),
+// except in K splits, whose waves run few steps: every ring slot beyond
+// them is a step of zeros that still costs its copies and MFMAs.
+template <bool BOTH_INT4, bool SPLIT>
+constexpr int dec_ring_bytes() { return BOTH_INT4 ? 12 * 1024 : (SPLIT ? 18 * 1024 : 30 * 1024); }
 
 // f(integral_constant<int, J>) for J = J0 .. J1 - 1, in order.
 template <int J0, int J1, typename F>
@@ -103,7 +106,7 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
   constexpr int PER_STEP = NIA + NIB;                      // copy instructions per step (A first)
   constexpr int AREG = 16 * TI * SBA;                      // A rows' bytes in a slot; W rows follow
   constexpr int STEP_BYTES = AREG + 16 * TJ * SBB;
-  constexpr int NBUF0 = dec_ring_bytes<DF == DF_I4>() / STEP_BYTES;
+  constexpr int NBUF0 = dec_ring_bytes<DF == DF_I4, TJ == kDecTJ>() / STEP_BYTES;
   constexpr int NBUF = NBUF0 > 8 ? 8 : (NBUF0 < 2 ? 2 : NBUF0);   // ring slots per wave
   constexpr int WAVE_BYTES = NBUF * STEP_BYTES;
   constexpr int RED_BYTES = 4 * TI * TJ * 1024;
@@ -153,104 +156,111 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  auto compute = [&](const uint8_t* st) {   // the MFMAs of one step from its ring slot
-    if constexpr (DF == DF_I4) {
-      uint4 ra[TI], rb[TJ];
+  // Fragments of one step: int8 operands take a 16-byte chunk per half
+  // step (h), int4 operands one chunk for both halves.
+  struct Frags {
+    uint4 a[DecFmt<DF>::A4 ? 1 : 2][TI];
+    uint4 b[DecFmt<DF>::W4 ? 1 : 2][TJ];
+  };
+  // LDS reads of one step from its ring slot.  int4 rows: lane group lq
+  // holds K [32 lq, 32 lq + 32) of the step as one chunk.  int8 rows: half h
+  // of lane group lq is chunk 4 h + lq (both int8) or 2 lq + h (W4A8, whose
+  // activation chunks hold their codes in the widened int4 order).
+  auto load = [&](const uint8_t* st, Frags& f) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int R = i * 16 + lr;
+      if constexpr (F::A4) {
+        f.a[0][i] = *reinterpret_cast<const uint4*>(st + R * SBA + 16 * (lq ^ (R & 3)));
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = DF == DF_W4A8 ? 2 * lq + h : 4 * h + lq;
+          f.a[h][i] = *reinterpret_cast<const uint4*>(st + R * SBA + 16 * (c ^ (R & 7)));
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int R = j * 16 + lr;
+      if constexpr (F::W4) {
+        f.b[0][j] = *reinterpret_cast<const uint4*>(st + AREG + R * SBB + 16 * (lq ^ (R & 3)));
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          f.b[h][j] = *reinterpret_cast<const uint4*>(st + AREG + R * SBB + 16 * ((4 * h + lq) ^ (R & 7)));
+      }
+    }
+  };
+  // The MFMAs of one step (int4 chunks widened to 16 q per byte).
+  auto math = [&](const Frags& f) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v4i b[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        b[j] = F::W4 ? (h ? widen_int4(f.b[0][j].z, f.b[0][j].w) : widen_int4(f.b[0][j].x, f.b[0][j].y))
+                     : __builtin_bit_cast(v4i, f.b[F::W4 ? 0 : h][j]);
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int R = i * 16 + lr;
-        ra[i] = *reinterpret_cast<const uint4*>(st + R * SBA + 16 * (lq ^ (R & 3)));
-      }
+        const v4i a = F::A4 ? (h ? widen_int4(f.a[0][i].z, f.a[0][i].w) : widen_int4(f.a[0][i].x, f.a[0][i].y))
+                            : __builtin_bit_cast(v4i, f.a[F::A4 ? 0 : h][i]);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int R = j * 16 + lr;
-        rb[j] = *reinterpret_cast<const uint4*>(st + AREG + R * SBB + 16 * (lq ^ (R & 3)));
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            const v4i a = h ? widen_int4(ra[i].z, ra[i].w) : widen_int4(ra[i].x, ra[i].y);
-            const v4i b = h ? widen_int4(rb[j].z, rb[j].w) : widen_int4(rb[j].x, rb[j].y);
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i][j], 0, 0, 0);
-          }
-    } else if constexpr (DF == DF_I8) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        v4i a[TI], b[TJ];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int R = i * 16 + lr;
-          a[i] = *reinterpret_cast<const v4i*>(st + R * SBA + 16 * ((h * 4 + lq) ^ (R & 7)));
-        }
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int R = j * 16 + lr;
-          b[j] = *reinterpret_cast<const v4i*>(st + AREG + R * SBB + 16 * ((h * 4 + lq) ^ (R & 7)));
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // W4A8: lane group lq owns K [32 lq, 32 lq + 32) of the step, half h
-      // its 16 K from 16 h.  The weight chunk lq is widened as in the int4
-      // case; the activation chunk 2 lq + h already holds its codes in the
-      // widened order (even K, then odd K, of each group of 8).
-      uint4 rb[TJ];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int R = j * 16 + lr;
-        rb[j] = *reinterpret_cast<const uint4*>(st + AREG + R * SBB + 16 * (lq ^ (R & 3)));
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        v4i a[TI];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int R = i * 16 + lr;
-          a[i] = *reinterpret_cast<const v4i*>(st + R * SBA + 16 * ((2 * lq + h) ^ (R & 7)));
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            const v4i b = h ? widen_int4(rb[j].z, rb[j].w) : widen_int4(rb[j].x, rb[j].y);
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b, acc[i][j], 0, 0, 0);
-          }
+        for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[i][j], 0, 0, 0);
       }
     }
   };
 
   // Ring of NBUF step slots per wave: the copies of step t + NBUF - 1 are
-  // issued before step t is read.  A slot is refilled only after the reads
-  // of its previous step have returned (their MFMAs consumed them).  The
-  // last NBUF - 1 steps drain the ring with no further copies; each drain
+  // issued before step t's MFMAs.  With three or more slots, step t + 1's
+  // fragments are read from LDS while step t's MFMAs run on the fragments
+  // read one iteration earlier (a slot is refilled two iterations after
+  // its fragments were read); with two slots that would wait for the copy
+  // just issued, so a step is read and multiplied in one go.  The last
+  // NBUF - 1 steps drain the ring with no further copies; each drain
   // position has a fixed number of younger steps, so every wait is exact.
   // A wave with fewer than NBUF - 1 steps runs the missing ones on copies
   // past kz1, which read as zeros and add nothing: the code stays free of
   // branches around the waits.
+  constexpr int LA = NBUF >= 3 ? 1 : 0;   // steps of register lookahead
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p) issue(p, p);
-  int rslot = 0, wslot = NBUF - 1;
+  Frags cur, nxt;
+  int rslot = 0, wslot = NBUF - 1;   // rslot: slot of the next step to read
+  if constexpr (LA == 1) {
+    wait_vmcnt<(NBUF - 2) * PER_STEP>();
+    asm volatile("" ::: "memory");
+    load(area, cur);
+    rslot = 1;
+  }
   for (int t = 0; t < nsteps - (NBUF - 1); ++t) {
     issue(t + NBUF - 1, wslot);
     wslot = wslot == NBUF - 1 ? 0 : wslot + 1;
-    wait_vmcnt<(NBUF - 1) * PER_STEP>();
+    wait_vmcnt<(NBUF - 1 - LA) * PER_STEP>();   // steps up to t + LA are in LDS
     asm volatile("" ::: "memory");
-    compute(area + rslot * STEP_BYTES);
+    load(area + rslot * STEP_BYTES, nxt);
     rslot = rslot == NBUF - 1 ? 0 : rslot + 1;
+    if constexpr (LA == 1) {
+      math(cur);
+      cur = nxt;
+    } else {
+      math(nxt);
+    }
   }
   drain_ring<0, NBUF - 1>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    wait_vmcnt<(NBUF - 2 - j) * PER_STEP>();
-    asm volatile("" ::: "memory");
-    compute(area + rslot * STEP_BYTES);
-    rslot = rslot == NBUF - 1 ? 0 : rslot + 1;
+    if constexpr (LA == 0 || j < NBUF - 2) {
+      wait_vmcnt<(NBUF - 2 - LA - j) * PER_STEP>();
+      asm volatile("" ::: "memory");
+      load(area + rslot * STEP_BYTES, nxt);
+      rslot = rslot == NBUF - 1 ? 0 : rslot + 1;
+    }
+    if constexpr (LA == 1) {
+      math(cur);
+      cur = nxt;
+    } else {
+      math(nxt);
+    }
   });
   __syncthreads();   // every wave is done with its copy area; LDS now holds the partial tiles
   int (*red)[TI][TJ][4][64] = reinterpret_cast<int (*)[TI][TJ][4][64]>(smem);
