@@ -28,6 +28,7 @@
 // division of the unscaled value.
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace w4a4 {
 
@@ -413,14 +414,21 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
 // butterfly stage then runs inside one lane's registers, and the block's 64
 // smoothing factors are the same for the whole wave (scalar loads).  NVFP4
 // needs no row-wide reduction (its scales are per 16 elements and the tensor
-// scale is fixed), so every (rows, block) pair is independent.
+// scale is fixed), so every (rows, block) pair is an independent task.
+// The grid is sized to stay resident; each wave walks its tasks with two
+// LDS tiles, copying the next task's tile while it transforms and encodes
+// the current one, so the HBM reads overlap the vector work.
+template <bool BF16IN>
+constexpr int nvfp4_lanes_tile() { return 64 * 64 * (BF16IN ? 2 : 4); }
+
 template <bool BF16IN, bool ROT>
 __global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
   constexpr int ESZ = BF16IN ? 2 : 4;
   constexpr int RB = 64 * ESZ;              // bytes of one row's 64-element block
-  constexpr int TILE = 64 * RB;             // one wave's 64 x 64 tile
+  constexpr int TILE = nvfp4_lanes_tile<BF16IN>();   // one wave's 64 x 64 tile
+  constexpr int NCOPY = TILE / 1024;        // copy instructions per tile
   __shared__ float2 stab[128];
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][2][TILE];
   for (int e = threadIdx.x; e < 128; e += blockDim.x) {
     const float S = e < 0x7F ? e4m3_to_f32((uint32_t)e) * a.g : 0.f;
     stab[e] = make_float2(S, S > 0.f ? 1.0f / S : 0.f);  // IEEE division
@@ -431,33 +439,52 @@ __global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
   const bool has_scale = a.scale != nullptr;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint8_t* tile = tiles[wave];
   const int nblk = a.K >> 6;
   const int64_t ngrp = (a.R + 63) >> 6;
   const int64_t ntask = ngrp * nblk;
+  const int64_t stride = (int64_t)gridDim.x * 4;
   constexpr int CPR = RB / 16;              // 16-byte chunks per row of the tile
-  for (int64_t task = (int64_t)blockIdx.x * 4 + wave; task < ntask; task += (int64_t)gridDim.x * 4) {
+
+  // Coalesced copy of task t's 64 x 64 tile into buffer `buf` of this
+  // wave's LDS slice: copy instruction i covers tile bytes [1024 i,
+  // 1024 i + 1024); the chunk at slot q of tile row r holds logical chunk
+  // q ^ (r & 7) (so that the 64 rows read back by the 64 lanes spread over
+  // the banks).  Rows past R read zeros.
+  auto copy_tile = [&](int64_t t, int buf) {
+    const int64_t grp = t / nblk;
+    const int b = (int)(t - grp * nblk);
+    const v4u rs = rsrc_words(reinterpret_cast<const char*>(a.x) + (size_t)(grp * 64) * a.ldx * ESZ,
+                              (uint32_t)(min((int64_t)64, a.R - grp * 64) * a.ldx * ESZ));
+    uint8_t* tile = tiles[wave][buf];
+#pragma unroll
+    for (int i = 0; i < NCOPY; ++i) {
+      const int p = i * 1024 + lane * 16;
+      const int r = p / RB, q = (p % RB) / 16;
+      const int L = q ^ (r & 7 & (CPR - 1));
+      dma16(rs, tile + i * 1024, (uint32_t)(r * (int)(a.ldx * ESZ) + b * RB + L * 16), 0u);
+    }
+  };
+
+  int64_t task = (int64_t)blockIdx.x * 4 + wave;
+  if (task < ntask) copy_tile(task, 0);
+  for (int buf = 0; task < ntask; task += stride, buf ^= 1) {
     const int64_t grp = task / nblk;
     const int b = (int)(task - grp * nblk);
     const int64_t row = grp * 64 + lane;
     const bool live = row < a.R;
-    // Coalesced copy of the 64 x 64 tile into this wave's LDS slice: load
-    // instruction i covers tile bytes [1024 i, 1024 i + 1024); the chunk at
-    // slot q of tile row r holds logical chunk q ^ (r & 7) (so that the 64
-    // rows read back by the 64 lanes spread over the banks).  Rows past R
-    // read zeros.
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)(grp * 64) * a.ldx * ESZ,
-                  (uint32_t)(min((int64_t)64, a.R - grp * 64) * a.ldx * ESZ));
-#pragma unroll
-    for (int i = 0; i < TILE / 1024; ++i) {
-      const int p = i * 1024 + lane * 16;
-      const int r = p / RB, q = (p % RB) / 16;
-      const int L = q ^ (r & 7 & (CPR - 1));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + i * 1024), 16,
-                                               r * (int)(a.ldx * ESZ) + b * RB + L * 16, 0, 0, 0);
+    // Start the next task's copy, then wait for this task's tile only:
+    // loads complete in order, so at most NCOPY outstanding operations
+    // leaves just the copies issued last.
+    // (The copies are issued as inline assembly, which the compiler does
+    // not track, so these explicit waits are the only ones.)
+    if (task + stride < ntask) {
+      copy_tile(task + stride, buf ^ 1);
+      wait_vmcnt<NCOPY>();
+    } else {
+      wait_vmcnt<0>();
     }
-    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);   // vmcnt(0): this wave's copies are in LDS
+    asm volatile("" ::: "memory");
+    const uint8_t* tile = tiles[wave][buf];
     float v[64];
 #pragma unroll
     for (int c = 0; c < CPR; ++c) {
@@ -474,7 +501,9 @@ __global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
         v[4 * c + 2] = __uint_as_float(d.z); v[4 * c + 3] = __uint_as_float(d.w);
       }
     }
-    __builtin_amdgcn_wave_barrier();   // the next task's copies overwrite the slice only after these reads
+    // the copy two tasks ahead overwrites this buffer only after these
+    // reads have returned (their values are consumed below)
+    __builtin_amdgcn_wave_barrier();
     // the block's 64 factors are the same for the whole wave: scalar loads
     const __attribute__((address_space(4))) float* sc =
         (const __attribute__((address_space(4))) float*)(a.scale + (has_scale ? b * 64 : 0));
@@ -565,9 +594,11 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
                            float* amax_out, hipStream_t st) {
   QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, amax_out};
   if (mode == MODE_NVFP4 && R >= 256 && K % 64 == 0 && (rot == 0 || rot == 64)) {
+    // resident grid: as many four-wave blocks as the tiles' LDS lets every CU hold
     const int64_t tasks = ((R + 63) / 64) * (K / 64);
+    const int per_cu = (160 * 1024) / (8 * (bf16in ? nvfp4_lanes_tile<true>() : nvfp4_lanes_tile<false>()) + 1024);
     int64_t blocks = (tasks + 3) / 4;
-    if (blocks > 256 * 8) blocks = 256 * 8;
+    if (blocks > 256 * per_cu) blocks = 256 * per_cu;
     const dim3 grid((unsigned)blocks);
     if (bf16in) {
       if (rot) hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<true, true>), grid, dim3(256), 0, st, a);
