@@ -56,7 +56,7 @@ extern "C" {
 
 #define W4A4_ABI_VERSION 1
 #define W4A4_MAX_BRANCH 128 /* largest branch width (rank or kept channels) */
-#define W4A4_LOWRANK_MAX_PARTS 4 /* K parts of a low-rank projection (see w4a4_lowrank_width) */
+#define W4A4_LOWRANK_MAX_PARTS 4 /* hi/lo pairs a branch ``a`` operand may hold (ra = 2 P r) */
 
 typedef enum w4a4_status {
   W4A4_OK = 0,
@@ -194,6 +194,25 @@ int w8a8_linear(const void* a_codes, const void* a_scales,
                 const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* w4a8_linear -- W4A8: INT8 activation codes x INT4 weight codes, the GEMM
+ * of the denoising steps whose activations stay at 8 bits while the weights
+ * keep their 4-bit codes (QuantWAMs, Experimental Details, quantization
+ * configuration; sec. 4.4.3, fixed-intervention rollout scheduling).
+ *  a_codes / a_scales   M rows from quantize_act with W4A4_FMT_W4A8
+ *           (int8 M x K in the W4A8 layout, fp32[M]).
+ *  w_codes / w_scales   N rows from pack_weights with W4A4_FMT_INT4
+ *           (packed int4 N x K/2, fp32[N]).
+ *  Exact int32 accumulation of int8 x int4 products, then
+ *  y = fp32(fp32(acc) * a_scales[m]) * w_scales[n] * alpha, as for INT4.
+ *  br, y, y_dtype (I32 = raw accumulators), ldy, workspace and the shape
+ *  and alignment rules are those of w4a4_linear; size a workspace with
+ *  w4a4_workspace_size(M, N, K, W4A4_FMT_W4A8). */
+int w4a8_linear(const void* a_codes, const void* a_scales,
+                const void* w_codes, const void* w_scales,
+                int64_t M, int64_t N, int64_t K, float alpha,
+                const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
+                void* workspace, size_t workspace_bytes, void* stream);
+
 /* lowrank_add -- standalone 16-bit branch, y += (x L1) L2 or
  * y += x[:, idx] W_idx^T (Q-WAM abstract: 16-bit low-rank branch as a dense
  * product; QuantWAMs sec. 3.1 / 4.2: kept channels on a BF16 path).
@@ -216,22 +235,18 @@ int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx,
 /* w4a4_lowrank_project -- first half of the branch, producing the
  * w4a4_branch ``a`` operand.  For l1t != NULL (L1 transposed, bf16 r x K):
  * t = x L1 in fp32, written as bf16 hi = bf16(t) and lo = bf16(t - hi) in
- * columns [0, r) and [r, 2r) of out (the branch's ra = 2r).  For few rows K
- * is cut into P parts computed by separate workgroups (P is a function of
- * M and K); their fp32 partial products are staged in the rest of the row
- * and added in part order, so out needs w4a4_lowrank_width(M, K, r) = 2 P r
- * columns, of which the first 2r hold the result.  For idx != NULL,
- * out = x[:, idx] (M x r, exact).
- *  x bf16 M x K (row stride ldx); out bf16 with row stride
- *  ldo >= w4a4_lowrank_width(M, K, l1t ? r : -r). */
+ * columns [0, r) and [r, 2r) of out (the branch's ra = 2r).  For
+ * idx != NULL, out = x[:, idx] (M x r, exact).
+ *  x bf16 M x K (row stride ldx <= 2^26 elements, K <= 2^24); out bf16 with
+ *  row stride ldo >= w4a4_lowrank_width(M, K, l1t ? r : -r). */
 int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx,
                          const void* l1t, const int32_t* idx, int64_t r,
                          void* out, int64_t ldo, void* stream);
 
 /* w4a4_lowrank_width -- columns w4a4_lowrank_project needs in its output:
- * 2 P r for a rank-r projection of an M x K input (r > 0; the result is in
- * the first 2r), or |r| for a gather of |r| kept channels (r < 0).
- * Host-only, no device access. */
+ * 2r for a rank-r projection (r > 0), or |r| for a gather of |r| kept
+ * channels (r < 0); M and K do not change it.  Host-only, no device
+ * access. */
 int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r);
 
 /* w4a4_transform_amax -- max |transform(x)| over a whole R x K tensor,
@@ -239,25 +254,6 @@ int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r);
  * static NVFP4 tensor scale g = amax / (6 * 448) (QuantWAMs sec. 4.2:
  * statistics are collected after both transforms).  ``scale`` is 1/s for
  * activations and s for weights; q->fmt is ignored. */
-/* w4a8_linear -- W4A8: INT8 activation codes x INT4 weight codes, the GEMM
- * of the denoising steps whose activations stay at 8 bits while the weights
- * keep their 4-bit codes (QuantWAMs, Experimental Details, quantization
- * configuration; sec. 4.4.3, fixed-intervention rollout scheduling).
- *  a_codes / a_scales   M rows from quantize_act with W4A4_FMT_W4A8
- *           (int8 M x K in the W4A8 layout, fp32[M]).
- *  w_codes / w_scales   N rows from pack_weights with W4A4_FMT_INT4
- *           (packed int4 N x K/2, fp32[N]).
- *  Exact int32 accumulation of int8 x int4 products, then
- *  y = fp32(fp32(acc) * a_scales[m]) * w_scales[n] * alpha, as for INT4.
- *  br, y, y_dtype (I32 = raw accumulators), ldy, workspace and the shape
- *  and alignment rules are those of w4a4_linear; size a workspace with
- *  w4a4_workspace_size(M, N, K, W4A4_FMT_W4A8). */
-int w4a8_linear(const void* a_codes, const void* a_scales,
-                const void* w_codes, const void* w_scales,
-                int64_t M, int64_t N, int64_t K, float alpha,
-                const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
-                void* workspace, size_t workspace_bytes, void* stream);
-
 int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, int64_t ldx,
                         const float* scale, const w4a4_qdesc* q, float* amax_out,
                         void* stream);

@@ -44,11 +44,10 @@ def test_library_exports_every_declared_symbol(ops):
 
 def test_lowrank_width_host_query(ops):
     L = ops.LIB
-    # gather: |r| columns; projection: 2 P r with 1 <= P <= 4, P*64 <= K, more parts for fewer rows
+    # gather: |r| columns; projection: the hi/lo pair, 2r columns
     assert L.w4a4_lowrank_width(1024, 3072, -64) == 64
-    assert L.w4a4_lowrank_width(4096, 5120, 32) == 64           # 256 row blocks: no split
-    assert L.w4a4_lowrank_width(1024, 3072, 32) == 2 * 4 * 32   # 64 row blocks: four parts
-    assert L.w4a4_lowrank_width(50, 128, 24) == 2 * 2 * 24      # parts capped by K / 64
+    assert L.w4a4_lowrank_width(4096, 5120, 32) == 64
+    assert L.w4a4_lowrank_width(1024, 3072, 32) == 64
     assert L.w4a4_lowrank_width(50, 64, 8) == 16
 
 
@@ -177,5 +176,6 @@ def test_lowrank_rejects_bad_arguments(ops):
     assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 8, 8, 16, FAKE2, 2, 16, None) == -4    # y dtype
     assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 4, 8, 16, FAKE2, 1, 16, None) == -1    # ldlw
     assert L.w4a4_lowrank_project(FAKE, 4, 64, 64, FAKE, None, 8, FAKE2, 8, None) == -1           # ldo < 2r
+    assert L.w4a4_lowrank_project(FAKE, 4, 64, 1 << 27, FAKE, None, 8, FAKE2, 16, None) == -2     # ldx too large
     assert L.w4a4_transform_amax(FAKE, 1, 4, 96, 96, None, _q(ops), FAKE2, None) == -2
     assert L.w4a4_transform_amax(FAKE, 1, 4, 128, 128, None, _q(ops), None, None) == -1

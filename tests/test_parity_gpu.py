@@ -242,15 +242,23 @@ def test_lowrank_add_standalone(ops, pipe):
             check_output(_np(y), y0.astype(np.float64) + add, 1e-3 if ydt == torch.float32 else 1e-2)
 
 
-def test_lowrank_project(ops, pipe):
-    case = WL.linear_case(50, 8, 512, seed=41, lowrank=24)
+@pytest.mark.parametrize("M,K,r", [(50, 512, 24), (1, 64, 8), (33, 3072, 40), (130, 4104, 128)])
+def test_lowrank_project(ops, pipe, M, K, r):
+    """T = x L1 as the bf16 hi/lo pair: ragged rows, a rank that is not a
+    multiple of 16, K beyond one round of in-flight steps and not a multiple of 32."""
+    case = WL.linear_case(M, 8, K, seed=41 + r, lowrank=r)
     t = pipe.case_to_device(case)
-    assert ops.lowrank_width(50, 512, 24) >= 96          # few rows: K split in parts
+    assert ops.lowrank_width(M, K, r) == 2 * r
     out = _np(ops.lowrank_project(t["x"], l1t=t["branch"]["l1t"]))
     T = case.x.astype(np.float64) @ case.branch["l1"].astype(np.float64)
-    assert out.shape == (50, 48)
-    recon = out[:, :24].astype(np.float64) + out[:, 24:].astype(np.float64)
+    assert out.shape == (M, 2 * r)
+    recon = out[:, :r].astype(np.float64) + out[:, r:].astype(np.float64)
     assert np.max(np.abs(recon - T)) <= 2.0 ** -15 * np.max(np.abs(T))
+
+
+def test_lowrank_gather(ops, pipe):
+    case = WL.linear_case(50, 8, 512, seed=41, lowrank=24)
+    t = pipe.case_to_device(case)
     idx = torch.tensor([0, 5, 511, 100, 7, 8, 9, 300], dtype=torch.int32, device="cuda")
     g = _np(ops.lowrank_project(t["x"], idx=idx))
     assert np.array_equal(g, case.x[:, [0, 5, 511, 100, 7, 8, 9, 300]])

@@ -201,6 +201,8 @@ static int check_lowrank(const char* fn, const void* x, int64_t M, int64_t K, in
   if (r <= 0 || r > W4A4_MAX_BRANCH) return fail(W4A4_ERR_INVALID_ARG, "%s: r=%lld outside [1, %d]", fn, (long long)r, W4A4_MAX_BRANCH);
   if ((l1t == nullptr) == (idx == nullptr)) return fail(W4A4_ERR_INVALID_ARG, "%s: exactly one of l1t / idx", fn);
   if (K % 8 != 0) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K not a multiple of 8", fn);
+  if (K > (1LL << 24) || ldx > (1LL << 26))   // byte offsets of 16 rows (or r <= 128 rows of L1) fit 32 bits
+    return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K above 2^24 or ldx above 2^26", fn);
   if (ldx < K) return fail(W4A4_ERR_INVALID_ARG, "%s: ldx < K", fn);
   if (M > 0) {
     if (!x) return fail(W4A4_ERR_INVALID_ARG, "%s: x is NULL", fn);
@@ -231,9 +233,9 @@ int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1
 }
 
 int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r) {
-  if (r < 0) return -r;   // gather: r kept channels
-  if (M <= 0 || K <= 0 || r <= 0) return 2 * (r > 0 ? r : 0);
-  return 2 * (int64_t)w4a4::lowrank_parts(M, K) * r;
+  (void)M;
+  (void)K;
+  return r < 0 ? -r : 2 * r;   // gather: |r| kept channels; projection: the hi/lo pair
 }
 
 int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t, const int32_t* idx,

@@ -5,16 +5,16 @@
 // top-K mask, sec. 4.2).
 //
 //  * project: t = x L1 (fp32, v_mfma_f32_16x16x32_bf16 with L1 given
-//    transposed so both operands are K-contiguous).  K is cut into P parts
-//    (enough 16-row x part workgroups to fill the chip); each part's
-//    product is summed over its four waves in LDS and stored in fp32 in the
-//    output row, and a second kernel adds the P parts in order and writes
-//    the bf16 hi/lo pair the GEMM epilogue consumes; or the gather x[:, idx].
+//    transposed so both operands are K-contiguous), one 16 x 16 tile of t
+//    per workgroup with K split over its eight waves and summed in LDS,
+//    written as the bf16 hi/lo pair the GEMM epilogue consumes; or the
+//    gather x[:, idx].
 //  * lowrank_add: the same projection kept in fp32 in LDS, then
 //    y[m, n] += sum_j t[m, j] lw[n, j] on the vector ALUs, one rounding to
 //    the output type.
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace w4a4 {
 
@@ -80,106 +80,85 @@ __device__ void project_block(const uint16_t* x, int64_t ldx, int M, int K, cons
 
 // Number of K parts the projection is split into for M rows: enough
 // 16-row x part workgroups to fill the chip, each part at least 64 deep.
-int lowrank_parts(int64_t M, int64_t K) {
-  const int64_t rb = (M + kRows - 1) / kRows;
-  int64_t p = rb >= 256 ? 1 : (256 + rb - 1) / rb;
-  p = p > 4 ? 4 : p;
-  const int64_t pk = K / 64;
-  p = p > pk ? pk : p;
-  return (int)(p < 1 ? 1 : p);
-}
+// t = x L1 for one 16-row x 16-column tile per workgroup of eight waves;
+// wave w takes the w-th eighth of K.  A wave copies its operand rows into
+// its own LDS area by buffer-to-LDS loads of whole 128-byte row segments
+// (8 rows per instruction, 64 K per step), kProjChunk steps at a time, then
+// reads the MFMA layout back with ds_read_b128: loading that layout straight
+// from global memory touches 16 half-used cache lines per instruction and
+// streams about a third as fast.  Chunk c of a row segment sits at position
+// c ^ (row & 7).  Copies past K or past the last row or column read as
+// zeros.  The eight partial tiles are added in LDS in wave order and
+// written as bf16 hi = bf16(t), lo = bf16(t - hi) into columns c and r + c
+// of out.  One kernel: no partial products leave the workgroup.
+constexpr int kProjWaves = 8;
+constexpr int kProjChunk = 3;                 // 64-deep steps copied per round
+constexpr int kProjStepBytes = 2 * 16 * 128;  // x rows then L1 rows of one step
 
-// t_p = x[:, Kp] L1[Kp, :] for one 16-row block and one K part p, the part
-// split over the four waves (every load of a wave issued before its MFMAs;
-// out-of-range rows and columns read as zeros), summed in LDS, written as
-// bf16 hi/lo into columns [2 p r, 2 p r + 2r) of out.
-template <int TJ>
-__global__ void __launch_bounds__(256) project_parts_kernel(const uint16_t* x, int64_t ldx, int M, int K,
-                                                            const uint16_t* l1t, int r, int parts,
-                                                            uint16_t* out, int64_t ldo) {
-  __shared__ float sT[4][16][TJ * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ void __launch_bounds__(64 * kProjWaves) project_kernel(const uint16_t* x, int64_t ldx, int M, int K,
+                                                                 const uint16_t* l1t, int r, uint16_t* out,
+                                                                 int64_t ldo) {
+  __shared__ __attribute__((aligned(16))) uint8_t area[kProjWaves][kProjChunk * kProjStepBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
-  const int m0 = blockIdx.x * kRows, part = blockIdx.y;
-  const int kp = ((K + parts * 64 - 1) / (parts * 64)) * 64;   // K per part, multiple of 64
-  const int kb = part * kp, ke = min(K, kb + kp);
-  const int kw = kp / 4;                                       // K per wave, multiple of 16
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m0 * ldx, (uint32_t)(max(0, min(kRows, M - m0)) * ldx * 2));
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(l1t, (uint32_t)((int64_t)r * K * 2));
-  v4f acc[TJ];
+  const int m0 = blockIdx.x * kRows, c0 = blockIdx.y * 16;
+  const int64_t xrow = ldx * 2, lrow = (int64_t)K * 2;   // row bytes
+  const v4u rx = rsrc_words(x + (int64_t)m0 * ldx, (uint32_t)(min(kRows, M - m0) * xrow));
+  const v4u rl = rsrc_words(l1t + (int64_t)c0 * K, (uint32_t)(min(16, r - c0) * lrow));
+  const int kw = ((K + 64 * kProjWaves - 1) / (64 * kProjWaves)) * 64;   // K per wave, multiple of 64
+  const int k0 = wave * kw, k1 = min(K, k0 + kw);
+  uint8_t* const a = area[wave];
+  // copy instruction d of a step: rows 8 (d & 1) .. + 7 of x (d < 2) or of
+  // L1 (d >= 2); lane -> row 8 (d & 1) + lane / 8, chunk position lane % 8
+  const int crow = lane >> 3, cpos = lane & 7;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int kc = k0; kc < k1; kc += 64 * kProjChunk) {
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int k0 = kb + wave * kw, k1 = min(ke, k0 + kw);
-  constexpr int U = 4;   // 32-deep steps whose loads are in flight together
-  for (int k = k0; k < k1; k += 32 * U) {
-    uint4 xa[U], lb[U][TJ];
+    for (int u = 0; u < kProjChunk; ++u) {
+      const int k = kc + 64 * u;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kc = k + u * 32 + lq * 8;
-      const bool ok = kc < k1;
-      xa[u] = buf_load16(rx, ok ? (uint32_t)((lr * ldx + kc) * 2) : kOOB);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int col = j * 16 + lr;
-        lb[u][j] = buf_load16(rl, (ok && col < r) ? (uint32_t)(((int64_t)col * K + kc) * 2) : kOOB);
+      for (int d = 0; d < 4; ++d) {
+        const int row = 8 * (d & 1) + crow;
+        const int c = cpos ^ (row & 7);                  // logical chunk held at this position
+        const bool ok = k + 8 * c < k1;                  // chunk of 8 elements inside this wave's range
+        const int64_t rb = d < 2 ? xrow : lrow;
+        dma16(d < 2 ? rx : rl, a + u * kProjStepBytes + d * 1024,
+              ok ? (uint32_t)(row * rb + (int64_t)(k + 8 * c) * 2) : kOOB, 0u);
       }
     }
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < kProjChunk; ++u) {
+      const uint8_t* st = a + u * kProjStepBytes;
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xa[u]), __builtin_bit_cast(v8bf, lb[u][j]),
-                                                         acc[j], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const int pos = ((4 * h + lq) ^ (lr & 7)) * 16;
+        const uint4 xa = *reinterpret_cast<const uint4*>(st + lr * 128 + pos);
+        const uint4 lb = *reinterpret_cast<const uint4*>(st + 2048 + lr * 128 + pos);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, lb),
+                                                      acc, 0, 0, 0);
+      }
+    }
+    // the next round's copies overwrite this area only after these reads returned
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
+  __syncthreads();   // every wave is done with its copy area; reuse it for the partial tiles
+  float (*sT)[16][16] = reinterpret_cast<float (*)[16][16]>(&area[0][0]);
 #pragma unroll
-  for (int j = 0; j < TJ; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sT[wave][lq * 4 + q][j * 16 + lr] = acc[j][q];
+  for (int q = 0; q < 4; ++q) sT[wave][lq * 4 + q][lr] = acc[q];
   __syncthreads();
-  for (int e = tid; e < 16 * r; e += 256) {
-    const int row = e / r, col = e % r, m = m0 + row;
-    if (m >= M) continue;
-    const float t = sT[0][row][col] + sT[1][row][col] + sT[2][row][col] + sT[3][row][col];
-    if (parts == 1) {
+  if (tid < 256) {
+    const int row = tid >> 4, col = tid & 15, m = m0 + row, c = c0 + col;
+    if (m < M && c < r) {
+      float t = sT[0][row][col];
+#pragma unroll
+      for (int w = 1; w < kProjWaves; ++w) t = t + sT[w][row][col];
       const uint32_t hi = f32_to_bf16_bits(t);
       const float lo = t - bf16_bits_to_f32(hi);
       uint16_t* o = out + (int64_t)m * ldo;
-      o[col] = (uint16_t)hi;
-      o[r + col] = (uint16_t)f32_to_bf16_bits(lo);
-    } else {  // fp32 partial p at element p r + col of the row (the row holds 2 P r bf16 = P r fp32)
-      reinterpret_cast<float*>(out + (int64_t)m * ldo)[part * r + col] = t;
-    }
-  }
-}
-
-// Sum of the P fp32 partial products of each row (in part order), written
-// in place as the bf16 hi/lo pair in columns [0, 2r): one wave per row; every
-// lane reads its partials before any lane of the wave writes.
-__global__ void __launch_bounds__(64) project_sum_kernel(int M, int r, int parts, uint16_t* out, int64_t ldo) {
-  const int64_t m = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* pr = reinterpret_cast<const float*>(out + m * ldo);
-  float t[2] = {0.f, 0.f};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int col = lane + 64 * h;
-    if (col < r) {
-      float acc = pr[col];
-      for (int p = 1; p < parts; ++p) acc = acc + pr[p * r + col];
-      t[h] = acc;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);      // all of this wave's reads returned
-  __builtin_amdgcn_wave_barrier();
-  uint16_t* o = out + m * ldo;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int col = lane + 64 * h;
-    if (col < r) {
-      const uint32_t hi = f32_to_bf16_bits(t[h]);
-      const float lo = t[h] - bf16_bits_to_f32(hi);
-      o[col] = (uint16_t)hi;
-      o[r + col] = (uint16_t)f32_to_bf16_bits(lo);
+      o[c] = (uint16_t)hi;
+      o[r + c] = (uint16_t)f32_to_bf16_bits(lo);
     }
   }
 }
@@ -250,15 +229,8 @@ hipError_t launch_lowrank_project(const uint16_t* x, int64_t M, int64_t K, int64
                        out, ldo);
     return hipGetLastError();
   }
-  const int parts = lowrank_parts(M, K);
-  dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)parts);
-#define W4A4_PROJ(T)                                                                                       \
-  hipLaunchKernelGGL((project_parts_kernel<T>), grid, dim3(256), 0, st, x, ldx, (int)M, (int)K, l1t, r, parts, \
-                     out, ldo)
-  W4A4_TJ_SWITCH(r, W4A4_PROJ)
-#undef W4A4_PROJ
-  if (parts > 1)
-    hipLaunchKernelGGL(project_sum_kernel, dim3((unsigned)M), dim3(64), 0, st, (int)M, r, parts, out, ldo);
+  const dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)((r + 15) / 16));
+  hipLaunchKernelGGL(project_kernel, grid, dim3(64 * kProjWaves), 0, st, x, ldx, (int)M, (int)K, l1t, r, out, ldo);
   return hipGetLastError();
 }
 

@@ -46,7 +46,6 @@ size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st);
 
 // branch.hip ----------------------------------------------------------------
-int lowrank_parts(int64_t M, int64_t K);
 hipError_t launch_lowrank_project(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   const uint16_t* l1t, const int32_t* idx, int r,
                                   uint16_t* out, int64_t ldo, hipStream_t st);
