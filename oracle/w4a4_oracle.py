@@ -25,7 +25,9 @@ Sources (the pages this restates; no text is quoted):
   dense matrix products.
 * QuantWAMs, Experimental Details (quantization configuration) and
   sec. 4.4.3: some denoising steps keep their activations at 8 bits while
-  the weights stay at 4 bits (W4A8).
+  the weights stay at 4 bits (W4A8); sec. 4.2: upgraded layers run FP8
+  W8A8 (read here as OCP E4M3 codes with per-token and per-channel steps
+  amax/448, like the INT8 sibling).
 
 Readings where the pages are silent (each also listed in the design notes):
 
@@ -206,6 +208,31 @@ def e4m3_encode(v) -> np.ndarray:
     return _nearest_code(v, _E4M3_GRID).astype(np.uint8)
 
 
+def e4m3_encode_signed(v) -> np.ndarray:
+    """Sign-magnitude E4M3FN code: the magnitude rounded to nearest (ties to
+    the even code) onto the grid, saturating at 448; anything that rounds
+    to zero encodes +0 (0x00)."""
+    v = np.asarray(v, dtype=F64)
+    mag_code = _nearest_code(np.abs(v), _E4M3_GRID)
+    sign = ((v < 0) & (mag_code != 0)).astype(np.int64)
+    return (sign << 7 | mag_code).astype(np.uint8)
+
+
+def quantize_fp8(y: np.ndarray):
+    """FP8 W8A8 quantizer of the rows of y (QuantWAMs sec. 4.2: upgraded
+    layers run FP8 W8A8).  The reading: one step per row, as for INT8,
+    step = fp32(amax / 448), v = fp32(y / step), code = E4M3(v); an
+    all-zero row has step 0 and codes 0.  Returns (codes uint8, step fp32,
+    v fp32)."""
+    y = np.asarray(y, dtype=F32)
+    amax = np.abs(y).max(axis=1)
+    step = (amax / F32(E4M3_MAX)).astype(F32)
+    v = np.zeros_like(y)
+    nz = step > 0
+    v[nz] = (y[nz] / step[nz, None]).astype(F32)
+    return e4m3_encode_signed(v), step, v
+
+
 def nvfp4_tensor_scale(amax) -> np.float32:
     """Static per-tensor scale g = fp32(amax / (6 * 448)); 1 if amax is 0."""
     amax = F32(amax)
@@ -315,6 +342,14 @@ def dequant_epilogue(acc, step_a, step_w) -> np.ndarray:
     return np.asarray(acc, F64) * np.asarray(step_a, F64)[:, None] * np.asarray(step_w, F64)[None, :]
 
 
+def fp8_gemm(codes_a: np.ndarray, codes_w: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k value(a[m, k]) * value(w[n, k]) over E4M3 codes,
+    float64 and exact: every product is a multiple of 2^-18 below 2^18, so
+    for K <= 2^16 every partial sum fits 53 bits in any order."""
+    assert codes_a.shape[1] <= 1 << 16
+    return e4m3_value(codes_a) @ e4m3_value(codes_w).T
+
+
 def lowrank_branch(x, l1, lw) -> np.ndarray:
     """Q-WAM 16-bit branch: (x L1) L2 with L2 = lw^T, float64."""
     return (np.asarray(x, F64) @ np.asarray(l1, F64)) @ np.asarray(lw, F64).T
@@ -342,6 +377,9 @@ def quantize_operand(x, scale, fmt: str, fwht_block=FWHT_BLOCK,
         packed = {"int4": pack_nibbles, "int8": lambda c: c.view(np.uint8),
                   "w4a8": pack_w4a8_activations}[fmt](codes)
         return {"y": y, "codes": codes, "scales": step, "v": v, "packed": packed}
+    if fmt == "fp8":
+        codes, step, v = quantize_fp8(y)
+        return {"y": y, "codes": codes, "scales": step, "v": v, "packed": codes}
     if fmt == "nvfp4":
         if g is None:
             g = nvfp4_tensor_scale(np.abs(y).max() if y.size else 0.0)
@@ -363,7 +401,7 @@ def transformed_amax(x, scale, fwht_block=FWHT_BLOCK, order="smooth_then_rotate"
 # configuration; sec. 4.4.3), with the same 4-bit weight codes as W4A4; its
 # activations are the int8 quantization, stored in the W4A8 layout.
 OPERAND_FORMATS = {"int4": ("int4", "int4"), "int8": ("int8", "int8"),
-                   "nvfp4": ("nvfp4", "nvfp4"), "w4a8": ("w4a8", "int4")}
+                   "nvfp4": ("nvfp4", "nvfp4"), "w4a8": ("w4a8", "int4"), "fp8": ("fp8", "fp8")}
 
 
 def linear(case, order="smooth_then_rotate", g_a=None, g_w=None) -> dict:
@@ -377,6 +415,10 @@ def linear(case, order="smooth_then_rotate", g_a=None, g_w=None) -> dict:
     out = {"a": A, "w": W}
     if case.fmt in ("int4", "int8", "w4a8"):
         acc = int_gemm(A["codes"], W["codes"])
+        y = dequant_epilogue(acc, A["scales"], W["scales"])
+        out["acc"] = acc
+    elif case.fmt == "fp8":
+        acc = fp8_gemm(A["codes"], W["codes"])
         y = dequant_epilogue(acc, A["scales"], W["scales"])
         out["acc"] = acc
     else:

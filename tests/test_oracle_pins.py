@@ -479,3 +479,77 @@ def test_w4a8_activation_layout_is_the_int4_unpack_order():
     od = (words & np.uint32(0xF0F0F0F0)).astype("<u4")
     seq = np.stack([ev, od], axis=-1).reshape(5, -1).view(np.int8).astype(np.int64) // 16
     assert np.array_equal(seq, O.pack_w4a8_activations(c).view(np.int8))
+
+
+# --------------------------------------------------------------------- FP8
+def test_e4m3_signed_encode_roundtrip_sign_and_zero():
+    codes = np.arange(256)
+    finite = (codes & 0x7F) != 0x7F
+    enc = O.e4m3_encode_signed(O.e4m3_value(codes[finite]))
+    assert np.array_equal(enc, np.where(codes[finite] == 0x80, 0, codes[finite]))   # -0 encodes +0
+    rng = np.random.default_rng(8)
+    v = rng.uniform(-460.0, 460.0, 4000) * np.exp2(rng.integers(-12, 1, 4000))
+    e = O.e4m3_encode_signed(v)
+    mag = O.e4m3_encode(np.abs(v))
+    assert np.array_equal(e & 0x7F, mag)
+    assert np.array_equal(e >> 7, ((v < 0) & (mag != 0)).astype(np.uint8))
+    # half the smallest subnormal (2^-10) ties to the even code 0; anything below rounds to +0
+    assert O.e4m3_encode_signed(np.array([0.0, -0.0, -2.0 ** -10, 2.0 ** -11, -2.0 ** -11])).tolist() == [0] * 5
+    # nearest by brute force over the whole grid, ties to the even code
+    grid = O.e4m3_value(np.arange(0x7F))
+    for x in np.abs(v[:300]):
+        d = np.abs(grid - min(x, 448.0))
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+        assert O.e4m3_encode(np.array([x]))[0] == want
+
+
+def test_fp8_quantizer_invariants():
+    rng = np.random.default_rng(9)
+    y = (rng.standard_normal((6, 96)) * np.array([1, 1e3, 1e-4, 1, 7, 0.3])[:, None]).astype(np.float32)
+    y[3] = 0
+    codes, step, v = O.quantize_fp8(y)
+    dq = O.e4m3_value(codes) * step.astype(np.float64)[:, None]
+    nz = step > 0
+    assert not nz[3] and np.all(codes[3] == 0)
+    assert np.all(np.abs(O.e4m3_value(codes[nz])).max(axis=1) == 448.0)
+    # E4M3 keeps 3 mantissa bits: half-spacing 2^-4 relative in the normal range,
+    # 2^-10 (in units of the step) in the subnormal range
+    bound = 2.0 ** -4 * np.abs(y) + 2.0 ** -10 * step.astype(np.float64)[:, None]
+    assert np.all(np.abs(dq - y) <= bound * (1 + 1e-6))
+    assert np.all((dq == 0) | (np.sign(dq) == np.sign(y)))
+
+
+def test_fp8_gemm_is_exact():
+    """The float64 sum of E4M3 products equals the exact rational sum."""
+    from fractions import Fraction
+    rng = np.random.default_rng(10)
+    ca = rng.integers(0, 256, size=(2, 40)).astype(np.uint8)
+    cw = rng.integers(0, 256, size=(3, 40)).astype(np.uint8)
+    ca[(ca & 0x7F) == 0x7F] = 0x7E
+    cw[(cw & 0x7F) == 0x7F] = 0xFE
+    acc = O.fp8_gemm(ca, cw)
+    va, vw = O.e4m3_value(ca), O.e4m3_value(cw)
+    for m in range(2):
+        for n in range(3):
+            exact = sum(Fraction(float(va[m, k])) * Fraction(float(vw[n, k])) for k in range(40))
+            assert Fraction(float(acc[m, n])) == exact
+
+
+def test_fp8_linear_exact_on_grid_values():
+    """Rows whose values lie on the E4M3 grid and peak at 448 quantize with
+    step 1 to themselves, so FP8 W8A8 gives x w^T exactly."""
+    rng = np.random.default_rng(11)
+    M, N, K = 4, 5, 64
+
+    def grid_rows(R):
+        c = rng.integers(0, 0x7F, size=(R, K)) | (rng.integers(0, 2, size=(R, K)) << 7)
+        c[np.arange(R), rng.integers(0, K, R)] = 0x7E            # 448 in every row
+        return O.e4m3_value(c)
+
+    x, w = grid_rows(M), grid_rows(N)
+    out = O.linear(_plain_case(x, w, "fp8"))
+    assert np.all(out["a"]["scales"] == 1) and np.all(out["w"]["scales"] == 1)
+    assert np.array_equal(O.e4m3_value(out["a"]["codes"]), x)
+    assert np.array_equal(out["y"], x @ w.T)
+    assert out["a"]["packed"].shape == (M, K) and out["a"]["packed"].dtype == np.uint8
