@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-PEAK_TFLOPS = {"i8": 5000.0, "f16": 2500.0, "bf16": 2500.0, "fp4": 10100.0}
+PEAK_TFLOPS = {"i8": 5000.0, "fp8": 5000.0, "f16": 2500.0, "bf16": 2500.0, "fp4": 10100.0}
 
 
 def parse():
@@ -35,7 +35,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="batch1", choices=["batch1", "video4096", "prefill", "lowrank", "tiny", "batch1_a8", "video4096_a8"])
+    p.add_argument("--workload", default="batch1", choices=["batch1", "video4096", "prefill", "lowrank", "tiny", "batch1_a8", "video4096_a8",
+                                                      "batch1_fp8", "video4096_fp8"])
     p.add_argument("--no-also", action="store_true", help="skip the secondary 4096-token measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample duration")
@@ -68,8 +69,8 @@ def gemm_bytes(case):
     """Algorithmic HBM bytes of one GEMM launch: packed weight and activation
     codes, their scales, the output and the branch operands."""
     M, N, K = case.M, case.N, case.K
-    code_a = {"int4": 0.5, "int8": 1.0, "nvfp4": 0.5, "w4a8": 1.0}[case.fmt]
-    code_w = {"int4": 0.5, "int8": 1.0, "nvfp4": 0.5, "w4a8": 0.5}[case.fmt]
+    code_a = {"int4": 0.5, "int8": 1.0, "nvfp4": 0.5, "w4a8": 1.0, "fp8": 1.0}[case.fmt]
+    code_w = {"int4": 0.5, "int8": 1.0, "nvfp4": 0.5, "w4a8": 0.5, "fp8": 1.0}[case.fmt]
     if case.fmt == "nvfp4":
         scales = (M + N) * K / 16
     else:
@@ -134,8 +135,8 @@ def dominant_kernel_time(torch, case, layer, t, steps):
         br = ops.branch_desc(layer.branch_operand(case.M, t["x"].device), layer.branch["lw"])
 
     def gemm():
-        if case.fmt in ("int8", "w4a8"):
-            fn = ops.w8a8_linear if case.fmt == "int8" else ops.w4a8_linear
+        if case.fmt in ("int8", "w4a8", "fp8"):
+            fn = {"int8": ops.w8a8_linear, "w4a8": ops.w4a8_linear, "fp8": ops.fp8_linear}[case.fmt]
             fn(b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K, branch=br,
                y=b["y"], workspace=b["ws"])
         else:
@@ -179,6 +180,8 @@ def cpu_baseline(names, target_s):
         A = O.quantize_operand(c.x, c.inv_s, O.OPERAND_FORMATS[c.fmt][0], g=g_a)
         if c.fmt in ("int4", "int8", "w4a8"):
             y = O.dequant_epilogue(O.int_gemm(A["codes"], W["codes"]), A["scales"], W["scales"])
+        elif c.fmt == "fp8":
+            y = O.dequant_epilogue(O.fp8_gemm(A["codes"], W["codes"]), A["scales"], W["scales"])
         else:
             y = O.dequantize_nvfp4(A["codes"], A["scales"], A["g"]) @ O.dequantize_nvfp4(
                 W["codes"], W["scales"], W["g"]).T
@@ -220,6 +223,11 @@ WORKLOADS = {
                   "W4A8 64x2048x2048 + W4A8 64x2048x8192, smoothing + FWHT-64 + per-token int8"),
     "video4096_a8": (["video_w4a8"], "4096-token video-latent projection at 8-bit activations "
                                      "(protected denoising step), W4A8 4096x5120x5120 + 64 kept bf16 channels"),
+    "batch1_fp8": (["decode_w4a4", "decode_fp8"],
+                   "batch-1 64-token action-expert step with the upgraded projection in FP8: W4A4 64x2048x2048 "
+                   "+ FP8 (E4M3) W8A8 64x2048x8192"),
+    "video4096_fp8": (["video_fp8"], "4096-token video-latent projection upgraded to FP8 (E4M3) W8A8 "
+                                     "4096x5120x5120 + 64 kept bf16 channels"),
 }
 
 
@@ -235,7 +243,7 @@ def measure(torch, wl, steps, warmup):
     q_ms = quant_kernel_time(torch, c, layer, t, ksteps)
     flop_k = 2.0 * c.M * c.N * c.K
     bytes_k = gemm_bytes(c)
-    mtype = {"int4": "i8", "int8": "i8", "nvfp4": "f16", "w4a8": "i8"}[c.fmt]
+    mtype = {"int4": "i8", "int8": "i8", "nvfp4": "f16", "w4a8": "i8", "fp8": "fp8"}[c.fmt]
     intensity = flop_k / bytes_k
     ridge = PEAK_TFLOPS[mtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
     if intensity < ridge:
@@ -245,11 +253,11 @@ def measure(torch, wl, steps, warmup):
                 "unit": "TFLOP/s" if mtype != "i8" else "TOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = recorded_traffic(wl)
-    entry = {"int8": "w8a8_linear", "w4a8": "w4a8_linear"}.get(c.fmt, "w4a4_linear")
+    entry = {"int8": "w8a8_linear", "w4a8": "w4a8_linear", "fp8": "fp8_linear"}.get(c.fmt, "w4a4_linear")
     roof["kernel"] = f"{entry} {c.fmt} {c.M}x{c.N}x{c.K}"
     roof["kernel_us"] = k_ms * 1e3
     roof["algorithmic_bytes"] = bytes_k
-    qbytes = c.M * c.K * (2 if c.x_dtype == "bf16" else 4) + c.M * c.K * (1 if c.fmt in ("int8", "w4a8") else 0.5) + (
+    qbytes = c.M * c.K * (2 if c.x_dtype == "bf16" else 4) + c.M * c.K * (1 if c.fmt in ("int8", "w4a8", "fp8") else 0.5) + (
         c.M * c.K / 16 if c.fmt == "nvfp4" else 4 * c.M)
     quant = {"kernel": f"quantize_act {layer.a_fmt} {c.M}x{c.K}", "us": q_ms * 1e3,
              "achieved_GBs": qbytes / (q_ms * 1e-3) / 1e9, "frac_hbm": qbytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -283,6 +291,8 @@ DOMINANT = {
     "batch1": ("w8a8_linear int8 64x2048x8192", ["gemm_int_decode_kernel<1, 2, 1>"]),
     "batch1_a8": ("w4a8_linear w4a8 64x2048x8192", ["gemm_int_decode_kernel<2, 2, 1>"]),
     "video4096_a8": ("w4a8_linear w4a8 4096x5120x5120", ["gemm_wide_kernel<3,"]),
+    "batch1_fp8": ("fp8_linear fp8 64x2048x8192", ["gemm_int_decode_kernel<3, 2, 1>"]),
+    "video4096_fp8": ("fp8_linear fp8 4096x5120x5120", ["gemm_wide_kernel<4,"]),
     "video4096": ("w4a4_linear nvfp4 4096x5120x5120", ["gemm_wide_kernel<2,"]),
     "prefill": ("w4a4_linear int4 512x16384x2048", ["gemm_wide_kernel<0, 4, 4, 2, 4, 1>"]),
     "lowrank": ("w4a4_linear int4 1024x3072x3072", ["gemm_wide_kernel<0, 4, 6, 2, 1, 2>"]),
@@ -411,7 +421,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": r["roofline"]["kernel"].startswith("w4a4_linear nvfp4") and "f16" or "i8",
+        "dtype": {"nvfp4": "f16", "fp8": "fp8"}.get(r["roofline"]["kernel"].split()[1], "i8"),
         "data": "synthetic (seeded; shapes and outlier statistics of the workload descriptions)",
         "config": {"workload": r["desc"], "projections": r["names"],
                    "launch": "eager" if a.eager else f"HIP graph of {PER_GRAPH} steps, replayed"},

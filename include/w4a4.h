@@ -38,6 +38,8 @@
  *           (the order in which INT4 weight codes unpack to bytes, so the
  *           matrix cores take both operands without reordering).
  *           scales: fp32[R].  W4A8 weights are INT4.
+ *  - FP8  : R x K bytes of OCP E4M3 (E4M3FN) codes, zero encoded +0.
+ *           scales: fp32[R], step = fp32(amax/448).
  *  - NVFP4: R x K/2 bytes of E2M1 nibbles (same nibble order; sign bit 3,
  *           exponent bits 2..1 with bias 1, mantissa bit 0).  scales:
  *           R x K/16 bytes of OCP E4M3 (E4M3FN, bias 7, max 448), one per 16
@@ -69,7 +71,7 @@ typedef enum w4a4_status {
 } w4a4_status;
 
 /* Code formats. */
-enum { W4A4_FMT_INT4 = 0, W4A4_FMT_INT8 = 1, W4A4_FMT_NVFP4 = 2, W4A4_FMT_W4A8 = 3 };
+enum { W4A4_FMT_INT4 = 0, W4A4_FMT_INT8 = 1, W4A4_FMT_NVFP4 = 2, W4A4_FMT_W4A8 = 3, W4A4_FMT_FP8 = 4 };
 /* W4A4_FMT_W4A8 names the pairing of INT8 activation codes with INT4 weight
  * codes: quantize_act writes the activations in the W4A8 layout, the
  * weights come from pack_weights with W4A4_FMT_INT4 (pack_weights rejects
@@ -131,8 +133,9 @@ typedef struct w4a4_branch {
  *  q          format, rotation, order; NVFP4 needs q->tensor_scale.
  *  codes      output, packed layout of q->fmt (R = M).
  *  scales     output: fp32[M] steps (INT4/INT8; step = fp32(amax/7) or
- *             fp32(amax/127), codes = clamp(rne(fp32(y/step)))) or
- *             M x K/16 E4M3 bytes (NVFP4).
+ *             fp32(amax/127), codes = clamp(rne(fp32(y/step)))), fp32[M]
+ *             (FP8; step = fp32(amax/448), codes = E4M3 rne of
+ *             fp32(y/step)) or M x K/16 E4M3 bytes (NVFP4).
  * Shape rules: K % 16 == 0; K % 64 == 0 when fwht_block == 64.
  * Alignment: x, codes 16-byte aligned; ldx * elem_size % 16 == 0.
  */
@@ -213,6 +216,20 @@ int w4a8_linear(const void* a_codes, const void* a_scales,
                 const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* fp8_linear -- FP8 W8A8 (QuantWAMs sec. 4.2: upgraded layers run FP8
+ * W8A8 kernels).  a_codes / w_codes: OCP E4M3 codes from quantize_act /
+ * pack_weights with W4A4_FMT_FP8, fp32 steps per row.  The products of the
+ * codes' values are exact and accumulate in fp32 (order unspecified), then
+ * y = fp32(fp32(acc * a_scales[m]) * w_scales[n]) * alpha.  br, y (F32 or
+ * BF16; no I32), ldy, workspace and the shape and alignment rules are those
+ * of w4a4_linear; size a workspace with w4a4_workspace_size(M, N, K,
+ * W4A4_FMT_FP8). */
+int fp8_linear(const void* a_codes, const void* a_scales,
+               const void* w_codes, const void* w_scales,
+               int64_t M, int64_t N, int64_t K, float alpha,
+               const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
+               void* workspace, size_t workspace_bytes, void* stream);
+
 /* lowrank_add -- standalone 16-bit branch, y += (x L1) L2 or
  * y += x[:, idx] W_idx^T (Q-WAM abstract: 16-bit low-rank branch as a dense
  * product; QuantWAMs sec. 3.1 / 4.2: kept channels on a BF16 path).
@@ -258,8 +275,8 @@ int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, in
                         const float* scale, const w4a4_qdesc* q, float* amax_out,
                         void* stream);
 
-/* Bytes of workspace w4a4_linear / w8a8_linear / w4a8_linear use for
- * (M, N, K, fmt); 0 when the shape runs without one. */
+/* Bytes of workspace w4a4_linear / w8a8_linear / w4a8_linear / fp8_linear
+ * use for (M, N, K, fmt); 0 when the shape runs without one. */
 size_t w4a4_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt);
 
 const char* w4a4_status_string(int status);

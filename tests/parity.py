@@ -1,8 +1,8 @@
 """Comparison helpers for the GPU-vs-oracle parity tests.
 
-Bars: packed codes and E4M3 scale bytes equal, where any mismatch is
-counted and admissible only if the oracle's pre-rounding value lies within
-1e-6 relative of a rounding boundary; fp32 steps equal; raw int32
+Bars: packed codes (int, E2M1, E4M3) and E4M3 scale bytes equal, where any
+mismatch is counted and admissible only if the oracle's pre-rounding value
+lies within 1e-6 relative of a rounding boundary; fp32 steps equal; raw int32
 accumulators equal; outputs within ``rtol * (|y_ref| + rms(y_ref))``
 elementwise (rtol 1e-3 for fp32 output, 1e-2 for bf16).
 """
@@ -35,6 +35,8 @@ def unpack_codes(fmt, packed):
         return packed.view(np.int8)
     if fmt == "w4a8":
         return O.unpack_w4a8_activations(packed)
+    if fmt == "fp8":
+        return packed.view(np.uint8)
     return O.unpack_nibbles(packed.view(np.uint8))
 
 
@@ -61,7 +63,10 @@ def check_operand(fmt, gpu_codes, gpu_scales, ref, rows=None, what="operand"):
     assert np.array_equal(np.asarray(gpu_scales, np.float32), rs), f"{what}: fp32 steps differ"
     bad = codes != rc
     if bad.any():
-        assert near_half_integer(rv[bad]).all(), f"{what}: {int(bad.sum())} code mismatches outside the band"
+        if fmt == "fp8":   # E4M3 rounding boundaries: midpoints of the magnitude grid
+            assert near_boundary(rv[bad], E4M3_BOUNDS).all(), f"{what}: {int(bad.sum())} E4M3 mismatches outside the band"
+        else:
+            assert near_half_integer(rv[bad]).all(), f"{what}: {int(bad.sum())} code mismatches outside the band"
     return int(bad.sum())
 
 

@@ -28,7 +28,8 @@ def ops():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "lowrank_add"]:
+    for n in ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "fp8_linear",
+              "lowrank_add"]:
         assert n in names
 
 
@@ -95,13 +96,16 @@ def test_quantize_act_rejects_bad_arguments(ops):
     assert L.pack_weights(FAKE, 1, 4, 128, 128, None, _q(ops, fmt=3), FAKE2, FAKE2, None) == -4
     assert L.quantize_act(FAKE, 1, 4, 96, 96, None, _q(ops, fmt=3), FAKE2, FAKE2, None) == -2
     assert L.quantize_act(None, 1, 0, 128, 128, None, _q(ops, fmt=3), None, None, None) == 0
+    assert L.quantize_act(None, 1, 0, 128, 128, None, _q(ops, fmt=4), None, None, None) == 0
+    assert L.pack_weights(FAKE, 1, 4, 96, 96, None, _q(ops, fmt=4), FAKE2, FAKE2, None) == -2
+    assert L.quantize_act(FAKE, 1, 4, 128, 128, None, _q(ops, fmt=5), FAKE2, FAKE2, None) == -4
 
 
 def _lin(ops, fn="w4a4_linear", M=8, N=8, K=128, fmt=0, alpha=1.0, br=None, y=FAKE, ydt=1, ldy=None,
          ws=None, wsb=0, a=FAKE, sa=FAKE, w=FAKE, sw=FAKE):
     ldy = N if ldy is None else ldy
     brp = None if br is None else ctypes.byref(br)
-    if fn in ("w8a8_linear", "w4a8_linear"):
+    if fn in ("w8a8_linear", "w4a8_linear", "fp8_linear"):
         return getattr(ops.LIB, fn)(a, sa, w, sw, M, N, K, alpha, brp, y, ydt, ldy, ws, wsb, None)
     return ops.LIB.w4a4_linear(a, sa, w, sw, M, N, K, fmt, alpha, brp, y, ydt, ldy, ws, wsb, None)
 
@@ -116,6 +120,11 @@ def test_linear_rejects_bad_arguments(ops):
     assert _lin(ops, fn="w4a8_linear", K=96) == -2
     assert _lin(ops, fn="w4a8_linear", a=MISAL) == -3
     assert _lin(ops, fn="w4a8_linear", ydt=5) == -4
+    assert _lin(ops, fmt=4) == -4                 # FP8 codes go through fp8_linear
+    assert _lin(ops, fn="fp8_linear", ydt=2) == -4   # no raw accumulators for FP8
+    assert _lin(ops, fn="fp8_linear", K=96) == -2
+    assert _lin(ops, fn="fp8_linear", w=MISAL) == -3
+    assert _lin(ops, fn="fp8_linear", M=0, a=None, sa=None, y=None) == 0
     assert _lin(ops, fmt=2, ydt=2) == -4          # raw accumulators only for integer formats
     assert _lin(ops, ydt=5) == -4
     assert _lin(ops, ldy=4) == -1
@@ -158,7 +167,9 @@ def test_workspace_sizes(ops):
     assert L.w4a4_workspace_size(9, 768, 8192, 3) > 0             # W4A8 decode splits like INT4
     assert L.w4a4_workspace_size(64, 2048, 8192, 3) == 0
     assert L.w4a4_workspace_size(512, 5120, 5120, 3) == 0         # many tokens: tile kernel
-    assert L.w4a4_workspace_size(9, 768, 8192, 4) == 0            # unknown format
+    assert L.w4a4_workspace_size(9, 768, 8192, 4) > 0             # FP8 decode splits like INT8
+    assert L.w4a4_workspace_size(64, 512, 8192, 4) == L.w4a4_workspace_size(64, 512, 8192, 1)
+    assert L.w4a4_workspace_size(9, 768, 8192, 5) == 0            # unknown format
     assert L.w4a4_workspace_size(64, 256, 1024, 0) == 0           # small weight: no split
     assert L.w4a4_workspace_size(16, 256, 256, 0) == 0            # a single K split
     assert L.w4a4_workspace_size(0, 2048, 2048, 0) == 0

@@ -51,10 +51,10 @@ def _sides(fmt):
 
 
 def _raw_linear(ops, fmt, a, sa, w, sw, K, **kw):
-    """The integer linear entry point for ``fmt`` (int4, int8, w4a8)."""
+    """The linear entry point for ``fmt`` (int4, int8, w4a8, fp8)."""
     if fmt == "int4":
         return ops.w4a4_linear(a, sa, w, sw, K, "int4", **kw)
-    fn = ops.w8a8_linear if fmt == "int8" else ops.w4a8_linear
+    fn = {"int8": ops.w8a8_linear, "w4a8": ops.w4a8_linear, "fp8": ops.fp8_linear}[fmt]
     return fn(a, sa, w, sw, K, **kw)
 
 
@@ -92,6 +92,13 @@ SMALL = [
     ("w4a8_lowrank", 90, 200, 384, "w4a8", "bf16", dict(n_outliers=6, outlier_gain=25.0, lowrank=16)),
     ("w4a8_outlier", 33, 130, 320, "w4a8", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=8)),
     ("w4a8_long_rows", 5, 40, 4160, "w4a8", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
+    # FP8 (OCP E4M3) W8A8
+    ("fp8_ragged", 70, 96, 448, "fp8", "bf16", dict(n_outliers=6, outlier_gain=15.0)),
+    ("fp8_tiles", 160, 300, 512, "fp8", "bf16", dict(n_outliers=8, outlier_gain=15.0, row_gain_sigma=0.5)),
+    ("fp8_f32", 16, 256, 256, "fp8", "f32", dict(n_outliers=4, outlier_gain=20.0)),
+    ("fp8_lowrank", 90, 200, 384, "fp8", "bf16", dict(n_outliers=6, outlier_gain=25.0, lowrank=16)),
+    ("fp8_outlier", 33, 130, 320, "fp8", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=8)),
+    ("fp8_long_rows", 5, 40, 4160, "fp8", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
 ]
 
 
@@ -160,6 +167,53 @@ def test_extreme_codes_do_not_overflow(ops, fmt, val_a, val_w):
     ws = ops.make_workspace(M, N, K, fmt)
     _raw_linear(ops, fmt, a, ones_m, w, ones_n, K, y=y, workspace=ws)
     assert np.all(_np(y) == val_a * val_w * K)
+
+
+def _fp8_codes(rng, R, K):
+    c = rng.integers(0, 256, size=(R, K), dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] ^= 0x01     # no NaN codes
+    return c
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (17, 33, 192), (64, 2048, 2048), (64, 512, 8192),
+                                   (9, 768, 8192), (20, 512, 4096), (130, 260, 320), (300, 100, 64),
+                                   (512, 512, 4096), (40, 4096, 4160)])
+@pytest.mark.parametrize("split", [False, True])
+def test_fp8_accumulation(ops, M, N, K, split):
+    """FP8 GEMM on random E4M3 codes with unit steps and fp32 output, few-token
+    (with and without split K) and many-token kernels.  The fp8 matrix
+    instruction adds its products with its own internal precision (measured:
+    errors near 2^-15 of sum |products|, above fp32 rounding), so the bar is
+    2^-12 of sum |products| per output: a wrong pairing of codes, a dropped
+    term or a lost partial tile is of the order of sum |products| itself."""
+    rng = np.random.default_rng(M * 5 + N * 3 + K)
+    a_b, w_b = _fp8_codes(rng, M, K), _fp8_codes(rng, N, K)
+    exact = O.fp8_gemm(a_b, w_b)
+    absum = np.abs(O.e4m3_value(a_b)) @ np.abs(O.e4m3_value(w_b)).T
+    a, w = torch.from_numpy(a_b).cuda(), torch.from_numpy(w_b).cuda()
+    ones_m, ones_n = torch.ones(M, device="cuda"), torch.ones(N, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = ops.make_workspace(M, N, K, "fp8") if split else None
+    if split and ws is None:
+        pytest.skip("shape runs without a workspace")
+    ops.fp8_linear(a, ones_m, w, ones_n, K, y=y, workspace=ws)
+    err = np.abs(_np(y).astype(np.float64) - exact)
+    _report("fp8_accumulation", M=M, N=N, K=K, split=split, worst_rel=f"{np.max(err / absum):.3g}")
+    assert np.all(err <= 2.0 ** -12 * absum)
+
+
+@pytest.mark.parametrize("val_a,val_w", [(0x7E, 0x7E), (0x7E, 0xFE), (0x01, 0x81)])
+def test_fp8_extreme_codes(ops, val_a, val_w):
+    """448 x 448 (and the smallest subnormals) over K = 65536: every partial sum
+    is exact in fp32, so the result is exact."""
+    M, N, K = 32, 48, 65536
+    a = torch.full((M, K), val_a, dtype=torch.uint8, device="cuda")
+    w = torch.full((N, K), val_w, dtype=torch.uint8, device="cuda")
+    ones_m, ones_n = torch.ones(M, device="cuda"), torch.ones(N, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ops.fp8_linear(a, ones_m, w, ones_n, K, y=y, workspace=ops.make_workspace(M, N, K, "fp8"))
+    want = float(O.e4m3_value(np.array([val_a]))[0] * O.e4m3_value(np.array([val_w]))[0] * K)
+    assert np.all(_np(y) == np.float32(want))
 
 
 @pytest.mark.parametrize("M", [20, 127])

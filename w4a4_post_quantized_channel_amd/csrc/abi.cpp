@@ -47,7 +47,7 @@ int check_quant(const char* fn, const void* x, int32_t dt, int64_t R, int64_t K,
   if (dt != W4A4_DT_F32 && dt != W4A4_DT_BF16)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: input dtype %d not F32/BF16", fn, dt);
   if (q->fmt != W4A4_FMT_INT4 && q->fmt != W4A4_FMT_INT8 && q->fmt != W4A4_FMT_NVFP4 &&
-      q->fmt != W4A4_FMT_W4A8)
+      q->fmt != W4A4_FMT_W4A8 && q->fmt != W4A4_FMT_FP8)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: unknown fmt %d", fn, q->fmt);
   if (q->fwht_block != 0 && q->fwht_block != 64)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: fwht_block must be 0 or 64", fn);
@@ -80,7 +80,8 @@ int run_quant(const char* fn, const void* x, int32_t dt, int64_t R, int64_t K, i
               const float* scale, const w4a4_qdesc* q, void* codes, void* scales, void* stream) {
   int st = check_quant(fn, x, dt, R, K, ldx, scale, q, true, codes, scales);
   if (st != W4A4_OK || R == 0) return st;
-  const int mode = q->fmt == W4A4_FMT_W4A8 ? 4 : q->fmt;  // 0 int4, 1 int8, 2 nvfp4, 4 W4A8 int8
+  // quantizer modes: 0 int4, 1 int8, 2 nvfp4, 4 W4A8 int8, 5 fp8
+  const int mode = q->fmt == W4A4_FMT_W4A8 ? 4 : (q->fmt == W4A4_FMT_FP8 ? 5 : q->fmt);
   hipError_t e = w4a4::launch_quantize(mode, dt == W4A4_DT_BF16, x, R, K, ldx, scale, q->tensor_scale,
                                        q->fwht_block, q->order, codes, scales, nullptr,
                                        (hipStream_t)stream);
@@ -114,7 +115,7 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
   if (y_dtype != W4A4_DT_F32 && y_dtype != W4A4_DT_BF16 && y_dtype != W4A4_DT_I32)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: y dtype %d", fn, y_dtype);
   const bool has_br = br && br->kind != W4A4_BRANCH_NONE;
-  if (y_dtype == W4A4_DT_I32 && (fmt == W4A4_FMT_NVFP4 || has_br))
+  if (y_dtype == W4A4_DT_I32 && (fmt == W4A4_FMT_NVFP4 || fmt == W4A4_FMT_FP8 || has_br))
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: I32 output needs an integer format and no branch", fn);
   if (!std::isfinite(alpha)) return fail(W4A4_ERR_INVALID_ARG, "%s: alpha not finite", fn);
   int st = check_branch(fn, br, M, N);
@@ -195,6 +196,13 @@ int w4a8_linear(const void* a_codes, const void* a_scales, const void* w_codes, 
                     y_dtype, ldy, workspace, workspace_bytes, stream);
 }
 
+int fp8_linear(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+               int64_t M, int64_t N, int64_t K, float alpha, const w4a4_branch* br, void* y, int32_t y_dtype,
+               int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_linear("fp8_linear", W4A4_FMT_FP8, a_codes, a_scales, w_codes, w_scales, M, N, K, alpha, br, y,
+                    y_dtype, ldy, workspace, workspace_bytes, stream);
+}
+
 static int check_lowrank(const char* fn, const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t,
                          const int32_t* idx, int64_t r) {
   if (M < 0 || K <= 0) return fail(W4A4_ERR_INVALID_ARG, "%s: bad sizes", fn);
@@ -265,7 +273,7 @@ int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, in
 
 size_t w4a4_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0) return 0;
-  if (fmt != W4A4_FMT_INT4 && fmt != W4A4_FMT_INT8 && fmt != W4A4_FMT_W4A8) return 0;
+  if (fmt != W4A4_FMT_INT4 && fmt != W4A4_FMT_INT8 && fmt != W4A4_FMT_W4A8 && fmt != W4A4_FMT_FP8) return 0;
   return w4a4::gemm_int_workspace(fmt, M, N, K);
 }
 

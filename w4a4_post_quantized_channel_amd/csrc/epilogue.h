@@ -127,9 +127,19 @@ constexpr int epilogue_stage_bytes() {
   return TI * 16 * (TJ * 32 + 16);
 }
 
+// Accumulator kinds: 0 both int4 (x256), 1 int8, 2 float already scaled
+// (NVFP4: times alpha only), 3 int8 x int4 (x16), 4 float with per-row and
+// per-column steps (FP8).
+template <int KIND, typename T>
+__device__ __forceinline__ float epi_acc(T a) {
+  if constexpr (KIND == 0) return (float)(a >> 8);
+  else if constexpr (KIND == 3) return (float)(a >> 4);
+  else return (float)a;
+}
+
 // `pre`, when given, holds the scales already loaded (load_epi_scales);
 // `el`, when given, the LDS-staged scales and branch rows of the tile.
-template <int KIND /*0 int4, 1 int8, 2 float, 3 int8 x int4*/, typename AccT, int TI, int TJ>
+template <int KIND /*0 int4, 1 int8, 2 float, 3 int8 x int4, 4 fp8*/, typename AccT, int TI, int TJ>
 __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
                                                int lane, uint8_t* stage = nullptr,
                                                const EpiScales<TI, TJ>* pre = nullptr, const EpiLds* el = nullptr) {
@@ -145,7 +155,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
 #pragma unroll
     for (int r = 0; r < 4; ++r) roff[i][r] = (uint32_t)(i * 16 + lq * 4 + r) * rstride;
 
-  if constexpr (KIND != 2) {
+  if constexpr (KIND != 2 && KIND != 4) {
     if (g.y_dtype == 2) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
@@ -185,8 +195,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int q = KIND == 0 ? (acc[i][j][r] >> 8) : KIND == 3 ? (acc[i][j][r] >> 4) : acc[i][j][r];
-          float v = (float)q * sam[i][r];
+          float v = epi_acc<KIND>(acc[i][j][r]) * sam[i][r];
           v = v * swn;
           col[i][0][r] = v * g.alpha;
         }

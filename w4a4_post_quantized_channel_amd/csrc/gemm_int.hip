@@ -82,17 +82,34 @@ __device__ __forceinline__ void drain_ring(F&& f) {
   }
 }
 
-// Operand formats of the decode kernel: both int4, both int8, or int8
-// activations with int4 weights (W4A8).  int4 codes are widened to 16*q,
-// so the MFMA sum carries a factor 256 (both int4) or 16 (W4A8) that the
-// epilogue shifts out (KIND 0 / 3).
-enum { DF_I4 = 0, DF_I8 = 1, DF_W4A8 = 2 };
+// Operand formats of the decode kernel: both int4, both int8, int8
+// activations with int4 weights (W4A8), or both OCP E4M3 (FP8).  int4
+// codes are widened to 16*q, so the MFMA sum carries a factor 256 (both
+// int4) or 16 (W4A8) that the epilogue shifts out (KIND 0 / 3).  FP8
+// accumulates in fp32 on the 16x16x128 fp8 matrix instruction (KIND 4).
+enum { DF_I4 = 0, DF_I8 = 1, DF_W4A8 = 2, DF_F8 = 3 };
 template <int DF>
 struct DecFmt {
-  static constexpr bool A4 = DF == DF_I4, W4 = DF != DF_I8;   // operand packed as int4
+  static constexpr bool A4 = DF == DF_I4, W4 = DF == DF_I4 || DF == DF_W4A8;   // operand packed as int4
   static constexpr int SBA = A4 ? 64 : 128, SBB = W4 ? 64 : 128;   // bytes of a row per 128-element step
-  static constexpr int KIND = DF == DF_I4 ? 0 : (DF == DF_I8 ? 1 : 3);
+  static constexpr int KIND = DF == DF_I4 ? 0 : (DF == DF_I8 ? 1 : (DF == DF_W4A8 ? 3 : 4));
+  typedef typename std::conditional<DF == DF_F8, v4f, v4i>::type acc_t;
+  typedef typename std::conditional<DF == DF_F8, float, int>::type elem_t;
 };
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// 32 bytes of fp8 codes from two 16-byte LDS chunks, as one operand.
+__device__ __forceinline__ v8i lds_pair(const uint8_t* p0, const uint8_t* p1) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p0), b = *reinterpret_cast<const uint4*>(p1);
+  return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+// One 16x16x128 fp8 product (both sides in the same K order), unit scales
+// (E8M0 127 = 2^0).
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
 
 template <int DF, int TI, int TJ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -150,23 +167,39 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     }
   };
 
-  v4i acc[TI][TJ];
+  typedef typename F::acc_t acc_t;
+  typedef typename F::elem_t elem_t;
+  acc_t acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
   // Fragments of one step: int8 operands take a 16-byte chunk per half
   // step (h), int4 operands one chunk for both halves.
   struct Frags {
     uint4 a[DecFmt<DF>::A4 ? 1 : 2][TI];
     uint4 b[DecFmt<DF>::W4 ? 1 : 2][TJ];
+    v8i a8[TI], b8[TJ];   // FP8: both halves as one operand
   };
   // LDS reads of one step from its ring slot.  int4 rows: lane group lq
   // holds K [32 lq, 32 lq + 32) of the step as one chunk.  int8 rows: half h
   // of lane group lq is chunk 4 h + lq (both int8) or 2 lq + h (W4A8, whose
   // activation chunks hold their codes in the widened int4 order).
   auto load = [&](const uint8_t* st, Frags& f) {
+    if constexpr (DF == DF_F8) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int R = i * 16 + lr;
+        f.a8[i] = lds_pair(st + R * SBA + 16 * (lq ^ (R & 7)), st + R * SBA + 16 * ((4 + lq) ^ (R & 7)));
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int R = j * 16 + lr;
+        f.b8[j] = lds_pair(st + AREG + R * SBB + 16 * (lq ^ (R & 7)), st + AREG + R * SBB + 16 * ((4 + lq) ^ (R & 7)));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int R = i * 16 + lr;
@@ -192,8 +225,16 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
       }
     }
   };
-  // The MFMAs of one step (int4 chunks widened to 16 q per byte).
+  // The MFMAs of one step (int4 chunks widened to 16 q per byte; FP8: one
+  // 128-deep product of both halves).
   auto math = [&](const Frags& f) {
+    if constexpr (DF == DF_F8) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_fp8(f.a8[i], f.b8[j], acc[i][j]);
+      return;
+    } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       v4i b[TJ];
@@ -208,6 +249,7 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[i][j], 0, 0, 0);
       }
+    }
     }
   };
 
@@ -263,7 +305,7 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
     }
   });
   __syncthreads();   // every wave is done with its copy area; LDS now holds the partial tiles
-  int (*red)[TI][TJ][4][64] = reinterpret_cast<int (*)[TI][TJ][4][64]>(smem);
+  elem_t (*red)[TI][TJ][4][64] = reinterpret_cast<elem_t (*)[TI][TJ][4][64]>(smem);
 
   // sum the four waves' partial tiles; wave w < TI keeps row block w
 #pragma unroll
@@ -274,7 +316,7 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
       for (int r = 0; r < 4; ++r) red[wave][i][j][r][lane] = acc[i][j][r];
   __syncthreads();
   if (wave >= TI) return;
-  v4i tot[1][TJ];
+  acc_t tot[1][TJ];
 #pragma unroll
   for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -309,7 +351,8 @@ __global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, 
   EpiScales<1, 1> es;
   load_epi_scales(es, g, m0, n0, lane);
   const uint4* p = reinterpret_cast<const uint4*>(part + blk * S * 256) + lane;
-  v4i tot[1][1] = {{v4i{0, 0, 0, 0}}};
+  typedef typename std::conditional<KIND == 4, v4f, v4i>::type acc_t;   // FP8 partials are fp32
+  acc_t tot[1][1] = {{acc_t{0, 0, 0, 0}}};
   for (int z0 = 0; z0 < S; z0 += ZB) {
     uint4 v[ZB];
 #pragma unroll
@@ -317,7 +360,7 @@ __global__ void __launch_bounds__(64) gemm_int_reduce_kernel(GemmArgs g, int S, 
       if (z0 + dz < S) v[dz] = p[(z0 + dz) * 64];
 #pragma unroll
     for (int dz = 0; dz < ZB; ++dz)
-      if (z0 + dz < S) tot[0][0] += __builtin_bit_cast(v4i, v[dz]);
+      if (z0 + dz < S) tot[0][0] += __builtin_bit_cast(acc_t, v[dz]);
   }
   epilogue_tiles<KIND>(tot, g, m0, n0, lane, nullptr, &es);
 }
@@ -358,7 +401,7 @@ static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, bool int4) {
 
 // fmt: 0 int4 x int4, 1 int8 x int8, 3 int8 activations x int4 weights
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
-  return M <= 64 ? decode_plan(M, N, K, fmt != 1).ws_bytes : 0;
+  return M <= 64 ? decode_plan(M, N, K, fmt == 0 || fmt == 3).ws_bytes : 0;
 }
 
 template <int DF>
@@ -392,11 +435,12 @@ static void launch_decode(const GemmArgs& g, const DecodePlan& p, int32_t* part,
 
 hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st) {
   if (g.M <= 64) {
-    const DecodePlan p = decode_plan(g.M, g.N, g.K, fmt != 1);   // weights int4 unless W8A8
+    const DecodePlan p = decode_plan(g.M, g.N, g.K, fmt == 0 || fmt == 3);   // int4 weights
     const bool split = p.splits > 1 && workspace && ws_bytes >= p.ws_bytes;
     int32_t* part = split ? reinterpret_cast<int32_t*>(workspace) : nullptr;
     if (fmt == 0) launch_decode<DF_I4>(g, p, part, st);
     else if (fmt == 1) launch_decode<DF_I8>(g, p, part, st);
+    else if (fmt == 4) launch_decode<DF_F8>(g, p, part, st);
     else launch_decode<DF_W4A8>(g, p, part, st);
     return hipGetLastError();
   }

@@ -43,7 +43,8 @@ namespace w4a4 {
 
 namespace {
 
-enum { W_INT4 = 0, W_INT8 = 1, W_NVFP4 = 2, W_W4A8 = 3 };   // W4A8: int8 activations, int4 weights
+// W4A8: int8 activations, int4 weights; FP8: OCP E4M3 on both sides
+enum { W_INT4 = 0, W_INT8 = 1, W_NVFP4 = 2, W_W4A8 = 3, W_FP8 = 4 };
 
 template <int FMT>
 struct WFmt;
@@ -71,6 +72,26 @@ struct WFmt<W_W4A8> {               // per 64-byte weight segment; activations t
   static constexpr int STEPS = 2;
   typedef v4i acc_t;
 };
+template <>
+struct WFmt<W_FP8> {                // 128 bytes per row of either operand: one 16x16x128 product
+  static constexpr int KSEG = 128;
+  static constexpr int STEPS = 1;
+  typedef v4f acc_t;
+};
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// 32 bytes of fp8 codes from two 16-byte LDS slots, as one operand.
+__device__ __forceinline__ v8i lds_pair(const uint8_t* p0, const uint8_t* p1) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p0), b = *reinterpret_cast<const uint4*>(p1);
+  return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+// One 16x16x128 fp8 product (both sides in the same K order), unit scales
+// (E8M0 127 = 2^0).
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
 
 constexpr int kSeg = 64;     // packed weight bytes per row per K-group per stage
 
@@ -150,10 +171,11 @@ template <int FMT, int TI, int TJ, int WR, int WC, int WK>
 struct WCfg {
   static constexpr int BM = WR * TI * 16, BN = WC * TJ * 16;
   static constexpr int P = kSeg * WK;                // packed weight bytes per row per stage
-  static constexpr int PA = FMT == W_W4A8 ? 2 * P : P;   // activation bytes per row per stage
+  static constexpr int PA = (FMT == W_W4A8 || FMT == W_FP8) ? 2 * P : P;   // activation bytes per row per stage
+  static constexpr int PB = FMT == W_FP8 ? 2 * P : P;                      // weight bytes per row per stage
   static constexpr int KST = WFmt<FMT>::KSEG * WK;   // K elements per stage
   static constexpr int SP = (kSeg / 8) * WK;         // NVFP4 scale bytes per row per stage
-  static constexpr int A_BYTES = BM * PA, B_BYTES = BN * P;
+  static constexpr int A_BYTES = BM * PA, B_BYTES = BN * PB;
   static constexpr int SA_BYTES = FMT == W_NVFP4 ? BM * SP : 0;
   static constexpr int SB_BYTES = FMT == W_NVFP4 ? BN * SP : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
@@ -291,8 +313,8 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   const int kw = wave / (WR * WC), wrc = wave % (WR * WC);
   const int wm0 = (wrc / WC) * TI * 16, wn0 = (wrc % WC) * TJ * 16;
 
-  const int64_t rowbytes = FMT == W_INT8 ? g.K : (g.K >> 1);   // weight rows
-  const int64_t rbA = (FMT == W_INT8 || FMT == W_W4A8) ? g.K : (g.K >> 1);   // activation rows
+  const int64_t rowbytes = (FMT == W_INT8 || FMT == W_FP8) ? g.K : (g.K >> 1);   // weight rows
+  const int64_t rbA = (FMT == W_INT8 || FMT == W_W4A8 || FMT == W_FP8) ? g.K : (g.K >> 1);   // activation rows
   const int64_t srow = g.K >> 4;
   const int nk = (int)((g.K + C::KST - 1) / C::KST);
   const v4u rsA = rsrc_words(g.a + (int64_t)m0 * rbA, (uint32_t)(min(C::BM, g.M - m0) * rbA));
@@ -305,7 +327,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 
   uint8_t* pad = smem + C::NBUF * C::STAGE;
   CodeCopy<C::PA, C::NA, C::NW> cpA;
-  CodeCopy<C::P, C::NB, C::NW> cpB;
+  CodeCopy<C::PB, C::NB, C::NW> cpB;
   ScaleCopy<C::SP, (C::NSA > 0 ? C::NSA : 1), C::NW> cpSA;
   ScaleCopy<C::SP, (C::NSB > 0 ? C::NSB : 1), C::NW> cpSB;
   cpA.init(wave, lane, rbA);
@@ -348,15 +370,22 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   // group lq of K-group kw owns logical slot 4 kw + lq of each row.
   // W4A8 activations: lane group lq of K-group kw reads slot 8 kw + 2 lq + h
   // for MFMA step h (the 16 int8 codes of the same K as the weight's half h).
-  constexpr int NSA = FMT == W_W4A8 ? 2 : 1;   // activation slots per fragment row and stage
+  // FP8, both operands: slots 8 kw + 2 lq and 8 kw + 2 lq + 1, the lane's 32
+  // codes of one 16x16x128 product.
+  constexpr int NSA = (FMT == W_W4A8 || FMT == W_FP8) ? 2 : 1;   // activation slots per fragment row and stage
+  constexpr int NSB = FMT == W_FP8 ? 2 : 1;                       // weight slots
   const int L = kw * (kSeg / 16) + lq;
-  int aoff[NSA];
+  int aoff[NSA], boff[NSB];
 #pragma unroll
   for (int h = 0; h < NSA; ++h) {
-    const int La = FMT == W_W4A8 ? kw * 8 + 2 * lq + h : L;
+    const int La = NSA == 2 ? kw * 8 + 2 * lq + h : L;
     aoff[h] = (wm0 + lr) * C::PA + ((La ^ swz<C::PA>(wm0 + lr)) * 16);
   }
-  const int boff = C::A_BYTES + (wn0 + lr) * C::P + ((L ^ swz<C::P>(wn0 + lr)) * 16);
+#pragma unroll
+  for (int h = 0; h < NSB; ++h) {
+    const int Lb = NSB == 2 ? kw * 8 + 2 * lq + h : L;
+    boff[h] = C::A_BYTES + (wn0 + lr) * C::PB + ((Lb ^ swz<C::PB>(wn0 + lr)) * 16);
+  }
   const int saoff = C::A_BYTES + C::B_BYTES + (wm0 + lr) * C::SP + kw * (kSeg / 8) + lq * 2;
   const int sboff = C::A_BYTES + C::B_BYTES + C::SA_BYTES + (wn0 + lr) * C::SP + kw * (kSeg / 8) + lq * 2;
 
@@ -369,11 +398,19 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   // compute stage s.  Stages past the end are still copied (zeros) and
   // read, so every iteration waits on the same count and has no branches.
   struct Frags {
-    uint4 a[TI][NSA], b[TJ];
+    uint4 a[TI][NSA], b[TJ][NSB];
     uint32_t sa[TI], sb[TJ];
+    v8i a8[TI], b8[TJ];   // FP8: both slots as one operand
   };
   auto read_frags = [&](int s, Frags& f) {
     const uint8_t* base = smem + (s % C::NBUF) * C::STAGE;
+    if constexpr (FMT == W_FP8) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) f.a8[i] = lds_pair(base + aoff[0] + i * 16 * C::PA, base + aoff[1] + i * 16 * C::PA);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) f.b8[j] = lds_pair(base + boff[0] + j * 16 * C::PB, base + boff[NSB - 1] + j * 16 * C::PB);
+      return;
+    }
     if constexpr (FMT == W_NVFP4) {
 #pragma unroll
       for (int i = 0; i < TI; ++i) f.sa[i] = *reinterpret_cast<const uint16_t*>(base + saoff + i * 16 * C::SP);
@@ -385,7 +422,9 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 #pragma unroll
       for (int h = 0; h < NSA; ++h) f.a[i][h] = *reinterpret_cast<const uint4*>(base + aoff[h] + i * 16 * C::PA);
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) f.b[j] = *reinterpret_cast<const uint4*>(base + boff + j * 16 * C::P);
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int h = 0; h < NSB; ++h) f.b[j][h] = *reinterpret_cast<const uint4*>(base + boff[h] + j * 16 * C::PB);
   };
   struct Ops {
     uint4 a[TI], b[TJ];
@@ -397,13 +436,24 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
       else o.a[i] = operand<FMT>(f.a[i][0], st, FMT == W_NVFP4 ? f.sa[i] : 0u);
     }
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) o.b[j] = operand<FMT>(f.b[j], st, FMT == W_NVFP4 ? f.sb[j] : 0u);
+    for (int j = 0; j < TJ; ++j) o.b[j] = operand<FMT>(f.b[j][0], st, FMT == W_NVFP4 ? f.sb[j] : 0u);
   };
   auto mma_step = [&](const Ops& o) {
+    if constexpr (FMT != W_FP8) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) mfma_w<FMT>(acc[i][j], o.a[i], o.b[j]);
+        for (int j = 0; j < TJ; ++j) mfma_w<FMT>(acc[i][j], o.a[i], o.b[j]);
+    }
+  };
+  // FP8 multiplies straight from the fragments (nothing to widen)
+  auto mma_frags = [&](const Frags& f) {
+    if constexpr (FMT == W_FP8) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_fp8(f.a8[i], f.b8[j], acc[i][j]);
+    }
   };
   constexpr int NV = FMT == W_NVFP4 ? 3 : (FMT == W_INT4 || FMT == W_W4A8 ? 2 : 0);
   // wait_stages 1: stage s + 1 landed, with stages after it still in flight
@@ -418,7 +468,26 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 
 #pragma unroll
   for (int p = 0; p < C::NBUF - 1; ++p) copy_stage(p);
-  if constexpr (FMT != W_NVFP4) {
+  if constexpr (FMT == W_FP8) {
+    // Two fragment sets: iteration s waits for stage s + 1, copies stage
+    // s + NBUF - 1, reads stage s + 1 and multiplies stage s.
+    sync_stage(2);   // stage 0 landed
+    Frags f0, f1;
+    read_frags(0, f0);
+    auto iter8 = [&](int s8, const Frags& cur, Frags& nxt) {
+      sync_stage(1);
+      copy_stage(s8 + C::NBUF - 1);
+      read_frags(s8 + 1, nxt);
+      mma_frags(cur);
+      interleave_steps<TI * NSA + TJ * NSB, TI * TJ, 0>();
+    };
+    int s = 0;
+    for (; s + 1 < nk; s += 2) {
+      iter8(s, f0, f1);
+      iter8(s + 1, f1, f0);
+    }
+    if (s < nk) iter8(s, f0, f1);
+  } else if constexpr (FMT != W_NVFP4) {
     // Two fragment sets and two widened operand sets.  The operands of an
     // MFMA step are widened during the previous step's MFMAs; step 0 of
     // stage s + 1 is widened from the fragments read in iteration s.
@@ -522,7 +591,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   const EpiLds el{FMT == W_NVFP4 ? nullptr : lsc, FMT == W_NVFP4 ? nullptr : lsc + C::BM,
                   br_lds ? bra : nullptr, brb, m0, n0};
 
-  constexpr int KIND = FMT == W_NVFP4 ? 2 : (FMT == W_INT4 ? 0 : (FMT == W_W4A8 ? 3 : 1));
+  constexpr int KIND = FMT == W_NVFP4 ? 2 : (FMT == W_INT4 ? 0 : (FMT == W_W4A8 ? 3 : (FMT == W_FP8 ? 4 : 1)));
   if constexpr (WK == 1) {
     // bf16 output is staged through this wave's slice of the (now idle) LDS
     static_assert(C::NW * epilogue_stage_bytes<TI, TJ>() <= C::BR_OFF, "epilogue staging fits");
@@ -595,19 +664,28 @@ WideChoice choose(int64_t M, int64_t N, bool skip0) {
   return best;
 }
 
+// FP8 takes the 128x256 shape only: its stages (128 bytes per row on both
+// sides) leave LDS room for three of them there and for fewer elsewhere.
 template <int FMT>
 hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
-  const WideChoice c = choose(g.M, g.N, FMT == W_W4A8);
+  const WideChoice c = FMT == W_FP8 ? WideChoice{1, (g.M + 127) / 128, (g.N + 255) / 256}
+                                    : choose(g.M, g.N, FMT == W_W4A8);
   const dim3 grid((unsigned)(c.tm * c.tn));
   const int tm = (int)c.tm, tn = (int)c.tn;
   switch (c.cfg) {
     case 0:
-      if constexpr (FMT != W_W4A8)
+      if constexpr (FMT != W_W4A8 && FMT != W_FP8)
         hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 5, 4, 2, 1>), grid, dim3(512), 0, st, g, tm, tn);
       break;
     case 1: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 2, 4, 1>), grid, dim3(512), 0, st, g, tm, tn); break;
-    case 2: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 6, 2, 1, 2>), grid, dim3(256), 0, st, g, tm, tn); break;
-    default: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 1, 1, 4>), grid, dim3(256), 0, st, g, tm, tn); break;
+    case 2:
+      if constexpr (FMT != W_FP8)
+        hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 6, 2, 1, 2>), grid, dim3(256), 0, st, g, tm, tn);
+      break;
+    default:
+      if constexpr (FMT != W_FP8)
+        hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 1, 1, 4>), grid, dim3(256), 0, st, g, tm, tn);
+      break;
   }
   return hipGetLastError();
 }
@@ -618,6 +696,7 @@ hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st) {
   if (fmt == 0) return launch_wide_fmt<W_INT4>(g, st);
   if (fmt == 1) return launch_wide_fmt<W_INT8>(g, st);
   if (fmt == 3) return launch_wide_fmt<W_W4A8>(g, st);
+  if (fmt == 4) return launch_wide_fmt<W_FP8>(g, st);
   return launch_wide_fmt<W_NVFP4>(g, st);
 }
 

@@ -8,7 +8,8 @@ namespace w4a4 {
 
 // quantize.hip -------------------------------------------------------------
 // mode: 0 int4, 1 int8, 2 nvfp4, 3 transform-amax only, 4 int8 in the W4A8 order
-// (each aligned group of 8 codes stored even-K codes first, then odd-K codes).
+// (each aligned group of 8 codes stored even-K codes first, then odd-K codes),
+// 5 fp8 (OCP E4M3, step amax/448).
 hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int64_t K,
                            int64_t ldx, const float* scale, float g, int rot, int order,
                            void* codes, void* scales, float* amax_out, hipStream_t st);
@@ -37,12 +38,13 @@ struct GemmArgs {
   int64_t ldy;
 };
 
-// fmt: 0 int4, 1 int8, 3 int8 activations x int4 weights (W4A8).
+// fmt: 0 int4, 1 int8, 3 int8 activations x int4 weights (W4A8), 4 fp8 (E4M3).
 // workspace may be null (no split-K).
 hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st);
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 
-// gemm_wide.hip: many-token kernel with packed operands in LDS, fmt 0 int4, 1 int8, 2 nvfp4, 3 W4A8
+// gemm_wide.hip: many-token kernel with packed operands in LDS, fmt 0 int4, 1 int8, 2 nvfp4, 3 W4A8,
+// 4 fp8
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st);
 
 // branch.hip ----------------------------------------------------------------

@@ -49,7 +49,8 @@ struct QuantArgs {
 // MODE_INT8W: int8 codes for the W4A8 GEMM, every aligned group of 8 codes
 // stored as its even-K codes then its odd-K codes (the order packed int4
 // weight codes take when widened to bytes).
-enum { MODE_INT4 = 0, MODE_INT8 = 1, MODE_NVFP4 = 2, MODE_AMAX = 3, MODE_INT8W = 4 };
+// MODE_FP8: OCP E4M3 codes with one step amax/448 per row.
+enum { MODE_INT4 = 0, MODE_INT8 = 1, MODE_NVFP4 = 2, MODE_AMAX = 3, MODE_INT8W = 4, MODE_FP8 = 5 };
 
 constexpr float kTinyStep = 8.271806125530277e-25f;  // 2^-80
 
@@ -262,6 +263,8 @@ template <int MODE, bool BF16IN, int NC, int WPR>
 __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(QuantArgs a) {
   constexpr int QMAX = MODE == MODE_INT4 ? 7 : 127;
   constexpr bool I8 = MODE == MODE_INT8 || MODE == MODE_INT8W;
+  constexpr bool F8 = MODE == MODE_FP8;
+  constexpr float QDIV = F8 ? 448.0f : (float)QMAX;   // step = amax / QDIV
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   static_assert(WPR == 1 || WPR == 4 || WPR == 8, "waves per row");
@@ -305,7 +308,7 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
     // slot takes the exact path, which forms y itself.
     // Integer modes need the whole row for its maximum; NVFP4 transforms
     // and quantizes one slot at a time.
-    if constexpr (MODE == MODE_INT4 || I8 || MODE == MODE_AMAX) {
+    if constexpr (MODE == MODE_INT4 || I8 || F8 || MODE == MODE_AMAX) {
       float v[NC][16];
       float fl = 1.0f;
 #pragma unroll
@@ -329,7 +332,7 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
           if constexpr (WPR == 8) m = fmaxf(m, fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
           __syncthreads();
         }
-        const float step = m / (float)QMAX;   // IEEE division
+        const float step = m / QDIV;   // IEEE division
         const bool fast = step >= kTinyStep && step <= kBig;
         const float rstep = fast ? 1.0f / step : 0.f;
         const float D = step / fl, rD = rstep * fl;   // exact power-of-two rescaling
@@ -347,7 +350,19 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
             dmax = fmaxf(dmax, __builtin_fabsf(t[i] - r[i]));
           }
           constexpr float kEdge = I8 ? 0.5f - 3.0517578125e-05f : 0.5f - 1.9073486328125e-06f;
-          if (s < nslots && (!fast || dmax >= kEdge)) {
+          bool near;
+          if constexpr (F8) {
+            // E4M3 rounding boundaries have at most five significant bits, so
+            // the low 19 bits of their fp32 patterns are zero; a one-multiply
+            // quotient within three steps of one has low bits within 4 of 0.
+            uint32_t lo = 0xFFFFFFFFu;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) lo = min(lo, (__float_as_uint(t[i]) + 4u) & 0x7FFFFu);
+            near = lo <= 8u;
+          } else {
+            near = dmax >= kEdge;
+          }
+          if (s < nslots && (!fast || near)) {
             if (fast) {
 #pragma unroll
               for (int i = 0; i < 16; ++i) t[i] = div_rn(v[c][i], D, rD);
@@ -362,6 +377,24 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
             for (int i = 0; i < 16; ++i) r[i] = __builtin_rintf(t[i]);
           }
           if (s >= nslots) continue;
+          if constexpr (F8) {
+            // |t| <= 448 up to one rounding: the clamp is the nearest value
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float a0 = __builtin_amdgcn_fmed3f(t[4 * k], -448.0f, 448.0f);
+              const float a1 = __builtin_amdgcn_fmed3f(t[4 * k + 1], -448.0f, 448.0f);
+              const float a2 = __builtin_amdgcn_fmed3f(t[4 * k + 2], -448.0f, 448.0f);
+              const float a3 = __builtin_amdgcn_fmed3f(t[4 * k + 3], -448.0f, 448.0f);
+              uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+              d = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, d, true);
+              // the converter keeps the sign of zero; the format's zero is +0
+              const uint32_t mag = d & 0x7F7F7F7Fu;
+              w[k] = mag | (d & ((mag + 0x7F7F7F7Fu) & 0x80808080u));
+            }
+            *reinterpret_cast<uint4*>(a.codes + (size_t)row * a.K + s * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+            continue;
+          }
           uint32_t q[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i)
@@ -613,7 +646,7 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   // One wave per row when there are many rows and the row fits five chunks
   // per lane (the factors then stay in registers); else four waves per row,
   // eight for integer codes of rows longer than 4096.
-  const bool intmode = mode == MODE_INT4 || mode == MODE_INT8 || mode == MODE_INT8W;
+  const bool intmode = mode == MODE_INT4 || mode == MODE_INT8 || mode == MODE_INT8W || mode == MODE_FP8;
   int wpr = (R >= 1024 && nslots <= 5 * 64) ? 1 : 4;
   if (wpr == 4 && intmode && nslots > 4 * 64) wpr = 8;
   const int nc = round_nc((int)((nslots + 64 * wpr - 1) / (64 * wpr)));
@@ -632,6 +665,8 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
                                          : launch_nc<MODE_INT4, false, 8>(nc, grid, st, a);
     if (mode == MODE_INT8W) return bf16in ? launch_nc<MODE_INT8W, true, 8>(nc, grid, st, a)
                                           : launch_nc<MODE_INT8W, false, 8>(nc, grid, st, a);
+    if (mode == MODE_FP8) return bf16in ? launch_nc<MODE_FP8, true, 8>(nc, grid, st, a)
+                                        : launch_nc<MODE_FP8, false, 8>(nc, grid, st, a);
     return bf16in ? launch_nc<MODE_INT8, true, 8>(nc, grid, st, a) : launch_nc<MODE_INT8, false, 8>(nc, grid, st, a);
   }
 #define W4A4_DISPATCH(MODE)                                                          \
@@ -644,6 +679,7 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   W4A4_DISPATCH(MODE_INT4)
   W4A4_DISPATCH(MODE_INT8)
   W4A4_DISPATCH(MODE_INT8W)
+  W4A4_DISPATCH(MODE_FP8)
   W4A4_DISPATCH(MODE_NVFP4)
   W4A4_DISPATCH(MODE_AMAX)
 #undef W4A4_DISPATCH

@@ -16,17 +16,17 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a4.so")
 
-FMT_INT4, FMT_INT8, FMT_NVFP4, FMT_W4A8 = 0, 1, 2, 3
+FMT_INT4, FMT_INT8, FMT_NVFP4, FMT_W4A8, FMT_FP8 = 0, 1, 2, 3, 4
 DT_F32, DT_BF16, DT_I32 = 0, 1, 2
 ORDER_SMOOTH_THEN_ROTATE, ORDER_ROTATE_THEN_SMOOTH = 0, 1
 BRANCH_NONE, BRANCH_BF16 = 0, 1
 # w4a8: quantize_act writes W4A8-layout int8 activations; the weights are int4
-FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4, "w4a8": FMT_W4A8}
+FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4, "w4a8": FMT_W4A8, "fp8": FMT_FP8}
 ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
           "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
 ABI_VERSION = 1
 
-EXPORTS = ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "lowrank_add",
+EXPORTS = ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
            "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_workspace_size", "w4a4_status_string",
            "w4a4_last_error", "w4a4_abi_version"]
 
@@ -61,6 +61,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "w4a4_linear": [vp, vp, vp, vp, i64, i64, i64, i32, f32, br, vp, i32, i64, vp, sz, vp],
         "w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
         "w4a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
+        "fp8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
         "w4a4_workspace_size": [i64, i64, i64, i32],
         "lowrank_add": [vp, i64, i64, i64, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp],
         "w4a4_lowrank_project": [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp],
@@ -128,6 +129,8 @@ def code_shapes(fmt: str, R: int, K: int):
         return (R, K // 2), torch.uint8, (R,), torch.float32
     if fmt in ("int8", "w4a8"):   # w4a8: activation side, int8 in the W4A8 layout
         return (R, K), torch.int8, (R,), torch.float32
+    if fmt == "fp8":              # OCP E4M3 codes
+        return (R, K), torch.uint8, (R,), torch.float32
     if fmt == "nvfp4":
         return (R, K // 2), torch.uint8, (R, K // 16), torch.uint8
     raise ValueError(fmt)
@@ -205,7 +208,7 @@ def _linear(fn: str, fmt: str, a_codes, a_scales, w_codes, w_scales, K: int, *, 
     args = (_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     tail = (ctypes.byref(br), _ptr(y), _dtype_code(y), y.stride(0), _ptr(workspace), ws_bytes, _stream(stream))
-    if fn in ("w8a8_linear", "w4a8_linear"):
+    if fn in ("w8a8_linear", "w4a8_linear", "fp8_linear"):
         st = getattr(LIB, fn)(*args, float(alpha), *tail)
     else:
         st = LIB.w4a4_linear(*args, FMTS[fmt], float(alpha), *tail)
@@ -226,6 +229,11 @@ def w8a8_linear(a_codes, a_scales, w_codes, w_scales, K: int, **kw):
 def w4a8_linear(a_codes, a_scales, w_codes, w_scales, K: int, **kw):
     """INT8 activation codes x packed INT4 weight codes (W4A8)."""
     return _linear("w4a8_linear", "w4a8", a_codes, a_scales, w_codes, w_scales, K, **kw)
+
+
+def fp8_linear(a_codes, a_scales, w_codes, w_scales, K: int, **kw):
+    """FP8 (OCP E4M3) W8A8, fp32 accumulation."""
+    return _linear("fp8_linear", "fp8", a_codes, a_scales, w_codes, w_scales, K, **kw)
 
 
 def _check_branch_inputs(x, l1t, idx, lw=None):

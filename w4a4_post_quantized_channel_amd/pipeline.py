@@ -101,8 +101,8 @@ class QuantizedLinear:
                 a = ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
             bd = ops.branch_desc(a, self.branch["lw"])
         y = b["y"] if out is None else out
-        if self.fmt in ("int8", "w4a8"):
-            fn = ops.w8a8_linear if self.fmt == "int8" else ops.w4a8_linear
+        if self.fmt in ("int8", "w4a8", "fp8"):
+            fn = {"int8": ops.w8a8_linear, "w4a8": ops.w4a8_linear, "fp8": ops.fp8_linear}[self.fmt]
             return fn(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K,
                       branch=bd, y=y, workspace=b["ws"], stream=stream)
         return ops.w4a4_linear(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K, self.fmt,

@@ -65,7 +65,7 @@ class Case:
     M: int
     N: int
     K: int
-    fmt: str                 # "int4" | "int8" | "nvfp4" | "w4a8" (int8 x, int4 w)
+    fmt: str                 # "int4" | "int8" | "nvfp4" | "w4a8" (int8 x, int4 w) | "fp8"
     x_dtype: str             # "bf16" | "f32"
     y_dtype: str             # "bf16" | "f32"
     x: np.ndarray            # M x K fp32 values
@@ -224,8 +224,17 @@ def workload(name: str) -> Case:
     if name == "video_w4a8":    # protected video-denoising step, integer codes
         return linear_case(4096, 5120, 5120, seed=44, fmt="w4a8", n_outliers=64,
                            outlier_gain=30.0, keep_channels=64, name=name)
+    # FP8 W8A8 for upgraded layers (QuantWAMs sec. 4.2), on the shapes of
+    # the batch-1 down projection and the video projection
+    if name == "decode_fp8":
+        return linear_case(64, 2048, 8192, seed=121, fmt="fp8", n_outliers=16,
+                           outlier_gain=15.0, name=name)
+    if name == "video_fp8":
+        return linear_case(4096, 5120, 5120, seed=45, fmt="fp8", n_outliers=64,
+                           outlier_gain=30.0, keep_channels=64, name=name)
     raise KeyError(name)
 
 
 WORKLOADS = ["tiny", "decode_w4a4", "decode_w8a8", "prefill_gate_up", "prefill_down",
-             "lowrank", "video_nvfp4", "decode_w4a8", "decode_w4a8_down", "video_w4a8"]
+             "lowrank", "video_nvfp4", "decode_w4a8", "decode_w4a8_down", "video_w4a8",
+             "decode_fp8", "video_fp8"]
