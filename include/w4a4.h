@@ -143,6 +143,21 @@ int quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t l
                  const float* inv_smooth, const w4a4_qdesc* q,
                  void* codes, void* scales, void* stream);
 
+/* quantize_act_gather -- quantize_act that also writes the BF16 bypass
+ * operand of kept channels, xo[m, j] = x[m, idx[j]] (exact), from the same
+ * pass over x, so the 16-bit branch costs no second read of x (QuantWAMs
+ * sec. 3.1 / 4.2: the kept channels travel on a BF16 path next to the
+ * quantized ones).  Arguments as quantize_act, plus:
+ *  idx  int32[r] channel indices, 1 <= r <= W4A4_MAX_BRANCH; an index
+ *       outside [0, K) gives 0.
+ *  xo   bf16 M x r, row stride ldo >= r: the w4a4_branch ``a`` operand
+ *       (ra = r).
+ * x must be BF16.  Same result as quantize_act followed by
+ * w4a4_lowrank_project with idx. */
+int quantize_act_gather(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                        const float* inv_smooth, const w4a4_qdesc* q, void* codes, void* scales,
+                        const int32_t* idx, int64_t r, void* xo, int64_t ldo, void* stream);
+
 /* pack_weights -- offline weight packing with the inverse transform folded
  * in (FoldQuantVLA contribution 1: the inverse of every activation transform
  * is folded into each consuming weight; QuantWAMs sec. 3.2: the common

@@ -175,6 +175,19 @@ def test_workspace_sizes(ops):
     assert L.w4a4_workspace_size(0, 2048, 2048, 0) == 0
 
 
+def test_quantize_act_gather_rejects_bad_arguments(ops):
+    L = ops.LIB
+    g = lambda dt=1, M=4, r=8, ldo=8, idx=FAKE, xo=FAKE2, q=None: L.quantize_act_gather(
+        FAKE, dt, M, 128, 128, None, q or _q(ops), FAKE2, FAKE2, idx, r, xo, ldo, None)
+    assert g(dt=0) == -4                        # x must be bf16
+    assert g(r=0) == -1 and g(r=129, ldo=129) == -1
+    assert g(ldo=4) == -1
+    assert g(idx=None) == -1 and g(xo=None) == -1
+    assert g(xo=ctypes.c_void_p(0x20001)) == -3
+    assert g(q=_q(ops, fmt=9)) == -4
+    assert g(M=0, idx=None, xo=None) == 0       # empty batch
+
+
 def test_lowrank_rejects_bad_arguments(ops):
     L = ops.LIB
     # both or neither of l1 / idx

@@ -318,6 +318,30 @@ def test_lowrank_gather(ops, pipe):
     assert np.array_equal(g, case.x[:, [0, 5, 511, 100, 7, 8, 9, 300]])
 
 
+@pytest.mark.parametrize("M,K,fmt,r", [(300, 320, "nvfp4", 64), (260, 256, "nvfp4", 128), (70, 448, "int8", 65),
+                                       (5, 4160, "int4", 1), (33, 320, "fp8", 16), (16, 256, "w4a8", 8),
+                                       (40, 192, "nvfp4", 24)])
+def test_quantize_act_gather(ops, pipe, M, K, fmt, r):
+    """The fused gather leaves codes and scales as quantize_act writes them and
+    copies x[:, idx] exactly (indices at block edges, repeated, out of range)."""
+    case = WL.linear_case(M, 8, K, seed=61 + r, fmt=fmt, n_outliers=4, outlier_gain=10.0)
+    t = pipe.case_to_device(case)
+    x = t["x"]
+    rng = np.random.default_rng(r)
+    idx = rng.integers(0, K, size=r)
+    special = [0, K - 1, 63, 64, 127, 128, -1, K, 5, 5]
+    idx[:min(r, len(special))] = special[:min(r, len(special))]
+    idx_t = torch.from_numpy(idx.astype(np.int32)).cuda()
+    kw = dict(fwht_block=case.fwht_block, tensor_scale=1.0 / 64)
+    c0, s0 = ops.quantize_act(x, t["inv_s"], fmt, **kw)
+    c1, s1, xo = ops.quantize_act_gather(x, t["inv_s"], idx_t, fmt, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1) and torch.equal(s0, s1)
+    xb = case.x_bits
+    want = np.where((idx >= 0) & (idx < K), xb[:, np.clip(idx, 0, K - 1)], 0).astype(np.uint16)
+    assert np.array_equal(xo.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
 def test_determinism_and_side_stream(ops, pipe):
     case = WL.linear_case(64, 2048, 2048, seed=51, n_outliers=16, outlier_gain=15.0)
     layer, t = pipe.build_layer(case)

@@ -77,14 +77,15 @@ int check_quant(const char* fn, const void* x, int32_t dt, int64_t R, int64_t K,
 }
 
 int run_quant(const char* fn, const void* x, int32_t dt, int64_t R, int64_t K, int64_t ldx,
-              const float* scale, const w4a4_qdesc* q, void* codes, void* scales, void* stream) {
+              const float* scale, const w4a4_qdesc* q, void* codes, void* scales, void* stream,
+              const int32_t* gidx = nullptr, int64_t gr = 0, void* gout = nullptr, int64_t ldg = 0) {
   int st = check_quant(fn, x, dt, R, K, ldx, scale, q, true, codes, scales);
   if (st != W4A4_OK || R == 0) return st;
   // quantizer modes: 0 int4, 1 int8, 2 nvfp4, 4 W4A8 int8, 5 fp8
   const int mode = q->fmt == W4A4_FMT_W4A8 ? 4 : (q->fmt == W4A4_FMT_FP8 ? 5 : q->fmt);
   hipError_t e = w4a4::launch_quantize(mode, dt == W4A4_DT_BF16, x, R, K, ldx, scale, q->tensor_scale,
                                        q->fwht_block, q->order, codes, scales, nullptr,
-                                       (hipStream_t)stream);
+                                       (hipStream_t)stream, gidx, (int)gr, gout, ldg);
   return launch_status(e, fn);
 }
 
@@ -164,6 +165,21 @@ extern "C" {
 int quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const float* inv_smooth,
                  const w4a4_qdesc* q, void* codes, void* scales, void* stream) {
   return run_quant("quantize_act", x, x_dtype, M, K, ldx, inv_smooth, q, codes, scales, stream);
+}
+
+int quantize_act_gather(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const float* inv_smooth,
+                        const w4a4_qdesc* q, void* codes, void* scales, const int32_t* idx, int64_t r, void* xo,
+                        int64_t ldo, void* stream) {
+  const char* fn = "quantize_act_gather";
+  if (x_dtype != W4A4_DT_BF16) return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: x must be BF16", fn);
+  if (r <= 0 || r > W4A4_MAX_BRANCH)
+    return fail(W4A4_ERR_INVALID_ARG, "%s: r=%lld outside [1, %d]", fn, (long long)r, W4A4_MAX_BRANCH);
+  if (ldo < r) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo < r", fn);
+  if (M > 0) {
+    if (!idx || !xo) return fail(W4A4_ERR_INVALID_ARG, "%s: idx / xo is NULL", fn);
+    if (!aligned(idx, 4) || !aligned(xo, 2)) return fail(W4A4_ERR_MISALIGNED, "%s: idx / xo misaligned", fn);
+  }
+  return run_quant(fn, x, x_dtype, M, K, ldx, inv_smooth, q, codes, scales, stream, idx, r, xo, ldo);
 }
 
 int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const float* smooth,

@@ -10,9 +10,13 @@ namespace w4a4 {
 // mode: 0 int4, 1 int8, 2 nvfp4, 3 transform-amax only, 4 int8 in the W4A8 order
 // (each aligned group of 8 codes stored even-K codes first, then odd-K codes),
 // 5 fp8 (OCP E4M3, step amax/448).
+// gidx / gr / gout / ldg: optional kept-channel gather from the same pass
+// (bf16 input): gout[m * ldg + j] = x[m, gidx[j]] for j < gr <= 128.
 hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int64_t K,
                            int64_t ldx, const float* scale, float g, int rot, int order,
-                           void* codes, void* scales, float* amax_out, hipStream_t st);
+                           void* codes, void* scales, float* amax_out, hipStream_t st,
+                           const int32_t* gidx = nullptr, int gr = 0, void* gout = nullptr,
+                           int64_t ldg = 0);
 int64_t quant_max_k();
 
 // gemm_int.hip / gemm_nvfp4.hip --------------------------------------------

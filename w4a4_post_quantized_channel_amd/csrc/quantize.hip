@@ -44,6 +44,12 @@ struct QuantArgs {
   uint8_t* codes;
   void* scales;
   float* amax_out;      // transform_amax mode
+  // kept-channel gather (bf16 input only): gout[row * ldg + j] = x[row, gidx[j]]
+  // for j < gr (gr == 0: none); indices outside [0, K) give 0
+  const int32_t* gidx;
+  int gr;
+  uint16_t* gout;
+  int64_t ldg;
 };
 
 // MODE_INT8W: int8 codes for the W4A8 GEMM, every aligned group of 8 codes
@@ -299,6 +305,17 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
     SlotRaw<BF16IN> raw[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) raw[c] = load_slot<BF16IN>(rs, (c * WPR + sub) * 64 + lane);
+    // Kept channels of this row, from the lines this pass is reading anyway:
+    // lane j of the row's first wave copies x[row, gidx[j]] (j < gr).
+    if constexpr (BF16IN) {
+      if (a.gr > 0 && sub == 0) {
+        const uint16_t* xr = reinterpret_cast<const uint16_t*>(a.x) + (size_t)row * a.ldx;
+        for (int j = lane; j < a.gr; j += 64) {
+          const int c = a.gidx[j];
+          a.gout[(size_t)row * a.ldg + j] = (c >= 0 && c < a.K) ? xr[c] : (uint16_t)0;
+        }
+      }
+    }
     // --- transform --------------------------------------------------------
     // After this, the value the definition quantizes is y = v * fl exactly
     // (fl = +-1/8 after a smoothing-then-rotation; the power-of-two factor
@@ -498,6 +515,13 @@ __global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
     }
   };
 
+  // the kept-channel indices, two per lane (a gather of at most 128)
+  int gkeep[2] = {-1, -1};
+  if constexpr (BF16IN) {
+    if (lane < a.gr) gkeep[0] = a.gidx[lane];
+    if (64 + lane < a.gr) gkeep[1] = a.gidx[64 + lane];
+  }
+
   int64_t task = (int64_t)blockIdx.x * 4 + wave;
   if (task < ntask) copy_tile(task, 0);
   for (int buf = 0; task < ntask; task += stride, buf ^= 1) {
@@ -532,6 +556,33 @@ __global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
       } else {
         v[4 * c] = __uint_as_float(d.x); v[4 * c + 1] = __uint_as_float(d.y);
         v[4 * c + 2] = __uint_as_float(d.z); v[4 * c + 3] = __uint_as_float(d.w);
+      }
+    }
+    // Kept channels inside this 64-channel block, read from the tile: lane
+    // j holds gidx[j] and gidx[64 + j]; a ballot names the ones in block b,
+    // and for each, every lane (a row) copies its element.  The task of
+    // block 0 writes the zeros of indices outside [0, K).
+    if constexpr (BF16IN) {
+      if (a.gr > 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j = 64 * h + lane;
+          const int c = gkeep[h];
+          const bool in = c >= 0 && c < a.K;
+          uint64_t m = __builtin_amdgcn_ballot_w64(j < a.gr && ((in && (c >> 6) == b) || (!in && b == 0)));
+          while (m) {
+            const int jj = __builtin_ctzll(m);
+            m &= m - 1;
+            const int cj = __builtin_amdgcn_readlane(c, jj);
+            uint16_t val = 0;
+            if (cj >= 0 && cj < a.K) {
+              const int cc = cj & 63;
+              val = *reinterpret_cast<const uint16_t*>(
+                  tile + lane * RB + (((cc >> 3) ^ (lane & 7 & (CPR - 1))) * 16) + (cc & 7) * 2);
+            }
+            if (live) a.gout[(size_t)row * a.ldg + 64 * h + jj] = val;
+          }
+        }
       }
     }
     // the copy two tasks ahead overwrites this buffer only after these
@@ -624,8 +675,10 @@ int64_t quant_max_k() { return 8LL * 64 * 16 * 4; }
 
 hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int64_t K, int64_t ldx,
                            const float* scale, float g, int rot, int order, void* codes, void* scales,
-                           float* amax_out, hipStream_t st) {
-  QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, amax_out};
+                           float* amax_out, hipStream_t st, const int32_t* gidx, int gr, void* gout,
+                           int64_t ldg) {
+  QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, amax_out,
+              gidx, gr, (uint16_t*)gout, ldg};
   if (mode == MODE_NVFP4 && R >= 256 && K % 64 == 0 && (rot == 0 || rot == 64)) {
     // resident grid: as many four-wave blocks as the tiles' LDS lets every CU hold
     const int64_t tasks = ((R + 63) / 64) * (K / 64);

@@ -26,7 +26,7 @@ ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
           "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
 ABI_VERSION = 1
 
-EXPORTS = ["quantize_act", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
+EXPORTS = ["quantize_act", "quantize_act_gather", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
            "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_workspace_size", "w4a4_status_string",
            "w4a4_last_error", "w4a4_abi_version"]
 
@@ -57,6 +57,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     qd, br = ctypes.POINTER(QDesc), ctypes.POINTER(BranchDesc)
     sig = {
         "quantize_act": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
+        "quantize_act_gather": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp, i64, vp, i64, vp],
         "pack_weights": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
         "w4a4_linear": [vp, vp, vp, vp, i64, i64, i64, i32, f32, br, vp, i32, i64, vp, sz, vp],
         "w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
@@ -154,6 +155,24 @@ def quantize_act(x: torch.Tensor, inv_smooth: Optional[torch.Tensor], fmt: str =
     _check("quantize_act", LIB.quantize_act(_ptr(x), _dtype_code(x), R, K, ld, _ptr(inv_smooth),
                                             ctypes.byref(q), _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def quantize_act_gather(x: torch.Tensor, inv_smooth: Optional[torch.Tensor], idx: torch.Tensor,
+                        fmt: str = "int4", *, fwht_block: int = 64, order="smooth_then_rotate",
+                        tensor_scale: float = 1.0, codes=None, scales=None, xo=None, stream=None):
+    """quantize_act plus the kept-channel operand xo = x[:, idx] from the same pass."""
+    R, K, ld = _rowmajor(x)
+    r = idx.shape[0]
+    if codes is None:
+        codes, scales = _alloc_codes(fmt, R, K, x.device)
+    if xo is None:
+        xo = torch.empty((R, r), dtype=torch.bfloat16, device=x.device)
+    q = qdesc(fmt, fwht_block, order, tensor_scale)
+    _check("quantize_act_gather",
+           LIB.quantize_act_gather(_ptr(x), _dtype_code(x), R, K, ld, _ptr(inv_smooth), ctypes.byref(q),
+                                   _ptr(codes), _ptr(scales), _ptr(idx), r, _ptr(xo), xo.stride(0),
+                                   _stream(stream)))
+    return codes, scales, xo
 
 
 def pack_weights(w: torch.Tensor, smooth: Optional[torch.Tensor], fmt: str = "int4", *,

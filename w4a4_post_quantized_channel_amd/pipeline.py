@@ -91,15 +91,22 @@ class QuantizedLinear:
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
         M = x.shape[0]
         b = self.buffers(M, x.device)
-        ops.quantize_act(x, self.inv_s, self.a_fmt, fwht_block=self.fwht_block, order=self.order,
-                         tensor_scale=self.g_a, codes=b["codes"], scales=b["scales"], stream=stream)
         bd = None
-        if self.branch is not None:
-            if self.branch["kind"] == "lowrank":
-                a = ops.lowrank_project(x, l1t=self.branch["l1t"], out=b["br_a"], stream=stream)
-            else:
-                a = ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
-            bd = ops.branch_desc(a, self.branch["lw"])
+        if self.branch is not None and self.branch["kind"] == "outlier" and x.dtype == torch.bfloat16:
+            # one pass over x: codes, scales and the kept channels
+            ops.quantize_act_gather(x, self.inv_s, self.branch["idx"], self.a_fmt, fwht_block=self.fwht_block,
+                                    order=self.order, tensor_scale=self.g_a, codes=b["codes"],
+                                    scales=b["scales"], xo=b["br_a"], stream=stream)
+            bd = ops.branch_desc(b["br_a"], self.branch["lw"])
+        else:
+            ops.quantize_act(x, self.inv_s, self.a_fmt, fwht_block=self.fwht_block, order=self.order,
+                             tensor_scale=self.g_a, codes=b["codes"], scales=b["scales"], stream=stream)
+            if self.branch is not None:
+                if self.branch["kind"] == "lowrank":
+                    a = ops.lowrank_project(x, l1t=self.branch["l1t"], out=b["br_a"], stream=stream)
+                else:
+                    a = ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
+                bd = ops.branch_desc(a, self.branch["lw"])
         y = b["y"] if out is None else out
         if self.fmt in ("int8", "w4a8", "fp8"):
             fn = {"int8": ops.w8a8_linear, "w4a8": ops.w4a8_linear, "fp8": ops.fp8_linear}[self.fmt]
