@@ -23,6 +23,13 @@ Sources (the pages this restates; no text is quoted):
 * LatentQuant abstract: NVFP4 W4A4 and activation quantize-dequantize.
 * Q-WAM abstract: a 16-bit low-rank branch plus 4-bit complement, both as
   dense matrix products.
+* QuantWAMs sec. 3.3, Eq. 14 and the text after it (the weight distortion
+  is governed by the layer's activation second moments Sigma_L; GPTQ
+  compensation follows Sigma_L, column scores serve only as an ordering
+  inside GPTQ, and the common rotation is fused into the weights):
+  GPTQ-style rounding of the transformed weights, given the Cholesky
+  factor of the damped inverse second-moment matrix (calibration data) and
+  a column order.
 * QuantWAMs, Experimental Details (quantization configuration) and
   sec. 4.4.3: some denoising steps keep their activations at 8 bits while
   the weights stay at 4 bits (W4A8); sec. 4.2: upgraded layers run FP8
@@ -361,6 +368,44 @@ def outlier_branch(x, idx, lw) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# GPTQ-style rounding (pack time)
+# ----------------------------------------------------------------------------
+def gptq_rows(wt, step, u, qmax: int, perm=None):
+    """Round the transformed weight rows ``wt`` (N x K, fp32) column by column
+    with error feedback.
+
+    ``step`` holds the per-row steps of the round-to-nearest quantizer (fp32);
+    ``u`` (K x K, float64) is the upper Cholesky factor of (Sigma + lambda I)^-1
+    with Sigma's rows and columns taken in processing order; ``perm`` is that
+    order (natural when None).  Column t of the processing order is rounded
+    (nearest, ties to even, clamped) from its current value; its error,
+    divided by u[t, t], updates every later column v by -err * u[t, v] (one
+    float64 product and one float64 subtraction per element).  Returns
+    (codes int8 [N, K] in the original column order, err float64 [N, K] in
+    processing order)."""
+    wt = np.asarray(wt, dtype=F32)
+    N, K = wt.shape
+    perm = np.arange(K) if perm is None else np.asarray(perm)
+    W = wt[:, perm].astype(F64)
+    sf = np.asarray(step, dtype=F32).astype(F64)
+    nz = sf > 0
+    Q = np.zeros((N, K), dtype=np.int64)
+    E = np.zeros((N, K), dtype=F64)
+    for t in range(K):
+        col = W[:, t]
+        q = np.zeros(N, dtype=F64)
+        q[nz] = np.clip(np.rint(col[nz] / sf[nz]), -qmax - 1, qmax)
+        err = (col - q * sf) / u[t, t]
+        if t + 1 < K:
+            W[:, t + 1:] -= np.outer(err, u[t, t + 1:])
+        Q[:, t] = q
+        E[:, t] = err
+    codes = np.empty((N, K), dtype=np.int8)
+    codes[:, perm] = Q.astype(np.int8)
+    return codes, E
+
+
+# ----------------------------------------------------------------------------
 # Whole path
 # ----------------------------------------------------------------------------
 def quantize_operand(x, scale, fmt: str, fwht_block=FWHT_BLOCK,
@@ -412,6 +457,12 @@ def linear(case, order="smooth_then_rotate", g_a=None, g_w=None) -> dict:
     fa, fw = OPERAND_FORMATS[case.fmt]
     A = quantize_operand(case.x, case.inv_s, fa, fb, order, g_a)
     W = quantize_operand(case.w, case.s, fw, fb, order, g_w)
+    gq = getattr(case, "gptq", None)
+    if gq is not None:   # GPTQ rounding of the weights instead of round-to-nearest
+        assert fw in ("int4", "int8")
+        codes, _ = gptq_rows(W["y"], W["scales"], gq["u"], INT4_QMAX if fw == "int4" else INT8_QMAX,
+                             gq["perm"])
+        W = dict(W, codes=codes, packed=pack_nibbles(codes) if fw == "int4" else codes.view(np.uint8))
     out = {"a": A, "w": W}
     if case.fmt in ("int4", "int8", "w4a8"):
         acc = int_gemm(A["codes"], W["codes"])

@@ -553,3 +553,58 @@ def test_fp8_linear_exact_on_grid_values():
     assert np.array_equal(O.e4m3_value(out["a"]["codes"]), x)
     assert np.array_equal(out["y"], x @ w.T)
     assert out["a"]["packed"].shape == (M, K) and out["a"]["packed"].dtype == np.uint8
+
+
+# -------------------------------------------------------------------- GPTQ
+def _gptq_setup(N=12, K=128, seed=70):
+    rng = np.random.default_rng(seed)
+    wt = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    wt[3] = 0                                           # an all-zero row
+    _, step, _ = O.quantize_int(wt, O.INT4_QMAX)
+    cal = WL.gptq_calibration(K, seed + 1)
+    return wt, step, cal
+
+
+def test_gptq_reduces_to_round_to_nearest_without_feedback():
+    """With U = I (no correlations) or any diagonal U the error feedback is
+    zero, so GPTQ gives the round-to-nearest codes, in any column order."""
+    wt, step, _ = _gptq_setup()
+    rtn, _, _ = O.quantize_int(wt, O.INT4_QMAX)
+    K = wt.shape[1]
+    c, _ = O.gptq_rows(wt, step, np.eye(K), O.INT4_QMAX)
+    assert np.array_equal(c, rtn)
+    perm = np.random.default_rng(5).permutation(K)
+    c, _ = O.gptq_rows(wt, step, np.diag(np.linspace(0.5, 2.0, K)), O.INT4_QMAX, perm)
+    assert np.array_equal(c, rtn)
+
+
+def test_gptq_error_identity():
+    """The rounding errors satisfy w - q * step = err @ U in processing order
+    (each column's error is its own err times U[t, t] plus the feedback it
+    received): a wrong sign, index or dropped update breaks it."""
+    wt, step, cal = _gptq_setup()
+    c, E = O.gptq_rows(wt, step, cal["u"], O.INT4_QMAX, cal["perm"])
+    p = cal["perm"]
+    lhs = wt[:, p].astype(np.float64) - c[:, p].astype(np.float64) * step.astype(np.float64)[:, None]
+    rhs = E @ cal["u"]
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-12 * np.abs(wt).max())
+    assert np.all(c[3] == 0)
+    assert c.min() >= -8 and c.max() <= 7
+
+
+def test_gptq_lowers_the_proxy_loss_and_respects_the_order():
+    """GPTQ's purpose: sum over rows of d Sigma d^T (d = dequantised - float
+    weights) is lower than round-to-nearest's; and running with a column order
+    equals running on pre-permuted columns with U for that order."""
+    wt, step, cal = _gptq_setup(N=32, K=192, seed=80)
+    sig = cal["sigma"]
+    c, _ = O.gptq_rows(wt, step, cal["u"], O.INT4_QMAX, cal["perm"])
+    rtn, _, _ = O.quantize_int(wt, O.INT4_QMAX)
+    def loss(codes):
+        d = codes * step.astype(np.float64)[:, None] - wt
+        return np.sum((d @ sig) * d)
+
+    assert loss(c) < 0.9 * loss(rtn)
+    p = cal["perm"]
+    c2, _ = O.gptq_rows(np.ascontiguousarray(wt[:, p]), step, cal["u"], O.INT4_QMAX)
+    assert np.array_equal(c2, c[:, p])

@@ -77,11 +77,35 @@ class Case:
                                     # {"kind": "outlier", "idx": int32[R], "lw": NxR}
     w_full: Optional[np.ndarray] = None  # float weight the whole layer approximates
     meta: dict = field(default_factory=dict)
+    gptq: Optional[dict] = None   # {"u": K x K float64 upper factor, "perm": int32[K], "sigma": K x K}
 
     @property
     def x_bits(self) -> np.ndarray:
         assert self.x_dtype == "bf16"
         return bf16_bits(self.x)
+
+
+def gptq_calibration(K: int, seed: int, rows: int = 256, damp: float = 0.01) -> dict:
+    """Synthetic GPTQ calibration in the quantizer's (transformed) space.
+
+    Sigma = A^T A / rows for A = Z (I + 0.3 G / sqrt(K)) D with Z, G standard
+    normal and D a log-normal per-channel gain (sigma 0.5): correlated
+    channels of unequal energy, standing in for the layer's activation
+    second moments.  Processing order: diag(Sigma) descending (stable).
+    u is the upper Cholesky factor of (Sigma_pp + damp * mean(diag) * I)^-1,
+    Sigma_pp being Sigma in that order, so that the inverse equals u^T u.
+    All float64."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((rows, K))
+    g = rng.standard_normal((K, K))
+    d = rng.lognormal(0.0, 0.5, size=K)
+    a = (z @ (np.eye(K) + 0.3 * g / np.sqrt(K))) * d[None, :]
+    sigma = a.T @ a / rows
+    perm = np.argsort(-np.diag(sigma), kind="stable").astype(np.int32)
+    sp = sigma[np.ix_(perm, perm)]
+    sp = sp + damp * np.mean(np.diag(sp)) * np.eye(K)
+    lower = np.linalg.cholesky(np.linalg.inv(sp))
+    return {"u": np.ascontiguousarray(lower.T), "perm": perm, "sigma": sigma}
 
 
 def _outliers(rng, K, n):
