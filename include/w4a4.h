@@ -172,6 +172,33 @@ int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t l
                  const float* smooth, const w4a4_qdesc* q,
                  void* codes, void* scales, void* stream);
 
+/* pack_weights_gptq -- pack_weights with GPTQ-style rounding instead of
+ * round-to-nearest (QuantWAMs sec. 3.3: GPTQ compensation governed by the
+ * layer's activation second moments, column scores used only as an
+ * ordering inside GPTQ, the common rotation fused into the weights).  The
+ * rows are transformed as in pack_weights and keep its per-row steps; the
+ * columns are then rounded in the order perm (NULL: natural), each
+ * column's error over u[t][t] updating every later column v by
+ * w -= err * u[t][v] in float64 (one product, one subtraction, in t
+ * order).
+ *  q        fmt INT4 or INT8 (W4A8 weights are INT4).
+ *  u        device float64 K x K, row-major: the upper Cholesky factor of
+ *           (Sigma + lambda I)^-1 with Sigma, the activation second moments
+ *           in the quantizer's transformed space, in processing order
+ *           (calibration data; only the upper triangle is read, u[t][t] > 0).
+ *  perm     device int32[K], a permutation, or NULL.
+ *  workspace device scratch of at least w4a4_gptq_workspace_size(N, K)
+ *           bytes, 256-byte aligned (required).
+ * Shape rules: as pack_weights, and K % 32 == 0.  Offline: many launches,
+ * not for the hot path. */
+int pack_weights_gptq(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                      const float* smooth, const w4a4_qdesc* q, const double* u,
+                      const int32_t* perm, void* codes, void* scales,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pack_weights_gptq needs for N x K weights. */
+size_t w4a4_gptq_workspace_size(int64_t N, int64_t K);
+
 /* w4a4_linear -- y = alpha * dequant(A_codes . W_codes^T) (+ branch).
  * FoldQuantVLA contribution 4 (W4A4 projections) and overview (integer
  * GEMMs with per-token / per-channel scales); QuantWAMs sec. 4.2 (NVFP4

@@ -188,6 +188,23 @@ def test_quantize_act_gather_rejects_bad_arguments(ops):
     assert g(M=0, idx=None, xo=None) == 0       # empty batch
 
 
+def test_pack_weights_gptq_rejects_bad_arguments(ops):
+    L = ops.LIB
+    need = L.w4a4_gptq_workspace_size(64, 256)
+    assert need >= 64 * 256 * (4 + 8 + 1)
+    WS = ctypes.c_void_p(0x100000)
+    g = lambda K=256, fmt=0, u=FAKE, ws=WS, wsb=need, perm=None: L.pack_weights_gptq(
+        FAKE, 1, 64, K, K, None, _q(ops, fmt=fmt), u, perm, FAKE2, FAKE2, ws, wsb, None)
+    assert g(fmt=2) == -4 and g(fmt=4) == -4     # INT4 / INT8 only
+    assert g(K=96) == -2                         # K % 64 with the rotation
+    assert g(u=None) == -1
+    assert g(u=ctypes.c_void_p(0x10004)) == -3
+    assert g(perm=ctypes.c_void_p(0x10002)) == -3
+    assert g(ws=None) == -5 and g(wsb=need - 1) == -5
+    assert g(ws=ctypes.c_void_p(0x100080)) == -3
+    assert L.w4a4_gptq_workspace_size(0, 256) == 0
+
+
 def test_lowrank_rejects_bad_arguments(ops):
     L = ops.LIB
     # both or neither of l1 / idx

@@ -342,6 +342,45 @@ def test_quantize_act_gather(ops, pipe, M, K, fmt, r):
     assert np.array_equal(xo.view(torch.int16).cpu().numpy().view(np.uint16), want)
 
 
+@pytest.mark.parametrize("N,K,fmt,use_perm", [(64, 256, "int4", True), (130, 320, "int4", True),
+                                              (48, 1024, "int4", False), (70, 448, "int8", True),
+                                              (300, 192, "int4", True)])
+def test_pack_weights_gptq(ops, pipe, N, K, fmt, use_perm):
+    """GPTQ-style rounding on the GPU: codes and steps bit-exact against the
+    oracle's sequential float64 evaluation (with a zero row, ragged N)."""
+    case = WL.linear_case(8, N, K, seed=90 + N, fmt=fmt, n_outliers=4, outlier_gain=10.0, gptq=True)
+    case.w[5] = 0
+    if not use_perm:
+        case.gptq["perm"] = np.arange(K, dtype=np.int32)
+        sp = case.gptq["sigma"] + 0.01 * np.mean(np.diag(case.gptq["sigma"])) * np.eye(K)
+        case.gptq["u"] = np.ascontiguousarray(np.linalg.cholesky(np.linalg.inv(sp)).T)
+    t = pipe.case_to_device(case)
+    ref = O.quantize_operand(case.w, case.s, fmt, case.fwht_block)
+    qmax = O.INT4_QMAX if fmt == "int4" else O.INT8_QMAX
+    codes_ref, _ = O.gptq_rows(ref["y"], ref["scales"], case.gptq["u"], qmax, case.gptq["perm"])
+    import time
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    codes, scales = ops.pack_weights_gptq(t["w"], t["s"], t["gptq"]["u"], t["gptq"]["perm"], fmt,
+                                          fwht_block=case.fwht_block)
+    torch.cuda.synchronize()
+    _report("gptq", N=N, K=K, fmt=fmt, ms=f"{(time.perf_counter() - t0) * 1e3:.2f}",
+            changed_vs_rtn=f"{np.mean(codes_ref != ref['codes']):.3f}")
+    assert np.array_equal(_np(scales), ref["scales"])
+    assert np.array_equal(unpack_codes(fmt, _np(codes)), codes_ref)
+
+
+def test_gptq_linear_end_to_end(ops, pipe):
+    """A W4A4 layer packed with GPTQ rounding: output within tolerance of the
+    oracle's GPTQ linear."""
+    case = WL.linear_case(40, 96, 256, seed=95, fmt="int4", n_outliers=4, outlier_gain=15.0, gptq=True)
+    layer, t, y = _run(pipe, case)
+    ref = _oracle(case)
+    nw = check_operand("int4", _np(layer.w_codes), _np(layer.w_scales), ref["w"], what="weights")
+    assert nw == 0
+    check_output(_np(y), ref["y"], 1e-2)
+
+
 def test_determinism_and_side_stream(ops, pipe):
     case = WL.linear_case(64, 2048, 2048, seed=51, n_outliers=16, outlier_gain=15.0)
     layer, t = pipe.build_layer(case)

@@ -167,6 +167,34 @@ int quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t l
   return run_quant("quantize_act", x, x_dtype, M, K, ldx, inv_smooth, q, codes, scales, stream);
 }
 
+int pack_weights_gptq(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const float* smooth,
+                      const w4a4_qdesc* q, const double* u, const int32_t* perm, void* codes, void* scales,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pack_weights_gptq";
+  int st = check_quant(fn, w, w_dtype, N, K, ldw, smooth, q, true, codes, scales);
+  if (st != W4A4_OK) return st;
+  if (q->fmt != W4A4_FMT_INT4 && q->fmt != W4A4_FMT_INT8)
+    return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: GPTQ rounding is for INT4 / INT8 codes", fn);
+  if (K % 32 != 0) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld not a multiple of 32", fn, (long long)K);
+  if (N == 0) return ok();
+  if (N > INT32_MAX / 2 || K > (1 << 20)) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: too large", fn);
+  if (!u) return fail(W4A4_ERR_INVALID_ARG, "%s: u is NULL", fn);
+  if (!aligned(u, 8) || (perm && !aligned(perm, 4))) return fail(W4A4_ERR_MISALIGNED, "%s: u / perm misaligned", fn);
+  const size_t need = w4a4::gptq_workspace(N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(W4A4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(W4A4_ERR_MISALIGNED, "%s: workspace not 256-byte aligned", fn);
+  hipError_t e = w4a4::launch_gptq(q->fmt == W4A4_FMT_INT4 ? 7 : 127, w_dtype == W4A4_DT_BF16, w, N, K, ldw, smooth,
+                                   q->fwht_block, q->order, u, perm, codes, (float*)scales, workspace,
+                                   (hipStream_t)stream);
+  return launch_status(e, fn);
+}
+
+size_t w4a4_gptq_workspace_size(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return w4a4::gptq_workspace(N, K);
+}
+
 int quantize_act_gather(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const float* inv_smooth,
                         const w4a4_qdesc* q, void* codes, void* scales, const int32_t* idx, int64_t r, void* xo,
                         int64_t ldo, void* stream) {

@@ -51,6 +51,15 @@ size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 // 4 fp8
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st);
 
+// gptq.hip --------------------------------------------------------------------
+// GPTQ-style rounding at pack time: codes (int4 packed if qmax == 7, else
+// int8) and the per-row steps of N rows; u fp64 K x K (processing order),
+// perm int32[K] or null; workspace of gptq_workspace(N, K) bytes.
+size_t gptq_workspace(int64_t N, int64_t K);
+hipError_t launch_gptq(int qmax, bool bf16in, const void* x, int64_t N, int64_t K, int64_t ldx, const float* smooth,
+                       int rot, int order, const double* u, const int32_t* perm, void* codes, float* scales,
+                       void* workspace, hipStream_t st);
+
 // branch.hip ----------------------------------------------------------------
 hipError_t launch_lowrank_project(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   const uint16_t* l1t, const int32_t* idx, int r,

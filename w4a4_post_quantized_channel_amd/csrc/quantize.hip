@@ -56,7 +56,11 @@ struct QuantArgs {
 // stored as its even-K codes then its odd-K codes (the order packed int4
 // weight codes take when widened to bytes).
 // MODE_FP8: OCP E4M3 codes with one step amax/448 per row.
-enum { MODE_INT4 = 0, MODE_INT8 = 1, MODE_NVFP4 = 2, MODE_AMAX = 3, MODE_INT8W = 4, MODE_FP8 = 5 };
+// MODE_Y4 / MODE_Y8: no codes; the transformed row y itself (fp32, row-major
+// K) and the round-to-nearest step amax/7 or amax/127 (the input of
+// GPTQ-style rounding).
+enum { MODE_INT4 = 0, MODE_INT8 = 1, MODE_NVFP4 = 2, MODE_AMAX = 3, MODE_INT8W = 4, MODE_FP8 = 5,
+       MODE_Y4 = 6, MODE_Y8 = 7 };
 
 constexpr float kTinyStep = 8.271806125530277e-25f;  // 2^-80
 
@@ -267,8 +271,9 @@ __device__ __forceinline__ float transform_slot(const SlotRaw<BF16IN>& raw, floa
 
 template <int MODE, bool BF16IN, int NC, int WPR>
 __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(QuantArgs a) {
-  constexpr int QMAX = MODE == MODE_INT4 ? 7 : 127;
+  constexpr int QMAX = (MODE == MODE_INT4 || MODE == MODE_Y4) ? 7 : 127;
   constexpr bool I8 = MODE == MODE_INT8 || MODE == MODE_INT8W;
+  constexpr bool YOUT = MODE == MODE_Y4 || MODE == MODE_Y8;
   constexpr bool F8 = MODE == MODE_FP8;
   constexpr float QDIV = F8 ? 448.0f : (float)QMAX;   // step = amax / QDIV
   const int lane = threadIdx.x & 63;
@@ -325,7 +330,7 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
     // slot takes the exact path, which forms y itself.
     // Integer modes need the whole row for its maximum; NVFP4 transforms
     // and quantizes one slot at a time.
-    if constexpr (MODE == MODE_INT4 || I8 || F8 || MODE == MODE_AMAX) {
+    if constexpr (MODE == MODE_INT4 || I8 || F8 || YOUT || MODE == MODE_AMAX) {
       float v[NC][16];
       float fl = 1.0f;
 #pragma unroll
@@ -354,6 +359,18 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
         const float rstep = fast ? 1.0f / step : 0.f;
         const float D = step / fl, rD = rstep * fl;   // exact power-of-two rescaling
         if (lane == 0 && sub == 0) reinterpret_cast<float*>(a.scales)[row] = step;
+        if constexpr (YOUT) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int s = (c * WPR + sub) * 64 + lane;
+            if (s >= nslots) continue;
+            float4* yp = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.codes) + (size_t)row * a.K + s * 16);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              yp[k] = make_float4(v[c][4 * k] * fl, v[c][4 * k + 1] * fl, v[c][4 * k + 2] * fl, v[c][4 * k + 3] * fl);
+          }
+          continue;
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int s = (c * WPR + sub) * 64 + lane;
@@ -699,7 +716,8 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   // One wave per row when there are many rows and the row fits five chunks
   // per lane (the factors then stay in registers); else four waves per row,
   // eight for integer codes of rows longer than 4096.
-  const bool intmode = mode == MODE_INT4 || mode == MODE_INT8 || mode == MODE_INT8W || mode == MODE_FP8;
+  const bool intmode = mode == MODE_INT4 || mode == MODE_INT8 || mode == MODE_INT8W || mode == MODE_FP8 ||
+                       mode == MODE_Y4 || mode == MODE_Y8;
   int wpr = (R >= 1024 && nslots <= 5 * 64) ? 1 : 4;
   if (wpr == 4 && intmode && nslots > 4 * 64) wpr = 8;
   const int nc = round_nc((int)((nslots + 64 * wpr - 1) / (64 * wpr)));
@@ -720,6 +738,10 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
                                           : launch_nc<MODE_INT8W, false, 8>(nc, grid, st, a);
     if (mode == MODE_FP8) return bf16in ? launch_nc<MODE_FP8, true, 8>(nc, grid, st, a)
                                         : launch_nc<MODE_FP8, false, 8>(nc, grid, st, a);
+    if (mode == MODE_Y4) return bf16in ? launch_nc<MODE_Y4, true, 8>(nc, grid, st, a)
+                                       : launch_nc<MODE_Y4, false, 8>(nc, grid, st, a);
+    if (mode == MODE_Y8) return bf16in ? launch_nc<MODE_Y8, true, 8>(nc, grid, st, a)
+                                       : launch_nc<MODE_Y8, false, 8>(nc, grid, st, a);
     return bf16in ? launch_nc<MODE_INT8, true, 8>(nc, grid, st, a) : launch_nc<MODE_INT8, false, 8>(nc, grid, st, a);
   }
 #define W4A4_DISPATCH(MODE)                                                          \
@@ -733,6 +755,8 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   W4A4_DISPATCH(MODE_INT8)
   W4A4_DISPATCH(MODE_INT8W)
   W4A4_DISPATCH(MODE_FP8)
+  W4A4_DISPATCH(MODE_Y4)
+  W4A4_DISPATCH(MODE_Y8)
   W4A4_DISPATCH(MODE_NVFP4)
   W4A4_DISPATCH(MODE_AMAX)
 #undef W4A4_DISPATCH

@@ -26,7 +26,7 @@ ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
           "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
 ABI_VERSION = 1
 
-EXPORTS = ["quantize_act", "quantize_act_gather", "pack_weights", "w4a4_linear", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
+EXPORTS = ["quantize_act", "quantize_act_gather", "pack_weights", "pack_weights_gptq", "w4a4_gptq_workspace_size", "w4a4_linear", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
            "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_workspace_size", "w4a4_status_string",
            "w4a4_last_error", "w4a4_abi_version"]
 
@@ -59,6 +59,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "quantize_act": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
         "quantize_act_gather": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp, i64, vp, i64, vp],
         "pack_weights": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
+        "pack_weights_gptq": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp, vp, vp, sz, vp],
+        "w4a4_gptq_workspace_size": [i64, i64],
         "w4a4_linear": [vp, vp, vp, vp, i64, i64, i64, i32, f32, br, vp, i32, i64, vp, sz, vp],
         "w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
         "w4a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
@@ -77,6 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = ctypes.c_int
     lib.w4a4_workspace_size.restype = ctypes.c_size_t
+    lib.w4a4_gptq_workspace_size.restype = ctypes.c_size_t
     lib.w4a4_lowrank_width.restype = ctypes.c_int64
     lib.w4a4_status_string.restype = ctypes.c_char_p
     lib.w4a4_last_error.restype = ctypes.c_char_p
@@ -154,6 +157,23 @@ def quantize_act(x: torch.Tensor, inv_smooth: Optional[torch.Tensor], fmt: str =
     q = qdesc(fmt, fwht_block, order, tensor_scale)
     _check("quantize_act", LIB.quantize_act(_ptr(x), _dtype_code(x), R, K, ld, _ptr(inv_smooth),
                                             ctypes.byref(q), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def pack_weights_gptq(w: torch.Tensor, smooth: Optional[torch.Tensor], u: torch.Tensor,
+                      perm: Optional[torch.Tensor] = None, fmt: str = "int4", *, fwht_block: int = 64,
+                      order="smooth_then_rotate", codes=None, scales=None, workspace=None, stream=None):
+    """pack_weights with GPTQ-style rounding (u: float64 K x K upper factor, perm: int32[K] or None)."""
+    R, K, ld = _rowmajor(w)
+    if codes is None:
+        codes, scales = _alloc_codes(fmt, R, K, w.device)
+    if workspace is None:
+        workspace = torch.empty(int(LIB.w4a4_gptq_workspace_size(R, K)), dtype=torch.uint8, device=w.device)
+    assert u.dtype == torch.float64 and u.is_contiguous()
+    q = qdesc(fmt, fwht_block, order)
+    _check("pack_weights_gptq", LIB.pack_weights_gptq(
+        _ptr(w), _dtype_code(w), R, K, ld, _ptr(smooth), ctypes.byref(q), _ptr(u), _ptr(perm), _ptr(codes),
+        _ptr(scales), _ptr(workspace), workspace.numel(), _stream(stream)))
     return codes, scales
 
 

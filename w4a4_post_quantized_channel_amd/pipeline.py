@@ -39,7 +39,7 @@ class QuantizedLinear:
     def __init__(self, w: torch.Tensor, s: Optional[torch.Tensor], inv_s: Optional[torch.Tensor],
                  fmt: str = "int4", *, fwht_block: int = 64, order: str = "smooth_then_rotate",
                  branch: Optional[dict] = None, y_dtype=torch.bfloat16, use_workspace: bool = True,
-                 stream=None):
+                 gptq: Optional[dict] = None, stream=None):
         self.fmt, self.fwht_block, self.order = fmt, fwht_block, order
         # W4A8 (the 8-bit-activation denoising steps) keeps 4-bit weight codes;
         # its activations are int8 codes in the W4A8 layout
@@ -53,8 +53,12 @@ class QuantizedLinear:
         if fmt == "nvfp4":
             amax = ops.transform_amax(w, s, fwht_block=fwht_block, order=order, stream=stream)
             self.g_w = nvfp4_scale_from_amax(float(amax.item()))
-        self.w_codes, self.w_scales = ops.pack_weights(w, s, w_fmt, fwht_block=fwht_block, order=order,
-                                                       tensor_scale=self.g_w, stream=stream)
+        if gptq is not None:   # GPTQ-style rounding: {"u": float64 K x K, "perm": int32[K] or None}
+            self.w_codes, self.w_scales = ops.pack_weights_gptq(w, s, gptq["u"], gptq.get("perm"), w_fmt,
+                                                                fwht_block=fwht_block, order=order, stream=stream)
+        else:
+            self.w_codes, self.w_scales = ops.pack_weights(w, s, w_fmt, fwht_block=fwht_block, order=order,
+                                                           tensor_scale=self.g_w, stream=stream)
         self.g_a = 1.0
         self._bufs = {}
 
@@ -146,6 +150,10 @@ def case_to_device(case, device="cuda"):
         else:
             br["idx"] = torch.from_numpy(case.branch["idx"].astype(np.int32)).to(device)
     t["branch"] = br
+    t["gptq"] = None
+    if getattr(case, "gptq", None) is not None:
+        t["gptq"] = {"u": torch.from_numpy(np.ascontiguousarray(case.gptq["u"])).to(device),
+                     "perm": torch.from_numpy(case.gptq["perm"].astype(np.int32)).to(device)}
     return t
 
 
@@ -154,7 +162,7 @@ def build_layer(case, device="cuda", order="smooth_then_rotate", calibrate=True,
     t = case_to_device(case, device)
     y_dtype = torch.float32 if case.y_dtype == "f32" else torch.bfloat16
     layer = QuantizedLinear(t["w"], t["s"], t["inv_s"], case.fmt, fwht_block=case.fwht_block, order=order,
-                            branch=t["branch"], y_dtype=y_dtype, use_workspace=use_workspace)
+                            branch=t["branch"], y_dtype=y_dtype, use_workspace=use_workspace, gptq=t["gptq"])
     if calibrate:
         layer.calibrate(t["x"])
     return layer, t

@@ -141,14 +141,15 @@ def linear_case(M: int, N: int, K: int, *, seed: int, fmt: str = "int4",
                 smooth: bool = True, fwht_block: int = 64,
                 lowrank: int = 0, lowrank_std: float = 0.05,
                 keep_channels: int = 0, name: str = "case",
-                x_override: Optional[np.ndarray] = None) -> Case:
+                x_override: Optional[np.ndarray] = None, gptq: bool = False) -> Case:
     """Draw one seeded linear case.
 
     Draw order (fixed): X, outlier channel indices, per-row gains, W, U, V, R0.
     ``keep_channels`` > 0 selects the top-energy raw channels of X (sum of
     squares in float64, ties to the lower index) for the bf16 outlier branch.
     ``lowrank`` > 0 builds W = U V^T + R0 and keeps the bf16 rank-r factors as
-    the branch, quantizing the residual W - L1 L2.
+    the branch, quantizing the residual W - L1 L2.  ``gptq`` attaches the
+    synthetic GPTQ calibration of ``gptq_calibration(K, seed + 7)``.
     """
     if y_dtype is None:
         y_dtype = "f32" if x_dtype == "f32" else "bf16"
@@ -202,7 +203,8 @@ def linear_case(M: int, N: int, K: int, *, seed: int, fmt: str = "int4",
         s = inv_s = None
     return Case(name=name, M=M, N=N, K=K, fmt=fmt, x_dtype=x_dtype, y_dtype=y_dtype,
                 x=x, w=w, s=s, inv_s=inv_s, fwht_block=fwht_block, branch=branch,
-                w_full=w_full, meta={"seed": seed, "outliers": idx})
+                w_full=w_full, meta={"seed": seed, "outliers": idx},
+                gptq=gptq_calibration(K, seed + 7) if gptq else None)
 
 
 def _silu(v):
