@@ -482,20 +482,25 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
 // smoothing factors are the same for the whole wave (scalar loads).  NVFP4
 // needs no row-wide reduction (its scales are per 16 elements and the tensor
 // scale is fixed), so every (rows, block) pair is an independent task.
-// The grid is sized to stay resident; each wave walks its tasks with two
-// LDS tiles, copying the next task's tile while it transforms and encodes
-// the current one, so the HBM reads overlap the vector work.
+// The grid is sized to stay resident; each wave walks its tasks and copies
+// the next task's tile while it transforms and encodes the current one, so
+// the HBM reads overlap the vector work.  NB = 2: two LDS tiles per wave,
+// the next copy issued before the current tile is read; NB = 1: one tile,
+// the next copy issued as soon as the current tile's reads have returned,
+// which halves the LDS per wave and lets twice as many waves share a SIMD
+// (the vector work of one wave then hides the stalls of the others).
 template <bool BF16IN>
 constexpr int nvfp4_lanes_tile() { return 64 * 64 * (BF16IN ? 2 : 4); }
 
-template <bool BF16IN, bool ROT>
-__global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
+template <bool BF16IN, bool ROT, int NB>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1)))
+quant_nvfp4_lanes_kernel(QuantArgs a) {
   constexpr int ESZ = BF16IN ? 2 : 4;
   constexpr int RB = 64 * ESZ;              // bytes of one row's 64-element block
   constexpr int TILE = nvfp4_lanes_tile<BF16IN>();   // one wave's 64 x 64 tile
   constexpr int NCOPY = TILE / 1024;        // copy instructions per tile
   __shared__ float2 stab[128];
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][2][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][NB][TILE];
   for (int e = threadIdx.x; e < 128; e += blockDim.x) {
     const float S = e < 0x7F ? e4m3_to_f32((uint32_t)e) * a.g : 0.f;
     stab[e] = make_float2(S, S > 0.f ? 1.0f / S : 0.f);  // IEEE division
@@ -541,7 +546,7 @@ __global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
 
   int64_t task = (int64_t)blockIdx.x * 4 + wave;
   if (task < ntask) copy_tile(task, 0);
-  for (int buf = 0; task < ntask; task += stride, buf ^= 1) {
+  for (int buf = 0; task < ntask; task += stride, buf ^= (NB - 1)) {
     const int64_t grp = task / nblk;
     const int b = (int)(task - grp * nblk);
     const int64_t row = grp * 64 + lane;
@@ -551,7 +556,7 @@ __global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
     // leaves just the copies issued last.
     // (The copies are issued as inline assembly, which the compiler does
     // not track, so these explicit waits are the only ones.)
-    if (task + stride < ntask) {
+    if (NB == 2 && task + stride < ntask) {
       copy_tile(task + stride, buf ^ 1);
       wait_vmcnt<NCOPY>();
     } else {
@@ -602,9 +607,19 @@ __global__ void __launch_bounds__(256) quant_nvfp4_lanes_kernel(QuantArgs a) {
         }
       }
     }
-    // the copy two tasks ahead overwrites this buffer only after these
-    // reads have returned (their values are consumed below)
+    // NB = 2: the copy two tasks ahead overwrites this buffer only after
+    // these reads have returned (their values are consumed below).  NB = 1:
+    // wait for every LDS read of this tile, then start the next task's copy
+    // into it.
     __builtin_amdgcn_wave_barrier();
+    if constexpr (NB == 1) {
+      if (task + stride < ntask) {
+        asm volatile("" ::: "memory");         // every tile read issued above this point
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited on
+        asm volatile("" ::: "memory");
+        copy_tile(task + stride, 0);
+      }
+    }
     // the block's 64 factors are the same for the whole wave: scalar loads
     const __attribute__((address_space(4))) float* sc =
         (const __attribute__((address_space(4))) float*)(a.scale + (has_scale ? b * 64 : 0));
@@ -699,16 +714,17 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
   if (mode == MODE_NVFP4 && R >= 256 && K % 64 == 0 && (rot == 0 || rot == 64)) {
     // resident grid: as many four-wave blocks as the tiles' LDS lets every CU hold
     const int64_t tasks = ((R + 63) / 64) * (K / 64);
-    const int per_cu = (160 * 1024) / (8 * (bf16in ? nvfp4_lanes_tile<true>() : nvfp4_lanes_tile<false>()) + 1024);
+    constexpr int NB = 1;
+    const int per_cu = (160 * 1024) / (NB * 4 * (bf16in ? nvfp4_lanes_tile<true>() : nvfp4_lanes_tile<false>()) + 1024);
     int64_t blocks = (tasks + 3) / 4;
     if (blocks > 256 * per_cu) blocks = 256 * per_cu;
     const dim3 grid((unsigned)blocks);
     if (bf16in) {
-      if (rot) hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<true, true>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<true, false>), grid, dim3(256), 0, st, a);
+      if (rot) hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<true, true, NB>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<true, false, NB>), grid, dim3(256), 0, st, a);
     } else {
-      if (rot) hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<false, true>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<false, false>), grid, dim3(256), 0, st, a);
+      if (rot) hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<false, true, NB>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((quant_nvfp4_lanes_kernel<false, false, NB>), grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();
   }
