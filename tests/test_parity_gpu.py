@@ -85,6 +85,9 @@ SMALL = [
     # >= 256 rows: the row-per-lane NVFP4 quantizer (ragged last group of 64 rows)
     ("nvfp4_rows", 300, 96, 320, "nvfp4", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=8)),
     ("nvfp4_rows_f32", 260, 64, 256, "nvfp4", "f32", dict(n_outliers=4, outlier_gain=20.0)),
+    # the 256x160 NVFP4 tile (weights widened once per workgroup): ragged M and N,
+    # and a last K stage of half length
+    ("nvfp4_wide_tile", 2600, 3210, 1088, "nvfp4", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=16)),
     # W4A8: int8 activation codes x int4 weight codes
     ("w4a8_ragged", 70, 96, 448, "w4a8", "bf16", dict(n_outliers=6, outlier_gain=15.0)),
     ("w4a8_tiles", 160, 256, 512, "w4a8", "bf16", dict(n_outliers=8, outlier_gain=15.0, row_gain_sigma=0.5)),

@@ -633,6 +633,218 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   }
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4, many tokens, weights widened once per workgroup.
+//
+// In the kernel above every wave widens its own operand fragments, so in a
+// 256x160 tile each weight fragment is widened by all four wave rows (and
+// each activation fragment by both wave columns).  Here the workgroup
+// widens each stage of its weight tile once: every thread loads 16-byte
+// chunks of packed codes (32 E2M1 codes of one row, two 16-element blocks)
+// and the word holding their two E4M3 scales, widens them to exact fp16
+// value(code) * value(scale), and stores them in an fp16 stage in LDS.  The
+// waves read their weight operands from that stage and still widen their
+// activation operands from the packed stage.
+//
+// fp16 weight stage: 160 rows x 128 K values (256 bytes, 16 slots of 16).
+// Logical slot 4q + t of a row holds K values 32q + 8t .. 32q + 8t + 7 (the
+// ones lane group q multiplies at MFMA step t, in the same order as the
+// activation side) at physical slot (4q + t) ^ (row & 15), so the 16 rows
+// read by one fragment, and the rows written by one wave, fall on distinct
+// banks.
+//
+// Iteration s: wait for everything issued in iteration s - 1 (activation
+// stage s + 1, weight chunks s + 1); widen the chunks into fp16 buffer
+// (s + 1) % 2; copy activation stage s + 2; load weight chunks s + 2; run
+// stage s; wait for the LDS stores and barrier.  Buffers written in
+// iteration s were last read in iteration s - 1, before its barrier.
+namespace {
+constexpr int kCbTI = 4, kCbTJ = 5, kCbWR = 4, kCbWC = 2, kCbNW = kCbWR * kCbWC;
+constexpr int kCbBM = kCbWR * kCbTI * 16, kCbBN = kCbWC * kCbTJ * 16;   // 256 x 160
+constexpr int kCbP = 64;                        // packed bytes per row per stage (128 K)
+constexpr int kCbSP = 8;                        // E4M3 scale bytes per row per stage
+constexpr int kCbA = kCbBM * kCbP, kCbSA = kCbBM * kCbSP;
+constexpr int kCbASTAGE = kCbA + kCbSA;         // one packed activation stage
+constexpr int kCbNA = 3;                        // activation stage buffers
+constexpr int kCbBROW = 256;                    // fp16 bytes per weight row per stage
+constexpr int kCbBSTAGE = kCbBN * kCbBROW;      // one fp16 weight stage
+constexpr int kCbBOFF = kCbNA * kCbASTAGE;
+constexpr int kCbPAD = kCbBOFF + 2 * kCbBSTAGE;  // DMA pad target
+constexpr int kCbPIPE = kCbPAD + 1024;
+constexpr int kCbEPI = kCbNW * epilogue_stage_bytes<kCbTI, kCbTJ>();
+constexpr int kCbBR_OFF = (kCbEPI + 1023) / 1024 * 1024;
+constexpr int kCbBR_END = kCbBR_OFF + (kCbBM + kCbBN) * 2 * kBrLdsMax;
+constexpr int kCbLDS = kCbPIPE > kCbBR_END ? kCbPIPE : kCbBR_END;
+constexpr int kCbCH = kCbBN * kCbP / 16;                            // weight chunks per stage
+constexpr int kCbNCH = (kCbCH + 64 * kCbNW - 1) / (64 * kCbNW);     // chunks per thread
+constexpr int kCbDA = kCbA / 1024 / kCbNW + kCbSA / 256 / kCbNW;    // activation copies per wave per stage
+static_assert(kCbA % (1024 * kCbNW) == 0 && kCbSA % (256 * kCbNW) == 0, "whole copy rounds");
+static_assert(kCbLDS <= 160 * 1024, "LDS");
+}  // namespace
+
+__global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    gemm_nvfp4_cb_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  constexpr int TI = kCbTI, TJ = kCbTJ, WC = kCbWC;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kCbLDS];
+
+  // tile order as in the kernel above
+  const int nwg = gridDim.x, wid = blockIdx.x;
+  const int t = (nwg % 8 == 0) ? (wid % 8) * (nwg / 8) + wid / 8 : wid;
+  constexpr int GM = 4;
+  const int gsz = GM * tiles_n;
+  const int grp = t / gsz, gm0 = grp * GM;
+  const int gh = min(GM, tiles_m - gm0);
+  const int tm = gm0 + (t % gsz) % gh, tn = (t % gsz) / gh;
+  const int m0 = tm * kCbBM, n0 = tn * kCbBN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int wm0 = (wave / WC) * TI * 16, wn0 = (wave % WC) * TJ * 16;
+
+  const int64_t rowbytes = g.K >> 1, srow = g.K >> 4;
+  const int nk = (g.K + 127) / 128;
+  const v4u rsA = rsrc_words(g.a + (int64_t)m0 * rowbytes, (uint32_t)(min(kCbBM, g.M - m0) * rowbytes));
+  const v4u rsSA = rsrc_words(reinterpret_cast<const uint8_t*>(g.sa) + (int64_t)m0 * srow,
+                              (uint32_t)(min(kCbBM, g.M - m0) * srow));
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.w + (int64_t)n0 * rowbytes, (uint32_t)(min(kCbBN, g.N - n0) * rowbytes));
+  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(reinterpret_cast<const uint8_t*>(g.sw) + (int64_t)n0 * srow,
+                                               (uint32_t)(min(kCbBN, g.N - n0) * srow));
+
+  uint8_t* pad = smem + kCbPAD;
+  CodeCopy<kCbP, kCbA / 1024, kCbNW> cpA;
+  ScaleCopy<kCbSP, kCbSA / 256, kCbNW> cpSA;
+  cpA.init(wave, lane, rowbytes);
+  cpSA.init(wave, lane, srow);
+  auto copy_a = [&](int s) {
+    uint8_t* base = smem + (s % kCbNA) * kCbASTAGE;
+    cpA.issue(rsA, base, pad, rowbytes, s, wave);
+    cpSA.issue(rsSA, base + kCbA, pad, srow, s, wave);
+  };
+
+  // this thread's weight chunks: c = tid + 512 h, row c / 4, quarter c % 4
+  int crow[kCbNCH], cq[kCbNCH];
+  bool cval[kCbNCH];
+#pragma unroll
+  for (int h = 0; h < kCbNCH; ++h) {
+    const int c = tid + 64 * kCbNW * h;
+    cval[h] = c < kCbCH;
+    crow[h] = c >> 2;
+    cq[h] = c & 3;
+  }
+  uint4 wc[kCbNCH];
+  uint32_t ws[kCbNCH];
+  auto load_w = [&](int s) {
+#pragma unroll
+    for (int h = 0; h < kCbNCH; ++h) {
+      const int64_t kb = (int64_t)s * kCbP + cq[h] * 16;   // byte of the chunk within its row
+      const bool ok = cval[h] && kb < rowbytes;
+      wc[h] = buf_load16(rW, ok ? (uint32_t)(crow[h] * rowbytes + kb) : kOOB);
+      ws[h] = buf_load4(rSW, ok ? (uint32_t)(crow[h] * srow + (int64_t)s * kCbSP + (cq[h] >> 1) * 4) : kOOB);
+    }
+  };
+  auto widen_w = [&](int s) {
+    uint8_t* bb = smem + kCbBOFF + (s & 1) * kCbBSTAGE;
+#pragma unroll
+    for (int h = 0; h < kCbNCH; ++h) {
+      if (!cval[h]) continue;
+      const uint32_t two = (ws[h] >> (16 * (cq[h] & 1))) & 0xFFFFu;   // scales of blocks 2q, 2q + 1
+      const uint2 sp0 = scale_pair(two & 0xFFu), sp1 = scale_pair(two >> 8);
+      uint8_t* rowp = bb + crow[h] * kCbBROW;
+      const int sw = crow[h] & 15;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        *reinterpret_cast<uint4*>(rowp + (((4 * cq[h] + tt) ^ sw) * 16)) = widen_fp4(dw(wc[h], tt), tt < 2 ? sp0 : sp1);
+    }
+  };
+  auto lds_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // per-lane LDS offsets: activation fragment rows (slot lq of the packed
+  // row, swizzled as the copies write it) and their scale bytes; weight rows
+  const int aoff = (wm0 + lr) * kCbP + ((lq ^ swz<kCbP>(wm0 + lr)) * 16);
+  const int saoff = kCbA + (wm0 + lr) * kCbSP + lq * 2;
+  const int boff = kCbBOFF + (wn0 + lr) * kCbBROW;
+
+  // prologue: activation stages 0 and 1, weight stage 0 widened, weight chunks 1 loaded
+  copy_a(0);
+  load_w(0);
+  wait_vmcnt<0>();
+  widen_w(0);
+  copy_a(1);
+  load_w(1);
+  lds_barrier();
+
+  for (int s = 0; s < nk; ++s) {
+    wait_vmcnt<0>();   // activation stage s + 1 and weight chunks s + 1 (issued last iteration)
+    asm volatile("" ::: "memory");
+    widen_w(s + 1);
+    copy_a(s + 2);
+    load_w(s + 2);
+    const uint8_t* ab = smem + (s % kCbNA) * kCbASTAGE;
+    const uint8_t* bb = smem + (s & 1) * kCbBSTAGE + boff;
+    uint4 fa[TI];
+    uint32_t fs[TI];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      fa[i] = *reinterpret_cast<const uint4*>(ab + aoff + i * 16 * kCbP);
+      fs[i] = *reinterpret_cast<const uint16_t*>(ab + saoff + i * 16 * kCbSP);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint4 oa[TI], ob[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) oa[i] = widen_fp4(dw(fa[i], st), scale_pair((fs[i] >> (8 * (st >> 1))) & 0xFFu));
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        ob[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * kCbBROW + (((4 * lq + st) ^ lr) * 16));
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) mfma_w<W_NVFP4>(acc[i][j], oa[i], ob[j]);
+    }
+    lds_barrier();
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // epilogue, as in the kernel above (NVFP4: no per-row or per-column scales)
+  const bool br_lds = g.br.r > 0 && g.br.ra <= kBrLdsMax && g.br.r <= kBrLdsMax && g.br.lda <= (1 << 20) &&
+                      g.br.ldb <= (1 << 20);
+  uint8_t* bra = smem + kCbBR_OFF;
+  uint8_t* brb = bra + kCbBM * 2 * kBrLdsMax;
+  if (br_lds) {
+    constexpr int NIA = kCbBM / 8, NIB = kCbBN / 8;
+    const v4u rbA = rsrc_words(g.br.a + (int64_t)m0 * g.br.lda, (uint32_t)(max(0, min(kCbBM, g.M - m0)) * g.br.lda * 2));
+    const v4u rbB = rsrc_words(g.br.b + (int64_t)n0 * g.br.ldb, (uint32_t)(max(0, min(kCbBN, g.N - n0)) * g.br.ldb * 2));
+    const int rl = lane >> 3, pos = lane & 7, chunk = pos ^ rl;
+    for (int n = wave; n < NIA + NIB; n += kCbNW) {   // wave-uniform
+      const bool isa = n < NIA;
+      const int row = (isa ? n : n - NIA) * 8 + rl;
+      const int64_t ld = isa ? g.br.lda : g.br.ldb;
+      const int klen = isa ? g.br.ra : g.br.r;
+      const uint32_t off = chunk * 8 < klen ? (uint32_t)(row * ld * 2 + chunk * 16) : kOOB;
+      dma16(isa ? rbA : rbB, (isa ? bra : brb) + (isa ? n : n - NIA) * 1024, off, 0u);
+    }
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  const EpiLds el{nullptr, nullptr, br_lds ? bra : nullptr, brb, m0, n0};
+  static_assert(kCbEPI <= kCbBR_OFF, "epilogue staging fits");
+  epilogue_tiles<2>(acc, g, m0 + wm0, n0 + wn0, lane, smem + wave * epilogue_stage_bytes<TI, TJ>(),
+                    static_cast<const EpiScales<TI, TJ>*>(nullptr), &el);
+}
+
 namespace {
 
 struct WideChoice {
@@ -688,7 +900,9 @@ hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
   const int tm = (int)c.tm, tn = (int)c.tn;
   switch (c.cfg) {
     case 0:
-      if constexpr (FMT != W_W4A8 && FMT != W_FP8)
+      if constexpr (FMT == W_NVFP4)
+        hipLaunchKernelGGL(gemm_nvfp4_cb_kernel, grid, dim3(64 * kCbNW), 0, st, g, tm, tn);
+      else if constexpr (FMT != W_W4A8 && FMT != W_FP8)
         hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 5, 4, 2, 1>), grid, dim3(512), 0, st, g, tm, tn);
       break;
     case 1: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 2, 4, 1>), grid, dim3(512), 0, st, g, tm, tn); break;
