@@ -653,11 +653,16 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 // read by one fragment, and the rows written by one wave, fall on distinct
 // banks.
 //
-// Iteration s: wait for everything issued in iteration s - 1 (activation
-// stage s + 1, weight chunks s + 1); widen the chunks into fp16 buffer
-// (s + 1) % 2; copy activation stage s + 2; load weight chunks s + 2; run
-// stage s; wait for the LDS stores and barrier.  Buffers written in
-// iteration s were last read in iteration s - 1, before its barrier.
+// Iteration s runs stage s from activation fragments read one iteration
+// earlier and from fp16 weight buffer s % 2.  After its first MFMA step it
+// widens weight chunks s + 1 into buffer (s + 1) % 2 (the compiler's wait
+// for those chunks also covers activation stage s + 2, copied just before
+// them), then copies activation stage s + 3 and loads weight chunks s + 2;
+// during the later steps it reads the activation fragments of stage s + 1
+// (landed one iteration ago, made visible by that iteration's barrier).
+// It ends with a wait for its LDS stores and a barrier.  Every buffer
+// written in iteration s was last read before the barrier of iteration
+// s - 1 (activation buffers hold four stages).
 namespace {
 constexpr int kCbTI = 4, kCbTJ = 5, kCbWR = 4, kCbWC = 2, kCbNW = kCbWR * kCbWC;
 constexpr int kCbBM = kCbWR * kCbTI * 16, kCbBN = kCbWC * kCbTJ * 16;   // 256 x 160
@@ -665,7 +670,7 @@ constexpr int kCbP = 64;                        // packed bytes per row per stag
 constexpr int kCbSP = 8;                        // E4M3 scale bytes per row per stage
 constexpr int kCbA = kCbBM * kCbP, kCbSA = kCbBM * kCbSP;
 constexpr int kCbASTAGE = kCbA + kCbSA;         // one packed activation stage
-constexpr int kCbNA = 3;                        // activation stage buffers
+constexpr int kCbNA = 4;                        // activation stage buffers
 constexpr int kCbBROW = 256;                    // fp16 bytes per weight row per stage
 constexpr int kCbBSTAGE = kCbBN * kCbBROW;      // one fp16 weight stage
 constexpr int kCbBOFF = kCbNA * kCbASTAGE;
@@ -776,45 +781,63 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
   const int saoff = kCbA + (wm0 + lr) * kCbSP + lq * 2;
   const int boff = kCbBOFF + (wn0 + lr) * kCbBROW;
 
-  // prologue: activation stages 0 and 1, weight stage 0 widened, weight chunks 1 loaded
+  struct AFrag {
+    uint4 c[TI];
+    uint32_t sc[TI];
+  };
+  auto read_a = [&](int s, AFrag& f) {
+    const uint8_t* ab = smem + (s % kCbNA) * kCbASTAGE;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      f.c[i] = *reinterpret_cast<const uint4*>(ab + aoff + i * 16 * kCbP);
+      f.sc[i] = *reinterpret_cast<const uint16_t*>(ab + saoff + i * 16 * kCbSP);
+    }
+  };
+  auto step = [&](int s, const AFrag& f, int st) {
+    const uint8_t* bb = smem + (s & 1) * kCbBSTAGE + boff;
+    uint4 oa[TI], ob[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      ob[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * kCbBROW + (((4 * lq + st) ^ lr) * 16));
+#pragma unroll
+    for (int i = 0; i < TI; ++i) oa[i] = widen_fp4(dw(f.c[i], st), scale_pair((f.sc[i] >> (8 * (st >> 1))) & 0xFFu));
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) mfma_w<W_NVFP4>(acc[i][j], oa[i], ob[j]);
+  };
+  auto iter = [&](int s, const AFrag& cur, AFrag& nxt) {
+    step(s, cur, 0);
+    wait_vmcnt<0>();   // activation stage s + 2 and weight chunks s + 1, issued last iteration
+    asm volatile("" ::: "memory");
+    widen_w(s + 1);
+    copy_a(s + 3);
+    load_w(s + 2);
+    step(s, cur, 1);
+    read_a(s + 1, nxt);
+    step(s, cur, 2);
+    step(s, cur, 3);
+    lds_barrier();
+  };
+
+  // prologue: activation stages 0 and 1 landed, weight stage 0 widened,
+  // activation stage 2 and weight chunks 1 in flight, stage 0's fragments read
   copy_a(0);
+  copy_a(1);
   load_w(0);
   wait_vmcnt<0>();
   widen_w(0);
-  copy_a(1);
+  copy_a(2);
   load_w(1);
   lds_barrier();
-
-  for (int s = 0; s < nk; ++s) {
-    wait_vmcnt<0>();   // activation stage s + 1 and weight chunks s + 1 (issued last iteration)
-    asm volatile("" ::: "memory");
-    widen_w(s + 1);
-    copy_a(s + 2);
-    load_w(s + 2);
-    const uint8_t* ab = smem + (s % kCbNA) * kCbASTAGE;
-    const uint8_t* bb = smem + (s & 1) * kCbBSTAGE + boff;
-    uint4 fa[TI];
-    uint32_t fs[TI];
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      fa[i] = *reinterpret_cast<const uint4*>(ab + aoff + i * 16 * kCbP);
-      fs[i] = *reinterpret_cast<const uint16_t*>(ab + saoff + i * 16 * kCbSP);
-    }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint4 oa[TI], ob[TJ];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) oa[i] = widen_fp4(dw(fa[i], st), scale_pair((fs[i] >> (8 * (st >> 1))) & 0xFFu));
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        ob[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * kCbBROW + (((4 * lq + st) ^ lr) * 16));
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) mfma_w<W_NVFP4>(acc[i][j], oa[i], ob[j]);
-    }
-    lds_barrier();
+  AFrag f0, f1;
+  read_a(0, f0);
+  int s = 0;
+  for (; s + 1 < nk; s += 2) {
+    iter(s, f0, f1);
+    iter(s + 1, f1, f0);
   }
+  if (s < nk) iter(s, f0, f1);
   wait_vmcnt<0>();
   __syncthreads();
 
