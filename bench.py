@@ -293,7 +293,7 @@ DOMINANT = {
     "video4096_a8": ("w4a8_linear w4a8 4096x5120x5120", ["gemm_wide_kernel<3,"]),
     "batch1_fp8": ("fp8_linear fp8 64x2048x8192", ["gemm_int_decode_kernel<3, 2, 1>"]),
     "video4096_fp8": ("fp8_linear fp8 4096x5120x5120", ["gemm_wide_kernel<4,"]),
-    "video4096": ("w4a4_linear nvfp4 4096x5120x5120", ["gemm_wide_kernel<2,"]),
+    "video4096": ("w4a4_linear nvfp4 4096x5120x5120", ["gemm_nvfp4_cb_kernel"]),
     "prefill": ("w4a4_linear int4 512x16384x2048", ["gemm_wide_kernel<0, 4, 4, 2, 4, 1>"]),
     "lowrank": ("w4a4_linear int4 1024x3072x3072", ["gemm_wide_kernel<0, 4, 6, 2, 1, 2>"]),
 }
