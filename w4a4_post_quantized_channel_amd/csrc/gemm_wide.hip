@@ -212,8 +212,12 @@ struct WCfg {
 // slot = physical slot ^ swizzle).  The last round is padded so every wave
 // issues the same count; padding instructions load out of range into the
 // pad area.  Per-lane offsets are fixed; a stage adds s * P through the
-// instruction's scalar offset, and only a stage that crosses the end of K
-// checks columns per lane.
+// instruction's scalar offset.  A lane whose column lies past the end of K
+// takes the out-of-range offset instead (no branch: a per-stage branch
+// between whole and partial stages cost more issue cycles than the
+// copies' own instructions).  In-range lanes address bytes of their own
+// row, so the range check's treatment of the scalar offset does not
+// matter.
 template <int P, int NI, int NW>
 struct CodeCopy {
   static constexpr int PW = (NI + NW - 1) / NW;
@@ -234,17 +238,12 @@ struct CodeCopy {
   __device__ __forceinline__ void issue(const v4u& rs, uint8_t* region, uint8_t* pad, int64_t rowbytes, int s,
                                         int wave) const {
     const int64_t k0 = (int64_t)s * P;
-    const bool full = k0 + P <= rowbytes;   // wave-uniform
 #pragma unroll
     for (int t = 0; t < PW; ++t) {
       const int n = NW * t + wave;
       uint8_t* dst = (NI % NW == 0 || n < NI) ? region + n * 1024 : pad;
-      if (full) {
-        dma16(rs, dst, off[t], (uint32_t)k0);
-      } else {
-        const bool ok = k0 + col[t] < rowbytes;
-        dma16(rs, dst, ok ? off[t] + (uint32_t)k0 : kOOB, 0u);
-      }
+      const bool ok = k0 + col[t] < rowbytes;
+      dma16(rs, dst, ok ? off[t] : kOOB, (uint32_t)k0);
     }
   }
 };
@@ -270,17 +269,12 @@ struct ScaleCopy {
   __device__ __forceinline__ void issue(const v4u& rs, uint8_t* region, uint8_t* pad, int64_t srow, int s,
                                         int wave) const {
     const int64_t k0 = (int64_t)s * SP;
-    const bool full = k0 + SP <= srow;
 #pragma unroll
     for (int t = 0; t < PW; ++t) {
       const int n = NW * t + wave;
       uint8_t* dst = (NI % NW == 0 || n < NI) ? region + n * 256 : pad;
-      if (full) {
-        dma4(rs, dst, off[t], (uint32_t)k0);
-      } else {
-        const bool ok = k0 + col[t] < srow;
-        dma4(rs, dst, ok ? off[t] + (uint32_t)k0 : kOOB, 0u);
-      }
+      const bool ok = k0 + col[t] < srow;
+      dma4(rs, dst, ok ? off[t] : kOOB, (uint32_t)k0);
     }
   }
 };
