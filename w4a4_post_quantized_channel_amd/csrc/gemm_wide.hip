@@ -235,15 +235,16 @@ struct CodeCopy {
       off[t] = (NI % NW == 0 || n < NI) ? (uint32_t)(row * rowbytes) + col[t] : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(const v4u& rs, uint8_t* region, uint8_t* pad, int64_t rowbytes, int s,
+  // region, pad: LDS byte addresses; rowbytes < 2^31
+  __device__ __forceinline__ void issue(const v4u& rs, uint32_t region, uint32_t pad, uint32_t rowbytes, int s,
                                         int wave) const {
-    const int64_t k0 = (int64_t)s * P;
+    const uint32_t k0 = (uint32_t)s * P;
 #pragma unroll
     for (int t = 0; t < PW; ++t) {
       const int n = NW * t + wave;
-      uint8_t* dst = (NI % NW == 0 || n < NI) ? region + n * 1024 : pad;
+      const uint32_t dst = (NI % NW == 0 || n < NI) ? region + n * 1024 : pad;
       const bool ok = k0 + col[t] < rowbytes;
-      dma16(rs, dst, ok ? off[t] : kOOB, (uint32_t)k0);
+      dma16_at(rs, dst, ok ? off[t] : kOOB, k0);
     }
   }
 };
@@ -266,15 +267,15 @@ struct ScaleCopy {
       off[t] = (NI % NW == 0 || n < NI) ? (uint32_t)(row * srow + c) : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(const v4u& rs, uint8_t* region, uint8_t* pad, int64_t srow, int s,
+  __device__ __forceinline__ void issue(const v4u& rs, uint32_t region, uint32_t pad, uint32_t srow, int s,
                                         int wave) const {
-    const int64_t k0 = (int64_t)s * SP;
+    const uint32_t k0 = (uint32_t)s * SP;
 #pragma unroll
     for (int t = 0; t < PW; ++t) {
       const int n = NW * t + wave;
-      uint8_t* dst = (NI % NW == 0 || n < NI) ? region + n * 256 : pad;
+      const uint32_t dst = (NI % NW == 0 || n < NI) ? region + n * 256 : pad;
       const bool ok = k0 + col[t] < srow;
-      dma4(rs, dst, ok ? off[t] : kOOB, (uint32_t)k0);
+      dma4_at(rs, dst, ok ? off[t] : kOOB, k0);
     }
   }
 };
@@ -319,7 +320,8 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
     rsSB = rsrc_words(reinterpret_cast<const uint8_t*>(g.sw) + (int64_t)n0 * srow, (uint32_t)(min(C::BN, g.N - n0) * srow));
   }
 
-  uint8_t* pad = smem + C::NBUF * C::STAGE;
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t pad = lds0 + C::NBUF * C::STAGE;
   CodeCopy<C::PA, C::NA, C::NW> cpA;
   CodeCopy<C::PB, C::NB, C::NW> cpB;
   ScaleCopy<C::SP, (C::NSA > 0 ? C::NSA : 1), C::NW> cpSA;
@@ -331,12 +333,12 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
     cpSB.init(wave, lane, srow);
   }
   auto copy_stage = [&](int s) {
-    uint8_t* base = smem + (s % C::NBUF) * C::STAGE;
-    cpA.issue(rsA, base, pad, rbA, s, wave);
-    cpB.issue(rsB, base + C::A_BYTES, pad, rowbytes, s, wave);
+    const uint32_t base = lds0 + (uint32_t)(s % C::NBUF) * C::STAGE;
+    cpA.issue(rsA, base, pad, (uint32_t)rbA, s, wave);
+    cpB.issue(rsB, base + C::A_BYTES, pad, (uint32_t)rowbytes, s, wave);
     if constexpr (FMT == W_NVFP4) {
-      cpSA.issue(rsSA, base + C::A_BYTES + C::B_BYTES, pad, srow, s, wave);
-      cpSB.issue(rsSB, base + C::A_BYTES + C::B_BYTES + C::SA_BYTES, pad, srow, s, wave);
+      cpSA.issue(rsSA, base + C::A_BYTES + C::B_BYTES, pad, (uint32_t)srow, s, wave);
+      cpSB.issue(rsSB, base + C::A_BYTES + C::B_BYTES + C::SA_BYTES, pad, (uint32_t)srow, s, wave);
     }
   };
 
@@ -710,15 +712,16 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
   const __amdgpu_buffer_rsrc_t rSW = make_rsrc(reinterpret_cast<const uint8_t*>(g.sw) + (int64_t)n0 * srow,
                                                (uint32_t)(min(kCbBN, g.N - n0) * srow));
 
-  uint8_t* pad = smem + kCbPAD;
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t pad = lds0 + kCbPAD;
   CodeCopy<kCbP, kCbA / 1024, kCbNW> cpA;
   ScaleCopy<kCbSP, kCbSA / 256, kCbNW> cpSA;
   cpA.init(wave, lane, rowbytes);
   cpSA.init(wave, lane, srow);
   auto copy_a = [&](int s) {
-    uint8_t* base = smem + (s % kCbNA) * kCbASTAGE;
-    cpA.issue(rsA, base, pad, rowbytes, s, wave);
-    cpSA.issue(rsSA, base + kCbA, pad, srow, s, wave);
+    const uint32_t base = lds0 + (uint32_t)(s % kCbNA) * kCbASTAGE;
+    cpA.issue(rsA, base, pad, (uint32_t)rowbytes, s, wave);
+    cpSA.issue(rsSA, base + kCbA, pad, (uint32_t)srow, s, wave);
   };
 
   // this thread's weight chunks: c = tid + 512 h, row c / 4, quarter c % 4

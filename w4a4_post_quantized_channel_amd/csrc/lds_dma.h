@@ -34,6 +34,24 @@ __device__ __forceinline__ void dma4(const v4u& rs, uint8_t* lds, uint32_t off, 
                : "memory", "m0");
 }
 
+// The same copies with the destination given as a 32-bit LDS byte address
+// (wave-uniform): a kernel that forms its LDS addresses from one base
+// avoids a generic-to-LDS pointer cast, with its null check, per copy.
+__device__ __forceinline__ void dma16_at(const v4u& rs, uint32_t lds, uint32_t off, uint32_t soff) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m), "v"(off), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_at(const v4u& rs, uint32_t lds, uint32_t off, uint32_t soff) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(m), "v"(off), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
 // s_waitcnt with vmcnt <= n and no wait on the other counters.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
