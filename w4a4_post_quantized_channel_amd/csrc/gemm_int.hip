@@ -150,20 +150,30 @@ gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
   if (!part && wave < TI) load_epi_scales(es, g, m0 + wave * 16, n0, lane);
 
   // copy instruction d: lane -> row d*RPI + lane/CPR of its operand, LDS
-  // chunk position lane%CPR holding chunk position^(row mod CPR)
+  // chunk position lane%CPR holding chunk position^(row mod CPR).  The
+  // lane's row offset and chunk byte are fixed; a step adds its K byte
+  // through the scalar offset, and a lane past K takes the out-of-range
+  // offset.  Destinations are 32-bit LDS addresses from one base.
+  uint32_t voff[PER_STEP], cpos[PER_STEP];
+#pragma unroll
+  for (int d = 0; d < PER_STEP; ++d) {
+    const bool isa = d < NIA;
+    const int cpr = isa ? CPRA : CPRB, rpi = isa ? RPIA : RPIB;
+    const int r = (isa ? d : d - NIA) * rpi + lane / cpr;
+    cpos[d] = 16u * (uint32_t)((lane % cpr) ^ (r & (cpr - 1)));
+    voff[d] = (uint32_t)(r * (isa ? rbA : rbB)) + cpos[d];
+  }
+  const uint32_t area_lds = lds_addr(area);
   auto issue = [&](int t, int slot) {   // copies of step t into ring slot `slot`
     const int k = kw + t * 4 * kBK;
-    uint8_t* st = area + slot * STEP_BYTES;
+    const uint32_t st = area_lds + (uint32_t)(slot * STEP_BYTES);
 #pragma unroll
     for (int d = 0; d < PER_STEP; ++d) {
       const bool isa = d < NIA;                   // compile-time per instruction
-      const int cpr = isa ? CPRA : CPRB, rpi = isa ? RPIA : RPIB;
-      const int64_t rb = isa ? rbA : rbB;
-      const int r = (isa ? d : d - NIA) * rpi + lane / cpr;
-      const int64_t kb = (isa ? F::A4 : F::W4) ? (k >> 1) : k;
-      const int64_t cb = kb + 16 * ((lane % cpr) ^ (r & (cpr - 1)));
-      const bool ok = k < kz1 && cb < rb;
-      dma16(isa ? rsA : rsB, st + d * 1024, ok ? (uint32_t)(r * rb + cb) : kOOB, 0u);
+      const uint32_t rb = (uint32_t)(isa ? rbA : rbB);
+      const uint32_t kb = (uint32_t)((isa ? F::A4 : F::W4) ? (k >> 1) : k);
+      const bool ok = k < kz1 && kb + cpos[d] < rb;
+      dma16_at(isa ? rsA : rsB, st + d * 1024, ok ? voff[d] : kOOB, kb);
     }
   };
 
