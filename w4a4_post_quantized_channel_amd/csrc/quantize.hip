@@ -511,30 +511,37 @@ quant_nvfp4_lanes_kernel(QuantArgs a) {
   const bool has_scale = a.scale != nullptr;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nblk = a.K >> 6;
-  const int64_t ngrp = (a.R + 63) >> 6;
-  const int64_t ntask = ngrp * nblk;
-  const int64_t stride = (int64_t)gridDim.x * 4;
+  // task indices fit 32 bits (the launch checks), so (rows, block) comes
+  // from a 32-bit division
+  const uint32_t nblk = (uint32_t)(a.K >> 6);
+  const uint32_t ngrp = (uint32_t)((a.R + 63) >> 6);
+  const uint32_t ntask = ngrp * nblk;
+  const uint32_t stride = gridDim.x * 4u;
   constexpr int CPR = RB / 16;              // 16-byte chunks per row of the tile
 
   // Coalesced copy of task t's 64 x 64 tile into buffer `buf` of this
   // wave's LDS slice: copy instruction i covers tile bytes [1024 i,
   // 1024 i + 1024); the chunk at slot q of tile row r holds logical chunk
   // q ^ (r & 7) (so that the 64 rows read back by the 64 lanes spread over
-  // the banks).  Rows past R read zeros.
-  auto copy_tile = [&](int64_t t, int buf) {
-    const int64_t grp = t / nblk;
-    const int b = (int)(t - grp * nblk);
-    const v4u rs = rsrc_words(reinterpret_cast<const char*>(a.x) + (size_t)(grp * 64) * a.ldx * ESZ,
-                              (uint32_t)(min((int64_t)64, a.R - grp * 64) * a.ldx * ESZ));
-    uint8_t* tile = tiles[wave][buf];
+  // the banks).  Rows past R read zeros.  The lane's offset inside the
+  // tile is fixed; the block's byte offset goes in the scalar operand.
+  uint32_t loff[NCOPY];
 #pragma unroll
-    for (int i = 0; i < NCOPY; ++i) {
-      const int p = i * 1024 + lane * 16;
-      const int r = p / RB, q = (p % RB) / 16;
-      const int L = q ^ (r & 7 & (CPR - 1));
-      dma16(rs, tile + i * 1024, (uint32_t)(r * (int)(a.ldx * ESZ) + b * RB + L * 16), 0u);
-    }
+  for (int i = 0; i < NCOPY; ++i) {
+    const int p = i * 1024 + lane * 16;
+    const int r = p / RB, q = (p % RB) / 16;
+    const int L = q ^ (r & 7 & (CPR - 1));
+    loff[i] = (uint32_t)(r * (int)(a.ldx * ESZ) + L * 16);
+  }
+  const uint32_t tiles_lds = lds_addr(&tiles[wave][0][0]);
+  auto copy_tile = [&](uint32_t t, int buf) {
+    const uint32_t grp = t / nblk;
+    const uint32_t b = t - grp * nblk;
+    const v4u rs = rsrc_words(reinterpret_cast<const char*>(a.x) + (size_t)grp * 64 * a.ldx * ESZ,
+                              (uint32_t)(min((int64_t)64, a.R - (int64_t)grp * 64) * a.ldx * ESZ));
+    const uint32_t tile = tiles_lds + (uint32_t)(buf * TILE);
+#pragma unroll
+    for (int i = 0; i < NCOPY; ++i) dma16_at(rs, tile + i * 1024, loff[i], b * RB);
   };
 
   // the kept-channel indices, two per lane (a gather of at most 128)
@@ -544,12 +551,12 @@ quant_nvfp4_lanes_kernel(QuantArgs a) {
     if (64 + lane < a.gr) gkeep[1] = a.gidx[64 + lane];
   }
 
-  int64_t task = (int64_t)blockIdx.x * 4 + wave;
+  uint32_t task = blockIdx.x * 4u + (uint32_t)wave;
   if (task < ntask) copy_tile(task, 0);
   for (int buf = 0; task < ntask; task += stride, buf ^= (NB - 1)) {
-    const int64_t grp = task / nblk;
+    const uint32_t grp = task / nblk;
     const int b = (int)(task - grp * nblk);
-    const int64_t row = grp * 64 + lane;
+    const int64_t row = (int64_t)grp * 64 + lane;
     const bool live = row < a.R;
     // Start the next task's copy, then wait for this task's tile only:
     // loads complete in order, so at most NCOPY outstanding operations
@@ -711,7 +718,8 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
                            int64_t ldg) {
   QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, amax_out,
               gidx, gr, (uint16_t*)gout, ldg};
-  if (mode == MODE_NVFP4 && R >= 256 && K % 64 == 0 && (rot == 0 || rot == 64)) {
+  if (mode == MODE_NVFP4 && R >= 256 && K % 64 == 0 && (rot == 0 || rot == 64) &&
+      ((R + 63) / 64) * (K / 64) < (1LL << 31)) {
     // resident grid: as many four-wave blocks as the tiles' LDS lets every CU hold
     const int64_t tasks = ((R + 63) / 64) * (K / 64);
     constexpr int NB = 1;
