@@ -88,6 +88,9 @@ SMALL = [
     # the 256x160 NVFP4 tile (weights widened once per workgroup): ragged M and N,
     # and a last K stage of half length
     ("nvfp4_wide_tile", 2600, 3210, 1088, "nvfp4", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=16)),
+    # shapes the tile model routes to the 128x256 and 128x96 NVFP4 tiles (ragged M, N and K)
+    ("nvfp4_tile_128x256", 3100, 1000, 320, "nvfp4", "bf16", dict(n_outliers=8, outlier_gain=30.0)),
+    ("nvfp4_tile_128x96", 777, 2600, 320, "nvfp4", "bf16", dict(n_outliers=8, outlier_gain=30.0)),
     # W4A8: int8 activation codes x int4 weight codes
     ("w4a8_ragged", 70, 96, 448, "w4a8", "bf16", dict(n_outliers=6, outlier_gain=15.0)),
     ("w4a8_tiles", 160, 256, 512, "w4a8", "bf16", dict(n_outliers=8, outlier_gain=15.0, row_gain_sigma=0.5)),
@@ -149,6 +152,27 @@ def test_raw_accumulators_exact(ops, fmt, M, N, K, split):
     _raw_linear(ops, fmt, a, sa, w, sw, K, y=y, workspace=ws)
     got = _np(y).astype(np.int64)
     assert np.array_equal(got, ref)
+
+
+# Shapes the many-token tile model routes to its 256x160, 128x256 and 128x96
+# tiles (the 64x64 tile is covered above); all ragged in M and N, with a
+# partial last K stage.
+@pytest.mark.parametrize("fmt", ["int4", "int8", "w4a8"])
+@pytest.mark.parametrize("M,N,K", [(3100, 2600, 320), (3100, 1000, 320), (777, 2600, 320)])
+def test_raw_accumulators_every_tile(ops, fmt, M, N, K):
+    """Bit-exact int32 accumulators on random codes through each many-token tile."""
+    rng = np.random.default_rng(M * 7 + N * 13 + K + 1)
+    fa, fw = _sides(fmt)
+    a_b = _random_codes(rng, fa, M, K)
+    w_b = _random_codes(rng, fw, N, K)
+    ref = O.int_gemm(unpack_codes(fa, a_b), unpack_codes(fw, w_b))
+    _report("raw_every_tile", fmt=fmt, M=M, N=N, K=K)
+    dev = "cuda"
+    a = torch.from_numpy(a_b).to(dev)
+    w = torch.from_numpy(w_b).to(dev)
+    y = torch.empty((M, N), dtype=torch.int32, device=dev)
+    _raw_linear(ops, fmt, a, torch.ones(M, device=dev), w, torch.ones(N, device=dev), K, y=y)
+    assert np.array_equal(_np(y).astype(np.int64), ref)
 
 
 @pytest.mark.parametrize("fmt,val_a,val_w", [("int4", 7, 7), ("int4", -8, -8), ("int4", -8, 7),
