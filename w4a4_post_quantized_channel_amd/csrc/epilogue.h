@@ -54,30 +54,39 @@ struct EpiLds {
   int m_tile, n_tile;
 };
 
-// acc[i][j] += A_br . B_br^T over ra (B_br index k mod r), operands from the
-// LDS-staged branch rows.  m_loc / n_loc: tile-relative first row / column.
-template <int TI, int TJ>
-__device__ __forceinline__ void branch_mfma_lds(v4f (&acc)[TI][TJ], const EpiLds& el, int ra, int r, int m_loc,
-                                                int n_loc, int lane) {
+// The A_br operands of a wave's TI row blocks for every K step of an
+// LDS-staged branch (ra <= kBrLdsMax = 64: two steps of 32), read once per
+// tile; branch_mfma_lds_pre then adds one 16-column block's products.
+template <int TI>
+struct BrAFrags {
+  v8bf a[kBrLdsMax / 32][TI];
+};
+template <int TI>
+__device__ __forceinline__ void load_br_a(BrAFrags<TI>& f, const EpiLds& el, int ra, int m_loc, int lane) {
   const int lr = lane & 15, lk = (lane >> 4) * 8;
-  for (int kk = 0; kk < ra; kk += 32) {
-    const int ka = kk + lk, kb = ka % r;
-    v8bf af[TI], bfr[TJ];
+#pragma unroll
+  for (int s = 0; s < kBrLdsMax / 32; ++s) {
+    if (s * 32 >= ra) break;
+    const int ka = s * 32 + lk;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int row = m_loc + i * 16 + lr;
-      af[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(el.bra + row * 128 + (((ka >> 3) ^ (row & 7)) << 4)));
+      f.a[s][i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(el.bra + row * 128 + (((ka >> 3) ^ (row & 7)) << 4)));
     }
+  }
+}
+template <int TI>
+__device__ __forceinline__ void branch_mfma_lds_pre(v4f (&acc)[TI][1], const BrAFrags<TI>& f, const EpiLds& el, int ra,
+                                                    int r, int n_loc, int lane) {
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int row = n_loc + lr;
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int row = n_loc + j * 16 + lr;
-      bfr[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(el.brb + row * 128 + (((kb >> 3) ^ (row & 7)) << 4)));
-    }
+  for (int s = 0; s < kBrLdsMax / 32; ++s) {
+    if (s * 32 >= ra) break;
+    const int kb = (s * 32 + lk) % r;
+    const v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(el.brb + row * 128 + (((kb >> 3) ^ (row & 7)) << 4)));
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < TI; ++i) acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[s][i], b, acc[i][0], 0, 0, 0);
   }
 }
 
@@ -184,6 +193,10 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
         sam[i][r] = pre ? pre->sa[i][r] : el ? el->sa[m - el->m_tile] : (m < g.M ? sa[m] : 0.f);
       }
   }
+  // LDS-staged branch: its A_br operands once for the whole grid
+  const bool br_pre = g.br.r > 0 && el && el->bra;
+  BrAFrags<TI> bra_f;
+  if (br_pre) load_br_a<TI>(bra_f, *el, g.br.ra, m_base - el->m_tile, lane);
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int n = n_base + j * 16 + lr;
@@ -206,8 +219,8 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
         for (int r = 0; r < 4; ++r) col[i][0][r] = acc[i][j][r] * g.alpha;
     }
     if (g.br.r > 0) {
-      if (el && el->bra)
-        branch_mfma_lds<TI, 1>(col, *el, g.br.ra, g.br.r, m_base - el->m_tile, n_base + j * 16 - el->n_tile, lane);
+      if (br_pre)
+        branch_mfma_lds_pre<TI>(col, bra_f, *el, g.br.ra, g.br.r, n_base + j * 16 - el->n_tile, lane);
       else
         branch_mfma<TI, 1>(col, g.br, g.M, g.N, m_base, n_base + j * 16, lane);
     }
