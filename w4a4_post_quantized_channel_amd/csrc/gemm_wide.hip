@@ -651,9 +651,9 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 //
 // Iteration s runs stage s from activation fragments read one iteration
 // earlier and from fp16 weight buffer s % 2.  After its first MFMA step it
-// widens weight chunks s + 1 into buffer (s + 1) % 2 (the compiler's wait
-// for those chunks also covers activation stage s + 2, copied just before
-// them), then copies activation stage s + 3 and loads weight chunks s + 2;
+// waits for everything issued in iteration s - 1 (activation stage s + 2,
+// weight chunks s + 1), widens the chunks into buffer (s + 1) % 2, then
+// copies activation stage s + 3 and loads weight chunks s + 2;
 // during the later steps it reads the activation fragments of stage s + 1
 // (landed one iteration ago, made visible by that iteration's barrier).
 // It ends with a wait for its LDS stores and a barrier.  Every buffer
@@ -678,7 +678,6 @@ constexpr int kCbBR_END = kCbBR_OFF + (kCbBM + kCbBN) * 2 * kBrLdsMax;
 constexpr int kCbLDS = kCbPIPE > kCbBR_END ? kCbPIPE : kCbBR_END;
 constexpr int kCbCH = kCbBN * kCbP / 16;                            // weight chunks per stage
 constexpr int kCbNCH = (kCbCH + 64 * kCbNW - 1) / (64 * kCbNW);     // chunks per thread
-constexpr int kCbDA = kCbA / 1024 / kCbNW + kCbSA / 256 / kCbNW;    // activation copies per wave per stage
 static_assert(kCbA % (1024 * kCbNW) == 0 && kCbSA % (256 * kCbNW) == 0, "whole copy rounds");
 static_assert(kCbLDS <= 160 * 1024, "LDS");
 }  // namespace
