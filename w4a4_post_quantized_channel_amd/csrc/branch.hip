@@ -110,7 +110,18 @@ __global__ void __launch_bounds__(64 * kProjWaves) project_kernel(const uint16_t
   uint8_t* const a = area[wave];
   // copy instruction d of a step: rows 8 (d & 1) .. + 7 of x (d < 2) or of
   // L1 (d >= 2); lane -> row 8 (d & 1) + lane / 8, chunk position lane % 8
+  // (the lane's row and chunk offset are fixed; a step's K byte goes in the
+  // scalar operand, and destinations are 32-bit LDS addresses)
   const int crow = lane >> 3, cpos = lane & 7;
+  uint32_t loff[4], lcol[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int row = 8 * (d & 1) + crow;
+    const int c = cpos ^ (row & 7);                      // logical chunk held at this position
+    lcol[d] = 8u * (uint32_t)c;
+    loff[d] = (uint32_t)(row * (d < 2 ? xrow : lrow)) + 16u * (uint32_t)c;
+  }
+  const uint32_t a_lds = lds_addr(a);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   for (int kc = k0; kc < k1; kc += 64 * kProjChunk) {
 #pragma unroll
@@ -118,12 +129,9 @@ __global__ void __launch_bounds__(64 * kProjWaves) project_kernel(const uint16_t
       const int k = kc + 64 * u;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const int row = 8 * (d & 1) + crow;
-        const int c = cpos ^ (row & 7);                  // logical chunk held at this position
-        const bool ok = k + 8 * c < k1;                  // chunk of 8 elements inside this wave's range
-        const int64_t rb = d < 2 ? xrow : lrow;
-        dma16(d < 2 ? rx : rl, a + u * kProjStepBytes + d * 1024,
-              ok ? (uint32_t)(row * rb + (int64_t)(k + 8 * c) * 2) : kOOB, 0u);
+        const bool ok = (uint32_t)k + lcol[d] < (uint32_t)k1;   // chunk of 8 elements inside this wave's range
+        dma16_at(d < 2 ? rx : rl, a_lds + (uint32_t)(u * kProjStepBytes + d * 1024), ok ? loff[d] : kOOB,
+                 (uint32_t)k * 2u);
       }
     }
     wait_vmcnt<0>();
