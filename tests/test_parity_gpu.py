@@ -204,7 +204,9 @@ def _fp8_codes(rng, R, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (17, 33, 192), (64, 2048, 2048), (64, 512, 8192),
                                    (9, 768, 8192), (20, 512, 4096), (130, 260, 320), (300, 100, 64),
-                                   (512, 512, 4096), (40, 4096, 4160)])
+                                   (512, 512, 4096), (40, 4096, 4160),
+                                   # many tokens: the 128x128 and the 128x256 FP8 tiles
+                                   (1030, 3100, 576), (2600, 5200, 320)])
 @pytest.mark.parametrize("split", [False, True])
 def test_fp8_accumulation(ops, M, N, K, split):
     """FP8 GEMM on random E4M3 codes with unit steps and fp32 output, few-token

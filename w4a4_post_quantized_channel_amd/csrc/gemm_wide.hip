@@ -910,12 +910,22 @@ WideChoice choose(int64_t M, int64_t N, int64_t K, int fmt, bool skip0) {
   return best;
 }
 
-// FP8 takes the 128x256 shape only: its stages (128 bytes per row on both
-// sides) leave LDS room for three of them there and for fewer elsewhere.
+// FP8 stages hold 128 bytes per row on both sides: the 128x256 shape fits
+// three of them (one in flight), a 128x128 shape (eight waves of 64x32)
+// four.  The same timing model, fitted to FP8's measured times on six
+// shapes (it picks the faster at all six), decides between them: the
+// larger tile wins on the largest grids, the smaller where the larger
+// leaves CUs idle or a round half-empty.
+WideChoice choose_fp8(int64_t M, int64_t N, int64_t K) {
+  const int64_t t1 = ((M + 127) / 128) * ((N + 255) / 256), t5 = ((M + 127) / 128) * ((N + 127) / 128);
+  const double c1 = (double)((t1 + 255) / 256) * (6.9 + 0.249 * 128.0 * 256.0 * (double)K * 1e-6);
+  const double c5 = (double)((t5 + 255) / 256) * (5.0 + 0.310 * 128.0 * 128.0 * (double)K * 1e-6);
+  return c1 <= c5 ? WideChoice{1, (M + 127) / 128, (N + 255) / 256} : WideChoice{5, (M + 127) / 128, (N + 127) / 128};
+}
+
 template <int FMT>
 hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
-  const WideChoice c = FMT == W_FP8 ? WideChoice{1, (g.M + 127) / 128, (g.N + 255) / 256}
-                                    : choose(g.M, g.N, g.K, FMT, FMT == W_W4A8);
+  const WideChoice c = FMT == W_FP8 ? choose_fp8(g.M, g.N, g.K) : choose(g.M, g.N, g.K, FMT, FMT == W_W4A8);
   const dim3 grid((unsigned)(c.tm * c.tn));
   const int tm = (int)c.tm, tn = (int)c.tn;
   switch (c.cfg) {
@@ -926,6 +936,10 @@ hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
         hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 5, 4, 2, 1>), grid, dim3(512), 0, st, g, tm, tn);
       break;
     case 1: hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 2, 4, 1>), grid, dim3(512), 0, st, g, tm, tn); break;
+    case 5:
+      if constexpr (FMT == W_FP8)
+        hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 2, 2, 4, 1>), grid, dim3(512), 0, st, g, tm, tn);
+      break;
     case 2:
       if constexpr (FMT != W_FP8)
         hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 6, 2, 1, 2>), grid, dim3(256), 0, st, g, tm, tn);
