@@ -115,6 +115,11 @@ template <int DF, int TI, int TJ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_int_decode_kernel(GemmArgs g, int kwg, int32_t* part) {
   static_assert(TI == 1 || TI == 2 || TI == 4, "row blocks per workgroup");
+  // every argument in scalar registers before any branch: one batch of
+  // argument loads and one wait
+  asm volatile("" ::"s"(g.a), "s"(g.sa), "s"(g.w), "s"(g.sw), "s"(g.M), "s"(g.N), "s"(g.K), "s"(g.alpha),
+               "s"(g.br.a), "s"(g.br.lda), "s"(g.br.b), "s"(g.br.ldb), "s"(g.br.r), "s"(g.br.ra), "s"(g.y),
+               "s"(g.y_dtype), "s"(g.ldy), "s"(kwg), "s"(part));
   typedef DecFmt<DF> F;
   constexpr int SBA = F::SBA, SBB = F::SBB;
   constexpr int CPRA = SBA / 16, CPRB = SBB / 16;          // 16-byte chunks per row and step

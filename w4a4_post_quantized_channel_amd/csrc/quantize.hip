@@ -271,6 +271,11 @@ __device__ __forceinline__ float transform_slot(const SlotRaw<BF16IN>& raw, floa
 
 template <int MODE, bool BF16IN, int NC, int WPR>
 __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(QuantArgs a) {
+  // Every argument the kernel reads goes into scalar registers before any
+  // branch, so the argument loads issue as one batch with one wait (left to
+  // itself the compiler fetched them in three dependent rounds).
+  asm volatile("" ::"s"(a.x), "s"(a.R), "s"(a.K), "s"(a.ldx), "s"(a.scale), "s"(a.g), "s"(a.rot), "s"(a.order),
+               "s"(a.codes), "s"(a.scales), "s"(a.amax_out), "s"(a.gidx), "s"(a.gr), "s"(a.gout), "s"(a.ldg));
   constexpr int QMAX = (MODE == MODE_INT4 || MODE == MODE_Y4) ? 7 : 127;
   constexpr bool I8 = MODE == MODE_INT8 || MODE == MODE_INT8W;
   constexpr bool YOUT = MODE == MODE_Y4 || MODE == MODE_Y8;
