@@ -304,7 +304,19 @@ PROFILE_CMDS = {
     "pmc": "rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_{w}_{c} -o run -- "
            "python3 bench.py --workload {w} --steps 5 --warmup 1 --eager --no-cpu-baseline --no-also",
     "copy": "rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_copy_{c} -o run -- python3 bench.py --copy-calibration",
+    "group": "rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_{w}_{g} -o run -- "
+             "python3 bench.py --workload {w} --steps 5 --warmup 1 --eager --no-cpu-baseline --no-also",
 }
+
+# Counter groups for the matrix-core view of the many-token calls, one run
+# each: MFMA busy cycles (summed over SIMDs) against elapsed cycles (summed
+# over XCDs), and the MFMA work in units of 512 operations.
+COUNTER_GROUPS = {
+    "MFMA": "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE",
+    "MOPS": "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+            "SQ_INSTS_VALU_MFMA_MOPS_F6F4",
+}
+MFMA_WORKLOADS = ["video4096", "video4096_a8", "video4096_fp8", "prefill", "lowrank"]
 
 
 def kernel_source_hash():
@@ -337,10 +349,60 @@ def _csv_rows(path):
         return list(csv.DictReader(fh))
 
 
+def _quantizer_traffic(d, wl, stats, factor):
+    """HBM bytes and average duration of each quantize kernel that runs every
+    step (the activation quantizers; weight packing runs once)."""
+    import re
+    per = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        f = os.path.join(d, f"pmc_{wl}_{c}", "run_counter_collection.csv")
+        if not os.path.exists(f):
+            return None
+        vals = {}
+        for r in _csv_rows(f):
+            if "quant" in r["Kernel_Name"]:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        per[c] = {k: sum(v) / len(v) * factor[c] * 1024.0 for k, v in vals.items() if len(v) >= 5}
+    out = {}
+    for name in sorted(set(per["FETCH_SIZE"]) & set(per["WRITE_SIZE"])):
+        us = [float(r["AverageNs"]) / 1e3 for r in stats if r["Name"] == name]
+        if us:
+            out[re.sub(r"\(.*", "", name)] = (per["FETCH_SIZE"][name], per["WRITE_SIZE"][name], us[0])
+    return out
+
+
+def _mfma_counters(d, wl, kernels):
+    """Matrix-core busy fraction and MFMA work of the dominant call."""
+    base = {g: os.path.join(d, f"pmc_{wl}_{g}") for g in COUNTER_GROUPS}
+    if not all(os.path.exists(os.path.join(b, "run_counter_collection.csv")) for b in base.values()):
+        return None
+    agent = [r for r in _csv_rows(os.path.join(base["MFMA"], "run_agent_info.csv"))
+             if int(r.get("Simd_Count") or 0) > 0][0]
+    simds, xcc = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
+
+    def mean(g, counter):
+        rows = [r for r in _csv_rows(os.path.join(base[g], "run_counter_collection.csv"))
+                if r["Counter_Name"] == counter and any(k in r["Kernel_Name"] for k in kernels)]
+        if not rows:
+            return None, 0, 0.0
+        dur = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows) / len(rows)
+        return sum(float(r["Counter_Value"]) for r in rows) / len(rows), len(rows), dur
+
+    busy, calls, dur_ns = mean("MFMA", "SQ_VALU_MFMA_BUSY_CYCLES")
+    active, _, _ = mean("MFMA", "GRBM_GUI_ACTIVE")
+    if busy is None or not active:
+        return None
+    mops = sum(mean("MOPS", c)[0] or 0.0 for c in COUNTER_GROUPS["MOPS"].split())
+    busy, active = busy / simds, active / xcc
+    return {"calls": calls, "us": dur_ns / 1e3, "busy": busy, "active": active, "util": busy / active,
+            "clock_ghz": active / dur_ns, "gflop": mops * 512 / 1e9}
+
+
 def summarize_profiles(d):
     """Write profiles/<kernel>_<workload>.txt (kernel-trace statistics) and
-    profiles/traffic.json (FETCH_SIZE / WRITE_SIZE per dominant call, scaled
-    by the same counters read on a plain copy of known size)."""
+    profiles/traffic.json (FETCH_SIZE / WRITE_SIZE per dominant call and per
+    step quantizer, scaled by the same counters read on a plain copy of known
+    size; matrix-core busy fraction and MFMA work of the many-token calls)."""
     import re
     os.makedirs(PROFILES, exist_ok=True)
     factor = {}
@@ -385,6 +447,25 @@ def summarize_profiles(d):
         if len(per) == 2:
             traffic["workloads"][wl] = {"call": label, "fetch_bytes": per["FETCH_SIZE"],
                                         "write_bytes": per["WRITE_SIZE"], "avg_us": dom_us}
+        q = _quantizer_traffic(d, wl, stats, factor)
+        if q:
+            lines += ["", "per-step quantize kernels (HBM bytes from the same FETCH_SIZE / WRITE_SIZE runs, "
+                      "over the kernel-trace average):"]
+            for name, (fb, wb, us) in q.items():
+                lines.append(f"  {name}: {fb / 1e6:.2f} MB fetched + {wb / 1e6:.2f} MB written in {us:.2f} us = "
+                             f"{(fb + wb) / us / 1e3:.0f} GB/s ({(fb + wb) / us / 1e3 / HBM_PEAK_GBS:.1%} of HBM peak)")
+            traffic.setdefault("quantize", {})[wl] = {n: {"fetch_bytes": fb, "write_bytes": wb, "avg_us": us}
+                                                      for n, (fb, wb, us) in q.items()}
+        m = _mfma_counters(d, wl, kernels) if wl in MFMA_WORKLOADS else None
+        if m:
+            lines += ["", f"matrix cores ({m['calls']} calls under the counters, {m['us']:.2f} us each there):",
+                      f"  SQ_VALU_MFMA_BUSY_CYCLES / SIMDs = {m['busy']:.0f} busy cycles per SIMD; "
+                      f"GRBM_GUI_ACTIVE / XCDs = {m['active']:.0f} elapsed cycles ({m['clock_ghz']:.2f} GHz)",
+                      f"  MFMA busy {m['util']:.1%} of elapsed; MFMA work {m['gflop']:.1f} G operations "
+                      f"(512 per MOPS unit)",
+                      "  [" + PROFILE_CMDS["group"].format(w=wl, g="MFMA", c=COUNTER_GROUPS["MFMA"]) + "]",
+                      "  [" + PROFILE_CMDS["group"].format(w=wl, g="MOPS", c=COUNTER_GROUPS["MOPS"]) + "]"]
+            traffic.setdefault("mfma", {})[wl] = m
         slug = re.sub(r"[^a-z0-9]+", "_", label.lower()).strip("_")
         with open(os.path.join(PROFILES, f"{slug}_{wl}.txt"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
