@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+PEAK_CLOCK_GHZ = 2.4           # MI355X peak engine clock
 PEAK_TFLOPS = {"i8": 5000.0, "fp8": 5000.0, "f16": 2500.0, "bf16": 2500.0, "fp4": 10100.0}
 
 
@@ -295,7 +296,7 @@ DOMINANT = {
     "video4096_fp8": ("fp8_linear fp8 4096x5120x5120", ["gemm_wide_kernel<4,"]),
     "video4096": ("w4a4_linear nvfp4 4096x5120x5120", ["gemm_nvfp4_cb_kernel"]),
     "prefill": ("w4a4_linear int4 512x16384x2048", ["gemm_wide_kernel<0, 4, 4, 2, 4, 1>"]),
-    "lowrank": ("w4a4_linear int4 1024x3072x3072", ["gemm_wide_kernel<0, 4, 6, 2, 1, 2>"]),
+    "lowrank": ("w4a4_linear int4 1024x3072x3072", ["gemm_wide_kernel<0, 2, 6, 4, 1, 2>"]),
 }
 
 PROFILE_CMDS = {
@@ -390,12 +391,14 @@ def _mfma_counters(d, wl, kernels):
 
     busy, calls, dur_ns = mean("MFMA", "SQ_VALU_MFMA_BUSY_CYCLES")
     active, _, _ = mean("MFMA", "GRBM_GUI_ACTIVE")
-    if busy is None or not active:
+    if busy is None or not dur_ns:
         return None
     mops = sum(mean("MOPS", c)[0] or 0.0 for c in COUNTER_GROUPS["MOPS"].split())
-    busy, active = busy / simds, active / xcc
-    return {"calls": calls, "us": dur_ns / 1e3, "busy": busy, "active": active, "util": busy / active,
-            "clock_ghz": active / dur_ns, "gflop": mops * 512 / 1e9}
+    busy = busy / simds
+    # GRBM_GUI_ACTIVE also counts dispatch set-up around short calls, so the
+    # busy fraction is taken over the call's own duration at the peak clock
+    return {"calls": calls, "us": dur_ns / 1e3, "busy": busy, "grbm_active_per_xcd": (active or 0.0) / xcc,
+            "util": busy / (dur_ns * PEAK_CLOCK_GHZ), "gflop": mops * 512 / 1e9}
 
 
 def summarize_profiles(d):
@@ -459,10 +462,10 @@ def summarize_profiles(d):
         m = _mfma_counters(d, wl, kernels) if wl in MFMA_WORKLOADS else None
         if m:
             lines += ["", f"matrix cores ({m['calls']} calls under the counters, {m['us']:.2f} us each there):",
-                      f"  SQ_VALU_MFMA_BUSY_CYCLES / SIMDs = {m['busy']:.0f} busy cycles per SIMD; "
-                      f"GRBM_GUI_ACTIVE / XCDs = {m['active']:.0f} elapsed cycles ({m['clock_ghz']:.2f} GHz)",
-                      f"  MFMA busy {m['util']:.1%} of elapsed; MFMA work {m['gflop']:.1f} G operations "
-                      f"(512 per MOPS unit)",
+                      f"  SQ_VALU_MFMA_BUSY_CYCLES / SIMDs = {m['busy']:.0f} busy cycles per SIMD, "
+                      f"{m['util']:.1%} of the call's {m['us'] * PEAK_CLOCK_GHZ * 1e3:.0f} cycles at "
+                      f"{PEAK_CLOCK_GHZ} GHz",
+                      f"  MFMA work {m['gflop']:.1f} G operations (512 per MOPS unit)",
                       "  [" + PROFILE_CMDS["group"].format(w=wl, g="MFMA", c=COUNTER_GROUPS["MFMA"]) + "]",
                       "  [" + PROFILE_CMDS["group"].format(w=wl, g="MOPS", c=COUNTER_GROUPS["MOPS"]) + "]"]
             traffic.setdefault("mfma", {})[wl] = m
