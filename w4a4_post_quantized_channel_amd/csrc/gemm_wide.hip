@@ -881,10 +881,11 @@ struct WideChoice {
 // 2% off), with 7% rms error in the predicted time.  A format scales the
 // per-product part (int8 moves twice the bytes per product, NVFP4 adds the
 // block-scale decode), and NVFP4 on the 256x160 shape runs the kernel that
-// widens weights once per workgroup.  The 128x96 shape was fitted with four
-// waves of 64x96; it now runs eight waves of 32x96 (two per SIMD, two K
-// groups), 5-17% faster on the shapes that choose it, and keeps its old
-// constants, so the model never picks it where it did not before.
+// widens weights once per workgroup.  The 128x96 and 64x64 shapes were
+// fitted with four waves (64x96, and 64x64 in four K groups); they now run
+// eight, two per SIMD (32x96 in two K groups, 32x64 in four), 2-17% faster
+// on the shapes that choose them, and keep their old constants, so the
+// model never picks them where it did not before.
 constexpr int kNumCfg = 4;
 constexpr int kCfgBM[kNumCfg] = {256, 128, 128, 64};
 constexpr int kCfgBN[kNumCfg] = {160, 256, 96, 64};
@@ -949,7 +950,7 @@ hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
       break;
     default:
       if constexpr (FMT != W_FP8)
-        hipLaunchKernelGGL((gemm_wide_kernel<FMT, 4, 4, 1, 1, 4>), grid, dim3(256), 0, st, g, tm, tn);
+        hipLaunchKernelGGL((gemm_wide_kernel<FMT, 2, 4, 2, 1, 4>), grid, dim3(512), 0, st, g, tm, tn);
       break;
   }
   return hipGetLastError();
