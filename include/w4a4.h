@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define W4A4_ABI_VERSION 1
+#define W4A4_ABI_VERSION 2
 #define W4A4_MAX_BRANCH 128 /* largest branch width (rank or kept channels) */
 #define W4A4_LOWRANK_MAX_PARTS 4 /* hi/lo pairs a branch ``a`` operand may hold (ra = 2 P r) */
 
@@ -104,6 +104,9 @@ typedef struct w4a4_qdesc {
  * low-rank branch next to the 4-bit complement; QuantWAMs sec. 4.2: BF16
  * bypass of kept channels).  Adds  sum_j a[m, j] * b[n, j mod r]  for
  * j < ra to every output, in fp32 after the dequantised main product.
+ *  A kept-channel branch assumes the quantized operands were made with
+ *  smoothing factors 0 on those channels and smoothing before the rotation
+ *  (see quantize_act_gather).
  *  a   bf16, M x ra, row stride lda (elements).  For a rank-r factor product
  *      (x L1) L2 it holds the hi and lo bf16 halves of x L1 (ra = 2r, as
  *      produced by w4a4_lowrank_project), or P such pairs whose sum is
@@ -153,15 +156,18 @@ int quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t l
  *  xo   bf16 M x r, row stride ldo >= r: the w4a4_branch ``a`` operand
  *       (ra = r).
  * x must be BF16.  Same result as quantize_act followed by
- * w4a4_lowrank_project with idx. */
+ * w4a4_lowrank_project with idx.  Kept channels leave the quantized path
+ * through smoothing factors of 0, which removes raw channels only when
+ * smoothing precedes the rotation: q->order must be
+ * W4A4_ORDER_SMOOTH_THEN_ROTATE (else W4A4_ERR_UNSUPPORTED_FORMAT). */
 int quantize_act_gather(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
                         const float* inv_smooth, const w4a4_qdesc* q, void* codes, void* scales,
                         const int32_t* idx, int64_t r, void* xo, int64_t ldo, void* stream);
 
 /* pack_weights -- offline weight packing with the inverse transform folded
- * in (FoldQuantVLA contribution 1: the inverse of every activation transform
- * is folded into each consuming weight; QuantWAMs sec. 3.2: the common
- * Hadamard rotation is fused into the weights).  Same arithmetic as
+ * in (FoldQuantVLA contribution 1: every activation transform is undone
+ * inside the weight that consumes it; QuantWAMs sec. 3.3, after Eq. 14: the
+ * rotation shared by a layer group lives in its weights).  Same arithmetic as
  * quantize_act on the N rows of W (one scale per output channel), with the
  * smoothing factors s multiplied instead of 1/s.
  *  w       N x K weights (BF16 or F32), row stride ldw.
@@ -275,7 +281,8 @@ int fp8_linear(const void* a_codes, const void* a_scales,
 /* lowrank_add -- standalone 16-bit branch, y += (x L1) L2 or
  * y += x[:, idx] W_idx^T (Q-WAM abstract: 16-bit low-rank branch as a dense
  * product; QuantWAMs sec. 3.1 / 4.2: kept channels on a BF16 path).
- *  x    M x K bf16, row stride ldx.
+ *  x    M x K activations, row stride ldx; x_dtype must be W4A4_DT_BF16
+ *       (anything else is W4A4_ERR_UNSUPPORTED_FORMAT).
  *  l1t  bf16 r x K (row stride K, 16-byte aligned): L1 transposed, one
  *       K-contiguous row per rank component, for the low-rank form; NULL
  *       when idx is given.
@@ -286,7 +293,7 @@ int fp8_linear(const void* a_codes, const void* a_scales,
  *  Accumulation: x L1 in fp32, then the rank-r product in fp32, added to
  *  y in fp32, one rounding to y_dtype.
  */
-int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx,
+int lowrank_add(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
                 const void* l1t, const int32_t* idx, const void* lw, int64_t ldlw,
                 int64_t r, int64_t N, void* y, int32_t y_dtype, int64_t ldy,
                 void* stream);
@@ -296,9 +303,10 @@ int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx,
  * t = x L1 in fp32, written as bf16 hi = bf16(t) and lo = bf16(t - hi) in
  * columns [0, r) and [r, 2r) of out (the branch's ra = 2r).  For
  * idx != NULL, out = x[:, idx] (M x r, exact).
- *  x bf16 M x K (row stride ldx <= 2^26 elements, K <= 2^24); out bf16 with
- *  row stride ldo >= w4a4_lowrank_width(M, K, l1t ? r : -r). */
-int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx,
+ *  x M x K, x_dtype W4A4_DT_BF16 (else W4A4_ERR_UNSUPPORTED_FORMAT), row
+ *  stride ldx <= 2^26 elements, K <= 2^24; out bf16 with row stride
+ *  ldo >= w4a4_lowrank_width(M, K, l1t ? r : -r). */
+int w4a4_lowrank_project(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
                          const void* l1t, const int32_t* idx, int64_t r,
                          void* out, int64_t ldo, void* stream);
 
@@ -316,6 +324,18 @@ int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r);
 int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, int64_t ldx,
                         const float* scale, const w4a4_qdesc* q, float* amax_out,
                         void* stream);
+
+/* w4a4_linear_plan -- which kernel the linear entry points run for
+ * (M, N, K, fmt), without launching anything (host only, no device access).
+ * fmt is W4A4_FMT_INT4 (also for w4a4_linear), INT8 (w8a8_linear), NVFP4,
+ * W4A8 (w4a8_linear) or FP8 (fp8_linear); with_workspace says whether a
+ * workspace of w4a4_workspace_size bytes will be passed.  Writes
+ * plan[0] = W4A4_PLAN_* kernel family, plan[1] x plan[2] = rows x columns of
+ * one workgroup's output tile, plan[3] = K splits (1 = one kernel).
+ * Returns W4A4_OK, or a negative status for shapes / formats the linear
+ * entry points would reject (no kernel exists for the combination). */
+enum { W4A4_PLAN_DECODE = 1, W4A4_PLAN_DECODE_SPLIT = 2, W4A4_PLAN_TILE = 3, W4A4_PLAN_NVFP4_SHARED = 4 };
+int w4a4_linear_plan(int64_t M, int64_t N, int64_t K, int32_t fmt, int32_t with_workspace, int32_t* plan);
 
 /* Bytes of workspace w4a4_linear / w8a8_linear / w4a8_linear / fp8_linear
  * use for (M, N, K, fmt); 0 when the shape runs without one. */

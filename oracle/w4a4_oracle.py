@@ -44,8 +44,14 @@ Readings where the pages are silent (each also listed in the design notes):
   that order, then the exact factor 1/8;
 * the transform and every quantization decision are evaluated in IEEE
   binary32 with round-to-nearest-even (the precision of the kernels that
-  take the same decisions); the products, sums and dequantisation that do
-  not decide an integer are evaluated in binary64;
+  take the same decisions);
+* the dequantising epilogue of the integer (and FP8) GEMMs is IEEE binary32
+  in a fixed order, y = fp32(fp32(fp32(acc) * step_a) * step_w), so an
+  integer linear without a branch has one exact answer; the NVFP4 product
+  and the 16-bit branches, whose GPU sums have no fixed order, are
+  evaluated in binary64;
+* a kept-channel (bypass) branch is defined for smoothing before rotation
+  only: it removes the raw channels through s = inv_s = 0;
 * symmetric integer quantizers: step = amax/Q with Q = 7 (int4) or 127
   (int8), code = clamp(rne(fp32(y/step)), -Q-1, Q), all-zero rows give
   step 0 and codes 0;
@@ -304,28 +310,6 @@ def int4_from_nibbles(n: np.ndarray) -> np.ndarray:
     return np.where(n >= 8, n - 16, n).astype(np.int8)
 
 
-# W4A8 activation layout (a storage convention of this library, not of the
-# pages): the int8 codes of each aligned group of 8 K indices are stored
-# with the even indices first, then the odd ones -- the order in which the
-# nibbles of packed int4 weight codes come apart when unpacked to bytes.
-W4A8_GROUP_ORDER = np.array([0, 2, 4, 6, 1, 3, 5, 7])
-
-
-def pack_w4a8_activations(codes: np.ndarray) -> np.ndarray:
-    c = np.asarray(codes, dtype=np.int8)
-    R, K = c.shape
-    assert K % 8 == 0
-    return np.ascontiguousarray(c.reshape(R, K // 8, 8)[:, :, W4A8_GROUP_ORDER]).reshape(R, K).view(np.uint8)
-
-
-def unpack_w4a8_activations(packed: np.ndarray) -> np.ndarray:
-    p = np.asarray(packed).view(np.int8)
-    R, K = p.shape
-    out = np.empty((R, K // 8, 8), dtype=np.int8)
-    out[:, :, W4A8_GROUP_ORDER] = p.reshape(R, K // 8, 8)
-    return out.reshape(R, K)
-
-
 # ----------------------------------------------------------------------------
 # GEMM, epilogue, 16-bit branch
 # ----------------------------------------------------------------------------
@@ -345,8 +329,16 @@ def int_gemm(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
 
 
 def dequant_epilogue(acc, step_a, step_w) -> np.ndarray:
-    """y = acc * step_a[m] * step_w[n], float64."""
-    return np.asarray(acc, F64) * np.asarray(step_a, F64)[:, None] * np.asarray(step_w, F64)[None, :]
+    """Dequantising epilogue in IEEE binary32, one rounding per operation
+    (FoldQuantVLA overview: per-token activation steps and per-output-
+    channel weight steps applied to the integer GEMM result):
+    y = fp32(fp32(fp32(acc) * step_a[m]) * step_w[n]).  The conversion of
+    the accumulator rounds to nearest even (exact for |acc| <= 2^24).
+    Returns float32."""
+    a = np.asarray(acc)
+    a = a.astype(F32) if a.dtype != F32 else a
+    t = (a * np.asarray(step_a, F32)[:, None]).astype(F32)
+    return (t * np.asarray(step_w, F32)[None, :]).astype(F32)
 
 
 def fp8_gemm(codes_a: np.ndarray, codes_w: np.ndarray) -> np.ndarray:
@@ -416,11 +408,12 @@ def quantize_operand(x, scale, fmt: str, fwht_block=FWHT_BLOCK,
     channel scales): the arithmetic is the same."""
     y = transform(x, scale, fwht_block, order)
     if fmt in ("int4", "int8", "w4a8"):
-        # "w4a8": the activation side of W4A8, int8 codes in the W4A8 layout
+        # "w4a8": the activation side of W4A8 (int8 codes, Q = 127)
         qmax = INT4_QMAX if fmt == "int4" else INT8_QMAX
         codes, step, v = quantize_int(y, qmax)
-        packed = {"int4": pack_nibbles, "int8": lambda c: c.view(np.uint8),
-                  "w4a8": pack_w4a8_activations}[fmt](codes)
+        # "w4a8" activations are the int8 codes; any storage order a GEMM
+        # prefers is a library layout, not part of the method
+        packed = pack_nibbles(codes) if fmt == "int4" else codes.view(np.uint8)
         return {"y": y, "codes": codes, "scales": step, "v": v, "packed": packed}
     if fmt == "fp8":
         codes, step, v = quantize_fp8(y)
@@ -444,7 +437,7 @@ def transformed_amax(x, scale, fwht_block=FWHT_BLOCK, order="smooth_then_rotate"
 # Activation and weight formats of each linear: W4A8 is the 8-bit-activation
 # step of the QuantWAMs schedule (Experimental Details, quantization
 # configuration; sec. 4.4.3), with the same 4-bit weight codes as W4A4; its
-# activations are the int8 quantization, stored in the W4A8 layout.
+# activations are the int8 quantization.
 OPERAND_FORMATS = {"int4": ("int4", "int4"), "int8": ("int8", "int8"),
                    "nvfp4": ("nvfp4", "nvfp4"), "w4a8": ("w4a8", "int4"), "fp8": ("fp8", "fp8")}
 
@@ -454,6 +447,12 @@ def linear(case, order="smooth_then_rotate", g_a=None, g_w=None) -> dict:
     and weights, integer (or NVFP4) GEMM, dequant epilogue, 16-bit branch.
     Returns the intermediate codes, scales and accumulators and y (float64)."""
     fb = case.fwht_block
+    if case.branch is not None and case.branch["kind"] == "outlier" and order != "smooth_then_rotate":
+        # Kept channels leave the quantized path through s = inv_s = 0, which
+        # removes the raw channels only when smoothing precedes the rotation;
+        # after a rotation the zeros would land on rotated coordinates and the
+        # bypass would count the kept channels twice.
+        raise ValueError("a kept-channel branch needs smoothing before the rotation")
     fa, fw = OPERAND_FORMATS[case.fmt]
     A = quantize_operand(case.x, case.inv_s, fa, fb, order, g_a)
     W = quantize_operand(case.w, case.s, fw, fb, order, g_w)

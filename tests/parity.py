@@ -16,6 +16,29 @@ _E4 = O.e4m3_value(np.arange(0x7F))
 E4M3_BOUNDS = (_E4[1:] + _E4[:-1]) / 2
 
 
+# W4A8 activation storage (a layout of this library, not of the pages): the
+# int8 codes of each aligned group of 8 K indices are stored even indices
+# first, then odd ones -- the byte order in which packed int4 weight codes
+# come apart when widened, so both operands reach the matrix cores in the
+# same K order.  The oracle emits logical codes; these convert.
+W4A8_GROUP_ORDER = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+
+
+def pack_w4a8_activations(codes):
+    c = np.asarray(codes, dtype=np.int8)
+    R, K = c.shape
+    assert K % 8 == 0
+    return np.ascontiguousarray(c.reshape(R, K // 8, 8)[:, :, W4A8_GROUP_ORDER]).reshape(R, K).view(np.uint8)
+
+
+def unpack_w4a8_activations(packed):
+    p = np.asarray(packed).view(np.int8)
+    R, K = p.shape
+    out = np.empty((R, K // 8, 8), dtype=np.int8)
+    out[:, :, W4A8_GROUP_ORDER] = p.reshape(R, K // 8, 8)
+    return out.reshape(R, K)
+
+
 def near_boundary(v, bounds):
     v = np.abs(np.asarray(v, np.float64))
     d = np.min(np.abs(v[..., None] - bounds), axis=-1)
@@ -34,7 +57,7 @@ def unpack_codes(fmt, packed):
     if fmt == "int8":
         return packed.view(np.int8)
     if fmt == "w4a8":
-        return O.unpack_w4a8_activations(packed)
+        return unpack_w4a8_activations(packed)
     if fmt == "fp8":
         return packed.view(np.uint8)
     return O.unpack_nibbles(packed.view(np.uint8))
@@ -68,6 +91,25 @@ def check_operand(fmt, gpu_codes, gpu_scales, ref, rows=None, what="operand"):
         else:
             assert near_half_integer(rv[bad]).all(), f"{what}: {int(bad.sum())} code mismatches outside the band"
     return int(bad.sum())
+
+
+def bf16_round(a):
+    """fp32 -> nearest bf16 value (round to nearest even), as fp32."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    u = (u + ((u >> 16) & 1) + np.uint32(0x7FFF)) & np.uint32(0xFFFF0000)
+    return u.view(np.float32)
+
+
+def check_output_exact(y, y_ref_f32, y_dtype):
+    """Bit equality of an integer linear's output (no branch) with the
+    oracle's fp32-ordered epilogue: fp32 as is, bf16 after one RNE rounding."""
+    want = np.asarray(y_ref_f32, np.float32)
+    if y_dtype == "bf16":
+        want = bf16_round(want)
+    got = np.asarray(y, np.float32)
+    bad = got.view(np.uint32) != want.view(np.uint32)
+    assert not bad.any(), (f"{int(bad.sum())} outputs differ from the fp32-ordered epilogue, "
+                           f"first at {np.argwhere(bad)[0].tolist()}")
 
 
 def check_output(y, y_ref, rtol):

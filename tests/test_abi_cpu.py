@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(ops):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
-    assert ops.LIB.w4a4_abi_version() == 1
+    assert ops.LIB.w4a4_abi_version() == 2
 
 
 def test_lowrank_width_host_query(ops):
@@ -207,16 +207,67 @@ def test_pack_weights_gptq_rejects_bad_arguments(ops):
 
 def test_lowrank_rejects_bad_arguments(ops):
     L = ops.LIB
+    B = 1   # W4A4_DT_BF16
     # both or neither of l1 / idx
-    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, FAKE, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -1
-    assert L.lowrank_add(FAKE, 4, 64, 64, None, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -1
-    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 8, 0, 16, FAKE2, 1, 16, None) == -1    # r
-    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 8, 200, 16, FAKE2, 1, 16, None) == -1  # r max
-    assert L.lowrank_add(FAKE, 4, 60, 60, FAKE, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -2    # K % 8
-    assert L.lowrank_add(MISAL, 4, 64, 64, FAKE, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -3
-    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 8, 8, 16, FAKE2, 2, 16, None) == -4    # y dtype
-    assert L.lowrank_add(FAKE, 4, 64, 64, FAKE, None, FAKE, 4, 8, 16, FAKE2, 1, 16, None) == -1    # ldlw
-    assert L.w4a4_lowrank_project(FAKE, 4, 64, 64, FAKE, None, 8, FAKE2, 8, None) == -1           # ldo < 2r
-    assert L.w4a4_lowrank_project(FAKE, 4, 64, 1 << 27, FAKE, None, 8, FAKE2, 16, None) == -2     # ldx too large
+    assert L.lowrank_add(FAKE, B, 4, 64, 64, FAKE, FAKE, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -1
+    assert L.lowrank_add(FAKE, B, 4, 64, 64, None, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -1
+    assert L.lowrank_add(FAKE, B, 4, 64, 64, FAKE, None, FAKE, 8, 0, 16, FAKE2, 1, 16, None) == -1    # r
+    assert L.lowrank_add(FAKE, B, 4, 64, 64, FAKE, None, FAKE, 8, 200, 16, FAKE2, 1, 16, None) == -1  # r max
+    assert L.lowrank_add(FAKE, B, 4, 60, 60, FAKE, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -2    # K % 8
+    assert L.lowrank_add(MISAL, B, 4, 64, 64, FAKE, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -3
+    assert L.lowrank_add(FAKE, B, 4, 64, 64, FAKE, None, FAKE, 8, 8, 16, FAKE2, 2, 16, None) == -4    # y dtype
+    assert L.lowrank_add(FAKE, B, 4, 64, 64, FAKE, None, FAKE, 4, 8, 16, FAKE2, 1, 16, None) == -1    # ldlw
+    assert L.w4a4_lowrank_project(FAKE, B, 4, 64, 64, FAKE, None, 8, FAKE2, 8, None) == -1           # ldo < 2r
+    assert L.w4a4_lowrank_project(FAKE, B, 4, 64, 1 << 27, FAKE, None, 8, FAKE2, 16, None) == -2     # ldx too large
     assert L.w4a4_transform_amax(FAKE, 1, 4, 96, 96, None, _q(ops), FAKE2, None) == -2
     assert L.w4a4_transform_amax(FAKE, 1, 4, 128, 128, None, _q(ops), None, None) == -1
+
+
+@pytest.mark.parametrize("dt", [0, 2, 7])   # F32, I32, unknown
+def test_branch_calls_reject_non_bf16_activations(ops, dt):
+    """The branch kernels read bf16; any other x dtype is refused before a launch
+    (an fp32 tensor must not come back as silent garbage with status OK)."""
+    L = ops.LIB
+    assert L.lowrank_add(FAKE, dt, 4, 64, 64, FAKE, None, FAKE, 8, 8, 16, FAKE2, 1, 16, None) == -4
+    assert L.lowrank_add(FAKE, dt, 4, 64, 64, None, FAKE, FAKE, 8, 8, 16, FAKE2, 0, 16, None) == -4
+    assert L.w4a4_lowrank_project(FAKE, dt, 4, 64, 64, FAKE, None, 8, FAKE2, 16, None) == -4
+    assert L.w4a4_lowrank_project(FAKE, dt, 4, 64, 64, None, FAKE, 8, FAKE2, 16, None) == -4
+    assert b"BF16" in L.w4a4_last_error()
+
+
+def test_gather_rejects_rotation_before_smoothing(ops):
+    """Kept channels are removed by zero smoothing factors, which only removes
+    raw channels when smoothing comes first."""
+    L = ops.LIB
+    st = L.quantize_act_gather(FAKE, 1, 4, 128, 128, None, _q(ops, order=1), FAKE2, FAKE2, FAKE, 8, FAKE2, 8, None)
+    assert st == -4 and b"smoothing before the rotation" in L.w4a4_last_error()
+
+
+def test_linear_plan_names_a_kernel_for_every_supported_shape(ops):
+    """The host-side plan is what the linear entry points launch: every
+    format at a grid of shapes (the workloads' and ragged ones) has a kernel,
+    and the tile-shape dispatcher refuses (instead of silently launching
+    nothing) any combination without one."""
+    shapes = [(1, 1, 64), (16, 256, 256), (64, 2048, 2048), (64, 2048, 8192), (65, 2048, 2048),
+              (512, 16384, 2048), (512, 2048, 8192), (1024, 3072, 3072), (4096, 5120, 5120),
+              (3100, 2600, 320), (777, 2600, 320), (3100, 1000, 320), (300, 100, 64), (2600, 3210, 1088)]
+    for fmt in ["int4", "int8", "nvfp4", "w4a8", "fp8"]:
+        for (M, N, K) in shapes:
+            for ws in (False, True):
+                p = ops.linear_plan(M, N, K, fmt, ws)
+                if M <= 64 and fmt != "nvfp4":
+                    assert p["family"] in ("decode", "decode_split")
+                    assert (p["splits"] > 1) == (p["family"] == "decode_split")
+                    assert p["splits"] == 1 or (ws and ops.workspace_size(M, N, K, fmt) > 0)
+                else:
+                    assert p["family"] in ("tile", "nvfp4_shared") and p["splits"] == 1
+                    assert p["family"] != "nvfp4_shared" or fmt == "nvfp4"
+                    assert p["tile"] in [(256, 160), (128, 256), (128, 96), (64, 64), (128, 128)]
+                    assert p["tile"] != (256, 160) or fmt in ("int4", "int8", "nvfp4")
+                    assert p["tile"] != (128, 128) or fmt == "fp8"
+    out = (ctypes.c_int32 * 4)()
+    L = ops.LIB
+    assert L.w4a4_linear_plan(64, 64, 100, 0, 0, out) == -2           # K % 64
+    assert L.w4a4_linear_plan(64, 64, 128, 9, 0, out) == -4           # unknown format
+    assert L.w4a4_linear_plan(0, 64, 128, 0, 0, out) == -1
+    assert L.w4a4_linear_plan(64, 64, 128, 0, 0, None) == -1

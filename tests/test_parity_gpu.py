@@ -8,7 +8,7 @@ import pytest
 from oracle import w4a4_oracle as O
 from w4a4_post_quantized_channel_amd import workloads as WL
 
-from parity import check_operand, check_output, unpack_codes
+from parity import check_operand, check_output, check_output_exact, unpack_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +113,14 @@ SMALL = [
 def test_small_cases(ops, pipe, name, M, N, K, fmt, xdt, kw, order):
     case = WL.linear_case(M, N, K, seed=zlib.crc32(name.encode()) % 1000, fmt=fmt, x_dtype=xdt, name=name, **kw)
     _report(name, M=M, N=N, K=K, fmt=fmt, order=order)
+    if kw.get("keep_channels") and order != "smooth_then_rotate":
+        # kept channels are defined for smoothing first only (s = 0 removes raw
+        # channels); both sides refuse the other order before any launch
+        with pytest.raises(ValueError):
+            _oracle(case, order)
+        with pytest.raises(ValueError):
+            pipe.build_layer(case, order=order)
+        return
     layer, t, y = _run(pipe, case, order)
     ref = _oracle(case, order)
     if fmt == "nvfp4":
@@ -123,7 +131,10 @@ def test_small_cases(ops, pipe, name, M, N, K, fmt, xdt, kw, order):
     nw = check_operand(fw, _np(layer.w_codes), _np(layer.w_scales), ref["w"], what="weights")
     rtol = 1e-3 if case.y_dtype == "f32" else 1e-2
     worst = check_output(_np(y), ref["y"], rtol)
-    _report(name, band_mismatch_a=na, band_mismatch_w=nw, worst=f"{worst:.3g}")
+    exact = fmt in ("int4", "int8", "w4a8") and case.branch is None and na == 0 and nw == 0
+    if exact:   # one exact answer: integer accumulators and the fp32-ordered epilogue
+        check_output_exact(_np(y), ref["y_main"], case.y_dtype)
+    _report(name, band_mismatch_a=na, band_mismatch_w=nw, worst=f"{worst:.3g}", bit_exact=exact)
 
 
 @pytest.mark.parametrize("fmt", ["int4", "int8", "w4a8"])
@@ -399,6 +410,29 @@ def test_pack_weights_gptq(ops, pipe, N, K, fmt, use_perm):
     assert np.array_equal(unpack_codes(fmt, _np(codes)), codes_ref)
 
 
+@pytest.mark.slow
+def test_pack_weights_gptq_full_size(ops, pipe):
+    """GPTQ rounding at a workload's size: the 3072x3072 int4 residual weight
+    of the 1024-token low-rank case.  Steps are compared on every row; codes
+    on 128 sampled rows (GPTQ treats rows independently, so the oracle can
+    run the sampled rows alone), bit-exact."""
+    case = WL.workload("lowrank")
+    cal = WL.gptq_calibration(case.K, 3 + 7)
+    t = pipe.case_to_device(case)
+    u = torch.from_numpy(np.ascontiguousarray(cal["u"])).cuda()
+    perm = torch.from_numpy(cal["perm"].astype(np.int32)).cuda()
+    codes, scales = ops.pack_weights_gptq(t["w"], t["s"], u, perm, "int4", fwht_block=case.fwht_block)
+    ref = O.quantize_operand(case.w, case.s, "int4", case.fwht_block)
+    rows = np.sort(np.random.default_rng(12).choice(case.N, 128, replace=False))
+    codes_ref, _ = O.gptq_rows(ref["y"][rows], ref["scales"][rows], cal["u"], O.INT4_QMAX, cal["perm"])
+    got = unpack_codes("int4", _np(codes))
+    _report("gptq_full", N=case.N, K=case.K, rows=len(rows),
+            changed_vs_rtn=f"{np.mean(codes_ref != ref['codes'][rows]):.3f}")
+    assert np.array_equal(_np(scales), ref["scales"])
+    assert np.array_equal(got[rows], codes_ref)
+    assert np.mean(codes_ref != ref["codes"][rows]) > 0.05    # the feedback did change codes
+
+
 def test_gptq_linear_end_to_end(ops, pipe):
     """A W4A4 layer packed with GPTQ rounding: output within tolerance of the
     oracle's GPTQ linear."""
@@ -472,10 +506,13 @@ def test_full_workloads(ops, pipe, name):
     na = check_operand(fa, _np(b["codes"]), _np(b["scales"]), ref["a"], what="activations")
     nw = check_operand(fw, _np(layer.w_codes), _np(layer.w_scales), ref["w"], what="weights")
     worst = check_output(_np(y), ref["y"], 1e-3 if case.y_dtype == "f32" else 1e-2)
+    exact = case.fmt in ("int4", "int8", "w4a8") and case.branch is None and na == 0 and nw == 0
+    if exact:   # e.g. the 16x256x256 fp32 case: the output itself is bit-exact
+        check_output_exact(_np(y), ref["y_main"], case.y_dtype)
     if case.fmt in ("int4", "int8", "w4a8"):
         yi = torch.empty((case.M, case.N), dtype=torch.int32, device="cuda")
         _raw_linear(ops, case.fmt, b["codes"], b["scales"], layer.w_codes, layer.w_scales, case.K,
                     y=yi, workspace=b["ws"])
         acc = O.int_gemm(unpack_codes(fa, _np(b["codes"])), unpack_codes(fw, _np(layer.w_codes)))
         assert np.array_equal(_np(yi).astype(np.int64), acc)
-    _report(name, band_mismatch_a=na, band_mismatch_w=nw, worst=f"{worst:.3g}")
+    _report(name, band_mismatch_a=na, band_mismatch_w=nw, worst=f"{worst:.3g}", bit_exact=exact)

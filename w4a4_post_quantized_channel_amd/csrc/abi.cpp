@@ -144,6 +144,12 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
     g.br.r = br->r; g.br.ra = br->ra;
   }
   g.y = y; g.y_dtype = y_dtype; g.ldy = ldy;
+  if (M > 64 || fmt == W4A4_FMT_NVFP4) {
+    int bm = 0, bn = 0;
+    if (w4a4::wide_plan(fmt, M, N, K, &bm, &bn) < 0)
+      return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: no many-token kernel for fmt %d at %lldx%lldx%lld", fn, fmt,
+                  (long long)M, (long long)N, (long long)K);
+  }
   hipError_t e;
   if (fmt == W4A4_FMT_NVFP4) {
     e = w4a4::launch_gemm_wide(2, g, (hipStream_t)stream);
@@ -200,6 +206,9 @@ int quantize_act_gather(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
                         int64_t ldo, void* stream) {
   const char* fn = "quantize_act_gather";
   if (x_dtype != W4A4_DT_BF16) return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: x must be BF16", fn);
+  if (q && q->order != W4A4_ORDER_SMOOTH_THEN_ROTATE)
+    return fail(W4A4_ERR_UNSUPPORTED_FORMAT,
+                "%s: kept channels need smoothing before the rotation (order SMOOTH_THEN_ROTATE)", fn);
   if (r <= 0 || r > W4A4_MAX_BRANCH)
     return fail(W4A4_ERR_INVALID_ARG, "%s: r=%lld outside [1, %d]", fn, (long long)r, W4A4_MAX_BRANCH);
   if (ldo < r) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo < r", fn);
@@ -247,8 +256,10 @@ int fp8_linear(const void* a_codes, const void* a_scales, const void* w_codes, c
                     y_dtype, ldy, workspace, workspace_bytes, stream);
 }
 
-static int check_lowrank(const char* fn, const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t,
-                         const int32_t* idx, int64_t r) {
+static int check_lowrank(const char* fn, const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const void* l1t, const int32_t* idx, int64_t r) {
+  if (x_dtype != W4A4_DT_BF16)
+    return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: x dtype %d: the 16-bit branch takes BF16 activations", fn, x_dtype);
   if (M < 0 || K <= 0) return fail(W4A4_ERR_INVALID_ARG, "%s: bad sizes", fn);
   if (r <= 0 || r > W4A4_MAX_BRANCH) return fail(W4A4_ERR_INVALID_ARG, "%s: r=%lld outside [1, %d]", fn, (long long)r, W4A4_MAX_BRANCH);
   if ((l1t == nullptr) == (idx == nullptr)) return fail(W4A4_ERR_INVALID_ARG, "%s: exactly one of l1t / idx", fn);
@@ -265,11 +276,11 @@ static int check_lowrank(const char* fn, const void* x, int64_t M, int64_t K, in
   return ok();
 }
 
-int lowrank_add(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t, const int32_t* idx,
-                const void* lw, int64_t ldlw, int64_t r, int64_t N, void* y, int32_t y_dtype, int64_t ldy,
-                void* stream) {
+int lowrank_add(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const void* l1t,
+                const int32_t* idx, const void* lw, int64_t ldlw, int64_t r, int64_t N, void* y, int32_t y_dtype,
+                int64_t ldy, void* stream) {
   const char* fn = "lowrank_add";
-  int st = check_lowrank(fn, x, M, K, ldx, l1t, idx, r);
+  int st = check_lowrank(fn, x, x_dtype, M, K, ldx, l1t, idx, r);
   if (st != W4A4_OK) return st;
   if (N < 0) return fail(W4A4_ERR_INVALID_ARG, "%s: N < 0", fn);
   if (y_dtype != W4A4_DT_F32 && y_dtype != W4A4_DT_BF16)
@@ -290,10 +301,10 @@ int64_t w4a4_lowrank_width(int64_t M, int64_t K, int64_t r) {
   return r < 0 ? -r : 2 * r;   // gather: |r| kept channels; projection: the hi/lo pair
 }
 
-int w4a4_lowrank_project(const void* x, int64_t M, int64_t K, int64_t ldx, const void* l1t, const int32_t* idx,
-                         int64_t r, void* out, int64_t ldo, void* stream) {
+int w4a4_lowrank_project(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const void* l1t,
+                         const int32_t* idx, int64_t r, void* out, int64_t ldo, void* stream) {
   const char* fn = "w4a4_lowrank_project";
-  int st = check_lowrank(fn, x, M, K, ldx, l1t, idx, r);
+  int st = check_lowrank(fn, x, x_dtype, M, K, ldx, l1t, idx, r);
   if (st != W4A4_OK) return st;
   if (ldo < w4a4_lowrank_width(M, K, l1t ? r : -r)) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo too small", fn);
   if (M == 0) return ok();
@@ -313,6 +324,34 @@ int w4a4_transform_amax(const void* x, int32_t x_dtype, int64_t R, int64_t K, in
   hipError_t e = w4a4::launch_quantize(3, x_dtype == W4A4_DT_BF16, x, R, K, ldx, scale, 1.f, q->fwht_block,
                                        q->order, nullptr, nullptr, amax_out, (hipStream_t)stream);
   return launch_status(e, fn);
+}
+
+int w4a4_linear_plan(int64_t M, int64_t N, int64_t K, int32_t fmt, int32_t with_workspace, int32_t* plan) {
+  const char* fn = "w4a4_linear_plan";
+  if (!plan) return fail(W4A4_ERR_INVALID_ARG, "%s: plan is NULL", fn);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(W4A4_ERR_INVALID_ARG, "%s: sizes must be positive", fn);
+  if (K % 64 != 0 || K > 65536 || M > INT32_MAX || N > INT32_MAX)
+    return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: unsupported shape", fn);
+  if (fmt != W4A4_FMT_INT4 && fmt != W4A4_FMT_INT8 && fmt != W4A4_FMT_NVFP4 && fmt != W4A4_FMT_W4A8 &&
+      fmt != W4A4_FMT_FP8)
+    return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: unknown fmt %d", fn, fmt);
+  if (M <= 64 && fmt != W4A4_FMT_NVFP4) {
+    int rows = 0, cols = 0;
+    const int splits = w4a4::decode_shape(fmt, M, N, K, with_workspace != 0, &rows, &cols);
+    plan[0] = splits > 1 ? W4A4_PLAN_DECODE_SPLIT : W4A4_PLAN_DECODE;
+    plan[1] = rows;
+    plan[2] = cols;
+    plan[3] = splits;
+    return ok();
+  }
+  int bm = 0, bn = 0;
+  const int cfg = w4a4::wide_plan(fmt, M, N, K, &bm, &bn);
+  if (cfg < 0) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: no many-token kernel for fmt %d", fn, fmt);
+  plan[0] = (fmt == W4A4_FMT_NVFP4 && cfg == 0) ? W4A4_PLAN_NVFP4_SHARED : W4A4_PLAN_TILE;
+  plan[1] = bm;
+  plan[2] = bn;
+  plan[3] = 1;
+  return ok();
 }
 
 size_t w4a4_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt) {

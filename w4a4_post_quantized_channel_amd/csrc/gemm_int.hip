@@ -419,6 +419,14 @@ size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
   return M <= 64 ? decode_plan(M, N, K, fmt == 0 || fmt == 3).ws_bytes : 0;
 }
 
+int decode_shape(int fmt, int64_t M, int64_t N, int64_t K, bool with_workspace, int* rows, int* cols) {
+  const DecodePlan p = decode_plan(M, N, K, fmt == 0 || fmt == 3);
+  const bool split = with_workspace && p.splits > 1;
+  *rows = 16 * (split ? p.ti : decode_ti(M, false));
+  *cols = split ? 16 * kDecTJ : 16;
+  return split ? p.splits : 1;
+}
+
 template <int DF>
 static void launch_decode(const GemmArgs& g, const DecodePlan& p, int32_t* part, hipStream_t st) {
   constexpr int KIND = DecFmt<DF>::KIND;

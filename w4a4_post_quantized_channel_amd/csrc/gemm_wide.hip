@@ -927,9 +927,26 @@ WideChoice choose_fp8(int64_t M, int64_t N, int64_t K) {
   return c1 <= c5 ? WideChoice{1, (M + 127) / 128, (N + 255) / 256} : WideChoice{5, (M + 127) / 128, (N + 127) / 128};
 }
 
+// Which tile shapes have a kernel instance for a format: the 256x160 shape
+// is not built for W4A8 (register budget) nor FP8 (LDS), the 128x96 and
+// 64x64 shapes are not built for FP8, and the FP8-only 128x128 shape
+// (configuration 5) for FP8 alone.
+constexpr bool wide_has_kernel(int fmt, int cfg) {
+  return cfg == 0 ? (fmt != W_W4A8 && fmt != W_FP8)
+       : cfg == 1 ? true
+       : (cfg == 2 || cfg == 3) ? fmt != W_FP8
+       : cfg == 5 ? fmt == W_FP8
+       : false;
+}
+
+WideChoice wide_choice(int fmt, int64_t M, int64_t N, int64_t K) {
+  return fmt == W_FP8 ? choose_fp8(M, N, K) : choose(M, N, K, fmt, fmt == W_W4A8);
+}
+
 template <int FMT>
 hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
-  const WideChoice c = FMT == W_FP8 ? choose_fp8(g.M, g.N, g.K) : choose(g.M, g.N, g.K, FMT, FMT == W_W4A8);
+  const WideChoice c = wide_choice(FMT, g.M, g.N, g.K);
+  if (!wide_has_kernel(FMT, c.cfg)) return hipErrorInvalidConfiguration;   // nothing launched
   const dim3 grid((unsigned)(c.tm * c.tn));
   const int tm = (int)c.tm, tn = (int)c.tn;
   switch (c.cfg) {
@@ -948,22 +965,33 @@ hipError_t launch_wide_fmt(const GemmArgs& g, hipStream_t st) {
       if constexpr (FMT != W_FP8)
         hipLaunchKernelGGL((gemm_wide_kernel<FMT, 2, 6, 4, 1, 2>), grid, dim3(512), 0, st, g, tm, tn);
       break;
-    default:
+    case 3:
       if constexpr (FMT != W_FP8)
         hipLaunchKernelGGL((gemm_wide_kernel<FMT, 2, 4, 2, 1, 4>), grid, dim3(512), 0, st, g, tm, tn);
       break;
+    default: return hipErrorInvalidConfiguration;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
+int wide_plan(int fmt, int64_t M, int64_t N, int64_t K, int* bm, int* bn) {
+  if (fmt != W_INT4 && fmt != W_INT8 && fmt != W_NVFP4 && fmt != W_W4A8 && fmt != W_FP8) return -1;
+  const WideChoice c = wide_choice(fmt, M, N, K);
+  if (!wide_has_kernel(fmt, c.cfg)) return -1;
+  *bm = c.cfg == 5 ? 128 : kCfgBM[c.cfg];
+  *bn = c.cfg == 5 ? 128 : kCfgBN[c.cfg];
+  return c.cfg;
+}
+
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st) {
   if (fmt == 0) return launch_wide_fmt<W_INT4>(g, st);
   if (fmt == 1) return launch_wide_fmt<W_INT8>(g, st);
   if (fmt == 3) return launch_wide_fmt<W_W4A8>(g, st);
   if (fmt == 4) return launch_wide_fmt<W_FP8>(g, st);
-  return launch_wide_fmt<W_NVFP4>(g, st);
+  if (fmt == 2) return launch_wide_fmt<W_NVFP4>(g, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace w4a4

@@ -50,6 +50,12 @@ size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 // gemm_wide.hip: many-token kernel with packed operands in LDS, fmt 0 int4, 1 int8, 2 nvfp4, 3 W4A8,
 // 4 fp8
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st);
+// The many-token tile the launcher picks for (fmt, M, N, K): its
+// configuration index (>= 0, tile bm x bn), or -1 when no kernel exists.
+int wide_plan(int fmt, int64_t M, int64_t N, int64_t K, int* bm, int* bn);
+// Few-token plan (M <= 64): the number of K splits (1 = one kernel, no
+// reduction) and the rows x columns of one workgroup's output tile.
+int decode_shape(int fmt, int64_t M, int64_t N, int64_t K, bool with_workspace, int* rows, int* cols);
 
 // gptq.hip --------------------------------------------------------------------
 // GPTQ-style rounding at pack time: codes (int4 packed if qmax == 7, else

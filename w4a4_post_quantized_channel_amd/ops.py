@@ -24,10 +24,11 @@ BRANCH_NONE, BRANCH_BF16 = 0, 1
 FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4, "w4a8": FMT_W4A8, "fp8": FMT_FP8}
 ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
           "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTS = ["quantize_act", "quantize_act_gather", "pack_weights", "pack_weights_gptq", "w4a4_gptq_workspace_size", "w4a4_linear", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
-           "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_workspace_size", "w4a4_status_string",
+           "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_linear_plan",
+           "w4a4_workspace_size", "w4a4_status_string",
            "w4a4_last_error", "w4a4_abi_version"]
 
 
@@ -66,8 +67,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "w4a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
         "fp8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
         "w4a4_workspace_size": [i64, i64, i64, i32],
-        "lowrank_add": [vp, i64, i64, i64, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp],
-        "w4a4_lowrank_project": [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp],
+        "lowrank_add": [vp, i32, i64, i64, i64, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp],
+        "w4a4_lowrank_project": [vp, i32, i64, i64, i64, vp, vp, i64, vp, i64, vp],
+        "w4a4_linear_plan": [i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_int32)],
         "w4a4_lowrank_width": [i64, i64, i64],
         "w4a4_transform_amax": [vp, i32, i64, i64, i64, vp, qd, vp, vp],
         "w4a4_status_string": [ctypes.c_int],
@@ -227,6 +229,16 @@ def branch_desc(a: Optional[torch.Tensor], b: Optional[torch.Tensor], r: Optiona
     return BranchDesc(BRANCH_BF16, r, a.shape[1], 0, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0))
 
 
+PLAN_FAMILIES = {1: "decode", 2: "decode_split", 3: "tile", 4: "nvfp4_shared"}
+
+
+def linear_plan(M: int, N: int, K: int, fmt: str, with_workspace: bool = True) -> dict:
+    """The kernel the linear entry point runs for this shape (host query)."""
+    out = (ctypes.c_int32 * 4)()
+    _check("w4a4_linear_plan", LIB.w4a4_linear_plan(M, N, K, FMTS[fmt], int(with_workspace), out))
+    return {"family": PLAN_FAMILIES[out[0]], "tile": (out[1], out[2]), "splits": out[3]}
+
+
 def workspace_size(M: int, N: int, K: int, fmt: str) -> int:
     return int(LIB.w4a4_workspace_size(M, N, K, FMTS[fmt]))
 
@@ -293,8 +305,8 @@ def lowrank_add(x: torch.Tensor, y: torch.Tensor, lw: torch.Tensor, *, l1t: Opti
     _check_branch_inputs(x, l1t, idx, lw)
     M, K, ldx = _rowmajor(x)
     N, r = lw.shape
-    _check("lowrank_add", LIB.lowrank_add(_ptr(x), M, K, ldx, _ptr(l1t), _ptr(idx), _ptr(lw), lw.stride(0), r, N,
-                                          _ptr(y), _dtype_code(y), y.stride(0), _stream(stream)))
+    _check("lowrank_add", LIB.lowrank_add(_ptr(x), _dtype_code(x), M, K, ldx, _ptr(l1t), _ptr(idx), _ptr(lw),
+                                          lw.stride(0), r, N, _ptr(y), _dtype_code(y), y.stride(0), _stream(stream)))
     return y
 
 
@@ -315,6 +327,6 @@ def lowrank_project(x: torch.Tensor, *, l1t: Optional[torch.Tensor] = None, idx:
     width = lowrank_width(M, K, r if l1t is not None else -r)
     if out is None:
         out = torch.empty((M, width), dtype=torch.bfloat16, device=x.device)
-    _check("w4a4_lowrank_project", LIB.w4a4_lowrank_project(_ptr(x), M, K, ldx, _ptr(l1t), _ptr(idx), r, _ptr(out),
-                                                            out.stride(0), _stream(stream)))
+    _check("w4a4_lowrank_project", LIB.w4a4_lowrank_project(_ptr(x), _dtype_code(x), M, K, ldx, _ptr(l1t), _ptr(idx),
+                                                            r, _ptr(out), out.stride(0), _stream(stream)))
     return out[:, :2 * r] if l1t is not None else out

@@ -40,6 +40,10 @@ class QuantizedLinear:
                  fmt: str = "int4", *, fwht_block: int = 64, order: str = "smooth_then_rotate",
                  branch: Optional[dict] = None, y_dtype=torch.bfloat16, use_workspace: bool = True,
                  gptq: Optional[dict] = None, stream=None):
+        if branch is not None and branch["kind"] == "outlier" and order != "smooth_then_rotate":
+            # kept channels leave the quantized path through s = inv_s = 0,
+            # which removes raw channels only when smoothing comes first
+            raise ValueError("a kept-channel branch needs order='smooth_then_rotate'")
         self.fmt, self.fwht_block, self.order = fmt, fwht_block, order
         # W4A8 (the 8-bit-activation denoising steps) keeps 4-bit weight codes;
         # its activations are int8 codes in the W4A8 layout
