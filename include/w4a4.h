@@ -236,6 +236,28 @@ int w4a4_linear(const void* a_codes, const void* a_scales,
                 const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* w4a4_linear_noalloc -- w4a4_linear for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments and results as the
+ * linear entry point of fmt (W4A4_FMT_INT4 / NVFP4: w4a4_linear, INT8:
+ * w8a8_linear, W4A8: w4a8_linear, FP8: fp8_linear) given a workspace of
+ * w4a4_workspace_size bytes, but without a workspace argument: when the
+ * few-token plan splits K, the int32 partial tiles go to a static device
+ * buffer of W4A4_NOALLOC_SCRATCH_BYTES that the library owns, one per GPU,
+ * held until the process ends.  It calls no allocator.  Every call on a GPU
+ * shares that GPU's buffer: calls that can overlap on one GPU (unordered
+ * streams, concurrent host threads) race and must not be issued; calls
+ * ordered on one stream are fine.  No initialisation is needed (partials
+ * are fully written before they are read).  A plan needing more than the
+ * buffer is W4A4_ERR_WORKSPACE with nothing launched (no shape the linear
+ * entry points accept needs more). */
+#define W4A4_NOALLOC_SCRATCH_BYTES (4u << 20)
+int w4a4_linear_noalloc(const void* a_codes, const void* a_scales,
+                        const void* w_codes, const void* w_scales,
+                        int64_t M, int64_t N, int64_t K, int32_t fmt, float alpha,
+                        const w4a4_branch* br, void* y, int32_t y_dtype, int64_t ldy,
+                        void* stream);
+
 /* w8a8_linear -- INT8 W8A8 sibling (FoldQuantVLA contribution 3: INT8 at
  * o_proj / down_proj).  Same arguments and semantics as w4a4_linear with
  * W4A4_FMT_INT8 codes (exact int32 accumulation). */

@@ -271,3 +271,21 @@ def test_linear_plan_names_a_kernel_for_every_supported_shape(ops):
     assert L.w4a4_linear_plan(64, 64, 128, 9, 0, out) == -4           # unknown format
     assert L.w4a4_linear_plan(0, 64, 128, 0, 0, out) == -1
     assert L.w4a4_linear_plan(64, 64, 128, 0, 0, None) == -1
+
+
+def test_split_plans_fit_the_static_buffer(ops):
+    """w4a4_linear_noalloc keeps split-K partials in a 4 MiB static buffer per
+    GPU: no few-token plan needs more (at most 256 partial tiles of 64 x 64
+    int32), so its size check never refuses a shape the linear entry points
+    accept."""
+    worst = 0
+    for M in [1, 7, 16, 17, 32, 33, 48, 63, 64]:
+        for N in [16, 48, 64, 100, 256, 512, 768, 1000, 2048, 4096]:
+            for K in [64, 1024, 4096, 8192, 8256, 30016, 65536]:
+                for fmt in [0, 1, 3, 4]:
+                    worst = max(worst, ops.LIB.w4a4_workspace_size(M, N, K, fmt))
+    assert 0 < worst <= 4 << 20
+    args = [FAKE, FAKE, FAKE, FAKE, 4, 8, 128]
+    assert ops.LIB.w4a4_linear_noalloc(*args, 9, 1.0, None, FAKE2, 1, 8, None) == -4     # unknown format
+    assert ops.LIB.w4a4_linear_noalloc(*args[:6], 100, 0, 1.0, None, FAKE2, 1, 8, None) == -2   # K % 64
+    assert ops.LIB.w4a4_linear_noalloc(*args, 0, 1.0, None, FAKE2, 1, 4, None) == -1     # ldy < N

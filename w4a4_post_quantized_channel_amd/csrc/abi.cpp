@@ -11,6 +11,8 @@
 #include "../../include/w4a4.h"
 #include "launch.h"
 
+static_assert(w4a4::kNoAllocScratchBytes == W4A4_NOALLOC_SCRATCH_BYTES, "one size for the static split-K buffer");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -108,7 +110,8 @@ int check_branch(const char* fn, const w4a4_branch* br, int64_t M, int64_t N) {
 
 int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scales, const void* w_codes,
                const void* w_scales, int64_t M, int64_t N, int64_t K, float alpha, const w4a4_branch* br,
-               void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t ws_bytes, void* stream) {
+               void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t ws_bytes, void* stream,
+               bool check_only = false) {
   if (M < 0 || N < 0 || K <= 0) return fail(W4A4_ERR_INVALID_ARG, "%s: bad sizes", fn);
   if (K % 64 != 0) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld not a multiple of 64", fn, (long long)K);
   if (K > 65536) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld above 65536", fn, (long long)K);
@@ -130,6 +133,13 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
     return fail(W4A4_ERR_MISALIGNED, "%s: codes not 16-byte aligned", fn);
   if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(y, dt_size(y_dtype)))
     return fail(W4A4_ERR_MISALIGNED, "%s: scales / y misaligned", fn);
+  if (M > 64 || fmt == W4A4_FMT_NVFP4) {
+    int bm = 0, bn = 0;
+    if (w4a4::wide_plan(fmt, M, N, K, &bm, &bn) < 0)
+      return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: no many-token kernel for fmt %d at %lldx%lldx%lld", fn, fmt,
+                  (long long)M, (long long)N, (long long)K);
+  }
+  if (check_only) return ok();
 
   w4a4::GemmArgs g{};
   g.a = (const uint8_t*)a_codes;
@@ -144,12 +154,6 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
     g.br.r = br->r; g.br.ra = br->ra;
   }
   g.y = y; g.y_dtype = y_dtype; g.ldy = ldy;
-  if (M > 64 || fmt == W4A4_FMT_NVFP4) {
-    int bm = 0, bn = 0;
-    if (w4a4::wide_plan(fmt, M, N, K, &bm, &bn) < 0)
-      return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: no many-token kernel for fmt %d at %lldx%lldx%lld", fn, fmt,
-                  (long long)M, (long long)N, (long long)K);
-  }
   hipError_t e;
   if (fmt == W4A4_FMT_NVFP4) {
     e = w4a4::launch_gemm_wide(2, g, (hipStream_t)stream);
@@ -224,6 +228,30 @@ int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t l
   if (q && q->fmt == W4A4_FMT_W4A8)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "pack_weights: W4A8 weights are packed with W4A4_FMT_INT4");
   return run_quant("pack_weights", w, w_dtype, N, K, ldw, smooth, q, codes, scales, stream);
+}
+
+int w4a4_linear_noalloc(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                        int64_t M, int64_t N, int64_t K, int32_t fmt, float alpha, const w4a4_branch* br, void* y,
+                        int32_t y_dtype, int64_t ldy, void* stream) {
+  const char* fn = "w4a4_linear_noalloc";
+  if (fmt != W4A4_FMT_INT4 && fmt != W4A4_FMT_INT8 && fmt != W4A4_FMT_NVFP4 && fmt != W4A4_FMT_W4A8 &&
+      fmt != W4A4_FMT_FP8)
+    return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: unknown fmt %d", fn, fmt);
+  // every argument check first, so a rejected call touches no device
+  int st = run_linear(fn, fmt, a_codes, a_scales, w_codes, w_scales, M, N, K, alpha, br, y, y_dtype, ldy, nullptr,
+                      0, stream, true);
+  if (st != W4A4_OK) return st;
+  const size_t need = (fmt != W4A4_FMT_NVFP4 && M > 0 && N > 0) ? w4a4::gemm_int_workspace(fmt, M, N, K) : 0;
+  if (need > w4a4::kNoAllocScratchBytes)
+    return fail(W4A4_ERR_WORKSPACE, "%s: the split plan needs %zu bytes, above the %zu-byte static buffer", fn, need,
+                w4a4::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && M > 0 && N > 0) {
+    hipError_t e = w4a4::noalloc_scratch(&ws);
+    if (e != hipSuccess) return launch_status(e, fn);
+  }
+  return run_linear(fn, fmt, a_codes, a_scales, w_codes, w_scales, M, N, K, alpha, br, y, y_dtype, ldy, ws,
+                    ws ? w4a4::kNoAllocScratchBytes : 0, stream);
 }
 
 int w4a4_linear(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,

@@ -31,6 +31,7 @@
 //    epilogue.  Splits never hand off inside one kernel: on gfx950 a
 //    cross-workgroup handoff needs an agent-scope fence, which writes back
 //    and invalidates the XCD's L2.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -417,6 +418,38 @@ static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, bool int4) {
 // fmt: 0 int4 x int4, 1 int8 x int8, 3 int8 activations x int4 weights
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
   return M <= 64 ? decode_plan(M, N, K, fmt == 0 || fmt == 3).ws_bytes : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned split-K buffer for callers that cannot allocate.  Every GPU
+// holds its own copy of this array (kNoAllocScratchBytes, until the process
+// ends).  In host code ``scratch`` names a host-side stand-in, never the
+// device memory: its device address is looked up once per device with
+// hipGetSymbolAddress (that device current) and only that address is passed
+// to kernels.  The split plan needs at most 256 partial tiles of 64 x 64
+// int32 (4 MiB).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
 }
 
 int decode_shape(int fmt, int64_t M, int64_t N, int64_t K, bool with_workspace, int* rows, int* cols) {

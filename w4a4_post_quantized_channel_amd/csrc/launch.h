@@ -47,6 +47,12 @@ struct GemmArgs {
 hipError_t launch_gemm_int(int fmt, GemmArgs g, void* workspace, size_t ws_bytes, hipStream_t st);
 size_t gemm_int_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 
+// Size of the library-owned split-K buffer (one per GPU) behind
+// w4a4_linear_noalloc, and its device address on the current device
+// (looked up once per device; never allocates).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // gemm_wide.hip: many-token kernel with packed operands in LDS, fmt 0 int4, 1 int8, 2 nvfp4, 3 W4A8,
 // 4 fp8
 hipError_t launch_gemm_wide(int fmt, GemmArgs g, hipStream_t st);

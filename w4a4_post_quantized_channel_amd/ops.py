@@ -26,7 +26,7 @@ ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
           "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
 ABI_VERSION = 2
 
-EXPORTS = ["quantize_act", "quantize_act_gather", "pack_weights", "pack_weights_gptq", "w4a4_gptq_workspace_size", "w4a4_linear", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
+EXPORTS = ["quantize_act", "quantize_act_gather", "pack_weights", "pack_weights_gptq", "w4a4_gptq_workspace_size", "w4a4_linear", "w4a4_linear_noalloc", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
            "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_linear_plan",
            "w4a4_workspace_size", "w4a4_status_string",
            "w4a4_last_error", "w4a4_abi_version"]
@@ -63,6 +63,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pack_weights_gptq": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp, vp, vp, sz, vp],
         "w4a4_gptq_workspace_size": [i64, i64],
         "w4a4_linear": [vp, vp, vp, vp, i64, i64, i64, i32, f32, br, vp, i32, i64, vp, sz, vp],
+        "w4a4_linear_noalloc": [vp, vp, vp, vp, i64, i64, i64, i32, f32, br, vp, i32, i64, vp],
         "w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
         "w4a8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
         "fp8_linear": [vp, vp, vp, vp, i64, i64, i64, f32, br, vp, i32, i64, vp, sz, vp],
@@ -270,6 +271,23 @@ def _linear(fn: str, fmt: str, a_codes, a_scales, w_codes, w_scales, K: int, *, 
 def w4a4_linear(a_codes, a_scales, w_codes, w_scales, K: int, fmt: str = "int4", **kw):
     """y = alpha * dequant(A . W^T) (+ fused bf16 branch); fmt int4 or nvfp4."""
     return _linear("w4a4_linear", fmt, a_codes, a_scales, w_codes, w_scales, K, **kw)
+
+
+def linear_noalloc(a_codes, a_scales, w_codes, w_scales, K: int, fmt: str = "int4", *, alpha=1.0,
+                   branch: Optional[BranchDesc] = None, y=None, y_dtype=torch.bfloat16, stream=None,
+                   M: Optional[int] = None):
+    """The linear of ``fmt`` with split-K partials in the library's static
+    per-GPU buffer (no workspace, no allocation inside the call; ``y`` must
+    be given by callers that cannot allocate)."""
+    M = a_codes.shape[0] if M is None else M
+    N = w_codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=a_codes.device)
+    br = branch if branch is not None else branch_desc(None, None)
+    _check("w4a4_linear_noalloc", LIB.w4a4_linear_noalloc(
+        _ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K, FMTS[fmt], float(alpha),
+        ctypes.byref(br), _ptr(y), _dtype_code(y), y.stride(0), _stream(stream)))
+    return y
 
 
 def w8a8_linear(a_codes, a_scales, w_codes, w_scales, K: int, **kw):
