@@ -9,6 +9,7 @@ buffers and argument plumbing.
 """
 from __future__ import annotations
 
+import copy
 from typing import Optional
 
 import numpy as np
@@ -96,25 +97,39 @@ class QuantizedLinear:
             self._bufs[M] = b
         return b
 
-    def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-        M = x.shape[0]
-        b = self.buffers(M, x.device)
-        bd = None
+    def quantize(self, x: torch.Tensor, stream=None):
+        """quantize_act into this layer's M-row buffers; with kept channels
+        (bf16 x) the same pass also writes the bypass operand."""
+        b = self.buffers(x.shape[0], x.device)
         if self.branch is not None and self.branch["kind"] == "outlier" and x.dtype == torch.bfloat16:
-            # one pass over x: codes, scales and the kept channels
             ops.quantize_act_gather(x, self.inv_s, self.branch["idx"], self.a_fmt, fwht_block=self.fwht_block,
                                     order=self.order, tensor_scale=self.g_a, codes=b["codes"],
                                     scales=b["scales"], xo=b["br_a"], stream=stream)
-            bd = ops.branch_desc(b["br_a"], self.branch["lw"])
         else:
             ops.quantize_act(x, self.inv_s, self.a_fmt, fwht_block=self.fwht_block, order=self.order,
                              tensor_scale=self.g_a, codes=b["codes"], scales=b["scales"], stream=stream)
-            if self.branch is not None:
-                if self.branch["kind"] == "lowrank":
-                    a = ops.lowrank_project(x, l1t=self.branch["l1t"], out=b["br_a"], stream=stream)
-                else:
-                    a = ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
-                bd = ops.branch_desc(a, self.branch["lw"])
+
+    def has_projection(self, x_dtype=torch.bfloat16) -> bool:
+        """Whether the branch operand needs its own kernel (w4a4_lowrank_project)."""
+        if self.branch is None:
+            return False
+        return self.branch["kind"] == "lowrank" or x_dtype != torch.bfloat16
+
+    def project(self, x: torch.Tensor, stream=None):
+        """The branch operand when the quantizer pass does not write it."""
+        if not self.has_projection(x.dtype):
+            return
+        b = self.buffers(x.shape[0], x.device)
+        if self.branch["kind"] == "lowrank":
+            ops.lowrank_project(x, l1t=self.branch["l1t"], out=b["br_a"], stream=stream)
+        else:
+            ops.lowrank_project(x, idx=self.branch["idx"], out=b["br_a"], stream=stream)
+
+    def gemm(self, M: int, device, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """The linear on the quantized activations in the M-row buffers, with
+        the branch fused into its epilogue."""
+        b = self.buffers(M, device)
+        bd = None if self.branch is None else ops.branch_desc(self.branch_operand(M, device), self.branch["lw"])
         y = b["y"] if out is None else out
         if self.fmt in ("int8", "w4a8", "fp8"):
             fn = {"int8": ops.w8a8_linear, "w4a8": ops.w4a8_linear, "fp8": ops.fp8_linear}[self.fmt]
@@ -122,6 +137,21 @@ class QuantizedLinear:
                       branch=bd, y=y, workspace=b["ws"], stream=stream)
         return ops.w4a4_linear(b["codes"], b["scales"], self.w_codes, self.w_scales, self.K, self.fmt,
                                alpha=self.alpha, branch=bd, y=y, workspace=b["ws"], stream=stream)
+
+    def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        self.quantize(x, stream)
+        self.project(x, stream)
+        return self.gemm(x.shape[0], x.device, out, stream)
+
+    def replica(self) -> "QuantizedLinear":
+        """A layer with the same configuration and its own device copies of the
+        packed weights and branch operands (and its own buffers)."""
+        r = copy.copy(self)
+        r.w_codes, r.w_scales = self.w_codes.clone(), self.w_scales.clone()
+        if self.branch is not None:
+            r.branch = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in self.branch.items()}
+        r._bufs = {}
+        return r
 
     __call__ = forward
 
