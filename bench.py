@@ -155,13 +155,15 @@ def hbm_roof(byt, us):
 PHASE_LOG = []
 
 
-def marker(torch, name):
-    """A short spin kernel before each timed phase: it splits the profiler's
-    kernel trace into the phases listed under ``profile_phases``."""
+def marker(torch, name=None):
+    """A short spin kernel before and after each timed phase: the profiler's
+    kernel trace splits into the phases listed under ``profile_phases``
+    (dispatches between an end and the next start are set-up)."""
     torch.cuda.synchronize()
     torch.cuda._sleep(100)
     torch.cuda.synchronize()
-    PHASE_LOG.append(name)
+    if name is not None:
+        PHASE_LOG.append(name)
 
 
 def pct(v, q):
@@ -202,6 +204,7 @@ def time_graph(torch, fns, replays, name):
         e1.record(stream)
     torch.cuda.synchronize()
     per = [e0.elapsed_time(e1) * 1e3 / len(fns) for e0, e1 in ev]
+    marker(torch)
     del graph
     return {"median": pct(per, 0.5), "p10": pct(per, 0.1), "p90": pct(per, 0.9), "mean": sum(per) / len(per)}
 
@@ -496,12 +499,13 @@ def _phases_of(rows, phases, key):
     """Group dispatch rows (sorted in dispatch order) by the phase the marker
     kernels delimit: {phase name: {kernel name: [values]}}."""
     import re
-    out, cur = {}, -1
+    out, nmark = {}, 0
     for r in rows:
         name = r["Kernel_Name"]
         if _is_marker(name):
-            cur += 1
+            nmark += 1
             continue
+        cur = (nmark - 1) // 2 if nmark % 2 == 1 else -1    # inside start ... end of phase cur
         if 0 <= cur < len(phases):
             k = re.sub(r"\(.*", "", name)
             out.setdefault(phases[cur], {}).setdefault(k, []).append(key(r))
