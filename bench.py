@@ -246,6 +246,13 @@ def measure_case(torch, cid, name, replays, cold=True, built=None):
            "warm": {}, "cold": None}
     for k, f in kernels.items():
         res["warm"][k] = time_graph(torch, [lambda f=f: f(layer, x)] * G, replays, f"{cid} warm {k}")
+    if layer.branch is not None and layer.branch["kind"] == "lowrank" and not layer.fuse_lowrank:
+        # the single-read alternative (quantize_act_lowrank), timed beside the default two kernels
+        layer.fuse_lowrank = True
+        res["warm"]["fused_quantize_project"] = time_graph(torch, [lambda: layer.quantize(x)] * G, replays,
+                                                           f"{cid} warm fused_quantize_project")
+        layer.fuse_lowrank = False
+        layer.forward(x)
     if cold:
         S = max(2, int(math.ceil(COLD_BYTES / set_bytes(case, layer))))
         sets = [(layer, x)] + [(layer.replica(), x.clone()) for _ in range(S - 1)]
@@ -301,6 +308,11 @@ def summarize_case(case, layer, res):
         ks["quantize"] = {"us": r["quantize"], **hbm_roof(quant_bytes(case, fused_cols), r["quantize"]["median"])}
         if "project" in r:
             ks["project"] = {"us": r["project"], **hbm_roof(proj_bytes(case), r["project"]["median"])}
+        if "fused_quantize_project" in r:   # not part of the call: the single-read alternative
+            ks["fused_quantize_project"] = {"us": r["fused_quantize_project"], "in_call": False,
+                                            **hbm_roof(quant_bytes(case, 2 * layer.branch["lw"].shape[1])
+                                                       + 2 * layer.branch["lw"].shape[1] * case.K,
+                                                       r["fused_quantize_project"]["median"])}
         ks["gemm"] = {"us": r["gemm"], **gemm_roof(case, r["gemm"]["median"])}
         m["kernels"] = ks
         if mode == "cold":

@@ -289,3 +289,18 @@ def test_split_plans_fit_the_static_buffer(ops):
     assert ops.LIB.w4a4_linear_noalloc(*args, 9, 1.0, None, FAKE2, 1, 8, None) == -4     # unknown format
     assert ops.LIB.w4a4_linear_noalloc(*args[:6], 100, 0, 1.0, None, FAKE2, 1, 8, None) == -2   # K % 64
     assert ops.LIB.w4a4_linear_noalloc(*args, 0, 1.0, None, FAKE2, 1, 4, None) == -1     # ldy < N
+
+
+def test_quantize_act_lowrank_rejects_bad_arguments(ops):
+    L = ops.LIB
+    g = lambda dt=1, M=4, K=128, r=32, ldo=64, l1=FAKE, out=FAKE2, q=None: L.quantize_act_lowrank(
+        FAKE, dt, M, K, K, None, q or _q(ops), FAKE2, FAKE2, l1, r, out, ldo, None)
+    assert g(dt=0) == -4                          # x must be bf16
+    assert g(r=8) == -1 and g(r=24) == -1 and g(r=64, ldo=128) == -1
+    assert g(ldo=63) == -1                        # hi and lo need 2r columns
+    assert g(K=96 + 64) == -2                     # K % 64
+    assert g(K=4096 + 64, r=16) == -2             # the staged row fits LDS up to K = 4096
+    assert g(l1=None) == -1 and g(out=None) == -1
+    assert g(l1=ctypes.c_void_p(0x10008)) == -3
+    assert g(q=_q(ops, fmt=9)) == -4
+    assert g(M=0, l1=None, out=None) == 0         # empty batch

@@ -350,6 +350,49 @@ def test_lowrank_project(ops, pipe, M, K, r):
     assert np.max(np.abs(recon - T)) <= 2.0 ** -15 * np.max(np.abs(T))
 
 
+@pytest.mark.parametrize("M,K,r,fmt", [(1024, 3072, 32, "int4"), (77, 3072, 32, "int4"), (33, 256, 16, "int8"),
+                                       (130, 4096, 16, "w4a8"), (17, 512, 32, "fp8"), (300, 320, 32, "nvfp4"),
+                                       (16, 64, 16, "int4"), (1, 1024, 32, "int4"), (2051, 1536, 32, "int4")])
+def test_quantize_act_lowrank(ops, pipe, M, K, r, fmt):
+    """The fused pass: codes and scales exactly as quantize_act writes them,
+    and T = x L1 as the bf16 hi/lo pair within the projection's bound
+    (ragged row groups of 4, both ranks the kernel takes, K up to 4096, more
+    row groups than workgroups)."""
+    case = WL.linear_case(M, 8, K, seed=71 + r + K, fmt=fmt, n_outliers=4, outlier_gain=10.0, lowrank=r)
+    t = pipe.case_to_device(case)
+    kw = dict(fwht_block=case.fwht_block, tensor_scale=1.0 / 64)
+    _report("quantize_act_lowrank", M=M, K=K, r=r, fmt=fmt)
+    c0, s0 = ops.quantize_act(t["x"], t["inv_s"], fmt if fmt != "w4a8" else "w4a8", **kw)
+    c1, s1, out = ops.quantize_act_lowrank(t["x"], t["inv_s"], t["branch"]["l1t"], fmt, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1) and torch.equal(s0, s1)
+    o = _np(out)
+    T = case.x.astype(np.float64) @ case.branch["l1"].astype(np.float64)
+    recon = o[:, :r].astype(np.float64) + o[:, r:].astype(np.float64)
+    assert np.max(np.abs(recon - T)) <= 2.0 ** -15 * np.max(np.abs(T))
+    # the same operand as the separate projection, to its rounding
+    ref = _np(ops.lowrank_project(t["x"], l1t=t["branch"]["l1t"]))
+    rref = ref[:, :r].astype(np.float64) + ref[:, r:].astype(np.float64)
+    assert np.max(np.abs(recon - rref)) <= 2.0 ** -15 * np.max(np.abs(T))
+
+
+@pytest.mark.slow
+def test_lowrank_fused_end_to_end(ops, pipe):
+    """The 1024-token low-rank workload with the single-read quantizer
+    (quantize_act_lowrank feeding the fused epilogue): codes exact, output
+    within tolerance of the oracle."""
+    case = WL.workload("lowrank")
+    layer, t = pipe.build_layer(case)
+    layer.fuse_lowrank = True
+    assert not layer.has_projection()
+    y = layer.forward(t["x"])
+    ref = _oracle(case)
+    b = layer.buffers(case.M, t["x"].device)
+    assert check_operand("int4", _np(b["codes"]), _np(b["scales"]), ref["a"], what="activations") == 0
+    worst = check_output(_np(y), ref["y"], 1e-2)
+    _report("lowrank_fused", worst=f"{worst:.3g}")
+
+
 def test_lowrank_gather(ops, pipe):
     case = WL.linear_case(50, 8, 512, seed=41, lowrank=24)
     t = pipe.case_to_device(case)

@@ -223,6 +223,28 @@ int quantize_act_gather(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
   return run_quant(fn, x, x_dtype, M, K, ldx, inv_smooth, q, codes, scales, stream, idx, r, xo, ldo);
 }
 
+int quantize_act_lowrank(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const float* inv_smooth,
+                         const w4a4_qdesc* q, void* codes, void* scales, const void* l1t, int64_t r, void* out,
+                         int64_t ldo, void* stream) {
+  const char* fn = "quantize_act_lowrank";
+  if (x_dtype != W4A4_DT_BF16) return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: x must be BF16", fn);
+  if (r != 16 && r != 32) return fail(W4A4_ERR_INVALID_ARG, "%s: r=%lld must be 16 or 32", fn, (long long)r);
+  if (ldo < 2 * r) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo < 2r", fn);
+  if (!w4a4::quant_lowrank_fits(K, r))
+    return fail(W4A4_ERR_UNSUPPORTED_SHAPE,
+                "%s: K=%lld with r=%lld: K must be a multiple of 64, at most 4096", fn,
+                (long long)K, (long long)r);
+  int st = check_quant(fn, x, x_dtype, M, K, ldx, inv_smooth, q, true, codes, scales);
+  if (st != W4A4_OK || M == 0) return st;
+  if (!l1t || !out) return fail(W4A4_ERR_INVALID_ARG, "%s: l1t / out is NULL", fn);
+  if (!aligned(l1t, 16) || !aligned(out, 2)) return fail(W4A4_ERR_MISALIGNED, "%s: l1t / out misaligned", fn);
+  const int mode = q->fmt == W4A4_FMT_W4A8 ? 4 : (q->fmt == W4A4_FMT_FP8 ? 5 : q->fmt);
+  hipError_t e = w4a4::launch_quantize_lowrank(mode, x, M, K, ldx, inv_smooth, q->tensor_scale, q->fwht_block,
+                                               q->order, codes, scales, (const uint16_t*)l1t, (int)r,
+                                               (uint16_t*)out, ldo, (hipStream_t)stream);
+  return launch_status(e, fn);
+}
+
 int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const float* smooth,
                  const w4a4_qdesc* q, void* codes, void* scales, void* stream) {
   if (q && q->fmt == W4A4_FMT_W4A8)

@@ -18,6 +18,15 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
                            const int32_t* gidx = nullptr, int gr = 0, void* gout = nullptr,
                            int64_t ldg = 0);
 int64_t quant_max_k();
+// quantize_act fused with the low-rank projection T = x L1 (bf16 input):
+// out[m, j] = bf16(T), out[m, r + j] = bf16(T - bf16(T)) for j < r.
+// Shapes: quant_lowrank_fits(K, r) (r 16 or 32, K % 64 == 0, K <= 4096).
+hipError_t launch_quantize_lowrank(int mode, const void* x, int64_t R, int64_t K, int64_t ldx, const float* scale,
+                                   float g, int rot, int order, void* codes, void* scales, const uint16_t* l1t, int r,
+                                   uint16_t* out, int64_t ldo, hipStream_t st);
+int64_t quant_lowrank_max_k();
+int quant_lowrank_max_r();
+bool quant_lowrank_fits(int64_t K, int64_t r);
 
 // gemm_int.hip / gemm_nvfp4.hip --------------------------------------------
 struct BranchArgs {

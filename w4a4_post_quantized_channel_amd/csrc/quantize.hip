@@ -234,16 +234,19 @@ __device__ __forceinline__ uint32_t nvfp4_block16(const float (&v)[16], float fl
 
 // Smoothing and rotation of one slot in place; returns the factor fl with
 // y = v * fl (see the kernel).
-template <bool BF16IN>
+// PRESC: the slot's factors were loaded beforehand (``psc``).
+template <bool BF16IN, bool PRESC = false>
 __device__ __forceinline__ float transform_slot(const SlotRaw<BF16IN>& raw, float (&v)[16],
                                                 __amdgpu_buffer_rsrc_t rsc, bool has_scale, int rot, int order,
-                                                int s, int lane) {
+                                                int s, int lane, const uint4 (&psc)[4]) {
   unpack_slot<BF16IN>(raw, v);
   float sc[16];
   if (has_scale) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 u = buf_load16(rsc, (uint32_t)(s * 64 + i * 16));
+      uint4 u;
+      if constexpr (PRESC) u = psc[i];
+      else u = buf_load16(rsc, (uint32_t)(s * 64 + i * 16));
       sc[4 * i] = __uint_as_float(u.x); sc[4 * i + 1] = __uint_as_float(u.y);
       sc[4 * i + 2] = __uint_as_float(u.z); sc[4 * i + 3] = __uint_as_float(u.w);
     }
@@ -269,6 +272,182 @@ __device__ __forceinline__ float transform_slot(const SlotRaw<BF16IN>& raw, floa
   return fl;
 }
 
+// Per-row work of the row quantizer: transform the row held in ``raw``
+// (slot (c * WPR + sub) * 64 + lane in chunk c), quantize, store codes and
+// steps (or the transformed row, or the running maximum).  Waves of one row
+// (WPR > 1) meet through ``red`` with block barriers.
+// PRESC: the smoothing factors of every slot were loaded beforehand (psc[c]).
+template <int MODE, bool BF16IN, int NC, int WPR, bool PRESC = false>
+__device__ __forceinline__ void quant_row_body(const QuantArgs& a, int64_t row, const SlotRaw<BF16IN> (&raw)[NC],
+                                               int lane, int wave, int sub, float* red, const float2* stab,
+                                               __amdgpu_buffer_rsrc_t rsc, float rg, bool g_fast, float& tmax,
+                                               const uint4 (&psc)[PRESC ? NC : 1][4]) {
+  constexpr int QMAX = (MODE == MODE_INT4 || MODE == MODE_Y4) ? 7 : 127;
+  constexpr bool I8 = MODE == MODE_INT8 || MODE == MODE_INT8W;
+  constexpr bool YOUT = MODE == MODE_Y4 || MODE == MODE_Y8;
+  constexpr bool F8 = MODE == MODE_FP8;
+  constexpr float QDIV = F8 ? 448.0f : (float)QMAX;   // step = amax / QDIV
+  const int nslots = a.K >> 4;
+  const bool has_scale = a.scale != nullptr;
+  (void)wave;
+  (void)red;
+  (void)stab;
+  (void)rg;
+  (void)g_fast;
+  (void)tmax;
+  // --- transform --------------------------------------------------------
+  // After this, the value the definition quantizes is y = v * fl exactly
+  // (fl = +-1/8 after a smoothing-then-rotation; the power-of-two factor
+  // and the lane's butterfly sign are carried into the divisor instead of
+  // being multiplied into every element).  Where v * fl would fall below
+  // the normal range, every decision is code 0 on both readings, or the
+  // slot takes the exact path, which forms y itself.
+  // Integer modes need the whole row for its maximum; NVFP4 transforms
+  // and quantizes one slot at a time.
+  if constexpr (MODE == MODE_INT4 || I8 || F8 || YOUT || MODE == MODE_AMAX) {
+    float v[NC][16];
+    float fl = 1.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) fl = transform_slot<BF16IN, PRESC>(raw[c], v[c], rsc, has_scale, a.rot, a.order,
+                                                                    (c * WPR + sub) * 64 + lane, lane,
+                                                                    psc[PRESC ? c : 0]);
+    const float afl = __builtin_fabsf(fl);
+    float mv = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mv = fmaxf(mv, __builtin_fabsf(v[c][i]));
+    float m = wave_max(mv) * afl;   // = max |y| (rounding is monotone)
+    if constexpr (MODE == MODE_AMAX) {
+      tmax = fmaxf(tmax, m);
+      return;
+    } else {
+      if constexpr (WPR > 1) {
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        if constexpr (WPR == 8) m = fmaxf(m, fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
+        __syncthreads();
+      }
+      const float step = m / QDIV;   // IEEE division
+      const bool fast = step >= kTinyStep && step <= kBig;
+      const float rstep = fast ? 1.0f / step : 0.f;
+      const float D = step / fl, rD = rstep * fl;   // exact power-of-two rescaling
+      if (lane == 0 && sub == 0) reinterpret_cast<float*>(a.scales)[row] = step;
+      if constexpr (YOUT) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int s = (c * WPR + sub) * 64 + lane;
+          if (s >= nslots) continue;
+          float4* yp = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.codes) + (size_t)row * a.K + s * 16);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            yp[k] = make_float4(v[c][4 * k] * fl, v[c][4 * k + 1] * fl, v[c][4 * k + 2] * fl, v[c][4 * k + 3] * fl);
+        }
+        return;
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int s = (c * WPR + sub) * 64 + lane;
+        // One-multiply quotients; a boundary k + 1/2 lies between t and
+        // RN(v / D) only if |t - rint(t)| is within three steps of 1/2.
+        float t[16], r[16], dmax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          t[i] = v[c][i] * rD;
+          r[i] = __builtin_rintf(t[i]);
+          dmax = fmaxf(dmax, __builtin_fabsf(t[i] - r[i]));
+        }
+        constexpr float kEdge = I8 ? 0.5f - 3.0517578125e-05f : 0.5f - 1.9073486328125e-06f;
+        bool near;
+        if constexpr (F8) {
+          // E4M3 rounding boundaries have at most five significant bits, so
+          // the low 19 bits of their fp32 patterns are zero; a one-multiply
+          // quotient within three steps of one has low bits within 4 of 0.
+          uint32_t lo = 0xFFFFFFFFu;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) lo = min(lo, (__float_as_uint(t[i]) + 4u) & 0x7FFFFu);
+          near = lo <= 8u;
+        } else {
+          near = dmax >= kEdge;
+        }
+        if (s < nslots && (!fast || near)) {
+          if (fast) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] = div_rn(v[c][i], D, rD);
+          } else if (step > 0.f) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] = (v[c][i] * fl) / step;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] = 0.f;
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) r[i] = __builtin_rintf(t[i]);
+        }
+        if (s >= nslots) continue;
+        if constexpr (F8) {
+          // |t| <= 448 up to one rounding: the clamp is the nearest value
+          uint32_t w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float a0 = __builtin_amdgcn_fmed3f(t[4 * k], -448.0f, 448.0f);
+            const float a1 = __builtin_amdgcn_fmed3f(t[4 * k + 1], -448.0f, 448.0f);
+            const float a2 = __builtin_amdgcn_fmed3f(t[4 * k + 2], -448.0f, 448.0f);
+            const float a3 = __builtin_amdgcn_fmed3f(t[4 * k + 3], -448.0f, 448.0f);
+            uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+            d = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, d, true);
+            // the converter keeps the sign of zero; the format's zero is +0
+            const uint32_t mag = d & 0x7F7F7F7Fu;
+            w[k] = mag | (d & ((mag + 0x7F7F7F7Fu) & 0x80808080u));
+          }
+          *reinterpret_cast<uint4*>(a.codes + (size_t)row * a.K + s * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+          continue;
+        }
+        uint32_t q[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          q[i] = (uint32_t)(int)__builtin_amdgcn_fmed3f(r[i], (float)(-QMAX - 1), (float)QMAX);
+        if constexpr (MODE == MODE_INT4) {
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            w0 |= (q[i] & 0xFu) << (4 * i);
+            w1 |= (q[i + 8] & 0xFu) << (4 * i);
+          }
+          *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = make_uint2(w0, w1);
+        } else {
+          uint32_t w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            // natural order: dword k holds codes 4k .. 4k+3; W4A8 order: dword k
+            // holds the even (k even) or odd (k odd) codes of group k / 2
+            const int b = MODE == MODE_INT8W ? 8 * (k >> 1) + (k & 1) : 4 * k;
+            const int d = MODE == MODE_INT8W ? 2 : 1;
+            w[k] = (q[b] & 0xFFu) | ((q[b + d] & 0xFFu) << 8) | ((q[b + 2 * d] & 0xFFu) << 16) |
+                   ((q[b + 3 * d] & 0xFFu) << 24);
+          }
+          *reinterpret_cast<uint4*>(a.codes + (size_t)row * a.K + s * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
+  } else {  // NVFP4: one E4M3 scale per slot (16 elements)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int s = (c * WPR + sub) * 64 + lane;
+      float vs[16];
+      const float fl = transform_slot<BF16IN, PRESC>(raw[c], vs, rsc, has_scale, a.rot, a.order, s, lane,
+                                                     psc[PRESC ? c : 0]);
+      uint2 w;
+      const uint32_t e = nvfp4_block16(vs, fl, a.g, rg, g_fast, stab, s < nslots, w);
+      if (s < nslots) {
+        *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = w;
+        reinterpret_cast<uint8_t*>(a.scales)[(size_t)row * (a.K >> 4) + s] = (uint8_t)e;
+      }
+    }
+  }
+}
+
 template <int MODE, bool BF16IN, int NC, int WPR>
 __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(QuantArgs a) {
   // Every argument the kernel reads goes into scalar registers before any
@@ -276,11 +455,6 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
   // itself the compiler fetched them in three dependent rounds).
   asm volatile("" ::"s"(a.x), "s"(a.R), "s"(a.K), "s"(a.ldx), "s"(a.scale), "s"(a.g), "s"(a.rot), "s"(a.order),
                "s"(a.codes), "s"(a.scales), "s"(a.amax_out), "s"(a.gidx), "s"(a.gr), "s"(a.gout), "s"(a.ldg));
-  constexpr int QMAX = (MODE == MODE_INT4 || MODE == MODE_Y4) ? 7 : 127;
-  constexpr bool I8 = MODE == MODE_INT8 || MODE == MODE_INT8W;
-  constexpr bool YOUT = MODE == MODE_Y4 || MODE == MODE_Y8;
-  constexpr bool F8 = MODE == MODE_FP8;
-  constexpr float QDIV = F8 ? 448.0f : (float)QMAX;   // step = amax / QDIV
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   static_assert(WPR == 1 || WPR == 4 || WPR == 8, "waves per row");
@@ -288,7 +462,6 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
   constexpr int RPB = NWB / WPR;                    // rows per block
   const int sub = WPR == 1 ? 0 : wave;              // wave index inside the row group
   const int grp = WPR == 1 ? wave : 0;              // row group inside the block
-  const int nslots = a.K >> 4;
   const bool has_scale = a.scale != nullptr;
   constexpr int ESZ = BF16IN ? 2 : 4;
   __shared__ float red[NWB];
@@ -326,158 +499,199 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
         }
       }
     }
-    // --- transform --------------------------------------------------------
-    // After this, the value the definition quantizes is y = v * fl exactly
-    // (fl = +-1/8 after a smoothing-then-rotation; the power-of-two factor
-    // and the lane's butterfly sign are carried into the divisor instead of
-    // being multiplied into every element).  Where v * fl would fall below
-    // the normal range, every decision is code 0 on both readings, or the
-    // slot takes the exact path, which forms y itself.
-    // Integer modes need the whole row for its maximum; NVFP4 transforms
-    // and quantizes one slot at a time.
-    if constexpr (MODE == MODE_INT4 || I8 || F8 || YOUT || MODE == MODE_AMAX) {
-      float v[NC][16];
-      float fl = 1.0f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) fl = transform_slot<BF16IN>(raw[c], v[c], rsc, has_scale, a.rot, a.order,
-                                                               (c * WPR + sub) * 64 + lane, lane);
-      const float afl = __builtin_fabsf(fl);
-      float mv = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mv = fmaxf(mv, __builtin_fabsf(v[c][i]));
-      float m = wave_max(mv) * afl;   // = max |y| (rounding is monotone)
-      if constexpr (MODE == MODE_AMAX) {
-        tmax = fmaxf(tmax, m);
-        continue;
-      } else {
-        if constexpr (WPR > 1) {
-          if (lane == 0) red[wave] = m;
-          __syncthreads();
-          m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-          if constexpr (WPR == 8) m = fmaxf(m, fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
-          __syncthreads();
-        }
-        const float step = m / QDIV;   // IEEE division
-        const bool fast = step >= kTinyStep && step <= kBig;
-        const float rstep = fast ? 1.0f / step : 0.f;
-        const float D = step / fl, rD = rstep * fl;   // exact power-of-two rescaling
-        if (lane == 0 && sub == 0) reinterpret_cast<float*>(a.scales)[row] = step;
-        if constexpr (YOUT) {
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int s = (c * WPR + sub) * 64 + lane;
-            if (s >= nslots) continue;
-            float4* yp = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.codes) + (size_t)row * a.K + s * 16);
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              yp[k] = make_float4(v[c][4 * k] * fl, v[c][4 * k + 1] * fl, v[c][4 * k + 2] * fl, v[c][4 * k + 3] * fl);
-          }
-          continue;
-        }
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int s = (c * WPR + sub) * 64 + lane;
-          // One-multiply quotients; a boundary k + 1/2 lies between t and
-          // RN(v / D) only if |t - rint(t)| is within three steps of 1/2.
-          float t[16], r[16], dmax = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            t[i] = v[c][i] * rD;
-            r[i] = __builtin_rintf(t[i]);
-            dmax = fmaxf(dmax, __builtin_fabsf(t[i] - r[i]));
-          }
-          constexpr float kEdge = I8 ? 0.5f - 3.0517578125e-05f : 0.5f - 1.9073486328125e-06f;
-          bool near;
-          if constexpr (F8) {
-            // E4M3 rounding boundaries have at most five significant bits, so
-            // the low 19 bits of their fp32 patterns are zero; a one-multiply
-            // quotient within three steps of one has low bits within 4 of 0.
-            uint32_t lo = 0xFFFFFFFFu;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) lo = min(lo, (__float_as_uint(t[i]) + 4u) & 0x7FFFFu);
-            near = lo <= 8u;
-          } else {
-            near = dmax >= kEdge;
-          }
-          if (s < nslots && (!fast || near)) {
-            if (fast) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) t[i] = div_rn(v[c][i], D, rD);
-            } else if (step > 0.f) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) t[i] = (v[c][i] * fl) / step;
-            } else {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) t[i] = 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) r[i] = __builtin_rintf(t[i]);
-          }
-          if (s >= nslots) continue;
-          if constexpr (F8) {
-            // |t| <= 448 up to one rounding: the clamp is the nearest value
-            uint32_t w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const float a0 = __builtin_amdgcn_fmed3f(t[4 * k], -448.0f, 448.0f);
-              const float a1 = __builtin_amdgcn_fmed3f(t[4 * k + 1], -448.0f, 448.0f);
-              const float a2 = __builtin_amdgcn_fmed3f(t[4 * k + 2], -448.0f, 448.0f);
-              const float a3 = __builtin_amdgcn_fmed3f(t[4 * k + 3], -448.0f, 448.0f);
-              uint32_t d = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-              d = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, d, true);
-              // the converter keeps the sign of zero; the format's zero is +0
-              const uint32_t mag = d & 0x7F7F7F7Fu;
-              w[k] = mag | (d & ((mag + 0x7F7F7F7Fu) & 0x80808080u));
-            }
-            *reinterpret_cast<uint4*>(a.codes + (size_t)row * a.K + s * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-            continue;
-          }
-          uint32_t q[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            q[i] = (uint32_t)(int)__builtin_amdgcn_fmed3f(r[i], (float)(-QMAX - 1), (float)QMAX);
-          if constexpr (MODE == MODE_INT4) {
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              w0 |= (q[i] & 0xFu) << (4 * i);
-              w1 |= (q[i + 8] & 0xFu) << (4 * i);
-            }
-            *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = make_uint2(w0, w1);
-          } else {
-            uint32_t w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              // natural order: dword k holds codes 4k .. 4k+3; W4A8 order: dword k
-              // holds the even (k even) or odd (k odd) codes of group k / 2
-              const int b = MODE == MODE_INT8W ? 8 * (k >> 1) + (k & 1) : 4 * k;
-              const int d = MODE == MODE_INT8W ? 2 : 1;
-              w[k] = (q[b] & 0xFFu) | ((q[b + d] & 0xFFu) << 8) | ((q[b + 2 * d] & 0xFFu) << 16) |
-                     ((q[b + 3 * d] & 0xFFu) << 24);
-            }
-            *reinterpret_cast<uint4*>(a.codes + (size_t)row * a.K + s * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
-      }
-    } else {  // NVFP4: one E4M3 scale per slot (16 elements)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int s = (c * WPR + sub) * 64 + lane;
-        float vs[16];
-        const float fl = transform_slot<BF16IN>(raw[c], vs, rsc, has_scale, a.rot, a.order, s, lane);
-        uint2 w;
-        const uint32_t e = nvfp4_block16(vs, fl, a.g, rg, g_fast, stab, s < nslots, w);
-        if (s < nslots) {
-          *reinterpret_cast<uint2*>(a.codes + (size_t)row * (a.K >> 1) + s * 8) = w;
-          reinterpret_cast<uint8_t*>(a.scales)[(size_t)row * (a.K >> 4) + s] = (uint8_t)e;
-        }
-      }
-    }
+    const uint4 nopre[1][4] = {};
+    quant_row_body<MODE, BF16IN, NC, WPR>(a, row, raw, lane, wave, sub, red, stab, rsc, rg, g_fast, tmax, nopre);
   }
   if constexpr (MODE == MODE_AMAX) {
     if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(a.amax_out), __float_as_uint(tmax));
+  }
+}
+
+// Row quantizer fused with the low-rank branch projection (Q-WAM abstract:
+// the 16-bit branch x L1 L2 next to the 4-bit complement), so x is read
+// once.  A workgroup of four waves (one per SIMD) takes four rows at a
+// time, one per wave, and walks row groups with a grid-stride loop.
+// * Each wave loads its row and the row's smoothing factors into registers
+//   and writes the raw bf16 row into LDS (row pitch 2K + 16 bytes).
+// * Then it starts streaming its share of L1 (transposed, r x K) into a
+//   private three-slot LDS ring: K is cut into 128-element chunks, wave w
+//   owns chunks w, w + 4, ...; a chunk's r rows of 256 bytes arrive by
+//   buffer-to-LDS copies of whole lines, 16-byte slot q of row j stored at
+//   q XOR (j mod 16), so the 16 rows an MFMA fragment reads fall on
+//   distinct banks.  These copies are not tracked by the compiler, so they
+//   are issued only after the row's own loads have been consumed.
+// * The wave quantizes its row as quant_rows_kernel does while the copies
+//   fly, meets the others at a barrier (every row staged), and walks its
+//   chunks: wait for the chunk (a fixed vmcnt: chunks past K are copied as
+//   zeros, so the count never changes), two 64-element K pairs of bf16
+//   16x16x32 products per 16-column block (A = the four staged rows, read
+//   again by the lanes of rows 4..15, whose outputs are dropped; within a
+//   pair, lane group q holds K elements 16 q .. 16 q + 15 on both
+//   operands), then its LDS reads are waited for and the chunk three ahead
+//   is copied into the freed slot.
+// * The four partial 4 x r tiles are added in LDS in wave order and T goes
+//   out as the bf16 pair hi = bf16(T), lo = bf16(T - hi) (columns [0, r)
+//   and [r, 2r)).
+constexpr int kLrMaxK = 4096;                  // staged row length limit
+constexpr int kLrMaxR = 32;                    // rank limit (two 16-column blocks)
+constexpr int kLrPitch = 2 * kLrMaxK + 16;
+constexpr int kLrChunkK = 128;                 // K elements per L1 chunk
+constexpr int kLrRing = 3;                     // chunk slots per wave
+
+struct LowrankArgs {
+  const uint16_t* l1t;   // r x K bf16, row stride K
+  int r;
+  uint16_t* out;         // M x ldo bf16: hi in [0, r), lo in [r, 2r)
+  int64_t ldo;
+};
+
+template <int MODE, int NC, int JB>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+    quant_rows_lowrank_kernel(QuantArgs a, LowrankArgs p) {
+  asm volatile("" ::"s"(a.x), "s"(a.R), "s"(a.K), "s"(a.ldx), "s"(a.scale), "s"(a.g), "s"(a.rot), "s"(a.order),
+               "s"(a.codes), "s"(a.scales), "s"(p.l1t), "s"(p.r), "s"(p.out), "s"(p.ldo));
+  constexpr int R16 = 16 * JB;                 // rows of L1 transposed (p.r == R16)
+  constexpr int CHB = R16 * kLrChunkK * 2;     // bytes of one chunk
+  constexpr int NCP = CHB / 1024;              // copy instructions per chunk
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const bool has_scale = a.scale != nullptr;
+  const int nslots = a.K >> 4;
+  const int pitch = 2 * a.K + 16;
+  const int npairs = a.K >> 6;                 // 64-element K pairs
+  const int nchunks = (a.K + kLrChunkK - 1) / kLrChunkK;
+  const int nsteps = (nchunks + 3) / 4;        // chunks per wave (the last ones may lie past K)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * kLrRing * 16 * 2 * kLrChunkK * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[4 * kLrPitch];
+  __shared__ float part[4 * JB * 4 * 16];
+  __shared__ float2 stab[MODE == MODE_NVFP4 ? 128 : 1];
+  if constexpr (MODE == MODE_NVFP4) {
+    for (int e = threadIdx.x; e < 128; e += blockDim.x) {
+      const float S = e < 0x7F ? e4m3_to_f32((uint32_t)e) * a.g : 0.f;
+      stab[e] = make_float2(S, S > 0.f ? 1.0f / S : 0.f);
+    }
+    __syncthreads();
+  }
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.scale, has_scale ? (uint32_t)(a.K * 4) : 0u);
+  const float rg = MODE == MODE_NVFP4 ? 1.0f / a.g : 1.0f;
+  const bool g_fast = a.g >= kTinyStep && a.g <= kBig;
+  float tmax = 0.f;
+
+  // copies: instruction n of a chunk covers chunk bytes [1024 n, 1024 n + 1024),
+  // lane l the 16 bytes at 1024 n + 16 l: row 4 n + l / 16, physical slot l % 16
+  const v4u rl = rsrc_words(p.l1t, (uint32_t)(R16 * a.K * 2));
+  uint32_t coff[NCP], cslot[NCP];
+#pragma unroll
+  for (int n = 0; n < NCP; ++n) {
+    const int row = 4 * n + (lane >> 4);
+    cslot[n] = (uint32_t)((lane & 15) ^ (row & 15)) * 16;             // logical slot, bytes
+    coff[n] = (uint32_t)(row * a.K * 2) + cslot[n];
+  }
+  const uint32_t ring0 = lds_addr(ring) + (uint32_t)(wave * kLrRing * CHB);
+  auto copy_chunk = [&](int step) {            // this wave's chunk wave + 4 step into slot step % kLrRing
+    const int g = wave + 4 * step;              // wave-uniform
+    const uint32_t dst = ring0 + (uint32_t)((step % kLrRing) * CHB);
+    const uint32_t k0 = g < nchunks ? (uint32_t)(g * 256) : 0u;
+#pragma unroll
+    for (int n = 0; n < NCP; ++n) {
+      // the last chunk may be half a chunk: its other half would be the next row
+      const bool ok = g < nchunks && k0 + cslot[n] < (uint32_t)(a.K * 2);
+      dma16_at(rl, dst + n * 1024, ok ? coff[n] : kOOB, k0);
+    }
+  };
+
+  for (int64_t row0 = (int64_t)blockIdx.x * 4; row0 < a.R; row0 += (int64_t)gridDim.x * 4) {
+    const int64_t row = row0 + wave;
+    const bool live = row < a.R;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)(live ? row : 0) * a.ldx * 2,
+                                                live ? (uint32_t)(a.K * 2) : 0u);
+    SlotRaw<true> raw[NC];
+    uint4 sc[NC][4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) raw[c] = load_slot<true>(rs, c * 64 + lane);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sc[c][i] = has_scale ? buf_load16(rsc, (uint32_t)((c * 64 + lane) * 64 + i * 16)) : make_uint4(0, 0, 0, 0);
+    // the raw row into LDS (zeros for a row past M)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int s = c * 64 + lane;
+      if (s < nslots) {
+        uint4* d = reinterpret_cast<uint4*>(xs + wave * pitch + s * 32);
+        d[0] = raw[c].d[0];
+        d[1] = raw[c].d[1];
+      }
+    }
+    // the factors are consumed here, so no compiler wait on them comes after
+    // the untracked copies below
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(sc[c][i].x), "+v"(sc[c][i].y), "+v"(sc[c][i].z), "+v"(sc[c][i].w));
+#pragma unroll
+    for (int step = 0; step < kLrRing; ++step) copy_chunk(step);
+    if (live)
+      quant_row_body<MODE, true, NC, 1, true>(a, row, raw, lane, wave, 0, nullptr, stab, rsc, rg, g_fast, tmax, sc);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's row is in LDS
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    v4f acc[JB];
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) acc[jb] = v4f{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* arow = xs + (lr & 3) * pitch + lq * 32;
+    for (int step = 0; step < nsteps; ++step) {
+      wait_vmcnt<(kLrRing - 1) * NCP>();       // chunk `step` has landed
+      asm volatile("" ::: "memory");
+      const int g = wave + 4 * step;
+      const uint8_t* slot = ring + (wave * kLrRing + step % kLrRing) * CHB;
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        const int pp = 2 * g + pl;
+        if (pp < npairs) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const v8bf af = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(arow + pp * 128 + h * 16));
+            const int L = pl * 8 + lq * 2 + h;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+              const uint4 b = *reinterpret_cast<const uint4*>(slot + (jb * 16 + lr) * 256 + ((L ^ lr) * 16));
+              acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(v8bf, b), acc[jb], 0, 0, 0);
+            }
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this slot's reads are done
+      asm volatile("" ::: "memory");
+      copy_chunk(step + kLrRing);
+    }
+    wait_vmcnt<0>();                            // the trailing copies (past K: zeros) have landed
+    // lanes 0..15 hold rows 0..3 (one per register) of column lr of each block
+    if (lq == 0) {
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[((wave * JB + jb) * 4 + i) * 16 + lr] = acc[jb][i];
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < 4 * R16; t += 256) {
+      const int i = t / R16, j = t - i * R16;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += part[((w * JB + (j >> 4)) * 4 + i) * 16 + (j & 15)];
+      if (row0 + i < a.R) {
+        const uint32_t hi = f32_to_bf16_bits(v);
+        const float lo = v - bf16_bits_to_f32(hi);
+        uint16_t* o = p.out + (size_t)(row0 + i) * p.ldo;
+        o[j] = (uint16_t)hi;
+        o[R16 + j] = (uint16_t)f32_to_bf16_bits(lo);
+      }
+    }
+    __syncthreads();   // the staged rows and partial tiles are written again by the next row group
   }
 }
 
@@ -716,6 +930,49 @@ static int round_nc(int nc) {
 
 // Largest K a single launch supports: 8 chunks x 64 lanes x 16 elements x 4 waves.
 int64_t quant_max_k() { return 8LL * 64 * 16 * 4; }
+
+int64_t quant_lowrank_max_k() { return kLrMaxK; }
+int quant_lowrank_max_r() { return kLrMaxR; }
+bool quant_lowrank_fits(int64_t K, int64_t r) {
+  return K % 64 == 0 && K <= kLrMaxK && (r == 16 || r == 32);
+}
+
+template <int MODE, int JB>
+static hipError_t launch_lowrank_mode(int nc, dim3 grid, hipStream_t st, const QuantArgs& a, const LowrankArgs& p) {
+  switch (nc) {
+    case 1: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 1, JB>), grid, dim3(256), 0, st, a, p); break;
+    case 2: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 2, JB>), grid, dim3(256), 0, st, a, p); break;
+    case 3: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 3, JB>), grid, dim3(256), 0, st, a, p); break;
+    case 4: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 4, JB>), grid, dim3(256), 0, st, a, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_lowrank_r(int nc, int r, dim3 grid, hipStream_t st, const QuantArgs& a, const LowrankArgs& p) {
+  return r == 16 ? launch_lowrank_mode<MODE, 1>(nc, grid, st, a, p) : launch_lowrank_mode<MODE, 2>(nc, grid, st, a, p);
+}
+
+hipError_t launch_quantize_lowrank(int mode, const void* x, int64_t R, int64_t K, int64_t ldx, const float* scale,
+                                   float g, int rot, int order, void* codes, void* scales, const uint16_t* l1t, int r,
+                                   uint16_t* out, int64_t ldo, hipStream_t st) {
+  if (!quant_lowrank_fits(K, r)) return hipErrorInvalidValue;
+  QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, nullptr, nullptr, 0, nullptr, 0};
+  const LowrankArgs p{l1t, r, out, ldo};
+  const int nc = (int)((K / 16 + 63) / 64);       // slots per lane (K <= 4096: at most 4)
+  int64_t blocks = (R + 3) / 4;
+  if (blocks > 1024) blocks = 1024;               // grid-stride beyond four row groups per CU
+  const dim3 grid((unsigned)blocks);
+  switch (mode) {
+    case MODE_INT4: return launch_lowrank_r<MODE_INT4>(nc, r, grid, st, a, p);
+    case MODE_INT8: return launch_lowrank_r<MODE_INT8>(nc, r, grid, st, a, p);
+    case MODE_INT8W: return launch_lowrank_r<MODE_INT8W>(nc, r, grid, st, a, p);
+    case MODE_FP8: return launch_lowrank_r<MODE_FP8>(nc, r, grid, st, a, p);
+    case MODE_NVFP4: return launch_lowrank_r<MODE_NVFP4>(nc, r, grid, st, a, p);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int64_t K, int64_t ldx,
                            const float* scale, float g, int rot, int order, void* codes, void* scales,

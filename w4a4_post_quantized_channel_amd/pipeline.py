@@ -66,6 +66,11 @@ class QuantizedLinear:
                                                            tensor_scale=self.g_w, stream=stream)
         self.g_a = 1.0
         self._bufs = {}
+        # fuse_lowrank: take the low-rank operand from the quantizer's own
+        # pass over x (quantize_act_lowrank) instead of a second kernel.  Off
+        # by default: on MI355X the single-read kernel measured slower than
+        # the two kernels (every CU holding rows must stream all of L1).
+        self.fuse_lowrank = False
 
     # NVFP4 activations use a static per-tensor scale from calibration data
     # (statistics after both transforms, QuantWAMs sec. 4.2).
@@ -101,7 +106,13 @@ class QuantizedLinear:
         """quantize_act into this layer's M-row buffers; with kept channels
         (bf16 x) the same pass also writes the bypass operand."""
         b = self.buffers(x.shape[0], x.device)
-        if self.branch is not None and self.branch["kind"] == "outlier" and x.dtype == torch.bfloat16:
+        if self.branch is not None and self.branch["kind"] == "lowrank" and self.fuse_lowrank and \
+                ops.lowrank_fusable(x, self.branch["l1t"]):
+            # one pass over x: codes, scales and the low-rank operand x L1
+            ops.quantize_act_lowrank(x, self.inv_s, self.branch["l1t"], self.a_fmt, fwht_block=self.fwht_block,
+                                     order=self.order, tensor_scale=self.g_a, codes=b["codes"],
+                                     scales=b["scales"], out=b["br_a"], stream=stream)
+        elif self.branch is not None and self.branch["kind"] == "outlier" and x.dtype == torch.bfloat16:
             ops.quantize_act_gather(x, self.inv_s, self.branch["idx"], self.a_fmt, fwht_block=self.fwht_block,
                                     order=self.order, tensor_scale=self.g_a, codes=b["codes"],
                                     scales=b["scales"], xo=b["br_a"], stream=stream)
@@ -113,7 +124,9 @@ class QuantizedLinear:
         """Whether the branch operand needs its own kernel (w4a4_lowrank_project)."""
         if self.branch is None:
             return False
-        return self.branch["kind"] == "lowrank" or x_dtype != torch.bfloat16
+        if self.branch["kind"] == "lowrank":
+            return not (self.fuse_lowrank and ops.lowrank_fusable(torch.empty(0, dtype=x_dtype), self.branch["l1t"]))
+        return x_dtype != torch.bfloat16
 
     def project(self, x: torch.Tensor, stream=None):
         """The branch operand when the quantizer pass does not write it."""
