@@ -476,11 +476,12 @@ PROFILE_CMDS = {
            "-- python3 bench.py --no-cpu-baseline --replays 2",
     "copy": "rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_copy_{c} -o run -- python3 bench.py --copy-calibration",
 }
-COUNTER_GROUPS = {
-    "MFMA": "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE",
-    "MOPS": "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_MOPS_F8 "
-            "SQ_INSTS_VALU_MFMA_MOPS_F6F4",
-}
+# one counter run: matrix-core busy cycles, VALU instructions and activity,
+# wave cycles and waits, LDS bank conflicts (7 SQ counters + 1 GRBM)
+CORE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_WAIT_INST_ANY "
+                 "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE")
+PROFILE_CMDS["core"] = ("BENCH_PHASE_LOG=gpurun_out/pmc_core/phases.json rocprofv3 --pmc " + CORE_COUNTERS +
+                        " -f csv -d gpurun_out/pmc_core -o run -- python3 bench.py --no-cpu-baseline --replays 2")
 KERNEL_SOURCES = ["quantize.hip", "gemm_int.hip", "gemm_wide.hip", "branch.hip", "epilogue.h", "device_common.h",
                   "lds_dma.h"]
 
@@ -565,12 +566,25 @@ def summarize_profiles(d):
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             pd = os.path.join(d, f"pmc_{c}")
             if os.path.exists(pd):
-                prow = [r for r in _trace_rows(pd, "counter_collection") if r.get("Counter_Name", c) == c
-                        or _is_marker(r["Kernel_Name"])]
+                prow = [r for r in _trace_rows(pd, "counter_collection") if r.get("Counter_Name", c) == c]
                 pmc[c] = _phases_of(prow, _load_phases(pd), lambda r: float(r["Counter_Value"]) * 1024 * factor[c])
         rec["copy_scale"] = factor
         rec["pmc_commands"] = [PROFILE_CMDS["pmc"].format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")] + \
                               [PROFILE_CMDS["copy"].format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    core = {}
+    cd = os.path.join(d, "pmc_core")
+    if os.path.exists(cd):
+        crow = _trace_rows(cd, "counter_collection")
+        agent = [r for r in _csv_rows(os.path.join(cd, [f for f in os.listdir(cd) if f.endswith("agent_info.csv")][0]))
+                 if int(r.get("Simd_Count") or 0) > 0][0]
+        simds = int(agent["Simd_Count"])
+        for cn in CORE_COUNTERS.split():
+            rows_c = [r for r in crow if r["Counter_Name"] == cn]   # marker dispatches carry every counter too
+            core[cn] = _phases_of(rows_c, _load_phases(cd), lambda r: float(r["Counter_Value"]))
+        core["_dur"] = _phases_of([r for r in crow if r["Counter_Name"] == "GRBM_GUI_ACTIVE"], _load_phases(cd),
+                                  lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        rec["core_command"] = PROFILE_CMDS["core"]
+        rec["simds"] = simds
     for ph in phases:
         ks = dur.get(ph, {})
         if not ks:
@@ -584,10 +598,26 @@ def summarize_profiles(d):
                 if pv:
                     e[c.lower() + "_bytes"] = sum(pv) / len(pv)
                     extra += f"  {c} {e[c.lower() + '_bytes'] / 1e6:.2f} MB"
+            if core and core.get("SQ_INSTS_VALU", {}).get(ph, {}).get(k):
+                mean = lambda cn: sum(core[cn][ph][k]) / len(core[cn][ph][k])
+                us_c = mean("_dur")
+                e["mfma_busy"] = mean("SQ_VALU_MFMA_BUSY_CYCLES") / rec["simds"] / (us_c * 1e3 * PEAK_CLOCK_GHZ)
+                e["valu_insts"] = mean("SQ_INSTS_VALU")
+                e["valu_active_per_wave_cycle"] = mean("SQ_ACTIVE_INST_VALU") / max(1.0, mean("SQ_WAVE_CYCLES"))
+                e["wait_per_wave_cycle"] = mean("SQ_WAIT_INST_ANY") / max(1.0, mean("SQ_WAVE_CYCLES"))
+                e["lds_bank_conflict_frac"] = mean("SQ_LDS_BANK_CONFLICT") / max(1.0, mean("SQ_LDS_IDX_ACTIVE"))
+                e["us_under_counters"] = us_c
+                extra += (f"\n      MFMA busy {e['mfma_busy']:.1%}  VALU insts {e['valu_insts']:.3g}  "
+                          f"VALU-active/wave-cycle {e['valu_active_per_wave_cycle']:.2f}  "
+                          f"wait/wave-cycle {e['wait_per_wave_cycle']:.2f}  "
+                          f"LDS conflict/active {e['lds_bank_conflict_frac']:.3f}  ({us_c:.2f} us under counters)")
             rec["phases"].setdefault(ph, {})[k] = e
             lines.append(f"  {k[:78]:78s} n={len(v):5d} median {e['median_us']:9.2f} us  mean {e['mean_us']:9.2f} us"
                          + extra)
         lines.append("")
+    if core:
+        lines.append("core counters (SIMDs " + str(rec["simds"]) + "; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMDs over "
+                     "the dispatch's duration at " + str(PEAK_CLOCK_GHZ) + " GHz): " + PROFILE_CMDS["core"])
     if factor:
         lines.append(f"byte counters scaled by the copy calibration: FETCH_SIZE x {factor['FETCH_SIZE']:.4f}, "
                      f"WRITE_SIZE x {factor['WRITE_SIZE']:.4f} (256 MiB read + 256 MiB written per launch)")

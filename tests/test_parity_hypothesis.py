@@ -1,0 +1,87 @@
+"""Randomised parity sweep (hypothesis): the HIP path against the oracle on
+drawn shapes (ragged M and N, K up to 1024), formats, orders, input
+magnitudes, one-hot and zero rows, and NVFP4 tensor scales small enough to
+saturate the block scales.  Same bars as the fixed cases: codes and scales
+exact (band-admissible mismatches counted), outputs within tolerance, and
+for integer formats without a branch the output bit-exact."""
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings, strategies as st
+
+from oracle import w4a4_oracle as O
+from w4a4_post_quantized_channel_amd import workloads as WL
+
+from parity import check_operand, check_output, check_output_exact
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def env():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from w4a4_post_quantized_channel_amd import ops, pipeline
+    return ops, pipeline
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return WL.from_bf16_bits(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy()
+
+
+@st.composite
+def cases(draw):
+    fmt = draw(st.sampled_from(["int4", "int8", "w4a8", "fp8", "nvfp4"]))
+    M = draw(st.integers(1, 300))
+    N = draw(st.integers(1, 300))
+    K = 64 * draw(st.integers(1, 16))
+    seed = draw(st.integers(0, 10 ** 6))
+    xdt = draw(st.sampled_from(["bf16", "f32"]))
+    kw = dict(n_outliers=draw(st.integers(0, 4)), outlier_gain=draw(st.sampled_from([1.0, 20.0, 300.0])))
+    branch = draw(st.sampled_from(["none", "lowrank", "keep"]))
+    if branch == "lowrank" and xdt == "bf16":
+        kw["lowrank"] = 8 * draw(st.integers(1, 4))
+    if branch == "keep" and xdt == "bf16" and kw["n_outliers"] > 0:
+        kw["keep_channels"] = 8
+    case = WL.linear_case(M, N, K, seed=seed, fmt=fmt, x_dtype=xdt, name="hyp", **kw)
+    scale = np.float32(10.0 ** draw(st.floats(-4, 4)))
+    case.x = case.x * scale if xdt == "f32" else WL.bf16_round(case.x * scale)
+    rows = draw(st.sampled_from(["as_drawn", "one_hot", "zero_row"]))
+    if rows == "one_hot":
+        case.x[0] = 0
+        case.x[0, seed % K] = scale
+    elif rows == "zero_row":
+        case.x[M // 2] = 0
+    order = draw(st.sampled_from(["smooth_then_rotate", "rotate_then_smooth"]))
+    if case.branch is not None and case.branch["kind"] == "outlier":
+        order = "smooth_then_rotate"
+    gshrink = draw(st.sampled_from([1.0, 1.0, 1 / 64]))   # 1/64: block scales saturate at 448
+    return case, order, gshrink
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture,
+                                 HealthCheck.data_too_large])
+@given(cases())
+def test_random_parity(env, drawn):
+    ops, pipe = env
+    case, order, gshrink = drawn
+    print(f"[hyp] {case.fmt} {case.M}x{case.N}x{case.K} x={case.x_dtype} order={order} gshrink={gshrink} "
+          f"branch={None if case.branch is None else case.branch['kind']}", flush=True)
+    layer, t = pipe.build_layer(case, order=order)
+    g_a = g_w = None
+    if case.fmt == "nvfp4":
+        layer.g_a = float(np.float32(layer.g_a) * np.float32(gshrink))
+        g_a, g_w = np.float32(layer.g_a), np.float32(layer.g_w)
+    y = layer.forward(t["x"])
+    ref = O.linear(case, order=order, g_a=g_a, g_w=g_w)
+    b = layer.buffers(case.M, t["x"].device)
+    fa, fw = O.OPERAND_FORMATS[case.fmt]
+    na = check_operand(fa, _np(b["codes"]), _np(b["scales"]), ref["a"], what="activations")
+    nw = check_operand(fw, _np(layer.w_codes), _np(layer.w_scales), ref["w"], what="weights")
+    check_output(_np(y), ref["y"], 1e-3 if case.y_dtype == "f32" else 1e-2)
+    if case.fmt in ("int4", "int8", "w4a8") and case.branch is None and na == 0 and nw == 0:
+        check_output_exact(_np(y), ref["y_main"], case.y_dtype)

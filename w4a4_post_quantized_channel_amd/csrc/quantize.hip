@@ -711,6 +711,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 template <bool BF16IN>
 constexpr int nvfp4_lanes_tile() { return 64 * 64 * (BF16IN ? 2 : 4); }
 
+// 16-byte slot swizzle of tile row r (CPR slots per row): 16 consecutive
+// rows, read at the same logical slot by 16 lanes of one LDS pass, land on
+// 16 distinct 16-byte bank groups of the 256-byte bank window (128-byte
+// bf16 rows: two rows per window, so the row pair index picks the slot).
+template <int CPR>
+__device__ __forceinline__ int tile_swz(int r) {
+  return CPR >= 16 ? (r & 15) : ((r >> 1) & (CPR - 1));
+}
+
 template <bool BF16IN, bool ROT, int NB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 1)))
 quant_nvfp4_lanes_kernel(QuantArgs a) {
@@ -741,15 +750,15 @@ quant_nvfp4_lanes_kernel(QuantArgs a) {
   // Coalesced copy of task t's 64 x 64 tile into buffer `buf` of this
   // wave's LDS slice: copy instruction i covers tile bytes [1024 i,
   // 1024 i + 1024); the chunk at slot q of tile row r holds logical chunk
-  // q ^ (r & 7) (so that the 64 rows read back by the 64 lanes spread over
-  // the banks).  Rows past R read zeros.  The lane's offset inside the
+  // q ^ tile_swz(r) (so that the 64 rows read back by the 64 lanes spread
+  // over the banks).  Rows past R read zeros.  The lane's offset inside the
   // tile is fixed; the block's byte offset goes in the scalar operand.
   uint32_t loff[NCOPY];
 #pragma unroll
   for (int i = 0; i < NCOPY; ++i) {
     const int p = i * 1024 + lane * 16;
     const int r = p / RB, q = (p % RB) / 16;
-    const int L = q ^ (r & 7 & (CPR - 1));
+    const int L = q ^ tile_swz<CPR>(r);
     loff[i] = (uint32_t)(r * (int)(a.ldx * ESZ) + L * 16);
   }
   const uint32_t tiles_lds = lds_addr(&tiles[wave][0][0]);
@@ -793,7 +802,7 @@ quant_nvfp4_lanes_kernel(QuantArgs a) {
     float v[64];
 #pragma unroll
     for (int c = 0; c < CPR; ++c) {
-      const uint4 d = *reinterpret_cast<const uint4*>(tile + lane * RB + ((c ^ (lane & 7 & (CPR - 1))) * 16));
+      const uint4 d = *reinterpret_cast<const uint4*>(tile + lane * RB + ((c ^ tile_swz<CPR>(lane)) * 16));
       if constexpr (BF16IN) {
         const uint32_t w[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
@@ -826,7 +835,7 @@ quant_nvfp4_lanes_kernel(QuantArgs a) {
             if (cj >= 0 && cj < a.K) {
               const int cc = cj & 63;
               val = *reinterpret_cast<const uint16_t*>(
-                  tile + lane * RB + (((cc >> 3) ^ (lane & 7 & (CPR - 1))) * 16) + (cc & 7) * 2);
+                  tile + lane * RB + (((cc >> 3) ^ tile_swz<CPR>(lane)) * 16) + (cc & 7) * 2);
             }
             if (live) a.gout[(size_t)row * a.ldg + 64 * h + jj] = val;
           }
