@@ -55,6 +55,8 @@ def cases(draw):
         case.x[0, seed % K] = scale
     elif rows == "zero_row":
         case.x[M // 2] = 0
+    if xdt == "bf16":   # every activation value must be a bf16 value (both sides read bf16)
+        case.x = WL.bf16_round(case.x)
     order = draw(st.sampled_from(["smooth_then_rotate", "rotate_then_smooth"]))
     if case.branch is not None and case.branch["kind"] == "outlier":
         order = "smooth_then_rotate"
