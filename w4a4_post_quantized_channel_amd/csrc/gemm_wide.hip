@@ -96,13 +96,25 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
 constexpr int kSeg = 64;     // packed weight bytes per row per K-group per stage
 
 
-// XOR swizzle of the 16-byte slots of an LDS row of P bytes: the 16 rows
-// of one MFMA fragment, read at the same logical slot, land in 16
-// distinct 16-byte bank groups.
+// XOR swizzle of the 16-byte slots of an LDS row of P bytes, a function of
+// row mod 16 (fragments are 16 rows apart).  gfx950 serves a 16-byte LDS
+// read in four cycles of 16 lanes; a cycle takes the lanes that agree in
+// lane bit 5 and in the parity of lane bits 2..4 (lanes 0-3, 12-15, 20-23
+// and 24-27 share one), across 64 four-byte banks (256 bytes).  A
+// fragment read (lane -> row lane % 16, slot from lane / 16) is
+// conflict-free when every such cycle touches 16 distinct 16-byte bank
+// groups.  The functions below meet that for the one-slot reads (slot
+// 4 kw + lane / 16) and the two-slot reads (slot 8 kw + 2 (lane / 16) + h)
+// of every row length used here (bank-conflict counters confirm it); the
+// plainer row-pair swizzle of 64- and 128-byte rows left two-way conflicts
+// on these lane cycles.
 template <int P>
 __device__ __forceinline__ int swz(int row) {
   constexpr int S = P / 16;   // slots per row
-  return S >= 16 ? (row & 15) : ((row / (16 / S)) & (S - 1));
+  static_assert(S == 4 || S == 8 || S >= 16, "row length");
+  if constexpr (S == 4) return (row >> 2) & 2;
+  else if constexpr (S == 8) return ((row >> 1) & 1) ^ (row & 4) ^ (((row >> 3) & 1) * 6);
+  else return row & 15;
 }
 
 __device__ __forceinline__ uint2 scale_pair(uint32_t e) {
@@ -645,9 +657,10 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 // fp16 weight stage: 160 rows x 128 K values (256 bytes, 16 slots of 16).
 // Logical slot 4q + t of a row holds K values 32q + 8t .. 32q + 8t + 7 (the
 // ones lane group q multiplies at MFMA step t, in the same order as the
-// activation side) at physical slot (4q + t) ^ (row & 15), so the 16 rows
-// read by one fragment, and the rows written by one wave, fall on distinct
-// banks.
+// activation side) at physical slot (4q + t) ^ (row & 11): on the LDS
+// read cycles described at swz(), the 16 rows read by one fragment and the
+// rows written by one wave fall on distinct banks (row & 15 leaves two-way
+// conflicts on the reads).
 //
 // Iteration s runs stage s from activation fragments read one iteration
 // earlier and from fp16 weight buffer s % 2.  After its first MFMA step it
@@ -752,7 +765,7 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
       const uint32_t two = (ws[h] >> (16 * (cq[h] & 1))) & 0xFFFFu;   // scales of blocks 2q, 2q + 1
       const uint2 sp0 = scale_pair(two & 0xFFu), sp1 = scale_pair(two >> 8);
       uint8_t* rowp = bb + crow[h] * kCbBROW;
-      const int sw = crow[h] & 15;
+      const int sw = crow[h] & 11;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
         *reinterpret_cast<uint4*>(rowp + (((4 * cq[h] + tt) ^ sw) * 16)) = widen_fp4(dw(wc[h], tt), tt < 2 ? sp0 : sp1);
@@ -794,7 +807,7 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
     uint4 oa[TI], ob[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
-      ob[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * kCbBROW + (((4 * lq + st) ^ lr) * 16));
+      ob[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * kCbBROW + (((4 * lq + st) ^ (lr & 11)) * 16));
 #pragma unroll
     for (int i = 0; i < TI; ++i) oa[i] = widen_fp4(dw(f.c[i], st), scale_pair((f.sc[i] >> (8 * (st >> 1))) & 0xFFu));
 #pragma unroll
