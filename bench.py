@@ -66,6 +66,15 @@ EXTRA = {
     "batch1_fp8": (["decode_w4a4", "decode_fp8"], "batch-1 step with the down projection in FP8 (E4M3) W8A8"),
     "video4096_fp8": (["video_fp8"], "4096-token video projection in FP8 (E4M3) W8A8 4096x5120x5120"),
 }
+# the ranked next rows' workloads, measured in the default run after the
+# configurations: id, workload name, row
+NEXT = [
+    ("N1a", "decode_w4a8", "W4A8 (8-bit activations, 4-bit weights) 64x2048x2048"),
+    ("N1b", "decode_w4a8_down", "W4A8 64x2048x8192"),
+    ("N1c", "video_w4a8", "W4A8 4096x5120x5120 + 64 kept bf16 channels"),
+    ("N3a", "decode_fp8", "FP8 (E4M3) W8A8 64x2048x8192"),
+    ("N3b", "video_fp8", "FP8 (E4M3) W8A8 4096x5120x5120 + 64 kept bf16 channels"),
+]
 REPLAYS, WARMUP_REPLAYS = 20, 3
 
 
@@ -78,6 +87,7 @@ def parse():
                    help="measure one workload only (no headline, no CPU baseline)")
     p.add_argument("--replays", type=int, default=REPLAYS)
     p.add_argument("--no-configs", action="store_true", help="headline step only")
+    p.add_argument("--no-next", action="store_true", help="skip the next rows' workloads (W4A8, FP8)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain elementwise copy of 256 MiB five times (hardware-counter scale)")
@@ -698,6 +708,16 @@ def main():
             torch.cuda.empty_cache()
         order = [c[0] for c in CONFIGS]
         configs.sort(key=lambda c: order.index(c["id"]))
+    nexts = []
+    if not a.no_configs and not a.no_next:
+        for cid, name, what in NEXT:
+            case, layer, r = measure_case(torch, cid, name, a.replays)
+            sc = summarize_case(case, layer, r)
+            sc["row"] = what
+            sc["vendor_gemm"] = vendor_gemm(torch, case)
+            nexts.append(sc)
+            del layer
+            torch.cuda.empty_cache()
     ceil = ceilings(torch)
     g_cold = s2b["cold"]["kernels"]["gemm"]
     g_warm = s2b["warm"]["kernels"]["gemm"]
@@ -731,6 +751,7 @@ def main():
                    "launch": f"HIP graph of {min(a.steps, 200)} steps, replayed {a.replays} times; median"},
         "roofline": roof,
         "configs": configs,
+        "next": nexts,
         "ceilings": ceil,
     }
     if not a.no_cpu_baseline:
