@@ -105,6 +105,14 @@ SMALL = [
     ("fp8_lowrank", 90, 200, 384, "fp8", "bf16", dict(n_outliers=6, outlier_gain=25.0, lowrank=16)),
     ("fp8_outlier", 33, 130, 320, "fp8", "bf16", dict(n_outliers=8, outlier_gain=30.0, keep_channels=8)),
     ("fp8_long_rows", 5, 40, 4160, "fp8", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
+    # the largest K quantize_act accepts (32768): every format, the row kernels,
+    # and the row-per-lane NVFP4 quantizer with a ragged last group of rows
+    ("int4_max_k", 3, 24, 32768, "int4", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
+    ("int8_max_k", 2, 16, 32768, "int8", "f32", dict(n_outliers=6, outlier_gain=20.0)),
+    ("w4a8_max_k", 3, 16, 32768, "w4a8", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
+    ("fp8_max_k", 3, 16, 32768, "fp8", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
+    ("nvfp4_max_k", 5, 16, 32768, "nvfp4", "bf16", dict(n_outliers=6, outlier_gain=20.0, keep_channels=8)),
+    ("nvfp4_rows_max_k", 260, 16, 32768, "nvfp4", "bf16", dict(n_outliers=6, outlier_gain=20.0)),
 ]
 
 
@@ -141,7 +149,8 @@ def test_small_cases(ops, pipe, name, M, N, K, fmt, xdt, kw, order):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (17, 33, 192), (100, 200, 384), (130, 260, 320),
                                    (64, 2048, 2048), (64, 512, 8192), (512, 512, 4096), (300, 100, 64),
                                    (64, 2048, 8192), (40, 4096, 4160), (3, 8200, 2048), (30, 8192, 2048),
-                                   (20, 512, 4096), (9, 768, 8192), (50, 640, 8256)])
+                                   (20, 512, 4096), (9, 768, 8192), (50, 640, 8256),
+                                   (7, 40, 65536), (100, 72, 65536)])   # the largest K the linears accept
 @pytest.mark.parametrize("split", [False, True])
 def test_raw_accumulators_exact(ops, fmt, M, N, K, split):
     """Integer GEMM on random codes: bit-exact int32 accumulators (decode kernel with and
