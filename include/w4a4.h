@@ -231,8 +231,9 @@ size_t w4a4_gptq_workspace_size(int64_t N, int64_t K);
  *           y = fp32(fp32(acc) * a_scales[m]) * w_scales[n] * alpha.
  *           W4A4_FMT_NVFP4: sum of E2M1*E4M3 products (exact operands,
  *           fp32 accumulation), times alpha = fp32(g_a * g_w).
- *  a_codes / a_scales   M rows from quantize_act; w_codes / w_scales N rows
- *           from pack_weights (same fmt, same K).
+ *  a_codes / a_scales   M rows (M <= 2^28) from quantize_act; w_codes /
+ *           w_scales N rows from pack_weights (same fmt, same K; K a
+ *           multiple of 64, at most 65536).
  *  br       NULL or a w4a4_branch (kind NONE or BF16).
  *  y        M x N output, y_dtype F32 or BF16 (round to nearest even) with
  *           row stride N <= ldy <= 2^22 elements; y_dtype I32 writes the raw integer

@@ -115,6 +115,8 @@ def test_linear_rejects_bad_arguments(ops):
     assert _lin(ops, K=0) == -1
     assert _lin(ops, M=-1) == -1
     assert _lin(ops, K=1 << 20) == -2
+    assert _lin(ops, M=(1 << 28) + 1) == -2       # per-row scales take 32-bit offsets
+    assert _lin(ops, fn="w8a8_linear", M=(1 << 28) + 1) == -2
     assert _lin(ops, fmt=1) == -4                 # int8 codes go through w8a8_linear
     assert _lin(ops, fmt=3) == -4                 # int8 x int4 goes through w4a8_linear
     assert _lin(ops, fn="w4a8_linear", K=96) == -2

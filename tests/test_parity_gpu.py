@@ -536,6 +536,27 @@ def test_graph_capture_replays_match_eager(ops, pipe):
             assert torch.equal(out.view(torch.int16), y_eager.view(torch.int16)), (name, rep)
 
 
+def test_nvfp4_quantizer_long_row_stride(ops, pipe):
+    """Many NVFP4 rows whose row stride puts 64 rows beyond 31-bit offsets
+    (ldx = 2^24 + 64 bf16 elements, an 8.6 GB view): the launcher takes the
+    row kernels, and codes and scales match the oracle on the K real
+    columns of every row."""
+    M, K, ldx = 260, 256, (1 << 24) + 64
+    case = WL.linear_case(M, 16, K, seed=97, fmt="nvfp4", n_outliers=4, outlier_gain=20.0)
+    t = pipe.case_to_device(case)
+    big = torch.zeros((M, ldx), dtype=torch.bfloat16, device="cuda")
+    big[:, :K] = t["x"]
+    x = big[:, :K]
+    assert x.stride(0) == ldx
+    g = float(O.nvfp4_tensor_scale(O.transformed_amax(case.x, case.inv_s)))
+    codes, scales = ops.quantize_act(x, t["inv_s"], "nvfp4", tensor_scale=g)
+    ref = O.quantize_operand(case.x, case.inv_s, "nvfp4", g=np.float32(g))
+    n = check_operand("nvfp4", _np(codes), _np(scales), ref, what="activations")
+    assert n == 0
+    del big, x
+    torch.cuda.empty_cache()
+
+
 def test_empty_batch_is_noop(ops):
     x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
     codes, scales = ops.quantize_act(x, None, "int4")

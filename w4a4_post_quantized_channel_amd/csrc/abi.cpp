@@ -116,6 +116,8 @@ int run_linear(const char* fn, int fmt, const void* a_codes, const void* a_scale
   if (K % 64 != 0) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld not a multiple of 64", fn, (long long)K);
   if (K > 65536) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld above 65536", fn, (long long)K);
   if (M > INT32_MAX || N > INT32_MAX) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: M/N too large", fn);
+  // per-row scales are addressed with 32-bit byte offsets
+  if (M > (1LL << 28)) return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: M=%lld above 2^28", fn, (long long)M);
   if (y_dtype != W4A4_DT_F32 && y_dtype != W4A4_DT_BF16 && y_dtype != W4A4_DT_I32)
     return fail(W4A4_ERR_UNSUPPORTED_FORMAT, "%s: y dtype %d", fn, y_dtype);
   const bool has_br = br && br->kind != W4A4_BRANCH_NONE;

@@ -989,8 +989,11 @@ hipError_t launch_quantize(int mode, bool bf16in, const void* x, int64_t R, int6
                            int64_t ldg) {
   QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, amax_out,
               gidx, gr, (uint16_t*)gout, ldg};
+  // The row-per-lane kernel addresses a 64-row tile with 32-bit offsets
+  // (64 rows of ldx elements); longer strides take the row kernels, whose
+  // resources cover one row each.
   if (mode == MODE_NVFP4 && R >= 256 && K % 64 == 0 && (rot == 0 || rot == 64) &&
-      ((R + 63) / 64) * (K / 64) < (1LL << 31)) {
+      ((R + 63) / 64) * (K / 64) < (1LL << 31) && 64 * ldx * (bf16in ? 2 : 4) < (1LL << 31)) {
     // resident grid: as many four-wave blocks as the tiles' LDS lets every CU hold
     const int64_t tasks = ((R + 63) / 64) * (K / 64);
     constexpr int NB = 1;
