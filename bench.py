@@ -651,7 +651,8 @@ def profile_view(phase, kernel_prefix):
     if rec.get("source_hash") != kernel_source_hash():
         return None
     ks = rec.get("phases", {}).get(phase, {})
-    hits = [(k, v) for k, v in ks.items() if k.startswith(kernel_prefix)]
+    # trace names carry the full signature ("void w4a4::name<...>")
+    hits = [(k, v) for k, v in ks.items() if kernel_prefix in k]
     if not hits:
         return None
     k, v = max(hits, key=lambda kv: kv[1]["median_us"])
