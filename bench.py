@@ -306,16 +306,21 @@ def summarize_case(case, layer, res):
     """Effective TOPS and roofline fractions from the measured medians."""
     flop = 2.0 * case.M * case.N * case.K
     out = {"id": res["id"], "workload": res["workload"], "shape": f"{case.M}x{case.N}x{case.K}", "fmt": case.fmt}
-    fused_cols = 0
+    fused_cols, fused_extra = 0, 0
     if layer.branch is not None and not layer.has_projection():
-        fused_cols = layer.branch["lw"].shape[1]
+        r = layer.branch["lw"].shape[1]
+        if layer.branch["kind"] == "lowrank":   # T hi/lo written, L1 read by the same launch
+            fused_cols, fused_extra = 2 * r, 2 * r * case.K
+        else:                                   # the kept channels gathered from the same pass
+            fused_cols = r
     for mode in ("warm", "cold"):
         r = res[mode]
         if r is None:
             continue
         m = {"us_per_call": r["call"], "effective_TOPS": flop / (r["call"]["median"] * 1e-6) / 1e12}
         ks = {}
-        ks["quantize"] = {"us": r["quantize"], **hbm_roof(quant_bytes(case, fused_cols), r["quantize"]["median"])}
+        ks["quantize"] = {"us": r["quantize"], **hbm_roof(quant_bytes(case, fused_cols) + fused_extra,
+                                                          r["quantize"]["median"])}
         if "project" in r:
             ks["project"] = {"us": r["project"], **hbm_roof(proj_bytes(case), r["project"]["median"])}
         if "fused_quantize_project" in r:   # not part of the call: the single-read alternative
@@ -493,7 +498,7 @@ CORE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_
 PROFILE_CMDS["core"] = ("BENCH_PHASE_LOG=gpurun_out/pmc_core/phases.json rocprofv3 --pmc " + CORE_COUNTERS +
                         " -f csv -d gpurun_out/pmc_core -o run -- python3 bench.py --no-cpu-baseline --replays 2")
 KERNEL_SOURCES = ["quantize.hip", "gemm_int.hip", "gemm_wide.hip", "branch.hip", "epilogue.h", "device_common.h",
-                  "lds_dma.h"]
+                  "lds_dma.h", "project_body.h"]
 
 
 def kernel_source_hash():

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define W4A4_ABI_VERSION 2
+#define W4A4_ABI_VERSION 3
 #define W4A4_MAX_BRANCH 128 /* largest branch width (rank or kept channels) */
 #define W4A4_LOWRANK_MAX_PARTS 4 /* hi/lo pairs a branch ``a`` operand may hold (ra = 2 P r) */
 
@@ -179,6 +179,23 @@ int quantize_act_gather(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
  * w4a4_lowrank_project).
  * Codes and scales are those quantize_act writes. */
 int quantize_act_lowrank(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const float* inv_smooth, const w4a4_qdesc* q, void* codes, void* scales,
+                         const void* l1t, int64_t r, void* out, int64_t ldo, void* stream);
+
+/* quantize_act_project -- quantize_act and w4a4_lowrank_project (low-rank
+ * form) in one launch (Q-WAM abstract: the 16-bit low-rank branch x L1 L2
+ * beside the 4-bit complement).  Some workgroups quantize rows, the others
+ * compute tiles of T = x L1; both read x (the second read mostly from
+ * cache), and codes, scales and out are bit-identical to those of the two
+ * separate calls.  Arguments as quantize_act, plus:
+ *  l1t  bf16 r x K, row stride K, 16-byte aligned: L1 transposed.
+ *  r    1 .. W4A4_MAX_BRANCH.
+ *  out  bf16 M x ldo (ldo >= 2r): hi = bf16(T) in columns [0, r), lo =
+ *       bf16(T - hi) in [r, 2r), as w4a4_lowrank_project writes them.
+ * x must be BF16 (else W4A4_ERR_UNSUPPORTED_FORMAT); K a multiple of 16
+ * (64 with the rotation) and at most 5120 (one wave per row), else
+ * W4A4_ERR_UNSUPPORTED_SHAPE (use the two calls). */
+int quantize_act_project(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
                          const float* inv_smooth, const w4a4_qdesc* q, void* codes, void* scales,
                          const void* l1t, int64_t r, void* out, int64_t ldo, void* stream);
 

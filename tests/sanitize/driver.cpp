@@ -58,6 +58,15 @@ int main() {
          W4A4_ERR_UNSUPPORTED_FORMAT, false);
   EXPECT(quantize_act_lowrank(P, W4A4_DT_BF16, 64, 8192, 8192, nullptr, &q, Q, Q, P, 32, Q, 64, nullptr),
          W4A4_ERR_UNSUPPORTED_SHAPE, false);
+  EXPECT(quantize_act_project(P, W4A4_DT_BF16, 64, 3072, 3072, nullptr, &q, Q, Q, P, 32, Q, 64, nullptr), W4A4_OK, true);
+  EXPECT(quantize_act_project(P, W4A4_DT_F32, 64, 3072, 3072, nullptr, &q, Q, Q, P, 32, Q, 64, nullptr),
+         W4A4_ERR_UNSUPPORTED_FORMAT, false);
+  EXPECT(quantize_act_project(P, W4A4_DT_BF16, 64, 8192, 8192, nullptr, &q, Q, Q, P, 32, Q, 64, nullptr),
+         W4A4_ERR_UNSUPPORTED_SHAPE, false);
+  EXPECT(quantize_act_project(P, W4A4_DT_BF16, 64, 3072, 3072, nullptr, &q, Q, Q, P, 32, Q, 63, nullptr),
+         W4A4_ERR_INVALID_ARG, false);
+  EXPECT(quantize_act_project(P, W4A4_DT_BF16, 64, 3072, 3072, nullptr, &q, Q, Q, nullptr, 32, Q, 64, nullptr),
+         W4A4_ERR_INVALID_ARG, false);
   EXPECT(pack_weights_gptq(P, W4A4_DT_BF16, 64, 256, 256, nullptr, &q, reinterpret_cast<double*>(P), nullptr, Q, Q,
                            Q, w4a4_gptq_workspace_size(64, 256), nullptr), W4A4_OK, true);
   EXPECT(pack_weights_gptq(P, W4A4_DT_BF16, 64, 256, 256, nullptr, &q, reinterpret_cast<double*>(P), nullptr, Q, Q,

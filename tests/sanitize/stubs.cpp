@@ -25,6 +25,12 @@ hipError_t launch_quantize_lowrank(int, const void*, int64_t, int64_t, int64_t, 
 int64_t quant_lowrank_max_k() { return 4096; }
 int quant_lowrank_max_r() { return 32; }
 bool quant_lowrank_fits(int64_t K, int64_t r) { return K % 64 == 0 && K <= 4096 && (r == 16 || r == 32); }
+hipError_t launch_quantize_project(int, const void*, int64_t, int64_t, int64_t, const float*, float, int, int, void*,
+                                   void*, const uint16_t*, int, uint16_t*, int64_t, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+bool quant_project_fits(int64_t K, int64_t r) { return K % 16 == 0 && K <= 5 * 1024 && r >= 1 && r <= 128; }
 hipError_t launch_gemm_int(int, GemmArgs, void*, size_t, hipStream_t) {
   ++g_launches;
   return hipSuccess;

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(ops):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
-    assert ops.LIB.w4a4_abi_version() == 2
+    assert ops.LIB.w4a4_abi_version() == 3
 
 
 def test_lowrank_width_host_query(ops):
@@ -306,3 +306,18 @@ def test_quantize_act_lowrank_rejects_bad_arguments(ops):
     assert g(l1=ctypes.c_void_p(0x10008)) == -3
     assert g(q=_q(ops, fmt=9)) == -4
     assert g(M=0, l1=None, out=None) == 0         # empty batch
+
+
+def test_quantize_act_project_rejects_bad_arguments(ops):
+    L = ops.LIB
+    g = lambda dt=1, M=4, K=128, r=32, ldo=64, l1=FAKE, out=FAKE2, q=None: L.quantize_act_project(
+        FAKE, dt, M, K, K, None, q or _q(ops), FAKE2, FAKE2, l1, r, out, ldo, None)
+    assert g(dt=0) == -4                          # x must be bf16
+    assert g(r=0) == -1 and g(r=129, ldo=258) == -1
+    assert g(ldo=63) == -1                        # hi and lo need 2r columns
+    assert g(K=96 + 64 + 8) == -2                 # K % 16
+    assert g(K=5120 + 64) == -2                   # one wave per row: K <= 5120
+    assert g(l1=None) == -1 and g(out=None) == -1
+    assert g(l1=ctypes.c_void_p(0x10008)) == -3
+    assert g(q=_q(ops, fmt=9)) == -4
+    assert g(M=0, out=None) == 0                  # empty batch

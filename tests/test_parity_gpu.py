@@ -386,6 +386,40 @@ def test_quantize_act_lowrank(ops, pipe, M, K, r, fmt):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("M,K,r,fmt", [(1024, 3072, 32, "int4"), (77, 3072, 32, "int4"), (33, 256, 16, "int8"),
+                                        (130, 4096, 16, "w4a8"), (17, 512, 32, "fp8"), (300, 320, 32, "nvfp4"),
+                                        (5, 5120, 8, "int4"), (1, 64, 1, "int8"), (2051, 1536, 40, "int4")])
+def test_quantize_act_project_matches_the_two_calls(ops, pipe, M, K, r, fmt):
+    """quantize_act_project (quantizer and projection workgroups in one
+    launch): codes, scales and the hi/lo operand bit-identical to
+    quantize_act followed by w4a4_lowrank_project."""
+    rng = np.random.default_rng(M + 3 * K + r)
+    x = torch.from_numpy(WL.bf16_round(rng.standard_normal((M, K)).astype(np.float32) * 3)).to(torch.bfloat16).cuda()
+    inv_s = torch.from_numpy(np.exp2(rng.integers(-2, 3, K)).astype(np.float32)).cuda()
+    l1t = torch.from_numpy(WL.bf16_round(rng.standard_normal((r, K)).astype(np.float32) * 0.05)).to(torch.bfloat16).cuda()
+    g = 0.01 if fmt == "nvfp4" else 1.0
+    c1, s1, t1 = ops.quantize_act_project(x, inv_s, l1t, fmt, tensor_scale=g)
+    c0, s0 = ops.quantize_act(x, inv_s, fmt, tensor_scale=g)
+    t0 = ops.lowrank_project(x, l1t=l1t)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c0) and torch.equal(s1.view(torch.uint8), s0.view(torch.uint8))
+    assert torch.equal(t1.view(torch.int16), t0[:, :2 * r].view(torch.int16))
+    _report("quantize_act_project", M=M, K=K, r=r, fmt=fmt)
+
+
+def test_lowrank_layer_one_launch_matches_two_kernels(ops, pipe):
+    """The low-rank layer's default call (one launch for quantizer and
+    projection) equals the two-kernel call bit for bit."""
+    case = WL.workload("lowrank")
+    layer, t = pipe.build_layer(case)
+    assert layer.launch_lowrank and not layer.has_projection(t["x"].dtype)
+    y1 = layer.forward(t["x"]).clone()
+    layer.launch_lowrank = False
+    assert layer.has_projection(t["x"].dtype)
+    y0 = layer.forward(t["x"]).clone()
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+
+
 def test_lowrank_fused_end_to_end(ops, pipe):
     """The 1024-token low-rank workload with the single-read quantizer
     (quantize_act_lowrank feeding the fused epilogue): codes exact, output

@@ -247,6 +247,29 @@ int quantize_act_lowrank(const void* x, int32_t x_dtype, int64_t M, int64_t K, i
   return launch_status(e, fn);
 }
 
+static int check_lowrank(const char* fn, const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const void* l1t, const int32_t* idx, int64_t r);
+
+int quantize_act_project(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const float* inv_smooth,
+                         const w4a4_qdesc* q, void* codes, void* scales, const void* l1t, int64_t r, void* out,
+                         int64_t ldo, void* stream) {
+  const char* fn = "quantize_act_project";
+  int st = check_lowrank(fn, x, x_dtype, M, K, ldx, l1t, nullptr, r);
+  if (st != W4A4_OK) return st;
+  if (!l1t) return fail(W4A4_ERR_INVALID_ARG, "%s: l1t is NULL", fn);
+  if (ldo < 2 * r) return fail(W4A4_ERR_INVALID_ARG, "%s: ldo < 2r", fn);
+  if (!w4a4::quant_project_fits(K, r))
+    return fail(W4A4_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld above 5120 (one wave per row)", fn, (long long)K);
+  st = check_quant(fn, x, x_dtype, M, K, ldx, inv_smooth, q, true, codes, scales);
+  if (st != W4A4_OK || M == 0) return st;
+  if (!out || !aligned(out, 2)) return fail(W4A4_ERR_INVALID_ARG, "%s: out NULL or misaligned", fn);
+  const int mode = q->fmt == W4A4_FMT_W4A8 ? 4 : (q->fmt == W4A4_FMT_FP8 ? 5 : q->fmt);
+  hipError_t e = w4a4::launch_quantize_project(mode, x, M, K, ldx, inv_smooth, q->tensor_scale, q->fwht_block,
+                                               q->order, codes, scales, (const uint16_t*)l1t, (int)r,
+                                               (uint16_t*)out, ldo, (hipStream_t)stream);
+  return launch_status(e, fn);
+}
+
 int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const float* smooth,
                  const w4a4_qdesc* q, void* codes, void* scales, void* stream) {
   if (q && q->fmt == W4A4_FMT_W4A8)

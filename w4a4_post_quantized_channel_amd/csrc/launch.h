@@ -24,6 +24,13 @@ int64_t quant_max_k();
 hipError_t launch_quantize_lowrank(int mode, const void* x, int64_t R, int64_t K, int64_t ldx, const float* scale,
                                    float g, int rot, int order, void* codes, void* scales, const uint16_t* l1t, int r,
                                    uint16_t* out, int64_t ldo, hipStream_t st);
+// quantize_act and the low-rank projection in one launch (bf16 input):
+// codes / scales as launch_quantize, out as launch_lowrank_project.
+// Shapes: quant_project_fits(K, r) (K % 16 == 0, K <= 5120, 1 <= r <= 128).
+hipError_t launch_quantize_project(int mode, const void* x, int64_t R, int64_t K, int64_t ldx, const float* scale,
+                                   float g, int rot, int order, void* codes, void* scales, const uint16_t* l1t, int r,
+                                   uint16_t* out, int64_t ldo, hipStream_t st);
+bool quant_project_fits(int64_t K, int64_t r);
 int64_t quant_lowrank_max_k();
 int quant_lowrank_max_r();
 bool quant_lowrank_fits(int64_t K, int64_t r);

@@ -29,6 +29,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "lds_dma.h"
+#include "project_body.h"
 
 namespace w4a4 {
 
@@ -507,6 +508,57 @@ __global__ void __launch_bounds__(64 * (WPR > 4 ? WPR : 4)) quant_rows_kernel(Qu
   }
 }
 
+struct LowrankArgs {
+  const uint16_t* l1t;   // r x K bf16, row stride K
+  int r;
+  uint16_t* out;         // M x ldo bf16: hi in [0, r), lo in [r, 2r)
+  int64_t ldo;
+};
+
+// quantize_act and the low-rank projection t = x L1 in one launch (Q-WAM
+// abstract: the 16-bit branch x L1 L2 beside the 4-bit complement).  The
+// first nq workgroups quantize rows, eight at a time, one per wave, exactly
+// as quant_rows_kernel does with one wave per row; each of the others
+// computes one 16 x 16 tile of t (project_block, as project_kernel).  The
+// two parts read x independently and write separate outputs, so they run
+// side by side on different CUs, and both outputs are bit-identical to the
+// two separate calls; one launch replaces two.
+template <int MODE, int NC>
+__global__ void __launch_bounds__(64 * kProjWaves) quant_project_kernel(QuantArgs a, LowrankArgs p, int nq, int mt) {
+  __shared__ __attribute__((aligned(16))) uint8_t area[kProjLdsBytes];
+  __shared__ float2 stab[MODE == MODE_NVFP4 ? 128 : 1];
+  if ((int)blockIdx.x >= nq) {   // projection workgroup
+    const int t = (int)blockIdx.x - nq;
+    project_block(reinterpret_cast<const uint16_t*>(a.x), a.ldx, (int)a.R, a.K, p.l1t, p.r, p.out, p.ldo,
+                  (t % mt) * kProjRows, (t / mt) * 16, area);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int RPB = kProjWaves;   // rows per workgroup, one per wave
+  if constexpr (MODE == MODE_NVFP4) {
+    for (int e = threadIdx.x; e < 128; e += blockDim.x) {
+      const float S = e < 0x7F ? e4m3_to_f32((uint32_t)e) * a.g : 0.f;
+      stab[e] = make_float2(S, S > 0.f ? 1.0f / S : 0.f);  // IEEE division
+    }
+    __syncthreads();
+  }
+  const bool has_scale = a.scale != nullptr;
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.scale, has_scale ? (uint32_t)(a.K * 4) : 0u);
+  const float rg = MODE == MODE_NVFP4 ? 1.0f / a.g : 1.0f;   // RN(1/g), IEEE division
+  const bool g_fast = a.g >= kTinyStep && a.g <= kBig;
+  float tmax = 0.f;
+  for (int64_t row = (int64_t)blockIdx.x * RPB + wave; row < a.R; row += (int64_t)nq * RPB) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)row * a.ldx * 2, (uint32_t)(a.K * 2));
+    SlotRaw<true> raw[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) raw[c] = load_slot<true>(rs, c * 64 + lane);
+    const uint4 nopre[1][4] = {};
+    quant_row_body<MODE, true, NC, 1>(a, row, raw, lane, wave, 0, nullptr, stab, rsc, rg, g_fast, tmax, nopre);
+  }
+}
+
 // Row quantizer fused with the low-rank branch projection (Q-WAM abstract:
 // the 16-bit branch x L1 L2 next to the 4-bit complement), so x is read
 // once.  A workgroup of four waves (one per SIMD) takes four rows at a
@@ -538,12 +590,6 @@ constexpr int kLrPitch = 2 * kLrMaxK + 16;
 constexpr int kLrChunkK = 128;                 // K elements per L1 chunk
 constexpr int kLrRing = 3;                     // chunk slots per wave
 
-struct LowrankArgs {
-  const uint16_t* l1t;   // r x K bf16, row stride K
-  int r;
-  uint16_t* out;         // M x ldo bf16: hi in [0, r), lo in [r, 2r)
-  int64_t ldo;
-};
 
 template <int MODE, int NC, int JB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -961,6 +1007,45 @@ static hipError_t launch_lowrank_mode(int nc, dim3 grid, hipStream_t st, const Q
 template <int MODE>
 static hipError_t launch_lowrank_r(int nc, int r, dim3 grid, hipStream_t st, const QuantArgs& a, const LowrankArgs& p) {
   return r == 16 ? launch_lowrank_mode<MODE, 1>(nc, grid, st, a, p) : launch_lowrank_mode<MODE, 2>(nc, grid, st, a, p);
+}
+
+bool quant_project_fits(int64_t K, int64_t r) { return K % 16 == 0 && K <= 5 * 1024 && r >= 1 && r <= 128; }
+
+template <int MODE>
+static hipError_t launch_quant_project_nc(int nc, dim3 grid, hipStream_t st, const QuantArgs& a, const LowrankArgs& p,
+                                          int nq, int mt) {
+  switch (nc) {
+    case 1: hipLaunchKernelGGL((quant_project_kernel<MODE, 1>), grid, dim3(64 * kProjWaves), 0, st, a, p, nq, mt); break;
+    case 2: hipLaunchKernelGGL((quant_project_kernel<MODE, 2>), grid, dim3(64 * kProjWaves), 0, st, a, p, nq, mt); break;
+    case 3: hipLaunchKernelGGL((quant_project_kernel<MODE, 3>), grid, dim3(64 * kProjWaves), 0, st, a, p, nq, mt); break;
+    case 4: hipLaunchKernelGGL((quant_project_kernel<MODE, 4>), grid, dim3(64 * kProjWaves), 0, st, a, p, nq, mt); break;
+    case 5: hipLaunchKernelGGL((quant_project_kernel<MODE, 5>), grid, dim3(64 * kProjWaves), 0, st, a, p, nq, mt); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_project(int mode, const void* x, int64_t R, int64_t K, int64_t ldx, const float* scale,
+                                   float g, int rot, int order, void* codes, void* scales, const uint16_t* l1t, int r,
+                                   uint16_t* out, int64_t ldo, hipStream_t st) {
+  if (!quant_project_fits(K, r) || R < 1) return hipErrorInvalidValue;
+  QuantArgs a{x, R, (int)K, ldx, scale, g, rot, order, (uint8_t*)codes, scales, nullptr, nullptr, 0, nullptr, 0};
+  const LowrankArgs p{l1t, r, out, ldo};
+  const int nc = round_nc((int)((K / 16 + 63) / 64));   // slots per lane, one wave per row
+  int64_t nq = (R + kProjWaves - 1) / kProjWaves;       // quantizer workgroups (grid-stride beyond 1024)
+  if (nq > 1024) nq = 1024;
+  const int64_t mt = (R + kProjRows - 1) / kProjRows, ct = (r + 15) / 16;
+  const int64_t total = nq + mt * ct;
+  if (total > INT32_MAX || mt > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)total);
+  switch (mode) {
+    case MODE_INT4: return launch_quant_project_nc<MODE_INT4>(nc, grid, st, a, p, (int)nq, (int)mt);
+    case MODE_INT8: return launch_quant_project_nc<MODE_INT8>(nc, grid, st, a, p, (int)nq, (int)mt);
+    case MODE_INT8W: return launch_quant_project_nc<MODE_INT8W>(nc, grid, st, a, p, (int)nq, (int)mt);
+    case MODE_FP8: return launch_quant_project_nc<MODE_FP8>(nc, grid, st, a, p, (int)nq, (int)mt);
+    case MODE_NVFP4: return launch_quant_project_nc<MODE_NVFP4>(nc, grid, st, a, p, (int)nq, (int)mt);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_quantize_lowrank(int mode, const void* x, int64_t R, int64_t K, int64_t ldx, const float* scale,

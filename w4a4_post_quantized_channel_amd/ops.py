@@ -24,9 +24,10 @@ BRANCH_NONE, BRANCH_BF16 = 0, 1
 FMTS = {"int4": FMT_INT4, "int8": FMT_INT8, "nvfp4": FMT_NVFP4, "w4a8": FMT_W4A8, "fp8": FMT_FP8}
 ORDERS = {"smooth_then_rotate": ORDER_SMOOTH_THEN_ROTATE,
           "rotate_then_smooth": ORDER_ROTATE_THEN_SMOOTH}
-ABI_VERSION = 2
+ABI_VERSION = 3
+MAX_BRANCH = 128   # W4A4_MAX_BRANCH: largest branch width (rank or kept channels)
 
-EXPORTS = ["quantize_act", "quantize_act_gather", "quantize_act_lowrank", "pack_weights", "pack_weights_gptq", "w4a4_gptq_workspace_size", "w4a4_linear", "w4a4_linear_noalloc", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
+EXPORTS = ["quantize_act", "quantize_act_gather", "quantize_act_lowrank", "quantize_act_project", "pack_weights", "pack_weights_gptq", "w4a4_gptq_workspace_size", "w4a4_linear", "w4a4_linear_noalloc", "w8a8_linear", "w4a8_linear", "fp8_linear", "lowrank_add",
            "w4a4_lowrank_project", "w4a4_lowrank_width", "w4a4_transform_amax", "w4a4_linear_plan",
            "w4a4_workspace_size", "w4a4_status_string",
            "w4a4_last_error", "w4a4_abi_version"]
@@ -60,6 +61,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "quantize_act": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
         "quantize_act_gather": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp, i64, vp, i64, vp],
         "quantize_act_lowrank": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp, i64, vp, i64, vp],
+        "quantize_act_project": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp, i64, vp, i64, vp],
         "pack_weights": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp],
         "pack_weights_gptq": [vp, i32, i64, i64, i64, vp, qd, vp, vp, vp, vp, vp, sz, vp],
         "w4a4_gptq_workspace_size": [i64, i64],
@@ -218,6 +220,30 @@ def quantize_act_lowrank(x: torch.Tensor, inv_smooth: Optional[torch.Tensor], l1
     q = qdesc(fmt, fwht_block, order, tensor_scale)
     _check("quantize_act_lowrank",
            LIB.quantize_act_lowrank(_ptr(x), _dtype_code(x), R, K, ld, _ptr(inv_smooth), ctypes.byref(q),
+                                    _ptr(codes), _ptr(scales), _ptr(l1t), r, _ptr(out), out.stride(0),
+                                    _stream(stream)))
+    return codes, scales, out
+
+
+def project_fusable(x: torch.Tensor, l1t: torch.Tensor) -> bool:
+    """Whether quantize_act_project takes this activation / rank (see the header)."""
+    r, K = l1t.shape
+    return x.dtype == torch.bfloat16 and K % 16 == 0 and K <= 5120 and 1 <= r <= MAX_BRANCH
+
+
+def quantize_act_project(x: torch.Tensor, inv_smooth: Optional[torch.Tensor], l1t: torch.Tensor,
+                         fmt: str = "int4", *, fwht_block: int = 64, order="smooth_then_rotate",
+                         tensor_scale: float = 1.0, codes=None, scales=None, out=None, stream=None):
+    """quantize_act and lowrank_project (low-rank form) in one launch."""
+    R, K, ld = _rowmajor(x)
+    r = l1t.shape[0]
+    if codes is None:
+        codes, scales = _alloc_codes(fmt, R, K, x.device)
+    if out is None:
+        out = torch.empty((R, 2 * r), dtype=torch.bfloat16, device=x.device)
+    q = qdesc(fmt, fwht_block, order, tensor_scale)
+    _check("quantize_act_project",
+           LIB.quantize_act_project(_ptr(x), _dtype_code(x), R, K, ld, _ptr(inv_smooth), ctypes.byref(q),
                                     _ptr(codes), _ptr(scales), _ptr(l1t), r, _ptr(out), out.stride(0),
                                     _stream(stream)))
     return codes, scales, out

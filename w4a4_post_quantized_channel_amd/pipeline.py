@@ -71,6 +71,9 @@ class QuantizedLinear:
         # by default: on MI355X the single-read kernel measured slower than
         # the two kernels (every CU holding rows must stream all of L1).
         self.fuse_lowrank = False
+        # launch_lowrank: quantizer and projection workgroups in one launch
+        # (quantize_act_project); outputs identical to the two calls.
+        self.launch_lowrank = True
 
     # NVFP4 activations use a static per-tensor scale from calibration data
     # (statistics after both transforms, QuantWAMs sec. 4.2).
@@ -112,6 +115,11 @@ class QuantizedLinear:
             ops.quantize_act_lowrank(x, self.inv_s, self.branch["l1t"], self.a_fmt, fwht_block=self.fwht_block,
                                      order=self.order, tensor_scale=self.g_a, codes=b["codes"],
                                      scales=b["scales"], out=b["br_a"], stream=stream)
+        elif self._one_launch_lowrank(x):
+            # quantizer and projection workgroups side by side in one launch
+            ops.quantize_act_project(x, self.inv_s, self.branch["l1t"], self.a_fmt, fwht_block=self.fwht_block,
+                                     order=self.order, tensor_scale=self.g_a, codes=b["codes"],
+                                     scales=b["scales"], out=b["br_a"], stream=stream)
         elif self.branch is not None and self.branch["kind"] == "outlier" and x.dtype == torch.bfloat16:
             ops.quantize_act_gather(x, self.inv_s, self.branch["idx"], self.a_fmt, fwht_block=self.fwht_block,
                                     order=self.order, tensor_scale=self.g_a, codes=b["codes"],
@@ -120,12 +128,20 @@ class QuantizedLinear:
             ops.quantize_act(x, self.inv_s, self.a_fmt, fwht_block=self.fwht_block, order=self.order,
                              tensor_scale=self.g_a, codes=b["codes"], scales=b["scales"], stream=stream)
 
+    def _one_launch_lowrank(self, x) -> bool:
+        return (self.branch is not None and self.branch["kind"] == "lowrank" and self.launch_lowrank and
+                not (self.fuse_lowrank and ops.lowrank_fusable(x, self.branch["l1t"])) and
+                ops.project_fusable(x, self.branch["l1t"]))
+
     def has_projection(self, x_dtype=torch.bfloat16) -> bool:
         """Whether the branch operand needs its own kernel (w4a4_lowrank_project)."""
         if self.branch is None:
             return False
         if self.branch["kind"] == "lowrank":
-            return not (self.fuse_lowrank and ops.lowrank_fusable(torch.empty(0, dtype=x_dtype), self.branch["l1t"]))
+            xe = torch.empty(0, dtype=x_dtype)
+            if self.fuse_lowrank and ops.lowrank_fusable(xe, self.branch["l1t"]):
+                return False
+            return not self._one_launch_lowrank(xe)
         return x_dtype != torch.bfloat16
 
     def project(self, x: torch.Tensor, stream=None):
