@@ -66,13 +66,15 @@ class QuantizedLinear:
                                                            tensor_scale=self.g_w, stream=stream)
         self.g_a = 1.0
         self._bufs = {}
-        # fuse_lowrank: take the low-rank operand from the quantizer's own
-        # pass over x (quantize_act_lowrank) instead of a second kernel.  Off
-        # by default: on MI355X the single-read kernel measured slower than
-        # the two kernels (every CU holding rows must stream all of L1).
+        # Low-rank branch operand T = x L1:
+        # * launch_lowrank (default): quantizer and projection workgroups in
+        #   one launch (quantize_act_project), outputs identical to the two
+        #   calls;
+        # * fuse_lowrank: from the quantizer's own pass over x
+        #   (quantize_act_lowrank), which reads x once but measured slower on
+        #   MI355X (every CU holding rows must stream all of L1);
+        # * neither: quantize_act, then w4a4_lowrank_project.
         self.fuse_lowrank = False
-        # launch_lowrank: quantizer and projection workgroups in one launch
-        # (quantize_act_project); outputs identical to the two calls.
         self.launch_lowrank = True
 
     # NVFP4 activations use a static per-tensor scale from calibration data
