@@ -132,6 +132,8 @@ MUTANTS = {
     "ties to the larger code": {"_nearest_code": _nearest_ties_up},
     "E4M3 exponent bias 8": {"e4m3_value": _e4m3_bias8},
     "NVFP4 block scale from amax / 4": {"E2M1_MAX": 4.0},
+    "NVFP4 tensor scale from twice the range": {
+        "nvfp4_tensor_scale": lambda amax: F32(_orig["nvfp4_tensor_scale"](amax) / F32(2))},
     "NVFP4 dequantisation ignores g": {
         "dequantize_nvfp4": lambda c, e, g: _orig["dequantize_nvfp4"](c, e, 1.0)},
     "FP8 step amax / 240": {"E4M3_MAX": 240.0},

@@ -260,6 +260,13 @@ def test_nvfp4_quantizer_invariants():
     assert e[5, 1] == 0 and np.all(codes[5, 16:32] == 0)
     # the largest block of the tensor maps to the largest finite scale
     assert e.max() == 0x7E
+    # g = amax / (6 * 448) puts the tensor's largest element on the top of both
+    # grids: scale code 448, element code +-6, and it dequantizes back to
+    # +-amax (three binary32 roundings: g, S = 448 g, 6 S)
+    i, j = np.unravel_index(np.argmax(np.abs(y)), y.shape)
+    assert e[i, j // 16] == 0x7E and (codes[i, j] & 7) == 7
+    top = np.float32(6.0) * np.float32(np.float32(448.0) * np.float32(g))
+    assert abs(float(top) - float(np.abs(y).max())) <= 4 * np.spacing(np.float32(np.abs(y).max()))
     # blocks whose scale is in the normal E4M3 range reach the largest element code
     mag = codes & 7
     normal = sv >= 2.0 ** -6
