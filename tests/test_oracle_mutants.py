@@ -111,10 +111,47 @@ def _gptq_plus(wt, step, u, qmax, perm=None):
     return codes, E
 
 
+def _quantize_int_f64(y, qmax):
+    """Step and quotient evaluated in float64 instead of binary32."""
+    y = np.asarray(y, dtype=F32)
+    step = np.abs(y).max(axis=1).astype(np.float64) / qmax
+    v = np.zeros(y.shape)
+    nz = step > 0
+    v[nz] = y[nz].astype(np.float64) / step[nz, None]
+    return np.clip(np.rint(v), -qmax - 1, qmax).astype(np.int8), step.astype(F32), v.astype(F32)
+
+
+def _nvfp4_with(scale_of):
+    """quantize_nvfp4 whose element step comes from scale_of(sv, g) -> (e, S)."""
+    def q(y, g):
+        y = np.asarray(y, dtype=F32)
+        g = F32(g)
+        R, K = y.shape
+        yb = y.reshape(R, K // 16, 16)
+        sv = ((np.abs(yb).max(axis=2) / F32(6)).astype(F32) / g).astype(F32)
+        e, S = scale_of(sv, g)
+        v = np.zeros_like(yb)
+        nz = S > 0
+        v[nz] = (yb[nz] / S[nz][:, None]).astype(F32)
+        return O.e2m1_encode(v).reshape(R, K).astype(np.uint8), e, sv, v.reshape(R, K)
+    return q
+
+
+def _unrounded_scale(sv, g):
+    return O.e4m3_encode(sv), (sv * g).astype(F32)
+
+
+def _floor_scale(sv, g):
+    grid = O.e4m3_value(np.arange(0x7F)).astype(np.float64)
+    e = np.clip(np.searchsorted(grid, sv.astype(np.float64), side="right") - 1, 0, 0x7E).astype(np.uint8)
+    return e, (O.e4m3_value(e).astype(F32) * g).astype(F32)
+
+
 MUTANTS = {
     # FWHT and the transform
     "butterfly difference sign flipped": {"fwht_blocks": lambda u, block=64: _fwht(u, block, sign=-1)},
     "last butterfly stage dropped": {"fwht_blocks": lambda u, block=64: _fwht(u, block, stages=5)},
+    "rotation blocks of 32": {"fwht_blocks": lambda u, block=64: _orig["fwht_blocks"](u, 32)},
     "1/8 normalisation dropped": {"transform": lambda *a, **k: _orig["transform"](*a, **k) * 8},
     "smoothing by the reciprocal factor": {
         "transform": lambda x, scale, *a, **k: _orig["transform"](
@@ -128,10 +165,16 @@ MUTANTS = {
     "truncation instead of round-to-nearest-even": {"quantize_int": _quantize_int(np.trunc)},
     "ties away from zero": {"quantize_int": _quantize_int(lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5))},
     "Q off by one": {"quantize_int": lambda y, qmax: _orig["quantize_int"](y, qmax + 1)},
+    "integer step and quotient in float64": {"quantize_int": _quantize_int_f64},
+    "integer dequantisation ignores the step": {"dequantize_int": lambda c, s: np.asarray(c).astype(F32)},
     # NVFP4 / E4M3 codecs
     "ties to the larger code": {"_nearest_code": _nearest_ties_up},
     "E4M3 exponent bias 8": {"e4m3_value": _e4m3_bias8},
     "NVFP4 block scale from amax / 4": {"E2M1_MAX": 4.0},
+    "NVFP4 element codes from the unrounded block scale": {"quantize_nvfp4": _nvfp4_with(_unrounded_scale)},
+    "NVFP4 block scale rounded down": {"quantize_nvfp4": _nvfp4_with(_floor_scale)},
+    "FP8 pre-rounding values 0.1% high": {
+        "quantize_fp8": lambda y: (lambda c, st, v: (c, st, (v * F32(1.001)).astype(F32)))(*_orig["quantize_fp8"](y))},
     "NVFP4 tensor scale from twice the range": {
         "nvfp4_tensor_scale": lambda amax: F32(_orig["nvfp4_tensor_scale"](amax) / F32(2))},
     "NVFP4 dequantisation ignores g": {

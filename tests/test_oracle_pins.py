@@ -615,6 +615,30 @@ def test_fp8_quantizer_invariants():
     bound = 2.0 ** -4 * np.abs(y) + 2.0 ** -10 * step.astype(np.float64)[:, None]
     assert np.all(np.abs(dq - y) <= bound * (1 + 1e-6))
     assert np.all((dq == 0) | (np.sign(dq) == np.sign(y)))
+    # the pre-rounding value of each row's largest element is 448 up to the
+    # two binary32 roundings of the step and the quotient
+    imax = np.argmax(np.abs(y), axis=1)
+    top = np.abs(v[np.arange(len(y)), imax])[nz]
+    assert np.all(np.abs(top.astype(np.float64) - 448.0) <= 2 * 2.0 ** -15)
+
+
+def test_int_quantizer_decides_in_binary32():
+    """The step and the quotient are binary32 values (the precision of the
+    kernels), and the code follows from them.  Row [1, 1/2], Q = 7: the exact
+    step 1/7 would make 1/2 a tie at 3.5 (code 4); the binary32 step is
+    0x3E124925 = 1/7 + 3 / (7 * 2^26), slightly above 1/7, so the exact
+    quotient (1/2) / step = 3.49999984... lies below 3.5 and rounds to the
+    binary32 value 3.5 - 2^-22, and the code is 3.  Scaling the row by a
+    power of two changes nothing; negating it negates the codes."""
+    import struct
+    step_bits = struct.unpack("<f", struct.pack("<I", 0x3E124925))[0]
+    for scale in (1.0, 2.0 ** -6, 2.0 ** 20):
+        for sgn in (1.0, -1.0):
+            y = np.array([[sgn * scale, sgn * scale / 2]], np.float32)
+            codes, step, v = O.quantize_int(y, 7)
+            assert step[0] == np.float32(step_bits * scale)
+            assert v[0, 1] == np.float32(sgn * (3.5 - 2.0 ** -22))
+            assert codes[0].tolist() == [int(sgn * 7), int(sgn * 3)]
 
 
 def test_fp8_gemm_is_exact():
