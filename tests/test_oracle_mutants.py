@@ -147,6 +147,52 @@ def _floor_scale(sv, g):
     return e, (O.e4m3_value(e).astype(F32) * g).astype(F32)
 
 
+def _gptq_with(update):
+    """gptq_rows with the feedback step replaced by update(W, err, u, t)."""
+    def g(wt, step, u, qmax, perm=None):
+        wt = np.asarray(wt, dtype=F32)
+        N, K = wt.shape
+        perm = np.arange(K) if perm is None else np.asarray(perm)
+        W = wt[:, perm].astype(np.float64)
+        sf = np.asarray(step, F32).astype(np.float64)
+        nz = sf > 0
+        Q, E = np.zeros((N, K), np.int64), np.zeros((N, K))
+        for t in range(K):
+            q = np.zeros(N)
+            q[nz] = np.clip(np.rint(W[nz, t] / sf[nz]), -qmax - 1, qmax)
+            err = update(W, W[:, t] - q * sf, u, t)
+            Q[:, t], E[:, t] = q, err
+        codes = np.empty((N, K), np.int8)
+        codes[:, perm] = Q.astype(np.int8)
+        return codes, E
+    return g
+
+
+def _next_column_only(W, r, u, t):
+    err = r / u[t, t]
+    if t + 1 < W.shape[1]:
+        W[:, t + 1] -= err * u[t, t + 1]
+    return err
+
+
+def _no_pivot_division(W, r, u, t):
+    if t + 1 < W.shape[1]:
+        W[:, t + 1:] -= np.outer(r, u[t, t + 1:])
+    return r
+
+
+
+def _gptq_inverse_scatter(wt, step, u, qmax, perm=None):
+    """Codes written back with the inverse of the processing order."""
+    c, e = _orig["gptq_rows"](wt, step, u, qmax, perm)
+    if perm is None:
+        return c, e
+    perm = np.asarray(perm)
+    out = np.empty_like(c)
+    out[:, np.argsort(perm)] = c[:, perm]
+    return out, e
+
+
 MUTANTS = {
     # FWHT and the transform
     "butterfly difference sign flipped": {"fwht_blocks": lambda u, block=64: _fwht(u, block, sign=-1)},
@@ -158,6 +204,10 @@ MUTANTS = {
             x, None if scale is None else np.divide(1.0, np.asarray(scale, np.float64),
                                                     out=np.zeros(np.shape(scale)), where=np.asarray(scale) != 0),
             *a, **k)},
+    "the two transform orders swapped": {
+        "transform": lambda x, scale, fwht_block=64, order="smooth_then_rotate", dtype=F32: _orig["transform"](
+            x, scale, fwht_block, {"smooth_then_rotate": "rotate_then_smooth",
+                                   "rotate_then_smooth": "smooth_then_rotate"}[order], dtype)},
     "smoothing always after the rotation": {
         "transform": lambda x, scale, fwht_block=64, order="smooth_then_rotate", dtype=F32:
             _orig["transform"](x, scale, fwht_block, "rotate_then_smooth", dtype)},
@@ -177,6 +227,8 @@ MUTANTS = {
         "quantize_fp8": lambda y: (lambda c, st, v: (c, st, (v * F32(1.001)).astype(F32)))(*_orig["quantize_fp8"](y))},
     "NVFP4 tensor scale from twice the range": {
         "nvfp4_tensor_scale": lambda amax: F32(_orig["nvfp4_tensor_scale"](amax) / F32(2))},
+    "NVFP4 dequantisation applies g twice": {
+        "dequantize_nvfp4": lambda c, e, g: _orig["dequantize_nvfp4"](c, e, g) * np.float64(F32(g))},
     "NVFP4 dequantisation ignores g": {
         "dequantize_nvfp4": lambda c, e, g: _orig["dequantize_nvfp4"](c, e, 1.0)},
     "FP8 step amax / 240": {"E4M3_MAX": 240.0},
@@ -196,6 +248,9 @@ MUTANTS = {
     "low-rank branch with L2 transposed": {
         "lowrank_branch": lambda x, l1, lw: (np.asarray(x, np.float64) @ np.asarray(l1, np.float64))
         @ np.asarray(lw, np.float64)},
+    "low-rank T rounded to binary32": {
+        "lowrank_branch": lambda x, l1, lw: (np.asarray(x, np.float64) @ np.asarray(l1, np.float64)).astype(F32)
+        .astype(np.float64) @ np.asarray(lw, np.float64).T},
     "kept-channel index shifted by one": {
         "outlier_branch": lambda x, idx, lw: _orig["outlier_branch"](
             x, (np.asarray(idx) + 1) % np.shape(x)[1], lw)},
@@ -204,6 +259,9 @@ MUTANTS = {
         "transformed_amax": lambda x, scale, fwht_block=64, order="smooth_then_rotate":
             F32(np.abs(np.asarray(x, F32)).max()) if np.size(x) else F32(0)},
     "GPTQ feedback sign flipped": {"gptq_rows": _gptq_plus},
+    "GPTQ updates only the next column": {"gptq_rows": _gptq_with(_next_column_only)},
+    "GPTQ error not divided by the pivot": {"gptq_rows": _gptq_with(_no_pivot_division)},
+    "GPTQ codes scattered in the inverse order": {"gptq_rows": _gptq_inverse_scatter},
 }
 
 
