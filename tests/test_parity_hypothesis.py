@@ -4,9 +4,11 @@ magnitudes, one-hot and zero rows, and NVFP4 tensor scales small enough to
 saturate the block scales.  Same bars as the fixed cases: codes and scales
 exact (band-admissible mismatches counted), outputs within tolerance, and
 for integer formats without a branch the output bit-exact."""
+import os
+
 import numpy as np
 import pytest
-from hypothesis import HealthCheck, given, settings, strategies as st
+from hypothesis import HealthCheck, given, seed, settings, strategies as st
 
 from oracle import w4a4_oracle as O
 from w4a4_post_quantized_channel_amd import workloads as WL
@@ -64,9 +66,16 @@ def cases(draw):
     return case, order, gshrink
 
 
-@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+# W4A4_SWEEP_EXAMPLES widens the sweep; W4A4_SWEEP_SEED draws a different
+# (still reproducible) set of examples than the default derandomized one.
+_SWEEP_N = int(os.environ.get("W4A4_SWEEP_EXAMPLES", "40"))
+_SWEEP_SEED = os.environ.get("W4A4_SWEEP_SEED")
+
+
+@settings(max_examples=_SWEEP_N, deadline=None, derandomize=_SWEEP_SEED is None, database=None,
           suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture,
                                  HealthCheck.data_too_large])
+@(seed(int(_SWEEP_SEED)) if _SWEEP_SEED else (lambda f: f))
 @given(cases())
 def test_random_parity(env, drawn):
     ops, pipe = env
