@@ -43,7 +43,11 @@
  *  - NVFP4: R x K/2 bytes of E2M1 nibbles (same nibble order; sign bit 3,
  *           exponent bits 2..1 with bias 1, mantissa bit 0).  scales:
  *           R x K/16 bytes of OCP E4M3 (E4M3FN, bias 7, max 448), one per 16
- *           consecutive K elements.  The fp32 tensor scale g travels in the
+ *           consecutive K elements.  quantize_act and pack_weights write
+ *           non-negative scales; the GEMM reads a byte with the sign bit
+ *           set as the negated value, as the format defines it (0x7F and
+ *           0xFF, NaN in E4M3FN, are never written and give NaN outputs).
+ *           The fp32 tensor scale g travels in the
  *           w4a4_qdesc (quantize / pack) and in ``alpha`` (linear).
  */
 #ifndef W4A4_H

@@ -265,19 +265,26 @@ def test_fp8_extreme_codes(ops, val_a, val_w):
     assert np.all(_np(y) == np.float32(want))
 
 
+@pytest.mark.parametrize("signed", [False, True])
 @pytest.mark.parametrize("M", [20, 127])
-def test_nvfp4_every_scale_code(ops, M):
+def test_nvfp4_every_scale_code(ops, M, signed):
     """Every finite non-negative E4M3 block scale (codes 0..126) through the
     NVFP4 GEMM, on both operands: row m of A uses code m mod 127 for all
     its blocks, row n of W code 7n mod 127.  Divided by the two scale
     values, each output is a dot product of E2M1 codes (a multiple of 1/4),
-    so a wrong scale decode shows as a gross error on its own rows."""
+    so a wrong scale decode shows as a gross error on its own rows.
+    signed: odd rows of A and rows n = 1, 2 mod 3 of W carry the sign bit
+    as well (codes 128..254, -0 included); the format reads them as the
+    negated values, and the GEMM must too."""
     N, K = 160, 2048
     rng = np.random.default_rng(11)
     ca = rng.integers(0, 16, (M, K))
     cw = rng.integers(0, 16, (N, K))
     ea = (np.arange(M) % 127).astype(np.uint8)
     ew = ((7 * np.arange(N)) % 127).astype(np.uint8)
+    if signed:
+        ea = ea | np.where(np.arange(M) % 2 == 1, 0x80, 0).astype(np.uint8)
+        ew = ew | np.where(np.arange(N) % 3 != 0, 0x80, 0).astype(np.uint8)
     sa = np.repeat(ea[:, None], K // 16, axis=1)
     sw = np.repeat(ew[:, None], K // 16, axis=1)
     dot = O.e2m1_value(ca) @ O.e2m1_value(cw).T            # exact in fp64

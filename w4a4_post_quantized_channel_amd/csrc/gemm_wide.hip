@@ -14,9 +14,9 @@
 //     int4  -> bytes 16*q ((d << 4) & 0xF0F0F0F0: even codes, d & 0xF0F0F0F0:
 //              odd codes); v_mfma_i32_16x16x64_i8 returns 256 * sum(qa*qw);
 //     int8  -> used as loaded;
-//     NVFP4 -> exact fp16 value(c) * value(e): v_cvt_scalef32_pk_f16_fp4 by
-//              the power of two of the E4M3 scale, then one exact packed fp16
-//              multiply by its mantissa; v_mfma_f32_16x16x32_f16.
+//     NVFP4 -> exact fp16 value(c) * value(e): v_cvt_scalef32_pk_f16_fp4
+//              with unit scale, then one exact packed fp16 multiply by the
+//              E4M3 value (sign included); v_mfma_f32_16x16x32_f16.
 //   The widening of one MFMA step is interleaved with the MFMAs of the
 //   previous one.
 // * K order.  A stage holds 128 packed bytes per row for each of the WK
@@ -117,20 +117,24 @@ __device__ __forceinline__ int swz(int row) {
   else return row & 15;
 }
 
-__device__ __forceinline__ uint2 scale_pair(uint32_t e) {
-  const float S = __builtin_amdgcn_cvt_f32_fp8((int)e, 0);   // OCP E4M3, exact
-  const float mant = __uint_as_float((__float_as_uint(S) & 0x007FFFFFu) | 0x3F800000u);
-  return make_uint2(__float_as_uint(S), __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(mant, mant)));
+// E4M3 scale byte SEL of w as a pair of equal fp16 values (exact: every
+// finite E4M3 value, subnormals included, is a normal fp16).
+template <int SEL = 0>
+__device__ __forceinline__ uint32_t scale_h2(uint32_t w) {
+  const float S = __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);   // OCP E4M3, exact
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(S, S));
 }
 
-// 8 E2M1 codes times one scale pair -> 8 fp16 (exact)
-__device__ __forceinline__ uint4 widen_fp4(uint32_t d, uint2 sp) {
-  const float S = __uint_as_float(sp.x);
-  const v2h m2 = __builtin_bit_cast(v2h, sp.y);
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, S, 0) * m2;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, S, 1) * m2;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, S, 2) * m2;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, S, 3) * m2;
+// 8 E2M1 codes times one E4M3 scale (as scale_h2 gives it) -> 8 fp16.
+// Exact: a code has at most two significant bits and magnitude at most 6,
+// a scale at most four significant bits and magnitude in [2^-9, 448], so
+// every nonzero product is a normal fp16 of at most six significant bits.
+__device__ __forceinline__ uint4 widen_fp4(uint32_t d, uint32_t s2) {
+  const v2h m2 = __builtin_bit_cast(v2h, s2);
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * m2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * m2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * m2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * m2;
   return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
 }
@@ -163,7 +167,7 @@ __device__ __forceinline__ uint4 operand(const uint4& p, int t, uint32_t sc) {
   } else if constexpr (FMT == W_INT4 || FMT == W_W4A8) {
     return (t & 1) ? widen_i4(p.z, p.w) : widen_i4(p.x, p.y);
   } else {
-    return widen_fp4(dw(p, t), scale_pair((sc >> (8 * (t >> 1))) & 0xFFu));
+    return widen_fp4(dw(p, t), (t >> 1) ? scale_h2<1>(sc) : scale_h2<0>(sc));
   }
 }
 
@@ -247,10 +251,21 @@ struct CodeCopy {
       off[t] = (NI % NW == 0 || n < NI) ? (uint32_t)(row * rowbytes) + col[t] : kOOB;
     }
   }
-  // region, pad: LDS byte addresses; rowbytes < 2^31
+  // region, pad: LDS byte addresses; rowbytes < 2^31.  FULL: a stage
+  // wholly inside K skips the per-lane column test (a wave-uniform branch;
+  // measured faster for the NVFP4 and W4A8 loops, slower for the others).
+  template <bool FULL = false>
   __device__ __forceinline__ void issue(const v4u& rs, uint32_t region, uint32_t pad, uint32_t rowbytes, int s,
                                         int wave) const {
     const uint32_t k0 = (uint32_t)s * P;
+    if (FULL && k0 + P <= rowbytes) {
+#pragma unroll
+      for (int t = 0; t < PW; ++t) {
+        const int n = NW * t + wave;
+        dma16_at(rs, (NI % NW == 0 || n < NI) ? region + n * 1024 : pad, off[t], k0);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < PW; ++t) {
       const int n = NW * t + wave;
@@ -279,9 +294,18 @@ struct ScaleCopy {
       off[t] = (NI % NW == 0 || n < NI) ? (uint32_t)(row * srow + c) : kOOB;
     }
   }
+  template <bool FULL = false>
   __device__ __forceinline__ void issue(const v4u& rs, uint32_t region, uint32_t pad, uint32_t srow, int s,
                                         int wave) const {
     const uint32_t k0 = (uint32_t)s * SP;
+    if (FULL && k0 + SP <= srow) {   // the whole stage lies inside K (wave-uniform)
+#pragma unroll
+      for (int t = 0; t < PW; ++t) {
+        const int n = NW * t + wave;
+        dma4_at(rs, (NI % NW == 0 || n < NI) ? region + n * 256 : pad, off[t], k0);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < PW; ++t) {
       const int n = NW * t + wave;
@@ -346,8 +370,8 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   }
   auto copy_stage = [&](int s) {
     const uint32_t base = lds0 + (uint32_t)(s % C::NBUF) * C::STAGE;
-    cpA.issue(rsA, base, pad, (uint32_t)rbA, s, wave);
-    cpB.issue(rsB, base + C::A_BYTES, pad, (uint32_t)rowbytes, s, wave);
+    cpA.template issue<FMT == W_W4A8>(rsA, base, pad, (uint32_t)rbA, s, wave);
+    cpB.template issue<FMT == W_W4A8>(rsB, base + C::A_BYTES, pad, (uint32_t)rowbytes, s, wave);
     if constexpr (FMT == W_NVFP4) {
       cpSA.issue(rsSA, base + C::A_BYTES + C::B_BYTES, pad, (uint32_t)srow, s, wave);
       cpSB.issue(rsSB, base + C::A_BYTES + C::B_BYTES + C::SA_BYTES, pad, (uint32_t)srow, s, wave);
@@ -649,7 +673,7 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
 // each activation fragment by both wave columns).  Here the workgroup
 // widens each stage of its weight tile once: every thread loads 16-byte
 // chunks of packed codes (32 E2M1 codes of one row, two 16-element blocks)
-// and the word holding their two E4M3 scales, widens them to exact fp16
+// and the two bytes of their E4M3 scales, widens them to exact fp16
 // value(code) * value(scale), and stores them in an fp16 stage in LDS.  The
 // waves read their weight operands from that stage and still widen their
 // activation operands from the packed stage.
@@ -732,43 +756,59 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
   cpSA.init(wave, lane, srow);
   auto copy_a = [&](int s) {
     const uint32_t base = lds0 + (uint32_t)(s % kCbNA) * kCbASTAGE;
-    cpA.issue(rsA, base, pad, (uint32_t)rowbytes, s, wave);
-    cpSA.issue(rsSA, base + kCbA, pad, (uint32_t)srow, s, wave);
+    cpA.issue<true>(rsA, base, pad, (uint32_t)rowbytes, s, wave);
+    cpSA.issue<true>(rsSA, base + kCbA, pad, (uint32_t)srow, s, wave);
   };
 
-  // this thread's weight chunks: c = tid + 512 h, row c / 4, quarter c % 4
-  int crow[kCbNCH], cq[kCbNCH];
+  // this thread's weight chunks: c = tid + 512 h, row c / 4, quarter c % 4.
+  // Fixed per lane: the chunk's byte in the weight rows (a stage adds its K
+  // byte through the scalar offset), its two scale bytes, and the LDS
+  // offsets of its four fp16 slots in weight buffer 0 (buffer 1 follows at
+  // a fixed distance, which the stores take as an immediate offset).
   bool cval[kCbNCH];
+  uint32_t wvo[kCbNCH], wso[kCbNCH], wcol[kCbNCH], wlo[kCbNCH][4];
 #pragma unroll
   for (int h = 0; h < kCbNCH; ++h) {
     const int c = tid + 64 * kCbNW * h;
+    const int crow = c >> 2, cq = c & 3;
     cval[h] = c < kCbCH;
-    crow[h] = c >> 2;
-    cq[h] = c & 3;
+    wcol[h] = (uint32_t)(cq * 16);
+    wvo[h] = cval[h] ? (uint32_t)(crow * rowbytes) + wcol[h] : kOOB;
+    wso[h] = cval[h] ? (uint32_t)(crow * srow + cq * 2) : kOOB;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      wlo[h][tt] = (uint32_t)(kCbBOFF + crow * kCbBROW + (((4 * cq + tt) ^ (crow & 11)) * 16));
   }
   uint4 wc[kCbNCH];
   uint32_t ws[kCbNCH];
+  // Stages wholly inside K skip the per-lane column test (wave-uniform).
   auto load_w = [&](int s) {
+    const uint32_t kb0 = (uint32_t)s * kCbP, sb0 = (uint32_t)s * kCbSP;
+    if (kb0 + kCbP <= (uint32_t)rowbytes) {
 #pragma unroll
-    for (int h = 0; h < kCbNCH; ++h) {
-      const int64_t kb = (int64_t)s * kCbP + cq[h] * 16;   // byte of the chunk within its row
-      const bool ok = cval[h] && kb < rowbytes;
-      wc[h] = buf_load16(rW, ok ? (uint32_t)(crow[h] * rowbytes + kb) : kOOB);
-      ws[h] = buf_load4(rSW, ok ? (uint32_t)(crow[h] * srow + (int64_t)s * kCbSP + (cq[h] >> 1) * 4) : kOOB);
+      for (int h = 0; h < kCbNCH; ++h) {
+        wc[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)wvo[h], (int)kb0, 0));
+        ws[h] = __builtin_amdgcn_raw_buffer_load_b16(rSW, (int)wso[h], (int)sb0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < kCbNCH; ++h) {
+        const bool ok = kb0 + wcol[h] < (uint32_t)rowbytes;
+        wc[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(ok ? wvo[h] : kOOB), (int)kb0, 0));
+        ws[h] = __builtin_amdgcn_raw_buffer_load_b16(rSW, (int)(ok ? wso[h] : kOOB), (int)sb0, 0);
+      }
     }
   };
-  auto widen_w = [&](int s) {
-    uint8_t* bb = smem + kCbBOFF + (s & 1) * kCbBSTAGE;
+  // weight stage -> fp16 buffer PB (compile-time 0 or 1)
+  auto widen_w = [&](auto pb) {
+    constexpr uint32_t boff_b = decltype(pb)::value * kCbBSTAGE;
 #pragma unroll
     for (int h = 0; h < kCbNCH; ++h) {
       if (!cval[h]) continue;
-      const uint32_t two = (ws[h] >> (16 * (cq[h] & 1))) & 0xFFFFu;   // scales of blocks 2q, 2q + 1
-      const uint2 sp0 = scale_pair(two & 0xFFu), sp1 = scale_pair(two >> 8);
-      uint8_t* rowp = bb + crow[h] * kCbBROW;
-      const int sw = crow[h] & 11;
+      const uint32_t s0 = scale_h2<0>(ws[h]), s1 = scale_h2<1>(ws[h]);   // blocks 2q, 2q + 1
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
-        *reinterpret_cast<uint4*>(rowp + (((4 * cq[h] + tt) ^ sw) * 16)) = widen_fp4(dw(wc[h], tt), tt < 2 ? sp0 : sp1);
+        *reinterpret_cast<uint4*>(smem + wlo[h][tt] + boff_b) = widen_fp4(dw(wc[h], tt), tt < 2 ? s0 : s1);
     }
   };
   auto lds_barrier = [&]() {
@@ -785,10 +825,14 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // per-lane LDS offsets: activation fragment rows (slot lq of the packed
-  // row, swizzled as the copies write it) and their scale bytes; weight rows
+  // row, swizzled as the copies write it) and their scale bytes; weight
+  // fragment rows of buffer 0, one per MFMA step
   const int aoff = (wm0 + lr) * kCbP + ((lq ^ swz<kCbP>(wm0 + lr)) * 16);
   const int saoff = kCbA + (wm0 + lr) * kCbSP + lq * 2;
-  const int boff = kCbBOFF + (wn0 + lr) * kCbBROW;
+  uint32_t boff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    boff[st] = (uint32_t)(kCbBOFF + (wn0 + lr) * kCbBROW + (((4 * lq + st) ^ (lr & 11)) * 16));
 
   struct AFrag {
     uint4 c[TI];
@@ -802,30 +846,34 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
       f.sc[i] = *reinterpret_cast<const uint16_t*>(ab + saoff + i * 16 * kCbSP);
     }
   };
-  auto step = [&](int s, const AFrag& f, int st) {
-    const uint8_t* bb = smem + (s & 1) * kCbBSTAGE + boff;
+  // MFMA step st of a stage whose fp16 weights sit in buffer PB
+  auto step = [&](auto pb, const AFrag& f, int st) {
+    constexpr uint32_t boff_b = decltype(pb)::value * kCbBSTAGE;
     uint4 oa[TI], ob[TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      ob[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * kCbBROW + (((4 * lq + st) ^ (lr & 11)) * 16));
+    for (int j = 0; j < TJ; ++j) ob[j] = *reinterpret_cast<const uint4*>(smem + boff[st] + boff_b + j * 16 * kCbBROW);
 #pragma unroll
-    for (int i = 0; i < TI; ++i) oa[i] = widen_fp4(dw(f.c[i], st), scale_pair((f.sc[i] >> (8 * (st >> 1))) & 0xFFu));
+    for (int i = 0; i < TI; ++i) oa[i] = widen_fp4(dw(f.c[i], st), st < 2 ? scale_h2<0>(f.sc[i]) : scale_h2<1>(f.sc[i]));
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j) mfma_w<W_NVFP4>(acc[i][j], oa[i], ob[j]);
   };
-  auto iter = [&](int s, const AFrag& cur, AFrag& nxt) {
-    step(s, cur, 0);
+  const std::integral_constant<int, 0> B0{};
+  const std::integral_constant<int, 1> B1{};
+  // iteration s (weight buffer PB = s % 2, so stage s + 1 goes to 1 - PB)
+  auto iter = [&](int s, auto pb, const AFrag& cur, AFrag& nxt) {
+    constexpr int PB = decltype(pb)::value;
+    step(pb, cur, 0);
     wait_vmcnt<0>();   // activation stage s + 2 and weight chunks s + 1, issued last iteration
     asm volatile("" ::: "memory");
-    widen_w(s + 1);
+    widen_w(std::integral_constant<int, 1 - PB>{});
     copy_a(s + 3);
     load_w(s + 2);
-    step(s, cur, 1);
+    step(pb, cur, 1);
     read_a(s + 1, nxt);
-    step(s, cur, 2);
-    step(s, cur, 3);
+    step(pb, cur, 2);
+    step(pb, cur, 3);
     lds_barrier();
   };
 
@@ -835,7 +883,7 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
   copy_a(1);
   load_w(0);
   wait_vmcnt<0>();
-  widen_w(0);
+  widen_w(B0);
   copy_a(2);
   load_w(1);
   lds_barrier();
@@ -843,10 +891,10 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
   read_a(0, f0);
   int s = 0;
   for (; s + 1 < nk; s += 2) {
-    iter(s, f0, f1);
-    iter(s + 1, f1, f0);
+    iter(s, B0, f0, f1);
+    iter(s + 1, B1, f1, f0);
   }
-  if (s < nk) iter(s, f0, f1);
+  if (s < nk) iter(s, B0, f0, f1);
   wait_vmcnt<0>();
   __syncthreads();
 
