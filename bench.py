@@ -484,19 +484,20 @@ def copy_calibration(torch):
 # Profile summaries (rocprofv3 outputs -> profiles/)
 # ---------------------------------------------------------------------------
 PROFILES = os.path.join(ROOT, "profiles")
+# $OUT is the directory later given to --summarize-profiles
 PROFILE_CMDS = {
-    "trace": "BENCH_PHASE_LOG=gpurun_out/kt/phases.json rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/kt "
+    "trace": "BENCH_PHASE_LOG=$OUT/kt/phases.json rocprofv3 --kernel-trace --stats -f csv -d $OUT/kt "
              "-o run -- python3 bench.py",
-    "pmc": "BENCH_PHASE_LOG=gpurun_out/pmc_{c}/phases.json rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_{c} -o run "
+    "pmc": "BENCH_PHASE_LOG=$OUT/pmc_{c}/phases.json rocprofv3 --pmc {c} -f csv -d $OUT/pmc_{c} -o run "
            "-- python3 bench.py --no-cpu-baseline --replays 2",
-    "copy": "rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_copy_{c} -o run -- python3 bench.py --copy-calibration",
+    "copy": "rocprofv3 --pmc {c} -f csv -d $OUT/pmc_copy_{c} -o run -- python3 bench.py --copy-calibration",
 }
 # one counter run: matrix-core busy cycles, VALU instructions and activity,
 # wave cycles and waits, LDS bank conflicts (7 SQ counters + 1 GRBM)
 CORE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_WAIT_INST_ANY "
                  "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE")
-PROFILE_CMDS["core"] = ("BENCH_PHASE_LOG=gpurun_out/pmc_core/phases.json rocprofv3 --pmc " + CORE_COUNTERS +
-                        " -f csv -d gpurun_out/pmc_core -o run -- python3 bench.py --no-cpu-baseline --replays 2")
+PROFILE_CMDS["core"] = ("BENCH_PHASE_LOG=$OUT/pmc_core/phases.json rocprofv3 --pmc " + CORE_COUNTERS +
+                        " -f csv -d $OUT/pmc_core -o run -- python3 bench.py --no-cpu-baseline --replays 2")
 KERNEL_SOURCES = ["quantize.hip", "gemm_int.hip", "gemm_wide.hip", "branch.hip", "epilogue.h", "device_common.h",
                   "lds_dma.h", "project_body.h"]
 
