@@ -218,9 +218,10 @@ int pack_weights(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t l
                  void* codes, void* scales, void* stream);
 
 /* pack_weights_gptq -- pack_weights with GPTQ-style rounding instead of
- * round-to-nearest (QuantWAMs sec. 3.3: GPTQ compensation governed by the
- * layer's activation second moments, column scores used only as an
- * ordering inside GPTQ, the common rotation fused into the weights).  The
+ * round-to-nearest (QuantWAMs sec. 3.3: the error feedback of GPTQ is weighted by
+ * the layer's activation second moments, per-column scores at most decide
+ * the order in which GPTQ visits the columns, and the Hadamard transform,
+ * shared by every context, is folded into W before rounding).  The
  * rows are transformed as in pack_weights and keep its per-row steps; the
  * columns are then rounded in the order perm (NULL: natural), each
  * column's error over u[t][t] updating every later column v by

@@ -24,9 +24,10 @@ Sources (the pages this restates; no text is quoted):
 * Q-WAM abstract: a 16-bit low-rank branch plus 4-bit complement, both as
   dense matrix products.
 * QuantWAMs sec. 3.3, Eq. 14 and the text after it (the weight distortion
-  is governed by the layer's activation second moments Sigma_L; GPTQ
-  compensation follows Sigma_L, column scores serve only as an ordering
-  inside GPTQ, and the common rotation is fused into the weights):
+  is governed by the layer's activation second moments Sigma_L, which
+  also weight GPTQ's error feedback; per-column scores at most choose the
+  order of GPTQ's column sweep, and the Hadamard transform shared by every
+  context is folded into W before rounding):
   GPTQ-style rounding of the transformed weights, given the Cholesky
   factor of the damped inverse second-moment matrix (calibration data) and
   a column order.
