@@ -169,17 +169,18 @@ int quantize_act_gather(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
                         const int32_t* idx, int64_t r, void* xo, int64_t ldo, void* stream);
 
 /* quantize_act_lowrank -- quantize_act that also writes the low-rank branch
- * operand from the same pass over x (Q-WAM abstract: a 16-bit low-rank
- * branch x L1 L2 beside the 4-bit complement), so the branch costs no
- * second read of x.  Arguments as quantize_act, plus:
+ * operand (Q-WAM abstract: a 16-bit low-rank branch x L1 L2 beside the
+ * 4-bit complement); the workgroup that quantizes a group of rows also
+ * projects them, so x comes from HBM once (the projection's read of the
+ * same rows is served from cache).  Arguments as quantize_act, plus:
  *  l1t  bf16 r x K, row stride K, 16-byte aligned: L1 transposed.
  *  r    16 or 32.
  *  out  bf16 M x ldo (ldo >= 2r): T = x L1 evaluated in fp32 (exact bf16
  *       products, fp32 sums) and written as hi = bf16(T) in columns [0, r)
  *       and lo = bf16(T - hi) in [r, 2r): the w4a4_branch ``a`` operand
  *       (ra = 2r), as w4a4_lowrank_project writes it.
- * x must be BF16; K a multiple of 64, at most 4096 (the rows are staged in
- * LDS); other shapes are W4A4_ERR_UNSUPPORTED_SHAPE (use quantize_act and
+ * x must be BF16; K a multiple of 64, at most 4096 (a row is held in one
+ * wave's registers); other shapes are W4A4_ERR_UNSUPPORTED_SHAPE (use quantize_act and
  * w4a4_lowrank_project).
  * Codes and scales are those quantize_act writes. */
 int quantize_act_lowrank(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,

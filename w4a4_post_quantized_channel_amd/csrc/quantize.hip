@@ -560,56 +560,60 @@ __global__ void __launch_bounds__(64 * kProjWaves) quant_project_kernel(QuantArg
 }
 
 // Row quantizer fused with the low-rank branch projection (Q-WAM abstract:
-// the 16-bit branch x L1 L2 next to the 4-bit complement), so x is read
-// once.  A workgroup of four waves (one per SIMD) takes four rows at a
-// time, one per wave, and walks row groups with a grid-stride loop.
-// * Each wave loads its row and the row's smoothing factors into registers
-//   and writes the raw bf16 row into LDS (row pitch 2K + 16 bytes).
-// * Then it starts streaming its share of L1 (transposed, r x K) into a
-//   private three-slot LDS ring: K is cut into 128-element chunks, wave w
-//   owns chunks w, w + 4, ...; a chunk's r rows of 256 bytes arrive by
-//   buffer-to-LDS copies of whole lines, 16-byte slot q of row j stored at
-//   q XOR (j mod 16), so the 16 rows an MFMA fragment reads fall on
-//   distinct banks.  These copies are not tracked by the compiler, so they
-//   are issued only after the row's own loads have been consumed.
-// * The wave quantizes its row as quant_rows_kernel does while the copies
-//   fly, meets the others at a barrier (every row staged), and walks its
-//   chunks: wait for the chunk (a fixed vmcnt: chunks past K are copied as
-//   zeros, so the count never changes), two 64-element K pairs of bf16
-//   16x16x32 products per 16-column block (A = the four staged rows, read
-//   again by the lanes of rows 4..15, whose outputs are dropped; within a
-//   pair, lane group q holds K elements 16 q .. 16 q + 15 on both
-//   operands), then its LDS reads are waited for and the chunk three ahead
-//   is copied into the freed slot.
-// * The four partial 4 x r tiles are added in LDS in wave order and T goes
-//   out as the bf16 pair hi = bf16(T), lo = bf16(T - hi) (columns [0, r)
-//   and [r, 2r)).
-constexpr int kLrMaxK = 4096;                  // staged row length limit
+// the 16-bit branch x L1 L2 next to the 4-bit complement), so x leaves HBM
+// once.  A workgroup of eight waves takes four rows at a time and walks
+// row groups with a grid-stride loop.  Waves 0..3 quantize, one row each,
+// with quant_rows_kernel's body; waves 4..7 compute T = x L1 for the same
+// four rows, each over a quarter of K.  The two halves share no data and
+// run side by side; both read the rows, the second time from cache.
+// * Projection wave p owns the 128-element K chunks p, p + 4, ... and
+//   streams each through a private four-slot LDS ring: the chunk of L1
+//   (transposed, r x K: r rows of 256 bytes, 16-byte slot s of row j
+//   stored at s XOR (j mod 16), so the 16 rows an MFMA fragment reads fall
+//   on distinct banks) and the four rows' 256 bytes of the same K range,
+//   by buffer-to-LDS copies of whole lines.  Chunks past K are copied as
+//   zeros, so every wait is a fixed vmcnt.
+// * Per chunk: two 64-element K pairs of bf16 16x16x32 products per
+//   16-column block (A = the four rows, read again by the lanes of rows
+//   4..15, whose outputs are dropped; within a pair, lane group g holds K
+//   elements 16 g .. 16 g + 15 on both operands), then a wait for the
+//   slot's LDS reads and the copy of the chunk four ahead into it.
+// * A barrier; the four partial 4 x r tiles are added in LDS in wave
+//   order and T goes out as the bf16 pair hi = bf16(T), lo = bf16(T - hi)
+//   (columns [0, r) and [r, 2r)).
+// The barriers wait for LDS operations only (lgkmcnt), never for the
+// untracked copies in flight.
+constexpr int kLrMaxK = 4096;                  // row length limit (four slots per lane)
 constexpr int kLrMaxR = 32;                    // rank limit (two 16-column blocks)
-constexpr int kLrPitch = 2 * kLrMaxK + 16;
-constexpr int kLrChunkK = 128;                 // K elements per L1 chunk
-constexpr int kLrRing = 3;                     // chunk slots per wave
+constexpr int kLrChunkK = 128;                 // K elements per chunk
+constexpr int kLrRing = 4;                     // chunk slots per projection wave
 
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int MODE, int NC, int JB>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-    quant_rows_lowrank_kernel(QuantArgs a, LowrankArgs p) {
+__global__ void __launch_bounds__(512) quant_rows_lowrank_kernel(QuantArgs a, LowrankArgs p) {
   asm volatile("" ::"s"(a.x), "s"(a.R), "s"(a.K), "s"(a.ldx), "s"(a.scale), "s"(a.g), "s"(a.rot), "s"(a.order),
                "s"(a.codes), "s"(a.scales), "s"(p.l1t), "s"(p.r), "s"(p.out), "s"(p.ldo));
   constexpr int R16 = 16 * JB;                 // rows of L1 transposed (p.r == R16)
-  constexpr int CHB = R16 * kLrChunkK * 2;     // bytes of one chunk
-  constexpr int NCP = CHB / 1024;              // copy instructions per chunk
+  constexpr int CHB = R16 * kLrChunkK * 2;     // bytes of one chunk of L1
+  constexpr int NCP = CHB / 1024;              // its copy instructions
+  constexpr int SLOT = CHB + 1024;             // + the four rows' 256 bytes each
+  constexpr int PER = NCP + 1;                 // copy instructions per chunk
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool quantizer = wave < 4;             // wave-uniform role
+  const int q = wave & 3;                      // row (quantizer) or K share (projection)
   const int lr = lane & 15, lq = lane >> 4;
   const bool has_scale = a.scale != nullptr;
-  const int nslots = a.K >> 4;
-  const int pitch = 2 * a.K + 16;
   const int npairs = a.K >> 6;                 // 64-element K pairs
   const int nchunks = (a.K + kLrChunkK - 1) / kLrChunkK;
-  const int nsteps = (nchunks + 3) / 4;        // chunks per wave (the last ones may lie past K)
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * kLrRing * 16 * 2 * kLrChunkK * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t xs[4 * kLrPitch];
+  const int nsteps = (nchunks + 3) / 4;        // chunks per projection wave (the last ones may lie past K)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * kLrRing * (2 * 16 * kLrChunkK * 2 + 1024)];
   __shared__ float part[4 * JB * 4 * 16];
   __shared__ float2 stab[MODE == MODE_NVFP4 ? 128 : 1];
   if constexpr (MODE == MODE_NVFP4) {
@@ -624,8 +628,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const bool g_fast = a.g >= kTinyStep && a.g <= kBig;
   float tmax = 0.f;
 
-  // copies: instruction n of a chunk covers chunk bytes [1024 n, 1024 n + 1024),
-  // lane l the 16 bytes at 1024 n + 16 l: row 4 n + l / 16, physical slot l % 16
+  // L1 copies: instruction n of a chunk covers chunk bytes [1024 n, 1024 n
+  // + 1024), lane l the 16 bytes at 1024 n + 16 l: row 4 n + l / 16,
+  // physical slot l % 16.  Row copy: lane l, row l / 16, 16-byte piece
+  // l % 16 of the chunk's 256 bytes, unswizzled.
   const v4u rl = rsrc_words(p.l1t, (uint32_t)(R16 * a.K * 2));
   uint32_t coff[NCP], cslot[NCP];
 #pragma unroll
@@ -634,97 +640,82 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     cslot[n] = (uint32_t)((lane & 15) ^ (row & 15)) * 16;             // logical slot, bytes
     coff[n] = (uint32_t)(row * a.K * 2) + cslot[n];
   }
-  const uint32_t ring0 = lds_addr(ring) + (uint32_t)(wave * kLrRing * CHB);
-  auto copy_chunk = [&](int step) {            // this wave's chunk wave + 4 step into slot step % kLrRing
-    const int g = wave + 4 * step;              // wave-uniform
-    const uint32_t dst = ring0 + (uint32_t)((step % kLrRing) * CHB);
-    const uint32_t k0 = g < nchunks ? (uint32_t)(g * 256) : 0u;
-#pragma unroll
-    for (int n = 0; n < NCP; ++n) {
-      // the last chunk may be half a chunk: its other half would be the next row
-      const bool ok = g < nchunks && k0 + cslot[n] < (uint32_t)(a.K * 2);
-      dma16_at(rl, dst + n * 1024, ok ? coff[n] : kOOB, k0);
-    }
-  };
+  const uint32_t xpiece = (uint32_t)(lane & 15) * 16;
+  const uint32_t ring0 = lds_addr(ring) + (uint32_t)(q * kLrRing * SLOT);
 
   for (int64_t row0 = (int64_t)blockIdx.x * 4; row0 < a.R; row0 += (int64_t)gridDim.x * 4) {
-    const int64_t row = row0 + wave;
-    const bool live = row < a.R;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)(live ? row : 0) * a.ldx * 2,
-                                                live ? (uint32_t)(a.K * 2) : 0u);
-    SlotRaw<true> raw[NC];
-    uint4 sc[NC][4];
+    if (quantizer) {
+      const int64_t row = row0 + q;
+      if (row < a.R) {
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)row * a.ldx * 2, (uint32_t)(a.K * 2));
+        SlotRaw<true> raw[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) raw[c] = load_slot<true>(rs, c * 64 + lane);
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sc[c][i] = has_scale ? buf_load16(rsc, (uint32_t)((c * 64 + lane) * 64 + i * 16)) : make_uint4(0, 0, 0, 0);
-    // the raw row into LDS (zeros for a row past M)
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int s = c * 64 + lane;
-      if (s < nslots) {
-        uint4* d = reinterpret_cast<uint4*>(xs + wave * pitch + s * 32);
-        d[0] = raw[c].d[0];
-        d[1] = raw[c].d[1];
+        for (int c = 0; c < NC; ++c) raw[c] = load_slot<true>(rs, c * 64 + lane);
+        const uint4 nopre[1][4] = {};
+        quant_row_body<MODE, true, NC, 1>(a, row, raw, lane, q, 0, nullptr, stab, rsc, rg, g_fast, tmax, nopre);
       }
-    }
-    // the factors are consumed here, so no compiler wait on them comes after
-    // the untracked copies below
+    } else {
+      const int nrows = (int)min((int64_t)4, a.R - row0);
+      const v4u rx = rsrc_words(reinterpret_cast<const char*>(a.x) + (size_t)row0 * a.ldx * 2,
+                                (uint32_t)(nrows * a.ldx * 2));
+      const uint32_t xoff = (uint32_t)((lane >> 4) * a.ldx * 2) + xpiece;
+      auto copy_chunk = [&](int step) {        // chunk q + 4 step into slot step % kLrRing
+        const int g = q + 4 * step;             // wave-uniform
+        const uint32_t dst = ring0 + (uint32_t)((step % kLrRing) * SLOT);
+        const uint32_t k0 = g < nchunks ? (uint32_t)(g * 256) : 0u;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+        for (int n = 0; n < NCP; ++n) {
+          // the last chunk may be half a chunk: its other half would be the next row
+          const bool ok = g < nchunks && k0 + cslot[n] < (uint32_t)(a.K * 2);
+          dma16_at(rl, dst + n * 1024, ok ? coff[n] : kOOB, k0);
+        }
+        const bool okx = g < nchunks && k0 + xpiece < (uint32_t)(a.K * 2);
+        dma16_at(rx, dst + CHB, okx ? xoff : kOOB, k0);
+      };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(sc[c][i].x), "+v"(sc[c][i].y), "+v"(sc[c][i].z), "+v"(sc[c][i].w));
+      for (int step = 0; step < kLrRing - 1; ++step) copy_chunk(step);
+      v4f acc[JB];
 #pragma unroll
-    for (int step = 0; step < kLrRing; ++step) copy_chunk(step);
-    if (live)
-      quant_row_body<MODE, true, NC, 1, true>(a, row, raw, lane, wave, 0, nullptr, stab, rsc, rg, g_fast, tmax, sc);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's row is in LDS
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    v4f acc[JB];
+      for (int jb = 0; jb < JB; ++jb) acc[jb] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int step = 0; step < nsteps; ++step) {
+        copy_chunk(step + kLrRing - 1);        // into the slot read two steps ago (its reads waited for)
+        wait_vmcnt<(kLrRing - 1) * PER>();     // chunk `step` has landed
+        asm volatile("" ::: "memory");
+        const int g = q + 4 * step;
+        const uint8_t* slot = ring + (q * kLrRing + step % kLrRing) * SLOT;
+        const uint8_t* arow = slot + CHB + (lr & 3) * 256 + lq * 32;
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) acc[jb] = v4f{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* arow = xs + (lr & 3) * pitch + lq * 32;
-    for (int step = 0; step < nsteps; ++step) {
-      wait_vmcnt<(kLrRing - 1) * NCP>();       // chunk `step` has landed
-      asm volatile("" ::: "memory");
-      const int g = wave + 4 * step;
-      const uint8_t* slot = ring + (wave * kLrRing + step % kLrRing) * CHB;
+        for (int pl = 0; pl < 2; ++pl) {
+          const int pp = 2 * g + pl;
+          if (pp < npairs) {
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl) {
-        const int pp = 2 * g + pl;
-        if (pp < npairs) {
+            for (int h = 0; h < 2; ++h) {
+              const v8bf af = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(arow + pl * 128 + h * 16));
+              const int L = pl * 8 + lq * 2 + h;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const v8bf af = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(arow + pp * 128 + h * 16));
-            const int L = pl * 8 + lq * 2 + h;
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) {
-              const uint4 b = *reinterpret_cast<const uint4*>(slot + (jb * 16 + lr) * 256 + ((L ^ lr) * 16));
-              acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(v8bf, b), acc[jb], 0, 0, 0);
+              for (int jb = 0; jb < JB; ++jb) {
+                const uint4 b = *reinterpret_cast<const uint4*>(slot + (jb * 16 + lr) * 256 + ((L ^ lr) * 16));
+                acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(v8bf, b), acc[jb], 0, 0, 0);
+              }
             }
           }
         }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0): this slot's reads are done
+        asm volatile("" ::: "memory");
       }
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this slot's reads are done
-      asm volatile("" ::: "memory");
-      copy_chunk(step + kLrRing);
-    }
-    wait_vmcnt<0>();                            // the trailing copies (past K: zeros) have landed
-    // lanes 0..15 hold rows 0..3 (one per register) of column lr of each block
-    if (lq == 0) {
+      wait_vmcnt<0>();                          // the trailing copies (past K: zeros) have landed
+      // lanes 0..15 hold rows 0..3 (one per register) of column lr of each block
+      if (lq == 0) {
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
+        for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[((wave * JB + jb) * 4 + i) * 16 + lr] = acc[jb][i];
+          for (int i = 0; i < 4; ++i) part[((q * JB + jb) * 4 + i) * 16 + lr] = acc[jb][i];
+      }
     }
-    __syncthreads();
-    for (int t = threadIdx.x; t < 4 * R16; t += 256) {
+    lds_barrier();   // the partial tiles are written
+    for (int t = threadIdx.x; t < 4 * R16; t += blockDim.x) {
       const int i = t / R16, j = t - i * R16;
       float v = 0.f;
 #pragma unroll
@@ -737,7 +728,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         o[R16 + j] = (uint16_t)f32_to_bf16_bits(lo);
       }
     }
-    __syncthreads();   // the staged rows and partial tiles are written again by the next row group
+    lds_barrier();   // the partial tiles are written again by the next row group
   }
 }
 
@@ -995,10 +986,10 @@ bool quant_lowrank_fits(int64_t K, int64_t r) {
 template <int MODE, int JB>
 static hipError_t launch_lowrank_mode(int nc, dim3 grid, hipStream_t st, const QuantArgs& a, const LowrankArgs& p) {
   switch (nc) {
-    case 1: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 1, JB>), grid, dim3(256), 0, st, a, p); break;
-    case 2: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 2, JB>), grid, dim3(256), 0, st, a, p); break;
-    case 3: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 3, JB>), grid, dim3(256), 0, st, a, p); break;
-    case 4: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 4, JB>), grid, dim3(256), 0, st, a, p); break;
+    case 1: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 1, JB>), grid, dim3(512), 0, st, a, p); break;
+    case 2: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 2, JB>), grid, dim3(512), 0, st, a, p); break;
+    case 3: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 3, JB>), grid, dim3(512), 0, st, a, p); break;
+    case 4: hipLaunchKernelGGL((quant_rows_lowrank_kernel<MODE, 4, JB>), grid, dim3(512), 0, st, a, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
