@@ -695,6 +695,7 @@ def main():
         return
 
     built, warm, flops = measure_headline(torch, HEADLINE[1], a.steps, a.replays)
+    print("[bench] headline step measured", file=sys.stderr, flush=True)
     ms = warm["median"] * 1e-3
     # the headline's dominant kernel: the W8A8 down projection's GEMM (the larger projection)
     c2b = next(b for b in built if b[0].name == "decode_w8a8")
@@ -708,6 +709,7 @@ def main():
             if cid == "C2b":
                 continue
             case, layer, r = measure_case(torch, cid, name, a.replays, cold=(cid != "C1"), built=cached.get(name))
+            print(f"[bench] {cid} measured", file=sys.stderr, flush=True)
             sc = summarize_case(case, layer, r)
             sc["vendor_gemm"] = vendor_gemm(torch, case)
             configs.append(sc)
@@ -719,6 +721,7 @@ def main():
     if not a.no_configs and not a.no_next:
         for cid, name, what in NEXT:
             case, layer, r = measure_case(torch, cid, name, a.replays)
+            print(f"[bench] {cid} measured", file=sys.stderr, flush=True)
             sc = summarize_case(case, layer, r)
             sc["row"] = what
             sc["vendor_gemm"] = vendor_gemm(torch, case)
