@@ -779,37 +779,44 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
     for (int tt = 0; tt < 4; ++tt)
       wlo[h][tt] = (uint32_t)(kCbBOFF + crow * kCbBROW + (((4 * cq + tt) ^ (crow & 11)) * 16));
   }
-  uint4 wc[kCbNCH];
-  uint32_t ws[kCbNCH];
+  uint4 wc[2][kCbNCH];      // two register sets: stage s's chunks in set s % 2
+  uint32_t ws[2][kCbNCH];
   // Stages wholly inside K skip the per-lane column test (wave-uniform).
-  auto load_w = [&](int s) {
+  auto load_w = [&](int s, auto slot) {
+    constexpr int R = decltype(slot)::value;
     const uint32_t kb0 = (uint32_t)s * kCbP, sb0 = (uint32_t)s * kCbSP;
     if (kb0 + kCbP <= (uint32_t)rowbytes) {
 #pragma unroll
       for (int h = 0; h < kCbNCH; ++h) {
-        wc[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)wvo[h], (int)kb0, 0));
-        ws[h] = __builtin_amdgcn_raw_buffer_load_b16(rSW, (int)wso[h], (int)sb0, 0);
+        wc[R][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)wvo[h], (int)kb0, 0));
+        ws[R][h] = __builtin_amdgcn_raw_buffer_load_b16(rSW, (int)wso[h], (int)sb0, 0);
       }
     } else {
 #pragma unroll
       for (int h = 0; h < kCbNCH; ++h) {
         const bool ok = kb0 + wcol[h] < (uint32_t)rowbytes;
-        wc[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(ok ? wvo[h] : kOOB), (int)kb0, 0));
-        ws[h] = __builtin_amdgcn_raw_buffer_load_b16(rSW, (int)(ok ? wso[h] : kOOB), (int)sb0, 0);
+        wc[R][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(ok ? wvo[h] : kOOB), (int)kb0, 0));
+        ws[R][h] = __builtin_amdgcn_raw_buffer_load_b16(rSW, (int)(ok ? wso[h] : kOOB), (int)sb0, 0);
       }
     }
   };
-  // weight stage -> fp16 buffer PB (compile-time 0 or 1)
-  auto widen_w = [&](auto pb) {
+  // weight chunk h, from register set R, -> fp16 buffer PB (R and PB
+  // compile-time 0 or 1)
+  auto widen_chunk = [&](int h, auto pb, auto slot) {
     constexpr uint32_t boff_b = decltype(pb)::value * kCbBSTAGE;
+    constexpr int R = decltype(slot)::value;
 #pragma unroll
-    for (int h = 0; h < kCbNCH; ++h) {
-      if (!cval[h]) continue;
-      const uint32_t s0 = scale_h2<0>(ws[h]), s1 = scale_h2<1>(ws[h]);   // blocks 2q, 2q + 1
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        *reinterpret_cast<uint4*>(smem + wlo[h][tt] + boff_b) = widen_fp4(dw(wc[h], tt), tt < 2 ? s0 : s1);
+    for (int tt = 0; tt < 4; ++tt) {
+      const uint32_t sc = tt < 2 ? scale_h2<0>(ws[R][h]) : scale_h2<1>(ws[R][h]);   // blocks 2q, 2q + 1
+      *reinterpret_cast<uint4*>(smem + wlo[h][tt] + boff_b) = widen_fp4(dw(wc[R][h], tt), sc);
     }
+  };
+  // every thread holds chunk 0 (the stage has more chunks than threads);
+  // chunk 1 exists for the first waves only (a wave-uniform test)
+  static_assert(kCbCH >= 64 * kCbNW && kCbNCH <= 2, "chunk split");
+  auto widen_w = [&](auto pb, auto slot) {
+    widen_chunk(0, pb, slot);
+    if (kCbNCH > 1 && cval[kCbNCH - 1]) widen_chunk(kCbNCH - 1, pb, slot);
   };
   auto lds_barrier = [&]() {
     asm volatile("" ::: "memory");
@@ -864,12 +871,13 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
   // iteration s (weight buffer PB = s % 2, so stage s + 1 goes to 1 - PB)
   auto iter = [&](int s, auto pb, const AFrag& cur, AFrag& nxt) {
     constexpr int PB = decltype(pb)::value;
+    constexpr std::integral_constant<int, 1 - PB> NB{};
     step(pb, cur, 0);
     wait_vmcnt<0>();   // activation stage s + 2 and weight chunks s + 1, issued last iteration
     asm volatile("" ::: "memory");
-    widen_w(std::integral_constant<int, 1 - PB>{});
+    widen_w(NB, NB);   // stage s + 1: register set 1 - PB -> fp16 buffer 1 - PB
     copy_a(s + 3);
-    load_w(s + 2);
+    load_w(s + 2, pb);   // into register set PB, free since stage s was widened
     step(pb, cur, 1);
     read_a(s + 1, nxt);
     step(pb, cur, 2);
@@ -881,11 +889,11 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
   // activation stage 2 and weight chunks 1 in flight, stage 0's fragments read
   copy_a(0);
   copy_a(1);
-  load_w(0);
+  load_w(0, B0);
   wait_vmcnt<0>();
-  widen_w(B0);
+  widen_w(B0, B0);
   copy_a(2);
-  load_w(1);
+  load_w(1, B1);
   lds_barrier();
   AFrag f0, f1;
   read_a(0, f0);
