@@ -264,7 +264,9 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
       const int n = n_base + ch * 8;
       const uint32_t off = (uint32_t)row * rstride + (uint32_t)n * 2u;
       if (n + 8 <= g.N) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), ry, (int)off, 0, 0);
+        // non-temporal (cache policy 2, `nt`): the tile is written once and
+        // never read back here, so it need not stay in L2
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), ry, (int)off, 0, 2);
       } else {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
