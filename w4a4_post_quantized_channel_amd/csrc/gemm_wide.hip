@@ -636,7 +636,8 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
   } else {
     // Sum the WK partial tiles: every wave stores its tile, then wave group
     // kw adds up columns [kw * TJ / WK, (kw + 1) * TJ / WK) and runs the
-    // epilogue on them.
+    // epilogue on them (bf16 staged: 1024x3072x3072 int4 17.1 -> 16.8 us
+    // warm, 18.2 -> 17.2 cold, against per-element stores).
     constexpr int TJW = TJ / WK;
     typedef typename std::conditional<FMT == W_NVFP4, float, int32_t>::type el_t;
     el_t* red = reinterpret_cast<el_t*>(smem);
@@ -664,7 +665,12 @@ __global__ void __launch_bounds__(64 * WR * WC * WK)
           part[i][jj][r] = v;
         }
       }
-    epilogue_tiles<KIND>(part, g, m0 + wm0, n0 + wn0 + kw * TJW * 16, lane, nullptr,
+    // bf16 output staged through LDS as in the single-group case, in the
+    // partial-tile area once every wave has read its sums
+    static_assert(C::NW * epilogue_stage_bytes<TI, TJW>() <= C::BR_OFF, "epilogue staging fits");
+    __syncthreads();
+    epilogue_tiles<KIND>(part, g, m0 + wm0, n0 + wn0 + kw * TJW * 16, lane,
+                         smem + wave * epilogue_stage_bytes<TI, TJW>(),
                          static_cast<const EpiScales<TI, TJW>*>(nullptr), &el);
   }
 }
