@@ -197,6 +197,52 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
   const bool br_pre = g.br.r > 0 && el && el->bra;
   BrAFrags<TI> bra_f;
   if (br_pre) load_br_a<TI>(bra_f, *el, g.br.ra, m_base - el->m_tile, lane);
+  // Small grids (at most 8 tiles) dequantise every tile first and then run
+  // the branch products of all of them together, so the products of
+  // different tiles overlap instead of waiting on each other; each tile
+  // takes the same products in the same order as below.
+  if constexpr (KIND != 2 && TI * TJ <= 8) {
+    if (br_pre && stage != nullptr && g.y_dtype == 1) {
+      v4f yv[TI][TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int n = n_base + j * 16 + lr;
+        const float swn = pre ? pre->sw[j] : el->sw[n - el->n_tile];
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = epi_acc<KIND>(acc[i][j][r]) * sam[i][r];
+            v = v * swn;
+            yv[i][j][r] = v * g.alpha;
+          }
+      }
+      const int lk = lq * 8;
+#pragma unroll
+      for (int s = 0; s < kBrLdsMax / 32; ++s) {
+        if (s * 32 >= g.br.ra) break;
+        const int kb = (s * 32 + lk) % g.br.r;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int row = n_base + j * 16 - el->n_tile + lr;
+          const v8bf b = __builtin_bit_cast(
+              v8bf, *reinterpret_cast<const uint4*>(el->brb + row * 128 + (((kb >> 3) ^ (row & 7)) << 4)));
+#pragma unroll
+          for (int i = 0; i < TI; ++i)
+            yv[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bra_f.a[s][i], b, yv[i][j], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<uint16_t*>(stage + (i * 16 + lq * 4 + r) * (TJ * 32 + 16) + (j * 16 + lr) * 2) =
+                (uint16_t)f32_to_bf16_bits(yv[i][j][r]);
+      goto staged_out;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int n = n_base + j * 16 + lr;
@@ -249,6 +295,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
                                                 (int)(roff[i][r] + coff), 0, 0);
     }
   }
+staged_out:
   if (stage != nullptr && g.y_dtype == 1) {
     // Rows back out of LDS, 16 bytes (8 columns) per lane: every row of the
     // tile leaves as whole contiguous segments.
