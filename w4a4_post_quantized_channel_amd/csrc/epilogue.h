@@ -148,7 +148,10 @@ __device__ __forceinline__ float epi_acc(T a) {
 
 // `pre`, when given, holds the scales already loaded (load_epi_scales);
 // `el`, when given, the LDS-staged scales and branch rows of the tile.
-template <int KIND /*0 int4, 1 int8, 2 float, 3 int8 x int4, 4 fp8*/, typename AccT, int TI, int TJ>
+// GROUPS: the grouped branch pass below (off where its registers cost the
+// kernel's main loop more than it saves).
+template <int KIND /*0 int4, 1 int8, 2 float, 3 int8 x int4, 4 fp8*/, bool GROUPS = true, typename AccT, int TI,
+          int TJ>
 __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
                                                int lane, uint8_t* stage = nullptr,
                                                const EpiScales<TI, TJ>* pre = nullptr, const EpiLds* el = nullptr) {
@@ -197,49 +200,68 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
   const bool br_pre = g.br.r > 0 && el && el->bra;
   BrAFrags<TI> bra_f;
   if (br_pre) load_br_a<TI>(bra_f, *el, g.br.ra, m_base - el->m_tile, lane);
-  // Small grids (at most 8 tiles) dequantise every tile first and then run
-  // the branch products of all of them together, so the products of
-  // different tiles overlap instead of waiting on each other; each tile
-  // takes the same products in the same order as below.
-  if constexpr (KIND != 2 && TI * TJ <= 8) {
+  // The column blocks go in groups of at most eight tiles: a group's tiles
+  // are dequantised first and then take the branch products of all of
+  // them in one pass, so the products of different tiles overlap instead
+  // of waiting on each other; each tile takes the same products in the
+  // same order as in the loop below.
+  if constexpr (GROUPS) {
+    constexpr int GJ = (8 / TI) < 1 ? 1 : (8 / TI);   // column blocks per group
     if (br_pre && stage != nullptr && g.y_dtype == 1) {
-      v4f yv[TI][TJ];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int n = n_base + j * 16 + lr;
-        const float swn = pre ? pre->sw[j] : el->sw[n - el->n_tile];
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = epi_acc<KIND>(acc[i][j][r]) * sam[i][r];
-            v = v * swn;
-            yv[i][j][r] = v * g.alpha;
-          }
-      }
       const int lk = lq * 8;
 #pragma unroll
-      for (int s = 0; s < kBrLdsMax / 32; ++s) {
-        if (s * 32 >= g.br.ra) break;
-        const int kb = (s * 32 + lk) % g.br.r;
+      for (int j0 = 0; j0 < TJ; j0 += GJ) {
+        v4f yv[TI][GJ];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int row = n_base + j * 16 - el->n_tile + lr;
-          const v8bf b = __builtin_bit_cast(
-              v8bf, *reinterpret_cast<const uint4*>(el->brb + row * 128 + (((kb >> 3) ^ (row & 7)) << 4)));
+        for (int jj = 0; jj < GJ; ++jj) {
+          const int j = j0 + jj;
+          if (j >= TJ) break;
+          if constexpr (KIND != 2) {
+            const int n = n_base + j * 16 + lr;
+            const float swn = pre ? pre->sw[j] : el->sw[n - el->n_tile];
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                float v = epi_acc<KIND>(acc[i][j][r]) * sam[i][r];
+                v = v * swn;
+                yv[i][jj][r] = v * g.alpha;
+              }
+          } else {
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) yv[i][jj][r] = acc[i][j][r] * g.alpha;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < kBrLdsMax / 32; ++s) {
+          if (s * 32 >= g.br.ra) break;
+          const int kb = (s * 32 + lk) % g.br.r;
+#pragma unroll
+          for (int jj = 0; jj < GJ; ++jj) {
+            const int j = j0 + jj;
+            if (j >= TJ) break;
+            const int row = n_base + j * 16 - el->n_tile + lr;
+            const v8bf b = __builtin_bit_cast(
+                v8bf, *reinterpret_cast<const uint4*>(el->brb + row * 128 + (((kb >> 3) ^ (row & 7)) << 4)));
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+              yv[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bra_f.a[s][i], b, yv[i][jj], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < GJ; ++jj) {
+          const int j = j0 + jj;
+          if (j >= TJ) break;
 #pragma unroll
           for (int i = 0; i < TI; ++i)
-            yv[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bra_f.a[s][i], b, yv[i][j], 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              *reinterpret_cast<uint16_t*>(stage + (i * 16 + lq * 4 + r) * (TJ * 32 + 16) + (j * 16 + lr) * 2) =
+                  (uint16_t)f32_to_bf16_bits(yv[i][jj][r]);
         }
       }
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<uint16_t*>(stage + (i * 16 + lq * 4 + r) * (TJ * 32 + 16) + (j * 16 + lr) * 2) =
-                (uint16_t)f32_to_bf16_bits(yv[i][j][r]);
       goto staged_out;
     }
   }
