@@ -148,9 +148,10 @@ __device__ __forceinline__ float epi_acc(T a) {
 
 // `pre`, when given, holds the scales already loaded (load_epi_scales);
 // `el`, when given, the LDS-staged scales and branch rows of the tile.
-// GROUPS: the grouped branch pass below (off where its registers cost the
-// kernel's main loop more than it saves).
-template <int KIND /*0 int4, 1 int8, 2 float, 3 int8 x int4, 4 fp8*/, bool GROUPS = true, typename AccT, int TI,
+// GROUPS: the most tiles per group of the grouped branch pass below (0: no
+// grouped pass, where its registers cost the kernel's main loop more than
+// it saves).
+template <int KIND /*0 int4, 1 int8, 2 float, 3 int8 x int4, 4 fp8*/, int GROUPS = 8, typename AccT, int TI,
           int TJ>
 __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmArgs& g, int m_base, int n_base,
                                                int lane, uint8_t* stage = nullptr,
@@ -206,7 +207,7 @@ __device__ __forceinline__ void epilogue_tiles(AccT (&acc)[TI][TJ], const GemmAr
   // of waiting on each other; each tile takes the same products in the
   // same order as in the loop below.
   if constexpr (GROUPS) {
-    constexpr int GJ = (8 / TI) < 1 ? 1 : (8 / TI);   // column blocks per group
+    constexpr int GJ = (GROUPS / TI) < 1 ? 1 : (GROUPS / TI);   // column blocks per group
     if (br_pre && stage != nullptr && g.y_dtype == 1) {
       const int lk = lq * 8;
 #pragma unroll

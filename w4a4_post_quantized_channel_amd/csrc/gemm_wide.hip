@@ -939,7 +939,7 @@ __global__ void __launch_bounds__(64 * kCbNW) __attribute__((amdgpu_waves_per_eu
   __syncthreads();
   const EpiLds el{nullptr, nullptr, br_lds ? bra : nullptr, brb, m0, n0};
   static_assert(kCbEPI <= kCbBR_OFF, "epilogue staging fits");
-  epilogue_tiles<2, false>(acc, g, m0 + wm0, n0 + wn0, lane, smem + wave * epilogue_stage_bytes<TI, TJ>(),
+  epilogue_tiles<2, 0>(acc, g, m0 + wm0, n0 + wn0, lane, smem + wave * epilogue_stage_bytes<TI, TJ>(),
                     static_cast<const EpiScales<TI, TJ>*>(nullptr), &el);
 }
 
